@@ -1,0 +1,400 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix:
+the pages' worked top-k example, closed forms, library routines and brute
+force on tiny inputs.  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+from scipy.special import ndtr
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
+
+
+# ---------------------------------------------------------------- top-k + renorm
+
+def test_worked_example_exact():
+    g = _golden("worked_example_topk.json")
+    idx, w = O.topk_renorm(np.array([g["scores"]]), g["k"])
+    assert idx[0].tolist() == g["indices"]
+    np.testing.assert_allclose(w[0], g["weights"], rtol=0, atol=1e-15)
+
+
+def test_worked_example_via_router_softmax():
+    # Logits ln(p) reproduce the example's scores through the softmax gate.
+    g = _golden("worked_example_topk.json")
+    logits = np.log(np.array([g["scores"]]))
+    p = O.softmax(logits)
+    np.testing.assert_allclose(p[0], g["scores"], rtol=1e-14)
+    idx, w = O.topk_renorm(p, g["k"])
+    assert idx[0].tolist() == g["indices"]
+    np.testing.assert_allclose(w[0], g["weights"], rtol=1e-12)
+
+
+def test_topk_ties_go_to_lower_index():
+    idx, w = O.topk_renorm(np.array([[0.25, 0.25, 0.25, 0.25]]), 2)
+    assert idx[0].tolist() == [0, 1]
+    np.testing.assert_allclose(w[0], [0.5, 0.5])
+    idx, _ = O.topk_renorm(np.array([[0.1, 0.3, 0.3, 0.3]]), 2)
+    assert idx[0].tolist() == [1, 2]
+    # the worked example's tie (0.1 at experts 0 and 3) decides the third slot
+    idx, _ = O.topk_renorm(np.array([[0.1, 0.5, 0.3, 0.1]]), 3)
+    assert idx[0].tolist() == [1, 2, 0]
+    # many experts in few tie groups: within a group, ascending index
+    s = np.repeat(np.array([0.2, 0.5, 0.1, 0.5, 0.2]), 13)[None, :]
+    s = np.concatenate([s, s[:, ::-1]])
+    idx, _ = O.topk_renorm(s, 30)
+    n = s.shape[1]
+    for row in range(2):
+        order = sorted(range(n), key=lambda e: (-s[row, e], e))
+        assert idx[row].tolist() == order[:30]
+
+
+def test_topk_descending_slots_and_weights_sum_to_one():
+    rng = np.random.default_rng(7)
+    s = rng.random((200, 9))
+    for k in (1, 2, 3, 9):
+        idx, w = O.topk_renorm(s, k)
+        sel = np.take_along_axis(s, idx.astype(np.int64), axis=1)
+        assert np.all(np.diff(sel, axis=1) <= 0)
+        # every unselected score is below the k-th selected one
+        mask = np.ones_like(s, dtype=bool)
+        np.put_along_axis(mask, idx.astype(np.int64), False, axis=1)
+        other = np.where(mask, s, -np.inf).max(axis=1)
+        assert np.all(other <= sel[:, -1])
+        np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+        if k == 1:
+            assert np.all(w == 1.0)
+    # agrees with torch.topk where no ties exist
+    tv, ti = torch.topk(torch.from_numpy(s), 3, dim=1)
+    idx, _ = O.topk_renorm(s, 3)
+    assert np.array_equal(idx, ti.numpy())
+
+
+def test_selection_gap():
+    gap = O.selection_gap(np.array([[0.1, 0.5, 0.3, 0.1], [0.4, 0.4, 0.1, 0.1]]), 2)
+    np.testing.assert_allclose(gap, [0.2, 0.3])
+    assert O.selection_gap(np.array([[0.5, 0.5]]), 2)[0] == np.inf
+
+
+# ---------------------------------------------------------------- gates
+
+def test_softmax_closed_form():
+    p = O.softmax(np.log(np.array([[1.0, 2.0, 3.0, 4.0]])))
+    np.testing.assert_allclose(p[0], [0.1, 0.2, 0.3, 0.4], rtol=1e-14)
+    # shift invariance and large logits (max subtraction keeps it finite)
+    p2 = O.softmax(np.log(np.array([[1.0, 2.0, 3.0, 4.0]])) + 1000.0)
+    np.testing.assert_allclose(p2, p, rtol=1e-12)
+    rng = np.random.default_rng(1)
+    z = rng.normal(size=(50, 7)) * 3
+    np.testing.assert_allclose(O.softmax(z), torch.softmax(torch.from_numpy(z), 1).numpy(),
+                               rtol=1e-13)
+
+
+def test_sigmoid_normalized_closed_form():
+    # sigma(0) = 1/2, sigma(ln 3) = 3/4 -> normalized (0.4, 0.6)
+    p = O.sigmoid_normalized(np.array([[0.0, math.log(3.0)]]))
+    np.testing.assert_allclose(p[0], [0.4, 0.6], rtol=1e-14)
+    rng = np.random.default_rng(2)
+    z = rng.normal(size=(40, 6)) * 2
+    p = O.sigmoid_normalized(z)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=1e-14)
+    sig = torch.sigmoid(torch.from_numpy(z)).numpy()
+    np.testing.assert_allclose(p, sig / sig.sum(axis=1, keepdims=True), rtol=1e-13)
+
+
+def test_sigmoid_renorm_equals_selected_sigmoid_share():
+    # Renormalizing the globally normalized scores over the selected experts
+    # gives sigma_i / sum of the selected sigmas: logits (2, 1, 0, -1), k = 2.
+    z = np.array([[2.0, 1.0, 0.0, -1.0]])
+    idx, w = O.topk_renorm(O.sigmoid_normalized(z), 2)
+    s0, s1 = 1 / (1 + math.exp(-2.0)), 1 / (1 + math.exp(-1.0))
+    assert idx[0].tolist() == [0, 1]
+    np.testing.assert_allclose(w[0], [s0 / (s0 + s1), s1 / (s0 + s1)], rtol=1e-14)
+
+
+def test_router_logits_is_nn_linear():
+    rng = np.random.default_rng(3)
+    x, W, b = rng.normal(size=(11, 6)), rng.normal(size=(4, 6)), rng.normal(size=4)
+    ref = F.linear(torch.from_numpy(x), torch.from_numpy(W), torch.from_numpy(b)).numpy()
+    np.testing.assert_allclose(O.router_logits(x, W, b), ref, rtol=1e-13)
+    ref0 = F.linear(torch.from_numpy(x), torch.from_numpy(W)).numpy()
+    np.testing.assert_allclose(O.router_logits(x, W), ref0, rtol=1e-13)
+
+
+# ---------------------------------------------------------------- activations / FFN
+
+def test_gelu_is_exact_erf_form():
+    assert O.gelu(np.array([0.0]))[0] == 0.0
+    # gelu(z) = z * Phi(z); Phi(1) from the normal CDF
+    np.testing.assert_allclose(O.gelu(np.array([1.0, -1.0, 2.5])),
+                               np.array([1.0, -1.0, 2.5]) * ndtr([1.0, -1.0, 2.5]), rtol=1e-14)
+    z = np.linspace(-6, 6, 241)
+    ref = F.gelu(torch.from_numpy(z), approximate="none").numpy()
+    np.testing.assert_allclose(O.gelu(z), ref, rtol=1e-12, atol=1e-15)
+    tanh_form = F.gelu(torch.from_numpy(z), approximate="tanh").numpy()
+    assert np.abs(O.gelu(z) - tanh_form).max() > 1e-4
+
+
+def test_silu_values():
+    np.testing.assert_allclose(O.silu(np.array([0.0, 1.0])), [0.0, 1.0 / (1.0 + math.exp(-1.0))],
+                               rtol=1e-15)
+    z = np.linspace(-8, 8, 161)
+    np.testing.assert_allclose(O.silu(z), F.silu(torch.from_numpy(z)).numpy(), rtol=1e-13,
+                               atol=1e-16)
+
+
+def _torch_ffn(x, w_up, b_up, w_down, b_down, act):
+    t = lambda a: None if a is None else torch.from_numpy(a)
+    z = F.linear(t(x), t(w_up), t(b_up))
+    if act == "relu":
+        h = F.relu(z)
+    elif act == "gelu":
+        h = F.gelu(z)
+    else:
+        f = w_up.shape[0] // 2
+        h = F.silu(z[:, :f]) * z[:, f:]
+    return F.linear(h, t(w_down), t(b_down)).numpy()
+
+
+@pytest.mark.parametrize("act", ["relu", "gelu", "swiglu"])
+def test_expert_ffn_matches_linear_layers(act):
+    rng = np.random.default_rng(4)
+    d, f, m = 12, 20, 9
+    F1 = 2 * f if act == "swiglu" else f
+    x = rng.normal(size=(m, d))
+    wu, wd = rng.normal(size=(F1, d)) * 0.3, rng.normal(size=(d, f)) * 0.3
+    bu, bd = (None, None) if act == "swiglu" else (rng.normal(size=F1), rng.normal(size=d))
+    np.testing.assert_allclose(O.expert_ffn(x, wu, bu, wd, bd, act),
+                               _torch_ffn(x, wu, bu, wd, bd, act), rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- dispatch
+
+def _random_routing(rng, T, k, E, p=None):
+    idx = np.empty((T, k), dtype=np.int32)
+    for t in range(T):
+        idx[t] = rng.choice(E, size=k, replace=False, p=p)
+    return idx
+
+
+def _bruteforce_dispatch(idx, E, cap):
+    T, k = idx.shape
+    flat = idx.reshape(-1)
+    counts = np.array([np.count_nonzero(flat == e) for e in range(E)])
+    kept = counts if cap is None else np.array([min(c, cap) for c in counts])
+    rows, dropped = [], []
+    for e in range(E):
+        lst = np.nonzero(flat == e)[0]
+        rows += list(lst[: kept[e]])
+        dropped += list(lst[kept[e]:])
+    return counts, kept, np.array(rows + dropped)
+
+
+@pytest.mark.parametrize("T,k,E,cap", [(1, 1, 1, None), (37, 2, 5, None), (37, 2, 5, 9),
+                                       (64, 3, 8, 1), (50, 4, 4, 0), (200, 6, 64, 20)])
+def test_dispatch_bruteforce_and_invariants(T, k, E, cap):
+    rng = np.random.default_rng(T * 131 + E)
+    skew = np.arange(E, 0, -1, dtype=np.float64)
+    idx = _random_routing(rng, T, k, E, skew / skew.sum())
+    dsp = O.dispatch(idx, E, cap)
+    counts, kept, perm = _bruteforce_dispatch(idx, E, cap)
+    assert np.array_equal(dsp["counts"], counts)
+    assert np.array_equal(dsp["kept"], kept)
+    assert dsp["counts"].sum() == T * k
+    assert np.array_equal(dsp["offsets"], np.concatenate([[0], np.cumsum(kept)]))
+    assert np.array_equal(dsp["sorted_assign"], perm)
+    assert sorted(dsp["sorted_assign"].tolist()) == list(range(T * k))
+    nk = dsp["offsets"][-1]
+    assert np.array_equal(dsp["assign_row"][dsp["sorted_assign"][:nk]], np.arange(nk))
+    assert np.all(dsp["assign_row"][dsp["sorted_assign"][nk:]] == -1)
+    assert np.array_equal(dsp["drop_mask"], (dsp["assign_row"] < 0).astype(np.uint8))
+    # rows within each expert segment are in ascending token order
+    for e in range(E):
+        seg = dsp["sorted_assign"][dsp["offsets"][e]:dsp["offsets"][e + 1]]
+        assert np.all(np.diff(seg // k) > 0)
+        assert np.all(idx.reshape(-1)[seg] == e)
+
+
+def test_capacity_values():
+    assert O.capacity(4096, 2, 8, 1.25) == 1280
+    assert O.capacity(8192, 6, 64, 1.25) == 960
+    # the page's literal (tokens / experts) x CF for top-1
+    assert O.capacity(4096, 1, 8, 1.25) == 640
+    assert O.capacity(8192, 1, 64, 1.25) == 160
+    assert O.capacity(10, 1, 3, 1.0) == 4          # rounds up
+    assert O.capacity(10, 1, 3, None) is None
+
+
+# ---------------------------------------------------------------- aux statistics
+
+def test_aux_uniform_probs_gives_exactly_one():
+    rng = np.random.default_rng(5)
+    x = rng.normal(size=(64, 8))
+    for E, k in ((4, 1), (8, 2), (6, 3)):
+        p = O.softmax(O.router_logits(x, np.zeros((E, 8)), np.zeros(E)))
+        idx, _ = O.topk_renorm(p, k)
+        # ties send every token to experts 0..k-1, yet P is uniform
+        assert np.all(idx == np.arange(k))
+        f, P, L = O.aux_stats(idx, p, E)
+        assert abs(L - 1.0) < 1e-14
+        g = _golden("page_numbers.json")["uniform_aux"]["value"]
+        assert abs(L - g) < 1e-14
+
+
+def test_aux_uniform_assignment_gives_one_and_collapse_gives_E_P():
+    rng = np.random.default_rng(6)
+    E, k, T = 8, 2, 64
+    p = rng.dirichlet(np.ones(E), size=T)
+    idx = np.array([[(2 * t) % E, (2 * t + 1) % E] for t in range(T)], dtype=np.int32)
+    f, P, L = O.aux_stats(idx, p, E)
+    np.testing.assert_allclose(f, 1.0 / E)
+    assert abs(L - 1.0) < 1e-14
+    assert abs(f.sum() - 1.0) < 1e-15 and abs(P.sum() - 1.0) < 1e-14
+    # collapse onto expert 3 with top-1: L = E * P_3
+    idx1 = np.full((T, 1), 3, dtype=np.int32)
+    f, P, L = O.aux_stats(idx1, p, E)
+    assert abs(L - E * P[3]) < 1e-14
+    # a single expert
+    f, P, L = O.aux_stats(np.zeros((T, 1), dtype=np.int32), np.ones((T, 1)), 1)
+    assert L == 1.0
+
+
+# ---------------------------------------------------------------- whole forward
+
+def _tiny_problem(rng, T, d, f, E, S, act, bias, router_bias=True):
+    F1 = 2 * f if act == "swiglu" else f
+    return dict(
+        x=rng.normal(size=(T, d)),
+        w_router=rng.normal(size=(E, d)) * 0.7,
+        b_router=rng.normal(size=E) * 0.1 if router_bias else None,
+        w_up=rng.normal(size=(E + S, F1, d)) * 0.3,
+        b_up=rng.normal(size=(E + S, F1)) * 0.1 if bias else None,
+        w_down=rng.normal(size=(E + S, d, f)) * 0.3,
+        b_down=rng.normal(size=(E + S, d)) * 0.1 if bias else None)
+
+
+def _dense_masked(P, T, E, S, k, gating, act, cap):
+    """Every expert on every token, multiplied by a dense (token, expert)
+    weight that is w for kept selections and 0 otherwise, plus the shared
+    experts unmasked (the dense-masked MoE layer of the yunthe page).
+    Routing uses torch.topk on tie-free scores; drops use a direct recount."""
+    logits = F.linear(torch.from_numpy(P["x"]), torch.from_numpy(P["w_router"]),
+                      None if P["b_router"] is None else torch.from_numpy(P["b_router"]))
+    if gating == "softmax":
+        scores = torch.softmax(logits, dim=1)
+    else:
+        sg = torch.sigmoid(logits)
+        scores = sg / sg.sum(dim=1, keepdim=True)
+    top, ti = torch.topk(scores, k, dim=1)
+    tw = top / top.sum(dim=1, keepdim=True)
+    mask = torch.zeros(T, E, dtype=torch.float64)
+    seen = [0] * E
+    for t in range(T):
+        for s in range(k):
+            e = int(ti[t, s])
+            if cap is None or seen[e] < cap:
+                mask[t, e] = tw[t, s]
+            seen[e] += 1
+    y = torch.zeros(T, P["x"].shape[1], dtype=torch.float64)
+    bu = lambda q: None if P["b_up"] is None else P["b_up"][q]
+    bd = lambda q: None if P["b_down"] is None else P["b_down"][q]
+    for e in range(E):
+        out = _torch_ffn(P["x"], P["w_up"][e], bu(e), P["w_down"][e], bd(e), act)
+        y += mask[:, e:e + 1] * torch.from_numpy(out)
+    for q in range(E, E + S):
+        y += torch.from_numpy(_torch_ffn(P["x"], P["w_up"][q], bu(q), P["w_down"][q], bd(q), act))
+    return y.numpy(), scores.numpy(), ti.numpy()
+
+
+@pytest.mark.parametrize("T,d,f,E,S,k,gating,act,bias,cap", [
+    (23, 8, 12, 5, 0, 2, "softmax", "gelu", True, None),
+    (23, 8, 12, 5, 0, 2, "softmax", "relu", True, 7),
+    (30, 8, 6, 6, 2, 3, "sigmoid_norm", "swiglu", False, 12),
+    (17, 4, 8, 4, 1, 1, "softmax", "swiglu", False, 3),
+])
+def test_forward_equals_dense_masked_bruteforce(T, d, f, E, S, k, gating, act, bias, cap):
+    rng = np.random.default_rng(T + 100 * E + k)
+    P = _tiny_problem(rng, T, d, f, E, S, act, bias)
+    out = O.forward(**P, top_k=k, num_shared=S, gating=gating, activation=act, cap=cap)
+    y_ref, scores, ti = _dense_masked(P, T, E, S, k, gating, act, cap)
+    assert np.all(out["gap"] > 1e-6)          # tie-free, so torch.topk is unique
+    np.testing.assert_allclose(out["probs"], scores, rtol=1e-13)
+    assert np.array_equal(out["idx"], ti)
+    np.testing.assert_allclose(out["y"], y_ref, rtol=1e-11, atol=1e-12)
+    if cap is not None:
+        assert out["drop_mask"].sum() > 0 or k * T <= cap * E
+
+
+def test_single_expert_top1_is_the_dense_ffn():
+    # E = 1, k = 1: the layer reduces to one FFN (kamacoder section 一 FeedForward)
+    rng = np.random.default_rng(8)
+    P = _tiny_problem(rng, 19, 8, 16, 1, 0, "relu", True)
+    out = O.forward(**P, top_k=1, num_shared=0, gating="softmax", activation="relu")
+    ref = _torch_ffn(P["x"], P["w_up"][0], P["b_up"][0], P["w_down"][0], P["b_down"][0], "relu")
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-14)
+    assert out["l_aux"] == 1.0
+
+
+def test_all_experts_selected_is_probability_mixture():
+    # k = E with softmax and no capacity: y = sum_e p_e FFN_e(x)
+    rng = np.random.default_rng(9)
+    E = 4
+    P = _tiny_problem(rng, 15, 6, 10, E, 0, "gelu", True)
+    out = O.forward(**P, top_k=E, num_shared=0, gating="softmax", activation="gelu")
+    p = out["probs"]
+    ref = sum(p[:, e:e + 1] * _torch_ffn(P["x"], P["w_up"][e], P["b_up"][e], P["w_down"][e],
+                                         P["b_down"][e], "gelu") for e in range(E))
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-11, atol=1e-13)
+
+
+def test_token_subset_and_combine_rows_agree_with_full_forward():
+    rng = np.random.default_rng(10)
+    T, E, S, k = 40, 6, 2, 2
+    P = _tiny_problem(rng, T, 8, 12, E, S, "swiglu", False)
+    full = O.forward(**P, top_k=k, num_shared=S, gating="softmax", activation="swiglu", cap=12)
+    sub = [3, 17, 39]
+    part = O.forward(**P, top_k=k, num_shared=S, gating="softmax", activation="swiglu", cap=12,
+                     token_subset=sub)
+    np.testing.assert_allclose(part["y"], full["y"][sub], rtol=1e-13, atol=1e-15)
+    # combine_rows from per-row expert outputs
+    nk = int(full["offsets"][-1])
+    y_rows = np.zeros((nk + S * T, 8))
+    for r in range(nk):
+        a = int(full["sorted_assign"][r])
+        e = int(full["idx"].reshape(-1)[a])
+        y_rows[r] = O.expert_ffn(P["x"][a // k][None], P["w_up"][e], None, P["w_down"][e], None,
+                                 "swiglu")[0]
+    for q in range(S):
+        y_rows[nk + q * T: nk + (q + 1) * T] = O.expert_ffn(P["x"], P["w_up"][E + q], None,
+                                                             P["w_down"][E + q], None, "swiglu")
+    y = O.combine_rows(y_rows, full["w"], full["assign_row"], nk, S)
+    np.testing.assert_allclose(y, full["y"], rtol=1e-12, atol=1e-14)
+
+
+def test_page_parameter_counts():
+    g = _golden("page_numbers.json")
+    d, f = g["dense_ffn_params"]["d_model"], g["dense_ffn_params"]["ffn_dim"]
+    from synth import RUNS
+    r = RUNS["gpt2"]
+    assert (r.d_model, r.d_ff) == (d, f)
+    per_expert = r.up_rows * r.d_model + r.d_model * r.d_ff      # weight matrices
+    assert abs(per_expert / g["dense_ffn_params"]["approx_params"] - 1) < g["dense_ffn_params"]["rel_tol"]
+    four = g["four_expert_params"]
+    assert abs(four["num_experts"] * per_expert / four["approx_params"] - 1) < four["rel_tol"]
+    # k of E experts: the rows the experts evaluate are k/E of the dense all-expert work
+    sf = g["sparse_fraction"]
+    rng = np.random.default_rng(11)
+    idx = _random_routing(rng, 32, sf["top_k"], sf["num_experts"])
+    dsp = O.dispatch(idx, sf["num_experts"], None)
+    assert dsp["offsets"][-1] / (32 * sf["num_experts"]) == sf["fraction"]
