@@ -1,0 +1,277 @@
+"""Benchmark of the MoE-FFN forward on one MI355X.
+
+One step = one moe_ffn_forward call (router + top-k, dispatch, expert up and
+down projections, combine, aux statistics) over one batch of seeded
+synthetic input already resident in HBM.  Prints ONE JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+
+value = tokens per second of the whole step.  roofline = the up-projection
+kernel (the dominant one), timed with HIP events on the launch stream in a
+second pass of K steps made of the per-stage entry points.  cpu_baseline =
+the float64 oracle on the host cores (never tuned), on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+METRIC = "MoE-FFN fwd tokens/s + TFLOP/s (% bf16 MFMA peak / % HBM BW), 1 MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default=None, help="workload name (default: gpt2)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (for counter scaling)")
+    return ap.parse_args()
+
+
+def expert_flops(run, kept_rows):
+    F1 = 2 * run.d_ff if run.activation == "swiglu" else run.d_ff
+    up = 2.0 * kept_rows * run.d_model * F1
+    down = 2.0 * kept_rows * run.d_ff * run.d_model
+    return up, down
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {a.gpus}); the layer runs on a "
+              f"single MI355X with all experts resident, so there is no multi-GPU step.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from mixture_experts_sparse_gemv_amd import moe as M
+    from synth import HEADLINE_RUN, RUNS, make_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+
+    if a.copy_calibration_mb:
+        n = a.copy_calibration_mb * (1 << 20) // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": n * 4}))
+        return
+
+    name = a.config or HEADLINE_RUN
+    run = RUNS[name]
+    inp = make_inputs(run)
+    g = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    del inp
+    cap = M.moe_capacity(run.T, run.top_k, run.num_experts, run.capacity_factor or 0.0)
+    p = M.make_problem(T=run.T, d_model=run.d_model, d_ff=run.d_ff, num_experts=run.num_experts,
+                       top_k=run.top_k, num_shared=run.num_shared, capacity=cap,
+                       dtype=run.dtype, gating=run.gating, activation=run.activation,
+                       router_bias=run.router_bias != "none", expert_bias=run.expert_bias)
+    w = M.make_weights(g["w_router"], g["b_router"], g["w_up"], g["b_up"], g["w_down"],
+                       g["b_down"])
+    ws = M.workspace(p, dev)
+    y = torch.empty(run.T * run.d_model, dtype=torch.float32, device=dev)
+    E, k, T = run.num_experts, run.top_k, run.T
+    i32 = dict(dtype=torch.int32, device=dev)
+    r = dict(topk_idx=torch.empty(T * k, **i32), topk_w=torch.empty(T * k, dtype=torch.float32,
+                                                                      device=dev),
+             counts=torch.empty(E, **i32), kept=torch.empty(E, **i32),
+             offsets=torch.empty(E + 1, **i32), sorted_assign=torch.empty(T * k, **i32),
+             assign_row=torch.empty(T * k, **i32),
+             drop_mask=torch.empty(T * k, dtype=torch.uint8, device=dev),
+             f=torch.empty(E, device=dev), P=torch.empty(E, device=dev),
+             l_aux=torch.empty(1, device=dev))
+    print(f"bench: {name} T={T} d={run.d_model} f={run.d_ff} E={E} k={k} S={run.num_shared} "
+          f"cap={cap} warmup={a.warmup} steps={a.steps}", file=sys.stderr, flush=True)
+
+    # ---- headline: K whole forward calls
+    for _ in range(a.warmup):
+        M.moe_ffn_forward(p, w, g["x"], y, ws, routing=r)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        M.moe_ffn_forward(p, w, g["x"], y, ws, routing=r)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / a.steps
+
+    kept = int(r["offsets"][E].item())
+    rows = kept + run.num_shared * T
+    counts = r["counts"].cpu().numpy()
+    touched = int(np.count_nonzero(r["kept"].cpu().numpy())) + run.num_shared
+    up_fl, down_fl = expert_flops(run, rows)
+    router_fl = 2.0 * T * run.d_model * E
+    step_flops = up_fl + down_fl + router_fl
+    F1 = 2 * run.d_ff if run.activation == "swiglu" else run.d_ff
+    esz = 4 if run.dtype == "f32" else 2
+    w_bytes_touched = touched * (F1 * run.d_model + run.d_model * run.d_ff) * esz
+    step_bytes = (T * run.d_model * esz + E * run.d_model * esz + w_bytes_touched +
+                  T * run.d_model * 4)
+    decode = run.dtype == "bf16" and T <= 16
+
+    # ---- per-stage pass: the same steps through the stage entry points, with
+    # events around each stage on the launch stream
+    stream = torch.cuda.current_stream()
+    names = ["router_topk", "dispatch", "expert_up", "expert_down", "combine"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+          for _ in range(a.steps)]
+    h = torch.empty(M.max_rows(p) * run.d_ff, dtype=M.h_dtype(p), device=dev)
+    y_exp = torch.empty(M.max_rows(p) * run.d_model, dtype=torch.float32, device=dev)
+    part = torch.empty(E, dtype=torch.float32, device=dev)
+
+    def staged(evs=None):
+        rec = (lambda i: evs[i].record(stream)) if evs else (lambda i: None)
+        rec(0)
+        M.moe_router_topk(p, g["x"], w, r["topk_idx"], r["topk_w"], None, part, ws=ws)
+        rec(1)
+        M.moe_dispatch(p, r["topk_idx"], r["counts"], r["kept"], r["offsets"],
+                       r["sorted_assign"], r["assign_row"], r["drop_mask"])
+        rec(2)
+        M.moe_expert_up(p, g["x"], w, r["offsets"], r["sorted_assign"], h)
+        rec(3)
+        M.moe_expert_down(p, w, r["offsets"], h, y_exp, ws)
+        rec(4)
+        M.moe_combine(p, r["topk_w"], r["assign_row"], r["offsets"], y_exp, y)
+        rec(5)
+
+    for _ in range(a.warmup):
+        staged()
+    torch.cuda.synchronize()
+    for i in range(a.steps):
+        staged(ev[i])
+    torch.cuda.synchronize()
+    stage_ms = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(a.steps)]))
+                for j, n in enumerate(names)}
+    up_ms = stage_ms["expert_up"]
+
+    if decode:
+        up_bytes = (touched * F1 * run.d_model * esz + T * run.d_model * esz +
+                    rows * run.d_ff * 2)
+        achieved = up_bytes / (up_ms * 1e-3) / 1e9
+        roof = {"kernel": "decode_up_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                "traffic": traffic_for("decode_up_kernel", name, up_bytes)}
+    else:
+        achieved = up_fl / (up_ms * 1e-3) / 1e12
+        roof = {"kernel": "grouped_gemm_kernel (up)", "bound": "mfma",
+                "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_for("grouped_gemm_kernel", name, None)}
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        cpu = cpu_baseline(run, cap, a.cpu_seconds)
+
+    step_tflops = step_flops / step_s / 1e12
+    step_gbps = step_bytes / step_s / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(T / step_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if run.dtype == "f32" else "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the workload, random weights)",
+        "config": {"workload": run.description, "name": name, "T": T, "d_model": run.d_model,
+                   "d_ff": run.d_ff, "num_experts": E, "top_k": k, "num_shared": run.num_shared,
+                   "capacity": cap, "kept_rows": rows, "touched_experts": touched,
+                   "parallelism": "single GPU"},
+        "step_tflops": round(step_tflops, 2),
+        "step_pct_bf16_peak": round(100 * step_tflops / PEAK_BF16_TFLOPS, 2),
+        "step_gbps": round(step_gbps, 1),
+        "step_pct_hbm": round(100 * step_gbps / PEAK_HBM_GBPS, 2),
+        "stage_ms": {n: round(v, 5) for n, v in stage_ms.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+def traffic_for(kernel, workload, default):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/traffic.json),
+    used only while the kernel's source is unchanged since the measurement."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as fh:
+            db = json.load(fh)
+        ent = db.get(f"{kernel}:{workload}")
+        if not ent:
+            return None
+        src = os.path.join(ROOT, "mixture_experts_sparse_gemv_amd", "csrc", ent["source"])
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if digest != ent["source_sha256"]:
+            return None
+        return ent["bytes_per_launch"]
+    except Exception:
+        return None
+
+
+def cpu_baseline(run, cap, seconds):
+    """The oracle's whole forward on the same workload, repeated until about
+    `seconds` of host time have passed; tokens/s over the repetitions."""
+    import numpy as np
+
+    import oracle as O
+    from synth import make_inputs, to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    inp = make_inputs(run)
+    f64 = lambda t: None if t is None else _Lazy(t)
+    x, wr = to_f64(inp["x"]), to_f64(inp["w_router"])
+    br = None if inp["b_router"] is None else to_f64(inp["b_router"])
+    ocap = O.capacity(run.T, run.top_k, run.num_experts, run.capacity_factor)
+    # Bounded sample: at most 1024 tokens' expert FFNs per repetition (routing,
+    # dispatch and aux statistics always cover the whole batch).
+    sub = None if run.T <= 1024 else np.arange(1024)
+    n_tok = run.T if sub is None else len(sub)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.forward(x, wr, br, f64(inp["w_up"]), f64(inp["b_up"]), f64(inp["w_down"]),
+                  f64(inp["b_down"]), top_k=run.top_k, num_shared=run.num_shared,
+                  gating=run.gating, activation=run.activation, cap=ocap, token_subset=sub)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    sample = (f"oracle forward over the whole {run.T}-token batch (routing, dispatch, aux) "
+              f"with expert FFNs for {n_tok} tokens, x{reps} repetitions in {el:.1f} s")
+    return {"value": round(n_tok * reps / el, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "sample": sample}
+
+
+class _Lazy:
+    def __init__(self, t):
+        self.t = t
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, i):
+        return self.t[i].to(__import__("torch").float64).numpy()
+
+
+if __name__ == "__main__":
+    main()

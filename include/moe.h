@@ -1,0 +1,223 @@
+/*
+ * libmoe_mi355x — forward pass of one Mixture-of-Experts FFN layer on one
+ * AMD MI355X (gfx950), as a C ABI.
+ *
+ * The layer (pages cited by title and section):
+ *   router      logits = Wr x + br, one output per expert
+ *               ("MoE混合专家模型：Transformer稀疏前馈网络原理与PyTorch实现", 2.1;
+ *                "手撕一个极简 MoE-FFN", 三)
+ *   gate        softmax over experts, or per-expert sigmoid normalized over all
+ *               experts ("MoE架构解析", 四 技术飞跃③)
+ *   top-k       the k highest-scoring experts per token, their scores
+ *               renormalized to sum to 1 (0539edu page 2.1; kamacoder 三 and its
+ *               worked example)
+ *   dispatch    tokens grouped per expert, at most C per expert; the rest are
+ *               dropped and contribute nothing ("MoE架构解析", 三 关键技术①)
+ *   experts     Linear -> ReLU / GELU -> Linear with biases, or SwiGLU
+ *               (kamacoder 四; 0539edu 4.1; learn-minimind guide 二), plus
+ *               always-active shared experts ("MoE架构解析", 四 技术飞跃②)
+ *   combine     y = sum over the kept slots of w * Expert(x) (+ shared)
+ *               (0539edu 1.3; kamacoder 五)
+ *   aux stats   f_e, P_e, L_aux = E * sum f_e P_e (0539edu 2.3; kamacoder 七)
+ *
+ * Conventions for every entry point
+ *   - Array arguments are DEVICE pointers owned by the caller; moe_problem,
+ *     moe_weights and moe_routing are HOST structs holding device pointers.
+ *   - Work is enqueued on `stream` (NULL = the default stream) and nothing
+ *     synchronizes with the host; buffers must stay alive until the stream
+ *     has passed the work.  No entry point allocates or frees memory; scratch
+ *     space is the caller's workspace of moe_workspace_size() bytes (256-byte
+ *     aligned).  No pointer is kept after a call returns.
+ *   - All validation happens before anything is launched: on an error return
+ *     nothing was launched and no output was written.  MOE_ERR_HIP means a
+ *     launch failed (moe_last_hip_error() gives the hipError_t of the calling
+ *     thread); asynchronous faults surface at the caller's next sync.
+ *   - Identical inputs give bit-identical outputs (no floating-point atomics,
+ *     fixed reduction orders, stable dispatch).
+ *   - Layouts are row-major.  Weights use the nn.Linear [out, in] layout.
+ *     x and all weights and biases share `dtype`; y, topk_w, probs and the
+ *     statistics are float32; indices are int32.
+ *   - Shared experts are experts E .. E+S-1 of the weight arrays.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* a size, enum, flag or required pointer is invalid     */
+  MOE_ERR_UNSUPPORTED = 2,   /* valid, but outside this library's limits (see below)  */
+  MOE_ERR_WORKSPACE = 3,     /* workspace NULL or smaller than moe_workspace_size()   */
+  MOE_ERR_HIP = 4            /* a HIP launch failed                                   */
+};
+
+enum { MOE_F32 = 0, MOE_BF16 = 1 };                      /* dtype of x, weights, biases */
+enum { MOE_SOFTMAX = 0, MOE_SIGMOID_NORM = 1 };          /* gate                        */
+enum { MOE_RELU = 0, MOE_GELU = 1, MOE_SWIGLU = 2 };     /* expert activation           */
+enum { MOE_ROUTER_BIAS = 1, MOE_EXPERT_BIAS = 2 };       /* flags                       */
+
+/*
+ * The problem.  T tokens (the pages' [B, L, d] input flattened to [B*L, d],
+ * 0539edu page 4.1), E routed experts of which each token takes top_k, S
+ * always-on shared experts, per-expert capacity (<= 0: unlimited).
+ *
+ * Limits (MOE_ERR_UNSUPPORTED beyond them): E <= 64, top_k <= 8,
+ * E + S <= 128, T * (top_k + S) < 2^31; for MOE_BF16, d_model and d_ff are
+ * multiples of 64.  GELU is the exact erf form; SwiGLU has no biases.
+ */
+typedef struct moe_problem {
+  int32_t T, d_model, d_ff, num_experts, top_k, num_shared, capacity;
+  int32_t dtype, gating, activation, flags;
+} moe_problem;
+
+/*
+ * Weights (device pointers, `dtype`):
+ *   w_router [E, d]         b_router [E]   (MOE_ROUTER_BIAS, else ignored)
+ *   w_up     [E+S, F1, d]   b_up [E+S, F1] (MOE_EXPERT_BIAS, else ignored)
+ *            F1 = d_ff, or 2*d_ff for SwiGLU: rows 0..d_ff-1 are the gate
+ *            projection, rows d_ff..2*d_ff-1 the up projection
+ *   w_down   [E+S, d, d_ff] b_down [E+S, d] (MOE_EXPERT_BIAS, else ignored)
+ * For MOE_BF16 the down projection multiplies in fp16: each bf16 w_down value
+ * is converted exactly when 2^-14 <= |w| < 65504 (smaller magnitudes are
+ * truncated to fp16 subnormals, larger ones saturate).
+ */
+typedef struct moe_weights {
+  const void *w_router, *b_router;
+  const void *w_up, *b_up;
+  const void *w_down, *b_down;
+} moe_weights;
+
+/*
+ * Optional routing outputs of moe_ffn_forward (host struct; each device
+ * pointer may be NULL, in which case the value lives only in the workspace).
+ * Shapes and meaning as in moe_router_topk, moe_dispatch and moe_aux_stats.
+ */
+typedef struct moe_routing {
+  int32_t *topk_idx;      /* [T, k]  */
+  float *topk_w;          /* [T, k]  */
+  float *probs;           /* [T, E]  */
+  int32_t *counts;        /* [E]     */
+  int32_t *kept;          /* [E]     */
+  int32_t *offsets;       /* [E + 1] */
+  int32_t *sorted_assign; /* [T * k] */
+  int32_t *assign_row;    /* [T * k] */
+  uint8_t *drop_mask;     /* [T * k] */
+  float *f, *P, *l_aux;   /* [E], [E], [1] */
+} moe_routing;
+
+/* Host only.  Capacity ceil(capacity_factor * T * k / E): the page's
+ * (tokens / experts) x CF ("MoE架构解析", 三 关键技术①) with the even share of
+ * the T*k assignments as base (0539edu page 3.2: a multiple of the ideal even
+ * share).  Returns 0 (= unlimited) when capacity_factor <= 0, -1 on invalid
+ * T, k or E. */
+int32_t moe_capacity(int32_t T, int32_t k, int32_t E, float capacity_factor);
+
+/* Host only.  Workspace bytes needed by every entry point for this problem. */
+moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
+
+/*
+ * Router, gate, top-k and renormalization (0539edu page 2.1; kamacoder 三;
+ * "MoE架构解析" 四 技术飞跃③ for the normalized sigmoid).
+ *   x           [T, d]  dtype
+ *   topk_idx    [T, k]  out: experts in descending score, ties to the lower index
+ *   topk_w      [T, k]  out: selected scores / their sum (softmax: probabilities,
+ *                            sigmoid: sigma values; both give the same weights)
+ *   probs       [T, E]  out, nullable: softmax p, or sigma / sum_e sigma
+ *   prob_colsum [E]     out, nullable: sum over tokens of probs (fixed order)
+ */
+moe_status moe_router_topk(const moe_problem* p, const void* x, const moe_weights* w,
+                           int32_t* topk_idx, float* topk_w, float* probs,
+                           float* prob_colsum, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Capacity-limited dispatch ("MoE架构解析", 三 关键技术①): assignments
+ * a = t*k + s grouped by expert in ascending token order; each expert keeps
+ * its first min(count, capacity) and drops the rest.
+ *   topk_idx      [T, k] in   (each row: k distinct experts in [0, E))
+ *   counts        [E]    out  assignments per expert before drops
+ *   kept          [E]    out  min(counts, capacity)
+ *   offsets       [E+1]  out  first row of each expert's kept rows; offsets[E]
+ *                             = kept rows in total (shared expert q's rows then
+ *                             start at offsets[E] + q*T)
+ *   sorted_assign [T*k]  out  row r < offsets[E] holds assignment
+ *                             sorted_assign[r]; the dropped assignments follow,
+ *                             grouped by expert in token order
+ *   assign_row    [T*k]  out  row of each assignment, -1 if dropped
+ *   drop_mask     [T*k]  out  1 if dropped
+ * Results are exact integers (bit-identical to any correct implementation).
+ * Out-of-range ids are clamped into [0, E) (the result is then unspecified).
+ * ws is not used (may be NULL): the scratch of this step lives in LDS.
+ */
+moe_status moe_dispatch(const moe_problem* p, const int32_t* topk_idx, int32_t* counts,
+                        int32_t* kept, int32_t* offsets, int32_t* sorted_assign,
+                        int32_t* assign_row, uint8_t* drop_mask, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/*
+ * Expert FFNs over the dispatched rows (kamacoder 四 and 六: one batch per
+ * expert; shared experts on every token).  Row r < offsets[E] is token
+ * sorted_assign[r] / k through expert e with offsets[e] <= r < offsets[e+1];
+ * row offsets[E] + q*T + t is token t through shared expert q.
+ *   y_exp [T*k + S*T, d] float32 out (only rows < offsets[E] + S*T written)
+ * moe_expert_ffn = moe_expert_up followed by moe_expert_down with h in the
+ * workspace.  h is [T*k + S*T, d_ff], fp16 for MOE_BF16 problems (bit
+ * patterns in uint16) and float32 for MOE_F32.  moe_expert_up uses no
+ * workspace (ws may be NULL); the others need moe_workspace_size() bytes.
+ */
+moe_status moe_expert_ffn(const moe_problem* p, const void* x, const moe_weights* w,
+                          const int32_t* offsets, const int32_t* sorted_assign, float* y_exp,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+moe_status moe_expert_up(const moe_problem* p, const void* x, const moe_weights* w,
+                         const int32_t* offsets, const int32_t* sorted_assign, void* h,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+moe_status moe_expert_down(const moe_problem* p, const moe_weights* w, const int32_t* offsets,
+                           const void* h, float* y_exp, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/*
+ * Gate-weighted combine (0539edu 1.3 and 2.1; kamacoder 五):
+ *   y[t] = sum over s with assign_row[t*k+s] >= 0 of topk_w[t,s] * y_exp[assign_row[t*k+s]]
+ *          + sum over q < S of y_exp[offsets[E] + q*T + t]
+ * A dropped slot adds nothing and the other weights are not renormalized.
+ *   y [T, d] float32 out (every element written)
+ */
+moe_status moe_combine(const moe_problem* p, const float* topk_w, const int32_t* assign_row,
+                       const int32_t* offsets, const float* y_exp, float* y,
+                       hipStream_t stream);
+
+/*
+ * Load-balance statistics (0539edu 2.3; kamacoder 七):
+ *   f[e] = counts[e] / (T * k)   (routing decisions before capacity drops)
+ *   P[e] = prob_colsum[e] / T
+ *   l_aux[0] = E * sum_e f[e] * P[e]   (without the weight alpha)
+ */
+moe_status moe_aux_stats(const moe_problem* p, const float* prob_colsum, const int32_t* counts,
+                         float* f, float* P, float* l_aux, hipStream_t stream);
+
+/*
+ * The whole forward: router + top-k, dispatch, experts, combine, aux stats
+ * (0539edu page 1.3 and 4.1; kamacoder 二).
+ *   x [T, d] dtype in;  y [T, d] float32 out;  out: optional routing outputs.
+ */
+moe_status moe_ffn_forward(const moe_problem* p, const moe_weights* w, const void* x, float* y,
+                           const moe_routing* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_string(moe_status s);
+/* hipError_t of this thread's last MOE_ERR_HIP (0 if none). */
+int32_t moe_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,58 @@
+// Gate-weighted combine (0539edu 1.3 and 2.1; kamacoder 五; shared experts:
+// "MoE架构解析" 四 技术飞跃②):
+//   y[t] = sum over kept slots s of w[t, s] * y_exp[assign_row[t*k+s]]
+//          + sum over shared experts q of y_exp[offsets[E] + q*T + t]
+// One thread per 4 consecutive outputs of a token (16-byte loads and
+// stores); the sum runs in slot order, then shared-expert order, so the
+// result does not depend on scheduling.  Every element of y is written.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+template <int VEC>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ topk_w,
+                                                      const int32_t* __restrict__ assign_row,
+                                                      const int32_t* __restrict__ offsets,
+                                                      const float* __restrict__ y_exp,
+                                                      float* __restrict__ y, int T, int d, int k,
+                                                      int E, int S) {
+  const int dv = d / VEC;
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long long)T * dv) return;
+  const int t = (int)(gid / dv);
+  const int c = (int)(gid % dv) * VEC;
+  typedef float vec_t __attribute__((ext_vector_type(VEC)));
+  vec_t acc = {};
+  for (int s = 0; s < k; ++s) {
+    const int r = assign_row[(long long)t * k + s];
+    if (r >= 0) {
+      const float w = topk_w[(long long)t * k + s];
+      acc += w * *(const vec_t*)(y_exp + (long long)r * d + c);
+    }
+  }
+  if (S > 0) {
+    const long long base = offsets[E];
+    for (int q = 0; q < S; ++q)
+      acc += *(const vec_t*)(y_exp + (base + (long long)q * T + t) * d + c);
+  }
+  *(vec_t*)(y + (long long)t * d + c) = acc;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const Shape& s, const float* topk_w, const int32_t* assign_row,
+                          const int32_t* offsets, const float* y_exp, float* y, hipStream_t st) {
+  if (s.d % 4 == 0) {
+    const long long n = (long long)s.T * (s.d / 4);
+    combine_kernel<4><<<(int)((n + 255) / 256), 256, 0, st>>>(topk_w, assign_row, offsets, y_exp,
+                                                              y, s.T, s.d, s.k, s.E, s.S);
+  } else {
+    const long long n = (long long)s.T * s.d;
+    combine_kernel<1><<<(int)((n + 255) / 256), 256, 0, st>>>(topk_w, assign_row, offsets, y_exp,
+                                                              y, s.T, s.d, s.k, s.E, s.S);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,275 @@
+// Host side of the C ABI: argument validation, workspace layout and the
+// launch sequence of each entry point.  Nothing here synchronizes with the
+// device, reads device memory or allocates.
+#include <math.h>
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static thread_local int32_t g_last_hip_error = 0;
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const Shape& s) {
+  WsLayout w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  const size_t n = (size_t)s.T * s.k;
+  const size_t rows = (size_t)s.max_rows();
+  w.topk_idx = take(n * 4);
+  w.topk_w = take(n * 4);
+  w.prob_part = take((size_t)router_blocks(s) * s.E * 4);
+  w.prob_colsum = take((size_t)s.E * 4);
+  w.counts = take((size_t)s.E * 4);
+  w.kept = take((size_t)s.E * 4);
+  w.offsets = take((size_t)(s.E + 1) * 4);
+  w.sorted_assign = take(n * 4);
+  w.assign_row = take(n * 4);
+  w.drop_mask = take(n);
+  w.f = take((size_t)s.E * 4);
+  w.P = take((size_t)s.E * 4);
+  w.l_aux = take(4);
+  w.h = take(rows * s.f * (s.dtype == MOE_F32 ? 4 : 2));
+  w.y_exp = take(rows * s.d * 4);
+  w.y_part = s.decode() ? take((size_t)kDecodeSplitK * rows * s.d * 4) : o;
+  w.total = o;
+  return w;
+}
+
+static moe_status fail_hip(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip_error = (int32_t)e;
+  return MOE_ERR_HIP;
+}
+
+// Validate the problem; on success fill `s`.
+static moe_status check_problem(const moe_problem* p, Shape& s) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  if (p->T <= 0 || p->d_model <= 0 || p->d_ff <= 0 || p->num_experts <= 0 || p->top_k <= 0 ||
+      p->top_k > p->num_experts || p->num_shared < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (p->dtype != MOE_F32 && p->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (p->gating != MOE_SOFTMAX && p->gating != MOE_SIGMOID_NORM) return MOE_ERR_INVALID_ARG;
+  if (p->activation < MOE_RELU || p->activation > MOE_SWIGLU) return MOE_ERR_INVALID_ARG;
+  if (p->flags & ~(MOE_ROUTER_BIAS | MOE_EXPERT_BIAS)) return MOE_ERR_INVALID_ARG;
+  if (p->num_experts > kMaxExperts || p->top_k > kMaxTopK ||
+      p->num_experts + p->num_shared > kMaxSegments)
+    return MOE_ERR_UNSUPPORTED;
+  const long long rows = (long long)p->T * (p->top_k + p->num_shared);
+  if (rows >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  if ((long long)rows * p->d_ff >= (1LL << 40) || (long long)rows * p->d_model >= (1LL << 40))
+    return MOE_ERR_UNSUPPORTED;
+  if (p->dtype == MOE_BF16 && (p->d_model % 64 != 0 || p->d_ff % 64 != 0))
+    return MOE_ERR_UNSUPPORTED;
+  s.T = p->T;
+  s.d = p->d_model;
+  s.f = p->d_ff;
+  s.E = p->num_experts;
+  s.k = p->top_k;
+  s.S = p->num_shared;
+  s.cap = p->capacity > 0 ? p->capacity : 0;
+  s.dtype = p->dtype;
+  s.gating = p->gating;
+  s.act = p->activation;
+  s.flags = p->flags;
+  return MOE_OK;
+}
+
+static moe_status check_ws(const Shape& s, const void* ws, size_t ws_bytes, WsLayout& L) {
+  L = ws_layout(s);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)ws & 255) != 0) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+static moe_status check_weights(const Shape& s, const moe_weights* w, bool router, bool experts) {
+  if (!w) return MOE_ERR_INVALID_ARG;
+  if (router && (!w->w_router || (s.router_bias() && !w->b_router))) return MOE_ERR_INVALID_ARG;
+  if (experts && (!w->w_up || !w->w_down)) return MOE_ERR_INVALID_ARG;
+  if (experts && s.expert_bias() && (!w->b_up || !w->b_down)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+template <class T>
+static T* at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int32_t moe_capacity(int32_t T, int32_t k, int32_t E, float capacity_factor) {
+  if (T <= 0 || k <= 0 || E <= 0) return -1;
+  if (!(capacity_factor > 0.0f)) return 0;
+  const double c = ceil((double)capacity_factor * (double)T * (double)k / (double)E);
+  return c >= 2147483647.0 ? 2147483647 : (int32_t)c;
+}
+
+moe_status moe_workspace_size(const moe_problem* p, size_t* bytes) {
+  Shape s;
+  moe_status st = check_problem(p, s);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = ws_layout(s).total;
+  return MOE_OK;
+}
+
+moe_status moe_router_topk(const moe_problem* p, const void* x, const moe_weights* w,
+                           int32_t* topk_idx, float* topk_w, float* probs, float* prob_colsum,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  WsLayout L;
+  moe_status st = check_problem(p, s);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights(s, w, true, false)) != MOE_OK) return st;
+  if (!x || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(s, ws, ws_bytes, L)) != MOE_OK) return st;
+  float* part = at<float>(ws, L.prob_part);
+  hipError_t e = launch_router(s, x, w->w_router, w->b_router, topk_idx, topk_w, probs, part, stream);
+  if (e == hipSuccess && prob_colsum) e = launch_colsum(s, part, prob_colsum, stream);
+  return fail_hip(e);
+}
+
+moe_status moe_dispatch(const moe_problem* p, const int32_t* topk_idx, int32_t* counts,
+                        int32_t* kept, int32_t* offsets, int32_t* sorted_assign,
+                        int32_t* assign_row, uint8_t* drop_mask, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  Shape s;
+  WsLayout L;
+  moe_status st = check_problem(p, s);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !counts || !kept || !offsets || !sorted_assign || !assign_row || !drop_mask)
+    return MOE_ERR_INVALID_ARG;
+  (void)ws;  // dispatch keeps its scratch in LDS
+  (void)ws_bytes;
+  (void)L;
+  return fail_hip(launch_dispatch(s, topk_idx, counts, kept, offsets, sorted_assign, assign_row,
+                                  drop_mask, nullptr, nullptr, nullptr, nullptr, nullptr, stream));
+}
+
+moe_status moe_expert_up(const moe_problem* p, const void* x, const moe_weights* w,
+                         const int32_t* offsets, const int32_t* sorted_assign, void* h, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  WsLayout L;
+  moe_status st = check_problem(p, s);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights(s, w, false, true)) != MOE_OK) return st;
+  if (!x || !offsets || !sorted_assign || !h) return MOE_ERR_INVALID_ARG;
+  (void)ws;  // the up projection needs no scratch
+  (void)ws_bytes;
+  (void)L;
+  return fail_hip(launch_up(s, x, w->w_up, w->b_up, offsets, sorted_assign, h, stream));
+}
+
+moe_status moe_expert_down(const moe_problem* p, const moe_weights* w, const int32_t* offsets,
+                           const void* h, float* y_exp, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  Shape s;
+  WsLayout L;
+  moe_status st = check_problem(p, s);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights(s, w, false, true)) != MOE_OK) return st;
+  if (!offsets || !h || !y_exp) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(s, ws, ws_bytes, L)) != MOE_OK) return st;
+  return fail_hip(launch_down(s, h, w->w_down, w->b_down, offsets, y_exp,
+                              at<float>(ws, L.y_part), stream));
+}
+
+moe_status moe_expert_ffn(const moe_problem* p, const void* x, const moe_weights* w,
+                          const int32_t* offsets, const int32_t* sorted_assign, float* y_exp,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  WsLayout L;
+  moe_status st = check_problem(p, s);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights(s, w, false, true)) != MOE_OK) return st;
+  if (!x || !offsets || !sorted_assign || !y_exp) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(s, ws, ws_bytes, L)) != MOE_OK) return st;
+  void* h = at<void>(ws, L.h);
+  hipError_t e = launch_up(s, x, w->w_up, w->b_up, offsets, sorted_assign, h, stream);
+  if (e == hipSuccess)
+    e = launch_down(s, h, w->w_down, w->b_down, offsets, y_exp, at<float>(ws, L.y_part), stream);
+  return fail_hip(e);
+}
+
+moe_status moe_combine(const moe_problem* p, const float* topk_w, const int32_t* assign_row,
+                       const int32_t* offsets, const float* y_exp, float* y, hipStream_t stream) {
+  Shape s;
+  moe_status st = check_problem(p, s);
+  if (st != MOE_OK) return st;
+  if (!topk_w || !assign_row || !offsets || !y_exp || !y) return MOE_ERR_INVALID_ARG;
+  return fail_hip(launch_combine(s, topk_w, assign_row, offsets, y_exp, y, stream));
+}
+
+moe_status moe_aux_stats(const moe_problem* p, const float* prob_colsum, const int32_t* counts,
+                         float* f, float* P, float* l_aux, hipStream_t stream) {
+  Shape s;
+  moe_status st = check_problem(p, s);
+  if (st != MOE_OK) return st;
+  if (!prob_colsum || !counts || !f || !P || !l_aux) return MOE_ERR_INVALID_ARG;
+  return fail_hip(launch_aux(s, prob_colsum, counts, f, P, l_aux, stream));
+}
+
+moe_status moe_ffn_forward(const moe_problem* p, const moe_weights* w, const void* x, float* y,
+                           const moe_routing* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  Shape s;
+  WsLayout L;
+  moe_status st = check_problem(p, s);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights(s, w, true, true)) != MOE_OK) return st;
+  if (!x || !y) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(s, ws, ws_bytes, L)) != MOE_OK) return st;
+  moe_routing r{};
+  if (out) r = *out;
+  int32_t* topk_idx = r.topk_idx ? r.topk_idx : at<int32_t>(ws, L.topk_idx);
+  float* topk_w = r.topk_w ? r.topk_w : at<float>(ws, L.topk_w);
+  int32_t* counts = r.counts ? r.counts : at<int32_t>(ws, L.counts);
+  int32_t* kept = r.kept ? r.kept : at<int32_t>(ws, L.kept);
+  int32_t* offsets = r.offsets ? r.offsets : at<int32_t>(ws, L.offsets);
+  int32_t* sorted_assign = r.sorted_assign ? r.sorted_assign : at<int32_t>(ws, L.sorted_assign);
+  int32_t* assign_row = r.assign_row ? r.assign_row : at<int32_t>(ws, L.assign_row);
+  uint8_t* drop_mask = r.drop_mask ? r.drop_mask : at<uint8_t>(ws, L.drop_mask);
+  float* f = r.f ? r.f : at<float>(ws, L.f);
+  float* P = r.P ? r.P : at<float>(ws, L.P);
+  float* l_aux = r.l_aux ? r.l_aux : at<float>(ws, L.l_aux);
+  float* part = at<float>(ws, L.prob_part);
+  void* h = at<void>(ws, L.h);
+  float* y_exp = at<float>(ws, L.y_exp);
+
+  hipError_t e = launch_router(s, x, w->w_router, w->b_router, topk_idx, topk_w, r.probs, part,
+                               stream);
+  if (e == hipSuccess)
+    e = launch_dispatch(s, topk_idx, counts, kept, offsets, sorted_assign, assign_row, drop_mask,
+                        part, at<float>(ws, L.prob_colsum), f, P, l_aux, stream);
+  if (e == hipSuccess) e = launch_up(s, x, w->w_up, w->b_up, offsets, sorted_assign, h, stream);
+  if (e == hipSuccess)
+    e = launch_down(s, h, w->w_down, w->b_down, offsets, y_exp, at<float>(ws, L.y_part), stream);
+  if (e == hipSuccess) e = launch_combine(s, topk_w, assign_row, offsets, y_exp, y, stream);
+  return fail_hip(e);
+}
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+int32_t moe_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

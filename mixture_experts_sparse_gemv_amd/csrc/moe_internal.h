@@ -1,0 +1,129 @@
+// Internal declarations of libmoe_mi355x: problem shape, workspace layout,
+// device helpers and the host-side launchers each kernel file provides.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- limits
+constexpr int kMaxExperts = 64;       // routed experts: one wave lane per expert
+constexpr int kMaxTopK = 8;
+constexpr int kMaxSegments = 128;     // routed + shared experts
+constexpr int kDecodeMaxT = 16;       // T at or below which the streaming decode path runs
+
+// ---------------------------------------------------------------- shape
+struct Shape {
+  int T, d, f, E, k, S, cap;   // cap <= 0: unlimited
+  int dtype, gating, act, flags;
+  int up_rows() const { return act == MOE_SWIGLU ? 2 * f : f; }
+  long long max_rows() const { return (long long)T * k + (long long)S * T; }
+  bool router_bias() const { return flags & MOE_ROUTER_BIAS; }
+  bool expert_bias() const { return (flags & MOE_EXPERT_BIAS) && act != MOE_SWIGLU; }
+  bool decode() const { return dtype == MOE_BF16 && T <= kDecodeMaxT; }
+};
+
+// Router blocks each handle this many tokens (their per-expert probability
+// sums are the partial sums later reduced in block order).
+constexpr int kRouterTokens = 16;
+inline int router_blocks(const Shape& s) { return (s.T + kRouterTokens - 1) / kRouterTokens; }
+
+// Split of the reduction dimension in the decode down-projection.
+constexpr int kDecodeSplitK = 4;
+
+// ---------------------------------------------------------------- workspace
+struct WsLayout {
+  size_t topk_idx, topk_w, prob_part, prob_colsum, counts, kept, offsets, sorted_assign,
+      assign_row, drop_mask, f, P, l_aux, h, y_exp, y_part, total;
+};
+WsLayout ws_layout(const Shape& s);
+
+// ---------------------------------------------------------------- vector types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+  return __uint_as_float(((uint32_t)u) << 16);
+}
+
+// Eight bf16 values (16 bytes) -> eight fp16 values.  bf16 -> fp32 is exact
+// (a shift); fp32 -> fp16 is exact for magnitudes in [2^-14, 65504], which is
+// where bf16 weights of a trained or N(0, 0.02^2) layer lie; smaller values
+// become fp16 subnormals (truncated), larger ones saturate.
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float lo = __uint_as_float(v[i] << 16);
+    float hi = __uint_as_float(v[i] & 0xffff0000u);
+    fp16x2_t p = __builtin_amdgcn_cvt_pkrtz(lo, hi);
+    r[i] = __builtin_bit_cast(uint32_t, p);
+  }
+  return r;
+}
+
+// exp(x) through the hardware base-2 exponential.
+__device__ __forceinline__ float fast_exp(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+// silu(z) = z / (1 + exp(-z)).
+__device__ __forceinline__ float silu_f(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + fast_exp(-z));
+}
+
+// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, 7.1.26
+// (rational approximation in t = 1/(1 + p|x|) times exp(-x^2); absolute
+// error at most 1.5e-7).
+__device__ __forceinline__ float erf_as(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
+  float poly = fmaf(1.061405429f, t, -1.453152027f);
+  poly = fmaf(poly, t, 1.421413741f);
+  poly = fmaf(poly, t, -0.284496736f);
+  poly = fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  const float e = fast_exp(-ax * ax);
+  const float r = fmaf(-poly, e, 1.0f);
+  return copysignf(r, x);
+}
+
+// GELU in the exact erf form: 0.5 z (1 + erf(z / sqrt 2)).
+__device__ __forceinline__ float gelu_f(float z) {
+  const float hz = 0.5f * z;
+  return fmaf(hz, erf_as(z * 0.70710678118654752f), hz);
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; all are asynchronous on `st`.
+hipError_t launch_router(const Shape& s, const void* x, const void* wr, const void* br,
+                         int32_t* topk_idx, float* topk_w, float* probs, float* prob_part,
+                         hipStream_t st);
+hipError_t launch_colsum(const Shape& s, const float* prob_part, float* colsum, hipStream_t st);
+// Dispatch; when prob_part is non-null it also reduces the probability sums
+// into colsum and writes f, P, l_aux.
+hipError_t launch_dispatch(const Shape& s, const int32_t* topk_idx, int32_t* counts,
+                           int32_t* kept, int32_t* offsets, int32_t* sorted_assign,
+                           int32_t* assign_row, uint8_t* drop_mask, const float* prob_part,
+                           float* colsum, float* f, float* P, float* l_aux, hipStream_t st);
+hipError_t launch_aux(const Shape& s, const float* colsum, const int32_t* counts, float* f,
+                      float* P, float* l_aux, hipStream_t st);
+hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void* b_up,
+                     const int32_t* offsets, const int32_t* sorted_assign, void* h,
+                     hipStream_t st);
+hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const void* b_down,
+                       const int32_t* offsets, float* y_exp, float* y_part, hipStream_t st);
+hipError_t launch_combine(const Shape& s, const float* topk_w, const int32_t* assign_row,
+                          const int32_t* offsets, const float* y_exp, float* y, hipStream_t st);
+
+}  // namespace moe

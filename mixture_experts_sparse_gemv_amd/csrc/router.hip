@@ -1,0 +1,212 @@
+// Router + gate + top-k + renormalization, fused in one kernel.
+//
+//   logits[t, e] = sum_j x[t, j] Wr[e, j] + br[e]           (0539edu 2.1; kamacoder 三)
+//   softmax p = exp(l - max) / sum, or normalized sigmoid p = s / sum s
+//                                                            ("MoE架构解析" 四 技术飞跃③)
+//   top-k by descending score, ties to the lower expert index; weights =
+//   selected scores / their sum                              (0539edu 2.1; kamacoder 三)
+//
+// A block handles 16 tokens with 4 waves.  For bf16 inputs the router
+// product runs on bf16 MFMA 16x16x32 (A = 16 router rows, B = 16 token rows),
+// each wave covering every 4th 32-wide K step; the four partial logit tiles
+// are summed in LDS in a fixed order.  The gate and the top-k then run one
+// token per wave pass with one lane per expert (E <= 64): wave-wide max and
+// sum by butterfly shuffles, and k rounds of a wave-wide argmax in which the
+// lower lane wins a tie.  Experts are ranked by logit (monotone in both
+// gates, so ranking and weights match ranking by score).  Each block also
+// writes the sum of its 16 tokens' probabilities per expert (token order);
+// these partial sums are reduced in block order for P.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int RT = kRouterTokens;  // 16 tokens per block
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+// Wave-wide argmax; among equal values the lower index wins.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ov = __shfl_xor(v, o);
+    const int oi = __shfl_xor(i, o);
+    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+  }
+}
+
+struct RouterArgs {
+  const void* x;
+  const void* wr;
+  const void* br;       // null if no router bias
+  int32_t* topk_idx;
+  float* topk_w;
+  float* probs;         // null if not requested
+  float* prob_part;     // [blocks, E]
+  int T, d, E, k, gating, dtype;
+};
+
+template <int NE16>  // expert tiles of 16 (bf16 path); 0 = fp32 path
+__global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
+  __shared__ float red[4][RT][kMaxExperts + 1];
+  __shared__ float colp[4][kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * RT;
+  const int E = a.E;
+
+  if (NE16 > 0) {
+    // ---- logits on the matrix cores
+    const uint16_t* x = (const uint16_t*)a.x;
+    const uint16_t* wr = (const uint16_t*)a.wr;
+    const int tl = lane & 15, kg = lane >> 4;
+    const int t = min(t0 + tl, a.T - 1);
+    const uint16_t* xp = x + (long long)t * a.d + kg * 8;
+    const uint16_t* wp[NE16 > 0 ? NE16 : 1];
+#pragma unroll
+    for (int j = 0; j < NE16; ++j) {
+      const int e = min(j * 16 + (lane & 15), E - 1);
+      wp[j] = wr + (long long)e * a.d + kg * 8;
+    }
+    f32x4 acc[NE16 > 0 ? NE16 : 1];
+#pragma unroll
+    for (int j = 0; j < NE16; ++j) acc[j] = f32x4{};
+    const int nsteps = a.d / 32;
+#pragma unroll 4
+    for (int s = wave; s < nsteps; s += 4) {
+      const u32x4 xv = *(const u32x4*)(xp + s * 32);
+#pragma unroll
+      for (int j = 0; j < NE16; ++j) {
+        const u32x4 wv = *(const u32x4*)(wp[j] + s * 32);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv),
+                                                         __builtin_bit_cast(bf16x8, xv), acc[j],
+                                                         0, 0, 0);
+      }
+    }
+    // D[expert][token]: lane holds token lane & 15, experts 16j + 4*(lane>>4) + r
+#pragma unroll
+    for (int j = 0; j < NE16; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][tl][j * 16 + 4 * kg + r] = acc[j][r];
+  } else {
+    // ---- fp32: one thread per (token, expert) dot product
+    const float* x = (const float*)a.x;
+    const float* wr = (const float*)a.wr;
+    for (int p = tid; p < RT * kMaxExperts; p += 256) {
+      const int tl = p / kMaxExperts, e = p % kMaxExperts;
+      float z = 0.f;
+      if (e < E && t0 + tl < a.T) {
+        const float* xr = x + (long long)(t0 + tl) * a.d;
+        const float* wrow = wr + (long long)e * a.d;
+        for (int j = 0; j < a.d; ++j) z = fmaf(xr[j], wrow[j], z);
+      }
+      red[0][tl][e] = z;
+      red[1][tl][e] = 0.f;
+      red[2][tl][e] = 0.f;
+      red[3][tl][e] = 0.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- gate + top-k: wave w handles tokens 4w .. 4w+3, lane = expert
+  float bias = 0.f;
+  if (a.br && lane < E)
+    bias = a.dtype == MOE_BF16 ? bf16_to_f32(((const uint16_t*)a.br)[lane])
+                               : ((const float*)a.br)[lane];
+  const float NEG_INF = -__builtin_inff();
+  float psum = 0.f;
+#pragma unroll 1
+  for (int i = 0; i < 4; ++i) {
+    const int tl = wave * 4 + i;
+    const int t = t0 + tl;
+    if (t >= a.T) break;
+    float l = NEG_INF;
+    if (lane < E) l = ((red[0][tl][lane] + red[1][tl][lane]) + red[2][tl][lane]) + red[3][tl][lane] + bias;
+    float score, denom;
+    if (a.gating == MOE_SOFTMAX) {
+      const float mx = wave_max(l);
+      score = lane < E ? fast_exp(l - mx) : 0.f;   // unnormalized, exp(l - max)
+      denom = wave_sum(score);
+    } else {
+      score = lane < E ? __builtin_amdgcn_rcpf(1.0f + fast_exp(-l)) : 0.f;   // sigma(l)
+      denom = wave_sum(score);
+    }
+    const float p = score / denom;
+    if (lane < E) {
+      if (a.probs) a.probs[(long long)t * E + lane] = p;
+      psum += p;
+    }
+    // k rounds of argmax over the logits; remember each winner's score
+    float key = l;
+    int my_idx = 0;
+    float my_score = 0.f, sel_sum = 0.f;
+    for (int s = 0; s < a.k; ++s) {
+      float bv = key;
+      int bi = lane;
+      wave_argmax(bv, bi);
+      const float bs = __shfl(score, bi);
+      sel_sum += bs;
+      if (lane == s) { my_idx = bi; my_score = bs; }
+      if (lane == bi) key = NEG_INF;
+    }
+    if (lane < a.k) {
+      a.topk_idx[(long long)t * a.k + lane] = my_idx;
+      a.topk_w[(long long)t * a.k + lane] = my_score / sel_sum;
+    }
+  }
+  colp[wave][lane] = psum;
+  __syncthreads();
+  if (tid < E)
+    a.prob_part[(long long)blockIdx.x * E + tid] = ((colp[0][tid] + colp[1][tid]) + colp[2][tid]) + colp[3][tid];
+}
+
+// colsum[e] = sum over router blocks b (in order, 256 strided partial sums
+// then a fixed tree) of prob_part[b, e].  One block per expert.
+__global__ __launch_bounds__(256) void colsum_kernel(const float* prob_part, int nblk, int E,
+                                                     float* colsum) {
+  __shared__ float s[256];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  float v = 0.f;
+  for (int b = tid; b < nblk; b += 256) v += prob_part[(long long)b * E + e];
+  s[tid] = v;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) s[tid] += s[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0) colsum[e] = s[0];
+}
+
+}  // namespace
+
+hipError_t launch_router(const Shape& s, const void* x, const void* wr, const void* br,
+                         int32_t* topk_idx, float* topk_w, float* probs, float* prob_part,
+                         hipStream_t st) {
+  RouterArgs a{x, wr, s.router_bias() ? br : nullptr, topk_idx, topk_w, probs, prob_part,
+               s.T, s.d, s.E, s.k, s.gating, s.dtype};
+  const int blocks = router_blocks(s);
+  if (s.dtype == MOE_F32) {
+    router_kernel<0><<<blocks, 256, 0, st>>>(a);
+  } else {
+    const int ne16 = (s.E + 15) / 16;
+    if (ne16 == 1) router_kernel<1><<<blocks, 256, 0, st>>>(a);
+    else if (ne16 == 2) router_kernel<2><<<blocks, 256, 0, st>>>(a);
+    else if (ne16 == 3) router_kernel<3><<<blocks, 256, 0, st>>>(a);
+    else router_kernel<4><<<blocks, 256, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum(const Shape& s, const float* prob_part, float* colsum, hipStream_t st) {
+  colsum_kernel<<<s.E, 256, 0, st>>>(prob_part, router_blocks(s), s.E, colsum);
+  return hipGetLastError();
+}
+
+}  // namespace moe

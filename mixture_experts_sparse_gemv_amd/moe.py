@@ -1,0 +1,236 @@
+"""Python binding of libmoe_mi355x (ctypes).
+
+Argument marshalling only: every function takes torch tensors, checks their
+device, dtype and size on the host, and passes data pointers plus torch's
+current HIP stream to the C entry point of the same name.  Every step of the
+computation runs in the library's HIP kernels.  If the library is missing
+the import fails (run __graft_entry__.build() or
+python mixture_experts_sparse_gemv_amd/build.py first).
+"""
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads the HIP runtime the library links against)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SOFTMAX, MOE_SIGMOID_NORM = 0, 1
+MOE_RELU, MOE_GELU, MOE_SWIGLU = 0, 1, 2
+MOE_ROUTER_BIAS, MOE_EXPERT_BIAS = 1, 2
+
+# Every symbol include/moe.h declares.
+EXPORTS = ("moe_capacity", "moe_workspace_size", "moe_router_topk", "moe_dispatch",
+           "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_aux_stats",
+           "moe_ffn_forward", "moe_status_string", "moe_last_hip_error")
+
+
+class moe_problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("T", "d_model", "d_ff", "num_experts", "top_k", "num_shared", "capacity",
+                 "dtype", "gating", "activation", "flags")]
+
+
+class moe_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("w_router", "b_router", "w_up", "b_up", "w_down", "b_down")]
+
+
+class moe_routing(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("topk_idx", "topk_w", "probs", "counts", "kept", "offsets", "sorted_assign",
+                 "assign_row", "drop_mask", "f", "P", "l_aux")]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        msg = _lib.moe_status_string(status).decode()
+        if status == MOE_ERR_HIP:
+            msg += f" (hipError {_lib.moe_last_hip_error()})"
+        super().__init__(f"{fn}: {msg}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, V, I32, SZ = ctypes.POINTER, ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    pp, pw, pr = P(moe_problem), P(moe_weights), P(moe_routing)
+    sig = {
+        "moe_capacity": (I32, [I32, I32, I32, ctypes.c_float]),
+        "moe_workspace_size": (I32, [pp, P(SZ)]),
+        "moe_router_topk": (I32, [pp, V, pw, V, V, V, V, V, SZ, V]),
+        "moe_dispatch": (I32, [pp, V, V, V, V, V, V, V, V, SZ, V]),
+        "moe_expert_ffn": (I32, [pp, V, pw, V, V, V, V, SZ, V]),
+        "moe_expert_up": (I32, [pp, V, pw, V, V, V, V, SZ, V]),
+        "moe_expert_down": (I32, [pp, pw, V, V, V, V, SZ, V]),
+        "moe_combine": (I32, [pp, V, V, V, V, V, V]),
+        "moe_aux_stats": (I32, [pp, V, V, V, V, V, V]),
+        "moe_ffn_forward": (I32, [pp, pw, V, V, pr, V, SZ, V]),
+        "moe_status_string": (ctypes.c_char_p, [I32]),
+        "moe_last_hip_error": (I32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+_lib = _load()
+
+
+# ---------------------------------------------------------------- helpers
+
+def make_problem(T, d_model, d_ff, num_experts, top_k, num_shared=0, capacity=0,
+                 dtype="bf16", gating="softmax", activation="swiglu", router_bias=False,
+                 expert_bias=False):
+    return moe_problem(
+        T=T, d_model=d_model, d_ff=d_ff, num_experts=num_experts, top_k=top_k,
+        num_shared=num_shared, capacity=capacity or 0,
+        dtype={"f32": MOE_F32, "bf16": MOE_BF16}[dtype],
+        gating={"softmax": MOE_SOFTMAX, "sigmoid_norm": MOE_SIGMOID_NORM}[gating],
+        activation={"relu": MOE_RELU, "gelu": MOE_GELU, "swiglu": MOE_SWIGLU}[activation],
+        flags=(MOE_ROUTER_BIAS if router_bias else 0) | (MOE_EXPERT_BIAS if expert_bias else 0))
+
+
+def make_weights(w_router, b_router, w_up, b_up, w_down, b_down):
+    return moe_weights(*[_ptr(t) for t in (w_router, b_router, w_up, b_up, w_down, b_down)])
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(fn, status):
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+def _need(t, numel, dtype, name):
+    if t is None:
+        return
+    if t.dtype != dtype or t.numel() < numel:
+        raise ValueError(f"{name}: need >= {numel} elements of {dtype}, got {t.numel()} of {t.dtype}")
+
+
+def _ws(ws):
+    return (ws.data_ptr(), ws.numel() * ws.element_size()) if ws is not None else (None, 0)
+
+
+def h_dtype(p):
+    """Storage dtype of the intermediate h: fp16 for bf16 problems, fp32 for fp32."""
+    return torch.float16 if p.dtype == MOE_BF16 else torch.float32
+
+
+def max_rows(p):
+    return p.T * p.top_k + p.num_shared * p.T
+
+
+# ---------------------------------------------------------------- entry points
+
+def moe_capacity(T, k, E, capacity_factor):
+    return _lib.moe_capacity(T, k, E, float(capacity_factor))
+
+
+def moe_workspace_size(p):
+    n = ctypes.c_size_t(0)
+    _check("moe_workspace_size", _lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def workspace(p, device="cuda"):
+    """A workspace tensor of moe_workspace_size(p) bytes (torch allocations are
+    256-byte aligned)."""
+    return torch.empty(moe_workspace_size(p), dtype=torch.uint8, device=device)
+
+
+def moe_router_topk(p, x, w, topk_idx, topk_w, probs=None, prob_colsum=None, ws=None,
+                    stream=None):
+    _need(topk_idx, p.T * p.top_k, torch.int32, "topk_idx")
+    _need(topk_w, p.T * p.top_k, torch.float32, "topk_w")
+    _need(probs, p.T * p.num_experts, torch.float32, "probs")
+    _need(prob_colsum, p.num_experts, torch.float32, "prob_colsum")
+    wp, wb = _ws(ws)
+    _check("moe_router_topk", _lib.moe_router_topk(
+        ctypes.byref(p), _ptr(x), ctypes.byref(w), _ptr(topk_idx), _ptr(topk_w), _ptr(probs),
+        _ptr(prob_colsum), wp, wb, _stream(stream)))
+
+
+def moe_dispatch(p, topk_idx, counts, kept, offsets, sorted_assign, assign_row, drop_mask,
+                 ws=None, stream=None):
+    E, n = p.num_experts, p.T * p.top_k
+    _need(topk_idx, n, torch.int32, "topk_idx")
+    for t, m, nm in ((counts, E, "counts"), (kept, E, "kept"), (offsets, E + 1, "offsets"),
+                     (sorted_assign, n, "sorted_assign"), (assign_row, n, "assign_row")):
+        _need(t, m, torch.int32, nm)
+    _need(drop_mask, n, torch.uint8, "drop_mask")
+    wp, wb = _ws(ws)
+    _check("moe_dispatch", _lib.moe_dispatch(
+        ctypes.byref(p), _ptr(topk_idx), _ptr(counts), _ptr(kept), _ptr(offsets),
+        _ptr(sorted_assign), _ptr(assign_row), _ptr(drop_mask), wp, wb, _stream(stream)))
+
+
+def moe_expert_ffn(p, x, w, offsets, sorted_assign, y_exp, ws, stream=None):
+    _need(y_exp, max_rows(p) * p.d_model, torch.float32, "y_exp")
+    wp, wb = _ws(ws)
+    _check("moe_expert_ffn", _lib.moe_expert_ffn(
+        ctypes.byref(p), _ptr(x), ctypes.byref(w), _ptr(offsets), _ptr(sorted_assign),
+        _ptr(y_exp), wp, wb, _stream(stream)))
+
+
+def moe_expert_up(p, x, w, offsets, sorted_assign, h, ws=None, stream=None):
+    _need(h, max_rows(p) * p.d_ff, h_dtype(p), "h")
+    wp, wb = _ws(ws)
+    _check("moe_expert_up", _lib.moe_expert_up(
+        ctypes.byref(p), _ptr(x), ctypes.byref(w), _ptr(offsets), _ptr(sorted_assign), _ptr(h),
+        wp, wb, _stream(stream)))
+
+
+def moe_expert_down(p, w, offsets, h, y_exp, ws, stream=None):
+    _need(h, max_rows(p) * p.d_ff, h_dtype(p), "h")
+    _need(y_exp, max_rows(p) * p.d_model, torch.float32, "y_exp")
+    wp, wb = _ws(ws)
+    _check("moe_expert_down", _lib.moe_expert_down(
+        ctypes.byref(p), ctypes.byref(w), _ptr(offsets), _ptr(h), _ptr(y_exp), wp, wb,
+        _stream(stream)))
+
+
+def moe_combine(p, topk_w, assign_row, offsets, y_exp, y, stream=None):
+    _need(y, p.T * p.d_model, torch.float32, "y")
+    _check("moe_combine", _lib.moe_combine(
+        ctypes.byref(p), _ptr(topk_w), _ptr(assign_row), _ptr(offsets), _ptr(y_exp), _ptr(y),
+        _stream(stream)))
+
+
+def moe_aux_stats(p, prob_colsum, counts, f, P, l_aux, stream=None):
+    _check("moe_aux_stats", _lib.moe_aux_stats(
+        ctypes.byref(p), _ptr(prob_colsum), _ptr(counts), _ptr(f), _ptr(P), _ptr(l_aux),
+        _stream(stream)))
+
+
+def moe_ffn_forward(p, w, x, y, ws, routing=None, stream=None):
+    """routing: optional dict of output tensors named as moe_routing's fields."""
+    _need(y, p.T * p.d_model, torch.float32, "y")
+    r = None
+    if routing:
+        r = moe_routing(**{k: _ptr(v) for k, v in routing.items()})
+    wp, wb = _ws(ws)
+    _check("moe_ffn_forward", _lib.moe_ffn_forward(
+        ctypes.byref(p), ctypes.byref(w), _ptr(x), _ptr(y),
+        ctypes.byref(r) if r is not None else None, wp, wb, _stream(stream)))

@@ -1,0 +1,199 @@
+"""Shared helpers of the GPU parity tests: seeded inputs on the GPU, the
+oracle on the same bytes, and the comparison rules.
+
+Tolerances (from the statement of the layer's accuracy for bf16 inputs with
+fp32 accumulation):
+  * routing indices: identical sets on every token whose oracle score gap
+    between the k-th and (k+1)-th expert exceeds GAP; slot order identical
+    where adjacent selected scores differ by more than GAP; on the other
+    tokens every selected expert must score within GAP of the k-th best;
+  * dispatch outputs: bit-exact given the same routing;
+  * floating-point outputs: relative Frobenius error <= 1e-2 and max abs
+    error <= 2e-2 against the float64 oracle;
+  * L_aux: relative error <= 1e-4.
+"""
+import math
+
+import numpy as np
+import torch
+
+import oracle as O
+from mixture_experts_sparse_gemv_amd import moe as M
+from synth import make_inputs, to_f64
+
+GAP = 1e-4
+REL_FROB = 1e-2
+MAX_ABS = 2e-2
+LAUX_REL = 1e-4
+
+
+class LazyF64:
+    """Indexable view of a [n, ...] torch tensor that upcasts one slice at a
+    time to float64 numpy (keeps the oracle's memory bounded at large sizes)."""
+
+    def __init__(self, t):
+        self.t = t
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, i):
+        return self.t[i].to(torch.float64).numpy()
+
+
+def problem_of(run, capacity=None):
+    cap = capacity
+    if cap is None:
+        cap = M.moe_capacity(run.T, run.top_k, run.num_experts, run.capacity_factor or 0.0)
+    return M.make_problem(
+        T=run.T, d_model=run.d_model, d_ff=run.d_ff, num_experts=run.num_experts,
+        top_k=run.top_k, num_shared=run.num_shared, capacity=cap, dtype=run.dtype,
+        gating=run.gating, activation=run.activation,
+        router_bias=run.router_bias != "none", expert_bias=run.expert_bias)
+
+
+def oracle_capacity(run):
+    return O.capacity(run.T, run.top_k, run.num_experts, run.capacity_factor)
+
+
+def gpu_inputs(inp):
+    return {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+
+
+def weights_of(g):
+    return M.make_weights(g["w_router"], g["b_router"], g["w_up"], g["b_up"], g["w_down"],
+                          g["b_down"])
+
+
+def oracle_forward(run, inp, cap="run", token_subset=None):
+    c = oracle_capacity(run) if cap == "run" else cap
+    lazy = lambda t: None if t is None else LazyF64(t)
+    return O.forward(to_f64(inp["x"]), to_f64(inp["w_router"]), to_f64(inp["b_router"]),
+                     lazy(inp["w_up"]), lazy(inp["b_up"]), lazy(inp["w_down"]),
+                     lazy(inp["b_down"]), top_k=run.top_k, num_shared=run.num_shared,
+                     gating=run.gating, activation=run.activation, cap=c,
+                     token_subset=token_subset)
+
+
+def assert_close(got, ref, name, rel=REL_FROB, mabs=MAX_ABS):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    diff = got - ref
+    nref = np.linalg.norm(ref)
+    rf = np.linalg.norm(diff) / (nref if nref > 0 else 1.0)
+    ma = float(np.abs(diff).max()) if diff.size else 0.0
+    print(f"  {name}: rel_frob={rf:.3e} max_abs={ma:.3e}", flush=True)
+    assert rf <= rel, f"{name}: relative Frobenius error {rf:.3e} > {rel}"
+    assert ma <= mabs, f"{name}: max abs error {ma:.3e} > {mabs}"
+    return rf, ma
+
+
+def check_routing(gpu_idx, orc, k):
+    """Returns the mask of tokens whose selected set equals the oracle's."""
+    oi = orc["idx"]
+    gi = np.asarray(gpu_idx).reshape(oi.shape)
+    same = np.all(np.sort(gi, axis=1) == np.sort(oi, axis=1), axis=1)
+    gap = orc["gap"]
+    bad = ~same & (gap > GAP)
+    assert not bad.any(), f"routing differs on {int(bad.sum())} tokens with a clear gap"
+    probs = orc["probs"]
+    E = probs.shape[1]
+    assert gi.min() >= 0 and gi.max() < E
+    assert np.all(np.array([len(set(r)) for r in gi]) == k), "repeated expert in a token"
+    # near-tie tokens: the GPU's choices must be valid within GAP
+    kth = np.sort(probs, axis=1)[:, ::-1][:, k - 1]
+    sel = np.take_along_axis(probs, gi.astype(np.int64), axis=1)
+    assert np.all(sel >= kth[:, None] - GAP)
+    # slot order where it is well defined
+    osel = np.take_along_axis(probs, oi.astype(np.int64), axis=1)
+    if k > 1:
+        clear = np.all(np.abs(np.diff(osel, axis=1)) > GAP, axis=1) & same
+        assert np.array_equal(gi[clear], oi[clear]), "slot order differs"
+    return same
+
+
+def check_dispatch_bitexact(gpu, orc, E):
+    assert np.array_equal(gpu["counts"], orc["counts"]), "counts"
+    assert np.array_equal(gpu["kept"], orc["kept"]), "kept"
+    assert np.array_equal(gpu["offsets"], orc["offsets"]), "offsets"
+    assert np.array_equal(gpu["sorted_assign"], orc["sorted_assign"]), "sorted_assign"
+    assert np.array_equal(gpu["assign_row"], orc["assign_row"]), "assign_row"
+    assert np.array_equal(gpu["drop_mask"], orc["drop_mask"]), "drop_mask"
+
+
+def check_dispatch_consistent(gpu, gpu_idx, E, cap):
+    """Properties of a dispatch given its own routing (used where routing
+    differs from the oracle on near-tie tokens)."""
+    flat = np.asarray(gpu_idx).reshape(-1)
+    n = flat.size
+    counts = np.bincount(flat, minlength=E)
+    assert np.array_equal(gpu["counts"], counts)
+    kept = counts if not cap else np.minimum(counts, cap)
+    assert np.array_equal(gpu["kept"], kept)
+    assert np.array_equal(gpu["offsets"], np.concatenate([[0], np.cumsum(kept)]))
+    assert sorted(gpu["sorted_assign"].tolist()) == list(range(n))
+
+
+def routing_outputs(p, device="cuda"):
+    T, k, E = p.T, p.top_k, p.num_experts
+    i32 = dict(dtype=torch.int32, device=device)
+    f32 = dict(dtype=torch.float32, device=device)
+    return dict(topk_idx=torch.empty(T * k, **i32), topk_w=torch.empty(T * k, **f32),
+                probs=torch.empty(T * E, **f32), counts=torch.empty(E, **i32),
+                kept=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+                sorted_assign=torch.empty(T * k, **i32), assign_row=torch.empty(T * k, **i32),
+                drop_mask=torch.empty(T * k, dtype=torch.uint8, device=device),
+                f=torch.empty(E, **f32), P=torch.empty(E, **f32), l_aux=torch.empty(1, **f32))
+
+
+def run_forward(run, g, p=None, routing=True):
+    p = p or problem_of(run)
+    ws = M.workspace(p)
+    y = torch.empty(run.T * run.d_model, dtype=torch.float32, device="cuda")
+    r = routing_outputs(p) if routing else None
+    M.moe_ffn_forward(p, weights_of(g), g["x"], y, ws, routing=r)
+    torch.cuda.synchronize()
+    out = {k: v.cpu().numpy() for k, v in (r or {}).items()}
+    out["y"] = y.view(run.T, run.d_model).cpu().numpy()
+    return out
+
+
+def compare_forward(run, gpu, orc, token_subset=None):
+    """Full comparison of a forward pass against the oracle."""
+    k, E, T = run.top_k, run.num_experts, run.T
+    gi = gpu["topk_idx"].reshape(T, k)
+    same = check_routing(gi, orc, k)
+    cap = oracle_capacity(run)
+    if same.all():
+        check_dispatch_bitexact(gpu, orc, E)
+    else:
+        check_dispatch_consistent(gpu, gi, E, cap)
+    # weights and probabilities
+    exact = np.all(gi == orc["idx"], axis=1)
+    assert_close(gpu["topk_w"].reshape(T, k)[exact], orc["w"][exact], "topk_w")
+    assert_close(gpu["probs"].reshape(T, E), orc["probs"], "probs")
+    # y on tokens whose routing and drops agree
+    gdrop = gpu["drop_mask"].reshape(T, k)
+    odrop = orc["drop_mask"].reshape(T, k)
+    gperm = np.argsort(gi, axis=1)
+    operm = np.argsort(orc["idx"], axis=1)
+    agree = same & np.all(np.take_along_axis(gdrop, gperm, 1) ==
+                          np.take_along_axis(odrop, operm, 1), axis=1)
+    n_dis = int((~agree).sum())
+    assert n_dis <= max(2, int(0.002 * T)), f"{n_dis} tokens disagree"
+    toks = orc["tokens"]
+    mask = agree[toks]
+    assert_close(gpu["y"][toks][mask], orc["y"][mask], "y")
+    # aux statistics
+    n_flip = int((~same).sum())
+    tol = LAUX_REL * abs(orc["l_aux"]) + n_flip * E * float(orc["P"].max()) / (T * k)
+    print(f"  l_aux gpu={float(gpu['l_aux'][0]):.6f} oracle={orc['l_aux']:.6f}", flush=True)
+    assert abs(float(gpu["l_aux"][0]) - orc["l_aux"]) <= tol
+    assert_close(gpu["P"], orc["P"], "P", rel=1e-4, mabs=1e-5)
+    if same.all():
+        np.testing.assert_allclose(gpu["f"], orc["f"], rtol=1e-6)
+    return agree
+
+
+def inputs_for(run):
+    return make_inputs(run)

@@ -1,0 +1,134 @@
+"""The C-ABI library on the host: it loads, exports every symbol the header
+declares, and its host-only functions (capacity, workspace size, argument
+validation) behave as documented.  No kernel is launched: every call here
+fails validation or is host-only."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle as O
+from mixture_experts_sparse_gemv_amd import moe as M
+from synth import RUNS
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "moe.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(M.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(M.EXPORTS) == names
+
+
+def test_capacity_matches_oracle():
+    for name in ("gpt2", "fine_shared"):
+        r = RUNS[name]
+        c = M.moe_capacity(r.T, r.top_k, r.num_experts, r.capacity_factor)
+        assert c == O.capacity(r.T, r.top_k, r.num_experts, r.capacity_factor)
+    assert M.moe_capacity(4096, 2, 8, 1.25) == 1280
+    assert M.moe_capacity(8192, 6, 64, 1.25) == 960
+    assert M.moe_capacity(10, 1, 3, 1.0) == 4
+    assert M.moe_capacity(10, 1, 3, 0.0) == 0
+    assert M.moe_capacity(0, 1, 3, 1.0) == -1
+
+
+def _problem(**kw):
+    base = dict(T=64, d_model=128, d_ff=256, num_experts=8, top_k=2, dtype="bf16",
+                activation="swiglu")
+    base.update(kw)
+    return M.make_problem(**base)
+
+
+def test_workspace_size_grows_with_problem():
+    a = M.moe_workspace_size(_problem())
+    b = M.moe_workspace_size(_problem(T=128))
+    assert 0 < a < b
+    assert a % 256 == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), M.MOE_ERR_INVALID_ARG),
+    (dict(top_k=9, num_experts=8), M.MOE_ERR_INVALID_ARG),
+    (dict(top_k=0), M.MOE_ERR_INVALID_ARG),
+    (dict(num_experts=65, top_k=2), M.MOE_ERR_UNSUPPORTED),
+    (dict(num_experts=16, top_k=9), M.MOE_ERR_UNSUPPORTED),
+    (dict(num_experts=64, num_shared=65), M.MOE_ERR_UNSUPPORTED),
+    (dict(d_model=100), M.MOE_ERR_UNSUPPORTED),
+    (dict(d_ff=96), M.MOE_ERR_UNSUPPORTED),
+])
+def test_invalid_problems_rejected(kw, status):
+    p = _problem(**kw)
+    n = ctypes.c_size_t(0)
+    assert M._lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n)) == status
+
+
+def test_fp32_allows_any_width():
+    assert M.moe_workspace_size(_problem(dtype="f32", d_model=33, d_ff=70)) > 0
+
+
+def test_forward_rejects_before_launch():
+    p = _problem()
+    fake = 0x1000  # never dereferenced: every call below fails validation
+    w = M.moe_weights(fake, None, fake, None, fake, None)
+    need = M.moe_workspace_size(p)
+    lib = M._lib
+    # null x / y
+    assert lib.moe_ffn_forward(ctypes.byref(p), ctypes.byref(w), None, fake, None, fake, need,
+                               None) == M.MOE_ERR_INVALID_ARG
+    # workspace too small or missing
+    assert lib.moe_ffn_forward(ctypes.byref(p), ctypes.byref(w), fake, fake, None, fake, need - 1,
+                               None) == M.MOE_ERR_WORKSPACE
+    assert lib.moe_ffn_forward(ctypes.byref(p), ctypes.byref(w), fake, fake, None, None, need,
+                               None) == M.MOE_ERR_WORKSPACE
+    # misaligned workspace
+    assert lib.moe_ffn_forward(ctypes.byref(p), ctypes.byref(w), fake, fake, None, fake + 4,
+                               need, None) == M.MOE_ERR_INVALID_ARG
+    # router bias flag without a bias pointer
+    pb = _problem(router_bias=True)
+    assert lib.moe_ffn_forward(ctypes.byref(pb), ctypes.byref(w), fake, fake, None, fake,
+                               M.moe_workspace_size(pb), None) == M.MOE_ERR_INVALID_ARG
+    # expert bias flag without bias pointers (GELU experts)
+    pg = _problem(activation="gelu", expert_bias=True)
+    assert lib.moe_ffn_forward(ctypes.byref(pg), ctypes.byref(w), fake, fake, None, fake,
+                               M.moe_workspace_size(pg), None) == M.MOE_ERR_INVALID_ARG
+    # missing weights struct
+    assert lib.moe_ffn_forward(ctypes.byref(p), None, fake, fake, None, fake, need,
+                               None) == M.MOE_ERR_INVALID_ARG
+    # unknown flags / enums
+    for bad in (dict(flags=8), dict(dtype=7), dict(gating=3), dict(activation=5)):
+        q = _problem()
+        for k, v in bad.items():
+            setattr(q, k, v)
+        assert lib.moe_ffn_forward(ctypes.byref(q), ctypes.byref(w), fake, fake, None, fake, need,
+                                   None) == M.MOE_ERR_INVALID_ARG
+
+
+def test_stage_entry_points_reject_null_outputs():
+    p = _problem()
+    fake = 0x1000
+    w = M.moe_weights(fake, None, fake, None, fake, None)
+    need = M.moe_workspace_size(p)
+    lib = M._lib
+    byref = ctypes.byref
+    assert lib.moe_router_topk(byref(p), fake, byref(w), None, fake, None, None, fake, need,
+                               None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch(byref(p), fake, fake, fake, fake, fake, fake, None, None, 0,
+                            None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_ffn(byref(p), fake, byref(w), fake, fake, None, fake, need,
+                              None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_down(byref(p), byref(w), fake, fake, fake, fake, need - 1,
+                               None) == M.MOE_ERR_WORKSPACE
+    assert lib.moe_combine(byref(p), fake, fake, fake, fake, None, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_aux_stats(byref(p), fake, fake, fake, None, fake, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_status_string(M.MOE_ERR_HIP) == b"MOE_ERR_HIP"

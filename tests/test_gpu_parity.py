@@ -1,0 +1,187 @@
+"""GPU parity of every step of the MoE-FFN forward against the float64 oracle,
+through the C ABI.  Each test prints its case before the GPU work."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mixture_experts_sparse_gemv_amd import moe as M
+from synth import RUNS, make_inputs, scaled, to_f64
+
+from _parity import (GAP, assert_close, check_dispatch_bitexact, compare_forward, gpu_inputs,
+                     oracle_capacity, oracle_forward, problem_of, run_forward, weights_of)
+
+pytestmark = pytest.mark.gpu
+
+# Parity cases the oracle finishes in seconds: several tiles and a ragged tail.
+SMALL = {
+    "tiny": RUNS["tiny"],
+    "gpt2_T700": scaled(RUNS["gpt2"], T=700),
+    "gpt2_T700_cf1": scaled(RUNS["gpt2"], T=700, capacity_factor=1.0),
+    "swiglu_skew_T3000": scaled(RUNS["swiglu_skew"], T=3000),
+    "large_decode": RUNS["large_decode"],
+    "large_T300": scaled(RUNS["large_prefill"], T=300),
+    "fine_shared_T1000": scaled(RUNS["fine_shared"], T=1000),
+    "fine_shared_T1000_literal": scaled(RUNS["fine_shared"], T=1000, capacity_factor=1.25 / 6),
+}
+
+
+@functools.lru_cache(maxsize=None)
+def _inputs(name):
+    run = SMALL.get(name) or RUNS[name]
+    return run, make_inputs(run)
+
+
+@functools.lru_cache(maxsize=None)
+def _oracle(name):
+    run, inp = _inputs(name)
+    return oracle_forward(run, inp)
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small(name):
+    run, inp = _inputs(name)
+    _say(f"[forward] {name}: T={run.T} d={run.d_model} f={run.d_ff} E={run.num_experts} "
+         f"k={run.top_k} S={run.num_shared} seed={run.seed}")
+    g = gpu_inputs(inp)
+    gpu = run_forward(run, g)
+    compare_forward(run, gpu, _oracle(name))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_router_topk(name):
+    run, inp = _inputs(name)
+    _say(f"[router_topk] {name}")
+    g = gpu_inputs(inp)
+    p = problem_of(run)
+    T, k, E = run.T, run.top_k, run.num_experts
+    idx = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T * k, dtype=torch.float32, device="cuda")
+    probs = torch.empty(T * E, dtype=torch.float32, device="cuda")
+    colsum = torch.empty(E, dtype=torch.float32, device="cuda")
+    M.moe_router_topk(p, g["x"], weights_of(g), idx, w, probs, colsum, ws=M.workspace(p))
+    torch.cuda.synchronize()
+    logits = O.router_logits(to_f64(inp["x"]), to_f64(inp["w_router"]), to_f64(inp["b_router"]))
+    pr = O.gate(logits, run.gating)
+    oi, ow = O.topk_renorm(pr, k)
+    gi = idx.view(T, k).cpu().numpy()
+    gap = O.selection_gap(pr, k)
+    same = np.all(np.sort(gi, 1) == np.sort(oi, 1), axis=1)
+    assert np.all(same | (gap <= GAP))
+    ex = np.all(gi == oi, axis=1)
+    assert_close(w.view(T, k).cpu().numpy()[ex], ow[ex], "topk_w")
+    assert_close(probs.view(T, E).cpu().numpy(), pr, "probs")
+    assert_close(colsum.cpu().numpy(), pr.sum(0), "colsum", rel=1e-4, mabs=1e-2)
+
+
+def _dispatch_cases():
+    rng = np.random.default_rng(123)
+    cases = []
+    for name in ("gpt2_T700", "fine_shared_T1000"):
+        run = SMALL[name]
+        cases.append((name, run.T, run.top_k, run.num_experts, None))
+    # synthetic routings: skewed, all to one expert, many experts, > 64K assignments
+    def rand_idx(T, k, E, skew):
+        p = np.arange(E, 0, -1, dtype=np.float64) ** skew
+        p /= p.sum()
+        out = np.empty((T, k), dtype=np.int32)
+        for t in range(T):
+            out[t] = rng.choice(E, size=k, replace=False, p=p)
+        return out
+    cases.append(("skew_E64_k6", 3000, 6, 64, rand_idx(3000, 6, 64, 2.0)))
+    cases.append(("uniform_E8_k2", 4096, 2, 8, rand_idx(4096, 2, 8, 0.0)))
+    cases.append(("one_expert", 777, 1, 5, np.full((777, 1), 3, dtype=np.int32)))
+    big = rand_idx(20000, 4, 16, 1.0)
+    cases.append(("segments_80000", 20000, 4, 16, big))
+    return cases
+
+
+@pytest.mark.parametrize("case", _dispatch_cases(), ids=lambda c: c[0])
+@pytest.mark.parametrize("cap_mode", ["none", "cf1.25", "cf1.0", "tight"])
+def test_dispatch_bitexact(case, cap_mode):
+    name, T, k, E, idx = case
+    if idx is None:
+        run, inp = _inputs(name)
+        pr = O.gate(O.router_logits(to_f64(inp["x"]), to_f64(inp["w_router"]),
+                                    to_f64(inp["b_router"])), run.gating)
+        idx, _ = O.topk_renorm(pr, k)
+    cap = {"none": None, "cf1.25": O.capacity(T, k, E, 1.25), "cf1.0": O.capacity(T, k, E, 1.0),
+           "tight": 1}[cap_mode]
+    _say(f"[dispatch] {name} T={T} k={k} E={E} cap={cap}")
+    orc = O.dispatch(idx, E, cap)
+    p = M.make_problem(T=T, d_model=64, d_ff=64, num_experts=E, top_k=k, capacity=cap or 0)
+    n = T * k
+    i32 = dict(dtype=torch.int32, device="cuda")
+    out = dict(counts=torch.empty(E, **i32), kept=torch.empty(E, **i32),
+               offsets=torch.empty(E + 1, **i32), sorted_assign=torch.empty(n, **i32),
+               assign_row=torch.empty(n, **i32),
+               drop_mask=torch.empty(n, dtype=torch.uint8, device="cuda"))
+    M.moe_dispatch(p, torch.from_numpy(idx.reshape(-1).astype(np.int32)).cuda(), **out)
+    torch.cuda.synchronize()
+    check_dispatch_bitexact({k_: v.cpu().numpy() for k_, v in out.items()}, orc, E)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_expert_ffn_and_combine_given_oracle_routing(name):
+    run, inp = _inputs(name)
+    _say(f"[expert_ffn+combine] {name}")
+    g = gpu_inputs(inp)
+    p = problem_of(run)
+    orc = _oracle(name)
+    T, k, d = run.T, run.top_k, run.d_model
+    dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a).astype(dt)).cuda()
+    offsets = dev(orc["offsets"], np.int32)
+    sorted_assign = dev(orc["sorted_assign"], np.int32)
+    assign_row = dev(orc["assign_row"], np.int32)
+    topk_w = dev(orc["w"].reshape(-1), np.float32)
+    ws = M.workspace(p)
+    y_exp = torch.empty(M.max_rows(p) * d, dtype=torch.float32, device="cuda")
+    M.moe_expert_ffn(p, g["x"], weights_of(g), offsets, sorted_assign, y_exp, ws)
+    y = torch.empty(T * d, dtype=torch.float32, device="cuda")
+    M.moe_combine(p, topk_w, assign_row, offsets, y_exp, y)
+    torch.cuda.synchronize()
+    assert_close(y.view(T, d).cpu().numpy(), orc["y"], "y")
+
+
+def test_aux_stats_given_oracle_sums():
+    run, inp = _inputs("fine_shared_T1000")
+    _say("[aux_stats] fine_shared_T1000")
+    orc = _oracle("fine_shared_T1000")
+    p = problem_of(run)
+    E = run.num_experts
+    colsum = torch.from_numpy(orc["probs"].sum(0).astype(np.float32)).cuda()
+    counts = torch.from_numpy(orc["counts"].astype(np.int32)).cuda()
+    f = torch.empty(E, device="cuda")
+    P = torch.empty(E, device="cuda")
+    l = torch.empty(1, device="cuda")
+    M.moe_aux_stats(p, colsum, counts, f, P, l)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(f.cpu().numpy(), orc["f"], rtol=1e-6)
+    np.testing.assert_allclose(P.cpu().numpy(), orc["P"], rtol=1e-5)
+    assert abs(float(l.item()) - orc["l_aux"]) <= 1e-4 * orc["l_aux"]
+
+
+def test_deterministic_and_no_out_of_bounds_writes():
+    run, inp = _inputs("fine_shared_T1000")
+    _say("[determinism+canary] fine_shared_T1000")
+    g = gpu_inputs(inp)
+    p = problem_of(run)
+    T, d = run.T, run.d_model
+    pad = 4096
+    ys = []
+    for rep in range(2):
+        y = torch.full((T * d + 2 * pad,), float("nan"), device="cuda")
+        ws = M.workspace(p)
+        M.moe_ffn_forward(p, weights_of(g), g["x"], y[pad:pad + T * d], ws)
+        torch.cuda.synchronize()
+        yy = y.cpu().numpy()
+        assert np.all(np.isnan(yy[:pad])) and np.all(np.isnan(yy[-pad:])), "write outside y"
+        assert np.all(np.isfinite(yy[pad:-pad]))
+        ys.append(yy[pad:-pad].copy())
+    assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32)), "not bit-identical"
