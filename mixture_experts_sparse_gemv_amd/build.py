@@ -41,15 +41,16 @@ def _run(cmd, verbose):
             sys.stderr.write(msg + "\n")
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+def build(verbose: bool = False, jobs: int = 8, out: str = LIB, defines=(), build_dir: str = BUILD,
+          csrc: str = CSRC) -> str:
+    os.makedirs(build_dir, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(csrc, "*.hip")))
     objs = []
     procs = []
     for src in srcs:
-        obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+        obj = os.path.join(build_dir, os.path.basename(src) + ".o")
         objs.append(obj)
-        cmd = [HIPCC, *HIP_FLAGS, "-c", src, "-o", obj]
+        cmd = [HIPCC, *HIP_FLAGS, *["-D" + d for d in defines], "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
@@ -59,11 +60,11 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     for p in procs:
         _wait(p, verbose)
     tl = _torch_lib_dir()
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run(["g++", "-shared", "-o", tmp, *objs, "-L" + tl, "-l:libamdhip64.so",
           "-Wl,-rpath," + tl, "-Wl,--no-undefined"], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 def _wait(item, verbose):

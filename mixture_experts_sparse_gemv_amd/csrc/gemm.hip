@@ -13,8 +13,7 @@
 // fp16; each bf16 W2 tile is converted to fp16 while it is staged into LDS).
 // Accumulation is fp32.  Block = 4 waves in a 2x2 grid; block tile BM token
 // rows x BN weight rows x BK=64; tiles are double-buffered in LDS with an XOR
-// swizzle of the 16-byte chunks (chunk ^ row%8) so that the fragment reads of
-// 32 consecutive rows spread over all banks.  The MFMA "A" operand is the
+// swizzle of the 16-byte chunks that keeps fragment reads conflict-free.  The MFMA "A" operand is the
 // weight tile and "B" the token tile, so each lane's accumulator holds four
 // consecutive output columns of one token row: the epilogue stores 8-byte
 // (fp16 x4) or 16-byte (fp32 x4) vectors.
@@ -53,23 +52,62 @@ __device__ __forceinline__ void segment_rows(const GemmArgs& a, int seg, int off
   }
 }
 
-template <int BM, int BN, int MODE>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs a) {
-  constexpr int BK = 64;
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200;
+#define SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+
+// NM MFMAs, each followed by one instruction of group A (NA in total) and
+// one of group B (NB in total); leftovers of A and B follow the last MFMA.
+// N instructions of group A, the first NB of them each followed by one of group B.
+template <int N, int MA, int MB, int NB, int I = 0>
+__device__ __forceinline__ void sched_interleave_pair() {
+  if constexpr (I < N) {
+    SGB(MA, 1);
+    if constexpr (I < NB) SGB(MB, (I + 1 < N) ? 1 : NB - I);
+    sched_interleave_pair<N, MA, MB, NB, I + 1>();
+  }
+}
+
+template <int NM, int MA, int NA, int MB, int NB, int I = 0>
+__device__ __forceinline__ void sched_interleave() {
+  if constexpr (I < NM) {
+    SGB(SG_MFMA, 1);
+    if constexpr (I < NA) SGB(MA, (I + 1 < NM) ? 1 : NA - I);
+    if constexpr (I < NB) SGB(MB, (I + 1 < NM) ? 1 : NB - I);
+    sched_interleave<NM, MA, NA, MB, NB, I + 1>();
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int MODE>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_kernel(GemmArgs a) {
+  constexpr int BK = 32;                   // k-tile depth
+  constexpr int NSTAGE = 4;                // LDS ring stages (DMA runs NSTAGE-1 tiles ahead)
+  constexpr int NW = WGM * WGN;            // waves: WGM along tokens x WGN along weights
   constexpr bool SWIGLU = MODE == MODE_SWIGLU;
   constexpr bool DOWN = MODE == MODE_DOWN;
-  constexpr int WM = BM / 2, WN = BN / 2;  // wave tile: token rows x weight rows
+  constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile: token rows x weight rows
   constexpr int MI = WM / 32, NI = WN / 32;
   constexpr int NOUT_TILE = SWIGLU ? BN / 2 : BN;
-  constexpr int XCH = BM / 32, WCH = BN / 32;  // 16-byte chunks per thread per k-tile
+  constexpr int ROWCH = BK / 8;            // 16-byte chunks per tile row
+  constexpr int RPB = 16 / ROWCH;          // tile rows per 256 bytes (all 64 LDS banks)
+  constexpr int RI = 64 / ROWCH;           // tile rows filled by one DMA instruction
+  constexpr int NSUB = BK / 16;            // MFMA k-substeps per k-tile
+  constexpr int NFR = NI + MI;             // fragment reads per wave per k-substep
+  constexpr int NM = NI * MI;              // MFMAs per wave per k-substep
+  constexpr int QWW = BN / RI / NW, QWX = BM / RI / NW;   // DMA instructions per wave and k-tile
+  constexpr int STAGE = (BM + BN) * ROWCH;                // 16-byte chunks per stage
+  static_assert(MI >= 1 && NI >= 1 && QWW * RI * NW == BN && QWX * RI * NW == BM, "tile shape");
   static_assert(!SWIGLU || (NI % 2 == 0), "SwiGLU pairs gate and up sub-tiles");
+  static_assert(NSUB >= 2, "cross-barrier pipelining needs two k-substeps per tile");
 
-  __shared__ u32x4 smem[2][(BM + BN) * 8];
+  // The LDS ring as distinct arrays: the compiler sees that the DMA into one
+  // stage never aliases the fragment reads of another.
+  __shared__ u32x4 lds0[STAGE], lds1[STAGE], lds2[STAGE], lds3[STAGE];
   __shared__ int seg_tile[kMaxSegments + 1];
   __shared__ int sh_seg;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WGM, wn = wave / WGM;
   const int nseg = a.E + a.S;
   const int NT = (a.Nout + NOUT_TILE - 1) / NOUT_TILE;
   const int off_E = a.offsets[a.E];
@@ -106,25 +144,30 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs a) {
   int seg_rows, row_start;
   segment_rows(a, seg, off_E, seg_rows, row_start);
 
-  // ---- global source rows of this thread's chunks
-  const int kc_ld = tid & 7;
-  const uint16_t* xsrc[XCH];
+  // ---- LDS layout.  Row r of a tile (W rows first, then token rows) holds
+  // its ROWCH chunks of 16 bytes at chunk positions kc ^ ((r / RPB) % ROWCH).
+  // The LDS has 64 banks of 4 bytes (256 bytes, RPB rows) and serves 16 lanes
+  // of a ds_read_b128 per cycle; the fragment reads of 16 consecutive rows
+  // then use each (bank group, row % RPB) pair once: no bank conflicts.
+  //
+  // Tiles move from global memory straight into LDS (global_load_lds_dwordx4:
+  // lane l of a wave instruction writes 16 bytes at the instruction's LDS
+  // base + 16 l).  Instruction q of a k-tile fills rows RI*q .. RI*q+RI-1, so
+  // lane l fetches row RI*q + l/ROWCH, logical chunk
+  // (l % ROWCH) ^ ((4q + l/16) % ROWCH) (as RI = 4 RPB).
+  // Wave w issues the W instructions q = w*QWW + j and the token-row
+  // instructions q = BN/RI + w*QWX + j.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const char* xbase;
+  if (DOWN) xbase = (const char*)(a.X + (long long)row_start * a.K);
+  else xbase = (const char*)a.X;
+  const char* wbase = (const char*)(a.W + (long long)seg * a.Wrows * a.K);
+  auto kc_dma = [&](int q) { return (lane % ROWCH) ^ ((4 * q + lane / 16) % ROWCH); };
+  uint32_t woff[QWW], xoff[QWX];   // byte offsets of this lane's source chunks
 #pragma unroll
-  for (int i = 0; i < XCH; ++i) {
-    const int m = mt * BM + (tid >> 3) + 32 * i;
-    const int mm = m < seg_rows ? m : seg_rows - 1;
-    long long row;
-    if (DOWN) {
-      row = row_start + mm;
-    } else {
-      row = seg < a.E ? a.sorted_assign[row_start + mm] / a.k : mm;
-    }
-    xsrc[i] = a.X + row * a.K + kc_ld * 8;
-  }
-  const uint16_t* wsrc[WCH];
-#pragma unroll
-  for (int i = 0; i < WCH; ++i) {
-    const int rho = (tid >> 3) + 32 * i;
+  for (int j = 0; j < QWW; ++j) {
+    const int q = wave * QWW + j;
+    const int rho = RI * q + lane / ROWCH;
     int wr;
     if (SWIGLU) {
       const int half = BN / 2;
@@ -135,79 +178,134 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs a) {
       const int nn = nt * BN + rho;
       wr = nn < a.Wrows ? nn : a.Wrows - 1;
     }
-    wsrc[i] = a.W + ((long long)seg * a.Wrows + wr) * a.K + kc_ld * 8;
+    woff[j] = ((uint32_t)wr * (uint32_t)a.K + (uint32_t)kc_dma(q) * 8u) * 2u;
   }
-
-  u32x4 xr[XCH], wreg[WCH];
-  auto load_tile = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < WCH; ++i) wreg[i] = *(const u32x4*)(wsrc[i] + kt * BK);
+  for (int j = 0; j < QWX; ++j) {
+    const int q = BN / RI + wave * QWX + j;
+    const int rr = RI * q + lane / ROWCH - BN;
+    const int m = mt * BM + rr;
+    const int mm = m < seg_rows ? m : seg_rows - 1;
+    uint32_t row;
+    if (DOWN) row = (uint32_t)mm;
+    else row = seg < a.E ? (uint32_t)(a.sorted_assign[row_start + mm] / a.k) : (uint32_t)mm;
+    xoff[j] = (row * (uint32_t)a.K + (uint32_t)kc_dma(q) * 8u) * 2u;
+  }
+  // Fragment rows are 32-aligned bases plus lane & 31, so the swizzle term
+  // depends on the lane only: one per-lane offset per k-substep.
+  int fro[NSUB];
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) xr[i] = *(const u32x4*)(xsrc[i] + kt * BK);
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < WCH; ++i) {
-      const int rho = (tid >> 3) + 32 * i;
-      smem[buf][rho * 8 + (kc_ld ^ (rho & 7))] = DOWN ? bf16x8_to_f16x8(wreg[i]) : wreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int rho = (tid >> 3) + 32 * i;
-      smem[buf][BN * 8 + rho * 8 + (kc_ld ^ (rho & 7))] = xr[i];
-    }
-  };
-
-  // LDS rows of this wave's fragments
-  int wrow[NI], xrow[MI];
+  for (int s4 = 0; s4 < NSUB; ++s4)
+    fro[s4] = (lane & 31) * ROWCH + ((2 * s4 + (lane >> 5)) ^ (((lane & 31) / RPB) % ROWCH));
+  int wrb[NI], xrb[MI];  // 32-row base of each fragment, in chunks
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     if (SWIGLU) {
       const int jj = j < NI / 2 ? j : j - NI / 2;
-      wrow[j] = (j < NI / 2 ? 0 : BN / 2) + wn * (BN / 4) + jj * 32 + (lane & 31);
+      wrb[j] = ((j < NI / 2 ? 0 : BN / 2) + wn * (BN / 2 / WGN) + jj * 32) * ROWCH;
     } else {
-      wrow[j] = wn * WN + j * 32 + (lane & 31);
+      wrb[j] = (wn * WN + j * 32) * ROWCH;
     }
   }
 #pragma unroll
-  for (int i = 0; i < MI; ++i) xrow[i] = wm * WM + i * 32 + (lane & 31);
+  for (int i = 0; i < MI; ++i) xrb[i] = (BN + wm * WM + i * 32) * ROWCH;
+
+  typedef __attribute__((address_space(3))) void lds_void_t;
+  auto dma = [&](u32x4* buf, int kt) {
+    const char* wb = wbase + kt * (BK * 2);
+    const char* xb = xbase + kt * (BK * 2);
+    u32x4* wdst = buf + wv * QWW * 64;
+    u32x4* xdst = buf + BN * ROWCH + wv * QWX * 64;
+#pragma unroll
+    for (int j = 0; j < QWW; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(wb + woff[j]), (lds_void_t*)(wdst + j * 64),
+                                       16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < QWX; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(xb + xoff[j]), (lds_void_t*)(xdst + j * 64),
+                                       16, 0, 0);
+  };
+  auto frag_load = [&](const u32x4* buf, u32x4(&wf)[NI], u32x4(&xf)[MI], int s4) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) wf[j] = buf[wrb[j] + fro[s4]];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) xf[i] = buf[xrb[i] + fro[s4]];
+  };
 
   f32x16 acc[NI][MI];
 #pragma unroll
   for (int j = 0; j < NI; ++j)
 #pragma unroll
     for (int i = 0; i < MI; ++i) acc[j][i] = f32x16{};
-
-  const int nk = a.K / BK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_tile(kt + 1);
+  auto mfmas = [&](const u32x4(&wf)[NI], const u32x4(&xf)[MI]) {
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int kc = 2 * s + (lane >> 5);
-      u32x4 wf[NI], xf[MI];
+    for (int j = 0; j < NI; ++j) {
+      // the down projection's W2 tile is bf16 in LDS: fp16 for the fp16 MFMA
+      const u32x4 w = DOWN ? bf16x8_to_f16x8(wf[j]) : wf[j];
 #pragma unroll
-      for (int j = 0; j < NI; ++j) wf[j] = smem[cur][wrow[j] * 8 + (kc ^ (wrow[j] & 7))];
-#pragma unroll
-      for (int i = 0; i < MI; ++i) xf[i] = smem[cur][BN * 8 + xrow[i] * 8 + (kc ^ (xrow[i] & 7))];
-#pragma unroll
-      for (int j = 0; j < NI; ++j)
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-          if (DOWN)
-            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                __builtin_bit_cast(f16x8, wf[j]), __builtin_bit_cast(f16x8, xf[i]), acc[j][i], 0, 0, 0);
-          else
-            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, wf[j]), __builtin_bit_cast(bf16x8, xf[i]), acc[j][i], 0, 0, 0);
-        }
+      for (int i = 0; i < MI; ++i) {
+        if (DOWN)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              __builtin_bit_cast(f16x8, w), __builtin_bit_cast(f16x8, xf[i]), acc[j][i], 0, 0, 0);
+        else
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, xf[i]), acc[j][i], 0, 0, 0);
+      }
     }
-    if (kt + 1 < nk) store_tile(cur ^ 1);
-    __syncthreads();
+  };
+
+  // ---- main loop over k-tiles with an NSTAGE ring in LDS.  Iteration kt
+  // issues the DMA of tile kt+3 into the stage of tile kt-1 (all its reads
+  // finished before the previous barrier), computes tile kt, then waits until
+  // tile kt+1 has landed (the DMAs of tiles kt+2 and kt+3 may stay in
+  // flight: vmcnt(2 * DMAs per tile)) and crosses the barrier.  The last
+  // k-substep's MFMAs run after the barrier, under the fragment reads of the
+  // next tile, so the matrix pipe does not drain at tile boundaries.  The
+  // loop body is straight-line: DMAs past the last tile are clamped to it
+  // (into stages nobody reads again) and the tail iterations are peeled.
+  const int nk = a.K / BK;
+  constexpr int NDMA = QWW + QWX;
+  static_assert(2 * NDMA <= 63, "vmcnt range");
+  // s_waitcnt immediate: vmcnt = 2*NDMA, expcnt and lgkmcnt = 0 (every
+  // fragment read of this tile has completed before the barrier).
+  constexpr int WAIT_IMM = ((2 * NDMA) & 15) | (((2 * NDMA) >> 4) << 14);
+  u32x4 wf[2][NI], xf[2][MI];
+  auto clampk = [&](int t) { return t < nk ? t : nk - 1; };
+  dma(lds0, 0);
+  dma(lds1, clampk(1));
+  dma(lds2, clampk(2));
+  __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+  frag_load(lds0, wf[0], xf[0], 0);
+  auto iteration = [&](const u32x4* cur, const u32x4* next, u32x4* far, int kt) {
+    dma(far, clampk(kt + 3));
+#pragma unroll
+    for (int s4 = 0; s4 + 1 < NSUB; ++s4) {
+      frag_load(cur, wf[(s4 + 1) & 1], xf[(s4 + 1) & 1], s4 + 1);
+      mfmas(wf[s4 & 1], xf[s4 & 1]);
+    }
+    // substep 0: the DMA interleaved with its MFMAs and the next fragments
+    sched_interleave<NM, SG_VMEM_READ, NDMA, SG_DS_READ, NFR>();
+#pragma unroll
+    for (int s4 = 1; s4 + 1 < NSUB; ++s4) sched_interleave<NM, SG_DS_READ, NFR, SG_VMEM_READ, 0>();
+    __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");   // no LDS read moves above the barrier
+    frag_load(next, wf[0], xf[0], 0);
+    mfmas(wf[(NSUB - 1) & 1], xf[(NSUB - 1) & 1]);
+    sched_interleave<NM, SG_DS_READ, NFR, SG_VMEM_READ, 0>();
+  };
+  int kt = 0;
+  for (; kt + 3 < nk; kt += 4) {
+    iteration(lds0, lds1, lds3, kt);
+    iteration(lds1, lds2, lds0, kt + 1);
+    iteration(lds2, lds3, lds1, kt + 2);
+    iteration(lds3, lds0, lds2, kt + 3);
   }
+  if (kt < nk) iteration(lds0, lds1, lds3, kt);
+  if (kt + 1 < nk) iteration(lds1, lds2, lds0, kt + 1);
+  if (kt + 2 < nk) iteration(lds2, lds3, lds1, kt + 2);
 
   // ---- epilogue: lane holds token row (lane & 31) of each 32x32 tile and, in
   // register group g, the four consecutive weight rows 8g + 4*(lane>>5) + 0..3.
@@ -222,7 +320,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int nloc = j * 32 + 8 * g + 4 * (lane >> 5);
-        const int col = SWIGLU ? nt * (BN / 2) + wn * (BN / 4) + nloc : nt * BN + wn * WN + nloc;
+        const int col = SWIGLU ? nt * (BN / 2) + wn * (BN / 2 / WGN) + nloc : nt * BN + wn * WN + nloc;
         if (!valid || col >= a.Nout) continue;
         float v[4];
 #pragma unroll
@@ -298,9 +396,33 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* X, const flo
   out[r * Nout + n] = v;
 }
 
-// Block tiles per projection.
-constexpr int UP_BM = 256, UP_BN = 256;
-constexpr int DN_BM = 128, DN_BN = 128;
+// Block tiles per projection (token rows x weight rows).
+#ifndef MOE_UP_BM
+#define MOE_UP_BM 256
+#endif
+#ifndef MOE_UP_BN
+#define MOE_UP_BN 256
+#endif
+#ifndef MOE_DN_BM
+#define MOE_DN_BM 256
+#endif
+#ifndef MOE_DN_BN
+#define MOE_DN_BN 256
+#endif
+#ifndef MOE_UP_WGM
+#define MOE_UP_WGM 4
+#endif
+#ifndef MOE_UP_WGN
+#define MOE_UP_WGN 2
+#endif
+#ifndef MOE_DN_WGM
+#define MOE_DN_WGM 2
+#endif
+#ifndef MOE_DN_WGN
+#define MOE_DN_WGN 4
+#endif
+constexpr int UP_BM = MOE_UP_BM, UP_BN = MOE_UP_BN, UP_WGM = MOE_UP_WGM, UP_WGN = MOE_UP_WGN;
+constexpr int DN_BM = MOE_DN_BM, DN_BN = MOE_DN_BN, DN_WGM = MOE_DN_WGM, DN_WGN = MOE_DN_WGN;
 
 int grid_blocks(const Shape& s, int BM, int NT) {
   const long long mt = ((long long)s.T * s.k + BM - 1) / BM + s.E +
@@ -346,13 +468,16 @@ hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void
              sorted_assign, s.T, s.k, s.E, s.S, s.d, s.f, s.up_rows(), s.f};
   if (s.act == MOE_SWIGLU) {
     const int NT = (s.f + UP_BN / 2 - 1) / (UP_BN / 2);
-    grouped_gemm_kernel<UP_BM, UP_BN, MODE_SWIGLU><<<grid_blocks(s, UP_BM, NT), 256, 0, st>>>(a);
+    grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_SWIGLU>
+        <<<grid_blocks(s, UP_BM, NT), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
   } else {
     const int NT = (s.f + UP_BN - 1) / UP_BN;
     if (s.act == MOE_RELU)
-      grouped_gemm_kernel<UP_BM, UP_BN, MODE_RELU><<<grid_blocks(s, UP_BM, NT), 256, 0, st>>>(a);
+      grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_RELU>
+          <<<grid_blocks(s, UP_BM, NT), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
     else
-      grouped_gemm_kernel<UP_BM, UP_BN, MODE_GELU><<<grid_blocks(s, UP_BM, NT), 256, 0, st>>>(a);
+      grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_GELU>
+          <<<grid_blocks(s, UP_BM, NT), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
   }
   return hipGetLastError();
 }
@@ -372,7 +497,8 @@ hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const 
   GemmArgs a{(const uint16_t*)h, (const uint16_t*)w_down, (const uint16_t*)bias, y_exp, offsets,
              nullptr, s.T, s.k, s.E, s.S, s.f, s.d, s.d, s.f};
   const int NT = (s.d + DN_BN - 1) / DN_BN;
-  grouped_gemm_kernel<DN_BM, DN_BN, MODE_DOWN><<<grid_blocks(s, DN_BM, NT), 256, 0, st>>>(a);
+  grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DOWN>
+      <<<grid_blocks(s, DN_BM, NT), 64 * DN_WGM * DN_WGN, 0, st>>>(a);
   return hipGetLastError();
 }
 

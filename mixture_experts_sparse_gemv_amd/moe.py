@@ -53,10 +53,10 @@ class MoeError(RuntimeError):
         super().__init__(f"{fn}: {msg}")
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
-    lib = ctypes.CDLL(LIB_PATH)
+def _load(path=LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
     P, V, I32, SZ = ctypes.POINTER, ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     pp, pw, pr = P(moe_problem), P(moe_weights), P(moe_routing)
     sig = {
