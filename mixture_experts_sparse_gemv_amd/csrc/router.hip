@@ -6,12 +6,13 @@
 //   top-k by descending score, ties to the lower expert index; weights =
 //   selected scores / their sum                              (0539edu 2.1; kamacoder 三)
 //
-// A block handles 16 tokens with 4 waves.  For bf16 inputs the router
+// A block handles 16 tokens with 8 waves.  For bf16 inputs the router
 // product runs on bf16 MFMA 16x16x32 (A = 16 router rows, B = 16 token rows),
-// each wave covering every 4th 32-wide K step; the four partial logit tiles
-// are summed in LDS in a fixed order.  The gate and the top-k then run one
-// token per wave pass with one lane per expert (E <= 64): wave-wide max and
-// sum by butterfly shuffles, and k rounds of a wave-wide argmax in which the
+// each wave covering every 8th 32-wide K step and issuing the loads of 8
+// steps at once; the eight partial logit tiles are summed in LDS in a fixed
+// order.  The gate and the top-k then run one token per wave pass (two
+// tokens per wave) with one lane per expert (E <= 64): wave-wide max and sum
+// by butterfly shuffles, and k rounds of a wave-wide argmax in which the
 // lower lane wins a tie.  Experts are ranked by logit (monotone in both
 // gates, so ranking and weights match ranking by score).  Each block also
 // writes the sum of its 16 tokens' probabilities per expert (token order);
@@ -22,6 +23,8 @@ namespace moe {
 namespace {
 
 constexpr int RT = kRouterTokens;  // 16 tokens per block
+constexpr int RW = 8;              // waves per block
+constexpr int RB = 8;              // K steps whose loads a wave issues together
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -55,9 +58,9 @@ struct RouterArgs {
 };
 
 template <int NE16>  // expert tiles of 16 (bf16 path); 0 = fp32 path
-__global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
-  __shared__ float red[4][RT][kMaxExperts + 1];
-  __shared__ float colp[4][kMaxExperts];
+__global__ __launch_bounds__(64 * RW) void router_kernel(RouterArgs a) {
+  __shared__ float red[RW][RT][kMaxExperts + 1];
+  __shared__ float colp[RW][kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * RT;
   const int E = a.E;
@@ -79,15 +82,23 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
 #pragma unroll
     for (int j = 0; j < NE16; ++j) acc[j] = f32x4{};
     const int nsteps = a.d / 32;
-#pragma unroll 4
-    for (int s = wave; s < nsteps; s += 4) {
-      const u32x4 xv = *(const u32x4*)(xp + s * 32);
+    for (int s0 = wave; s0 < nsteps; s0 += RW * RB) {
+      u32x4 xv[RB], wv[RB][NE16 > 0 ? NE16 : 1];
 #pragma unroll
-      for (int j = 0; j < NE16; ++j) {
-        const u32x4 wv = *(const u32x4*)(wp[j] + s * 32);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv),
-                                                         __builtin_bit_cast(bf16x8, xv), acc[j],
-                                                         0, 0, 0);
+      for (int b = 0; b < RB; ++b) {
+        const int s = min(s0 + b * RW, nsteps - 1);   // clamped; masked below
+        xv[b] = *(const u32x4*)(xp + s * 32);
+#pragma unroll
+        for (int j = 0; j < NE16; ++j) wv[b][j] = *(const u32x4*)(wp[j] + s * 32);
+      }
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        if (s0 + b * RW >= nsteps) break;   // uniform
+#pragma unroll
+        for (int j = 0; j < NE16; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[b][j]),
+                                                           __builtin_bit_cast(bf16x8, xv[b]),
+                                                           acc[j], 0, 0, 0);
       }
     }
     // D[expert][token]: lane holds token lane & 15, experts 16j + 4*(lane>>4) + r
@@ -99,7 +110,7 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
     // ---- fp32: one thread per (token, expert) dot product
     const float* x = (const float*)a.x;
     const float* wr = (const float*)a.wr;
-    for (int p = tid; p < RT * kMaxExperts; p += 256) {
+    for (int p = tid; p < RT * kMaxExperts; p += 64 * RW) {
       const int tl = p / kMaxExperts, e = p % kMaxExperts;
       float z = 0.f;
       if (e < E && t0 + tl < a.T) {
@@ -108,14 +119,13 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
         for (int j = 0; j < a.d; ++j) z = fmaf(xr[j], wrow[j], z);
       }
       red[0][tl][e] = z;
-      red[1][tl][e] = 0.f;
-      red[2][tl][e] = 0.f;
-      red[3][tl][e] = 0.f;
+#pragma unroll
+      for (int w = 1; w < RW; ++w) red[w][tl][e] = 0.f;
     }
   }
   __syncthreads();
 
-  // ---- gate + top-k: wave w handles tokens 4w .. 4w+3, lane = expert
+  // ---- gate + top-k: wave w handles tokens 2w, 2w+1; lane = expert
   float bias = 0.f;
   if (a.br && lane < E)
     bias = a.dtype == MOE_BF16 ? bf16_to_f32(((const uint16_t*)a.br)[lane])
@@ -123,12 +133,17 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   const float NEG_INF = -__builtin_inff();
   float psum = 0.f;
 #pragma unroll 1
-  for (int i = 0; i < 4; ++i) {
-    const int tl = wave * 4 + i;
+  for (int i = 0; i < RT / RW; ++i) {
+    const int tl = wave * (RT / RW) + i;
     const int t = t0 + tl;
     if (t >= a.T) break;
     float l = NEG_INF;
-    if (lane < E) l = ((red[0][tl][lane] + red[1][tl][lane]) + red[2][tl][lane]) + red[3][tl][lane] + bias;
+    if (lane < E) {
+      float z = red[0][tl][lane];
+#pragma unroll
+      for (int w = 1; w < RW; ++w) z += red[w][tl][lane];   // fixed order
+      l = z + bias;
+    }
     float score, denom;
     if (a.gating == MOE_SOFTMAX) {
       const float mx = wave_max(l);
@@ -163,8 +178,12 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   }
   colp[wave][lane] = psum;
   __syncthreads();
-  if (tid < E)
-    a.prob_part[(long long)blockIdx.x * E + tid] = ((colp[0][tid] + colp[1][tid]) + colp[2][tid]) + colp[3][tid];
+  if (tid < E) {
+    float c = colp[0][tid];
+#pragma unroll
+    for (int w = 1; w < RW; ++w) c += colp[w][tid];   // wave order = token order
+    a.prob_part[(long long)blockIdx.x * E + tid] = c;
+  }
 }
 
 // colsum[e] = sum over router blocks b (in order, 256 strided partial sums
@@ -193,13 +212,13 @@ hipError_t launch_router(const Shape& s, const void* x, const void* wr, const vo
                s.T, s.d, s.E, s.k, s.gating, s.dtype};
   const int blocks = router_blocks(s);
   if (s.dtype == MOE_F32) {
-    router_kernel<0><<<blocks, 256, 0, st>>>(a);
+    router_kernel<0><<<blocks, 64 * RW, 0, st>>>(a);
   } else {
     const int ne16 = (s.E + 15) / 16;
-    if (ne16 == 1) router_kernel<1><<<blocks, 256, 0, st>>>(a);
-    else if (ne16 == 2) router_kernel<2><<<blocks, 256, 0, st>>>(a);
-    else if (ne16 == 3) router_kernel<3><<<blocks, 256, 0, st>>>(a);
-    else router_kernel<4><<<blocks, 256, 0, st>>>(a);
+    if (ne16 == 1) router_kernel<1><<<blocks, 64 * RW, 0, st>>>(a);
+    else if (ne16 == 2) router_kernel<2><<<blocks, 64 * RW, 0, st>>>(a);
+    else if (ne16 == 3) router_kernel<3><<<blocks, 64 * RW, 0, st>>>(a);
+    else router_kernel<4><<<blocks, 64 * RW, 0, st>>>(a);
   }
   return hipGetLastError();
 }
