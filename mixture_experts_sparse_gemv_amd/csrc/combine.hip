@@ -5,6 +5,8 @@
 // One thread per 4 consecutive outputs of a token (16-byte loads and
 // stores); the sum runs in slot order, then shared-expert order, so the
 // result does not depend on scheduling.  Every element of y is written.
+// When the down projection ran in K slices, a row of y_exp is its slice-0
+// value plus the other slices' partials, added here in slice order.
 #include "moe_internal.h"
 
 namespace moe {
@@ -15,6 +17,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ assign_row,
                                                       const int32_t* __restrict__ offsets,
                                                       const float* __restrict__ y_exp,
+                                                      const float* __restrict__ y_part,
+                                                      int nparts, long long part_elems,
                                                       float* __restrict__ y, int T, int d, int k,
                                                       int E, int S) {
   const int dv = d / VEC;
@@ -23,18 +27,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int t = (int)(gid / dv);
   const int c = (int)(gid % dv) * VEC;
   typedef float vec_t __attribute__((ext_vector_type(VEC)));
+  // row value: y_exp plus the K-slice partials, in slice order
+  auto row = [&](long long r) {
+    vec_t v = *(const vec_t*)(y_exp + r * d + c);
+    for (int p = 0; p < nparts; ++p) v += *(const vec_t*)(y_part + p * part_elems + r * d + c);
+    return v;
+  };
   vec_t acc = {};
   for (int s = 0; s < k; ++s) {
     const int r = assign_row[(long long)t * k + s];
-    if (r >= 0) {
-      const float w = topk_w[(long long)t * k + s];
-      acc += w * *(const vec_t*)(y_exp + (long long)r * d + c);
-    }
+    if (r >= 0) acc += topk_w[(long long)t * k + s] * row(r);
   }
   if (S > 0) {
     const long long base = offsets[E];
-    for (int q = 0; q < S; ++q)
-      acc += *(const vec_t*)(y_exp + (base + (long long)q * T + t) * d + c);
+    for (int q = 0; q < S; ++q) acc += row(base + (long long)q * T + t);
   }
   *(vec_t*)(y + (long long)t * d + c) = acc;
 }
@@ -42,15 +48,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }  // namespace
 
 hipError_t launch_combine(const Shape& s, const float* topk_w, const int32_t* assign_row,
-                          const int32_t* offsets, const float* y_exp, float* y, hipStream_t st) {
+                          const int32_t* offsets, const float* y_exp, const float* y_part,
+                          int nparts, float* y, hipStream_t st) {
+  const long long part_elems = s.max_rows() * s.d;
   if (s.d % 4 == 0) {
     const long long n = (long long)s.T * (s.d / 4);
-    combine_kernel<4><<<(int)((n + 255) / 256), 256, 0, st>>>(topk_w, assign_row, offsets, y_exp,
-                                                              y, s.T, s.d, s.k, s.E, s.S);
+    combine_kernel<4><<<(int)((n + 255) / 256), 256, 0, st>>>(
+        topk_w, assign_row, offsets, y_exp, y_part, nparts, part_elems, y, s.T, s.d, s.k, s.E, s.S);
   } else {
     const long long n = (long long)s.T * s.d;
-    combine_kernel<1><<<(int)((n + 255) / 256), 256, 0, st>>>(topk_w, assign_row, offsets, y_exp,
-                                                              y, s.T, s.d, s.k, s.E, s.S);
+    combine_kernel<1><<<(int)((n + 255) / 256), 256, 0, st>>>(
+        topk_w, assign_row, offsets, y_exp, y_part, nparts, part_elems, y, s.T, s.d, s.k, s.E, s.S);
   }
   return hipGetLastError();
 }

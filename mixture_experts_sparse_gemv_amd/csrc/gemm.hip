@@ -38,6 +38,10 @@ struct GemmArgs {
   const int32_t* offsets;  // [E + 1]
   const int32_t* sorted_assign;
   int T, k, E, S, K, Nout, Wrows, f;
+  // down only: K slices; slice i > 0 writes to out2 + (i - 1) * part_elems
+  int ksplit;
+  float* out2;
+  long long part_elems;
 };
 
 // Per-segment row count and first row.
@@ -130,11 +134,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_kernel(GemmArg
     if (lane == 63) seg_tile[nseg] = incl;
   }
   __syncthreads();
-  const int total = seg_tile[nseg] * NT;
+  // Tiles per K slice; with several slices the slice is the slowest index.
+  const int nsplit = DOWN ? a.ksplit : 1;
+  const int tiles = seg_tile[nseg] * NT;
+  const int total = tiles * nsplit;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int per = (total + 7) >> 3;
-  const int L = xcd * per + slot;
-  if (slot >= per || L >= total) return;  // uniform over the block
+  const int LL = xcd * per + slot;
+  if (slot >= per || LL >= total) return;  // uniform over the block
+  const int ks = LL / tiles;               // K slice
+  const int L = LL - ks * tiles;
   if (tid < nseg && seg_tile[tid] * NT <= L && L < seg_tile[tid + 1] * NT) sh_seg = tid;
   __syncthreads();
   const int seg = sh_seg;
@@ -158,10 +167,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_kernel(GemmArg
   // Wave w issues the W instructions q = w*QWW + j and the token-row
   // instructions q = BN/RI + w*QWX + j.
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int kslice = a.K / nsplit;         // K elements of this block's slice
   const char* xbase;
-  if (DOWN) xbase = (const char*)(a.X + (long long)row_start * a.K);
+  if (DOWN) xbase = (const char*)(a.X + (long long)row_start * a.K + (long long)ks * kslice);
   else xbase = (const char*)a.X;
-  const char* wbase = (const char*)(a.W + (long long)seg * a.Wrows * a.K);
+  const char* wbase = (const char*)(a.W + (long long)seg * a.Wrows * a.K + (long long)ks * kslice);
   auto kc_dma = [&](int q) { return (lane % ROWCH) ^ ((4 * q + lane / 16) % ROWCH); };
   uint32_t woff[QWW], xoff[QWX];   // byte offsets of this lane's source chunks
 #pragma unroll
@@ -263,7 +273,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_kernel(GemmArg
   // next tile, so the matrix pipe does not drain at tile boundaries.  The
   // loop body is straight-line: DMAs past the last tile are clamped to it
   // (into stages nobody reads again) and the tail iterations are peeled.
-  const int nk = a.K / BK;
+  const int nk = kslice / BK;
   constexpr int NDMA = QWW + QWX;
   static_assert(2 * NDMA <= 63, "vmcnt range");
   // s_waitcnt immediate: vmcnt = 2*NDMA, expcnt and lgkmcnt = 0 (every
@@ -307,46 +317,77 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_kernel(GemmArg
   if (kt + 1 < nk) iteration(lds1, lds2, lds0, kt + 1);
   if (kt + 2 < nk) iteration(lds2, lds3, lds1, kt + 2);
 
-  // ---- epilogue: lane holds token row (lane & 31) of each 32x32 tile and, in
-  // register group g, the four consecutive weight rows 8g + 4*(lane>>5) + 0..3.
+  // ---- epilogue.  Lane holds token row (lane & 31) of each 32x32 tile and,
+  // in register group g, the four consecutive weight rows 8g + 4*(lane>>5) +
+  // 0..3.  Stored directly, one instruction would touch 32 rows with 16-32
+  // bytes each; instead each wave stages one 32-row slab of its output (after
+  // bias and activation, in the output type) in a padded LDS region and
+  // writes it back as whole 16-byte chunks of rows, CPR lanes per row, so a
+  // store instruction covers RPI rows of contiguous bytes.  The padding keeps
+  // the staging writes and reads free of bank conflicts.
   constexpr int NJ = SWIGLU ? NI / 2 : NI;
+  constexpr int WNOUT = NJ * 32;                       // output columns of a wave
+  constexpr int ES = DOWN ? 4 : 2;                      // output element bytes
+  constexpr int PITCH = WNOUT * ES + (DOWN ? 16 : 8);   // staging row pitch, bytes
+  constexpr int CPR = WNOUT * ES / 16;                  // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;                         // rows per store instruction
+  constexpr int STG = 32 * PITCH;                       // staging bytes per wave
+  constexpr int WPA = (int)(sizeof(lds0) / STG);        // waves per ring array
+  static_assert(CPR >= 1 && CPR <= 64 && 64 % CPR == 0 && 32 % RPI == 0, "staging shape");
+  static_assert(WPA * 4 >= NW, "staging must fit in the LDS ring");
+  // Every DMA (including the clamped ones past the last tile) has landed and
+  // every wave's last fragment reads are done before the ring is reused.
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+  const int wa = wv / WPA;
+  char* stg = (char*)(wa == 0 ? lds0 : wa == 1 ? lds1 : wa == 2 ? lds2 : lds3) + (wv % WPA) * STG;
+  const int colw = SWIGLU ? nt * (BN / 2) + wn * (BN / 2 / WGN) : nt * BN + wn * WN;
+  char* obase = ks == 0 ? (char*)a.out : (char*)(a.out2 + (long long)(ks - 1) * a.part_elems);
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
+  for (int i = 0; i < MI; ++i) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int m = mt * BM + wm * WM + i * 32 + (lane & 31);
-      const bool valid = m < seg_rows;
-      const long long orow = (long long)row_start + m;
+    for (int j = 0; j < NJ; ++j) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int nloc = j * 32 + 8 * g + 4 * (lane >> 5);
-        const int col = SWIGLU ? nt * (BN / 2) + wn * (BN / 2 / WGN) + nloc : nt * BN + wn * WN + nloc;
-        if (!valid || col >= a.Nout) continue;
+        const int col = colw + nloc;
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = acc[j][i][4 * g + r];
         if (SWIGLU) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = silu_f(v[r]) * acc[j + NI / 2][i][4 * g + r];
-        } else if (a.bias) {
+        } else if (a.bias && ks == 0 && col < a.Nout) {
           const u32x2 b = *(const u32x2*)(a.bias + (long long)seg * a.Wrows + col);
           v[0] += __uint_as_float(b[0] << 16);
           v[1] += __uint_as_float(b[0] & 0xffff0000u);
           v[2] += __uint_as_float(b[1] << 16);
           v[3] += __uint_as_float(b[1] & 0xffff0000u);
         }
+        char* dst = stg + (lane & 31) * PITCH + nloc * ES;
         if (DOWN) {
-          *(f32x4*)((float*)a.out + orow * a.Nout + col) = f32x4{v[0], v[1], v[2], v[3]};
+          *(f32x4*)dst = f32x4{v[0], v[1], v[2], v[3]};
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             if (MODE == MODE_RELU) v[r] = fmaxf(v[r], 0.0f);
             if (MODE == MODE_GELU) v[r] = gelu_f(v[r]);
           }
-          f16x4 hv = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-          *(f16x4*)((_Float16*)a.out + orow * a.Nout + col) = hv;
+          *(f16x4*)dst = f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
         }
       }
+    }
+    // LDS operations of one wave complete in order: the reads below see the
+    // writes above, and the next slab's writes follow these reads.
+#pragma unroll
+    for (int q = 0; q < 32 / RPI; ++q) {
+      const int r = q * RPI + lane / CPR, c = lane % CPR;
+      const u32x4 val = *(const u32x4*)(stg + r * PITCH + c * 16);
+      const int m = mt * BM + wm * WM + i * 32 + r;
+      const int col = colw + c * (16 / ES);
+      if (m < seg_rows && col < a.Nout)
+        *(u32x4*)(obase + ((long long)(row_start + m) * a.Nout + col) * ES) = val;
     }
   }
 }
@@ -424,14 +465,48 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* X, const flo
 constexpr int UP_BM = MOE_UP_BM, UP_BN = MOE_UP_BN, UP_WGM = MOE_UP_WGM, UP_WGN = MOE_UP_WGN;
 constexpr int DN_BM = MOE_DN_BM, DN_BN = MOE_DN_BN, DN_WGM = MOE_DN_WGM, DN_WGN = MOE_DN_WGN;
 
-int grid_blocks(const Shape& s, int BM, int NT) {
+int grid_blocks(const Shape& s, int BM, int NT, int ksplit = 1) {
   const long long mt = ((long long)s.T * s.k + BM - 1) / BM + s.E +
                        (long long)s.S * ((s.T + BM - 1) / BM);
-  const long long g = NT * mt;
+  const long long g = NT * mt * ksplit;
   return (int)((g + 7) / 8 * 8);
 }
 
+// y_exp[r] += the K-slice partials of row r, in slice order.
+__global__ __launch_bounds__(256) void part_fold_kernel(float* __restrict__ y_exp,
+                                                        const float* __restrict__ y_part,
+                                                        const int32_t* offsets, int T, int E,
+                                                        int S, int d, int nparts,
+                                                        long long part_elems) {
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int d4 = d / 4;
+  const long long r = gid / d4;
+  const int c = (int)(gid % d4) * 4;
+  if (r >= (long long)offsets[E] + (long long)S * T) return;
+  f32x4 v = *(const f32x4*)(y_exp + r * d + c);
+  for (int p = 0; p < nparts; ++p) v += *(const f32x4*)(y_part + p * part_elems + r * d + c);
+  *(f32x4*)(y_exp + r * d + c) = v;
+}
+
 }  // namespace
+
+int down_ksplit(const Shape& s) {
+  if (s.dtype != MOE_BF16 || s.decode()) return 1;
+  // expected tiles with evenly routed experts (capacity-limited)
+  long long per = ((long long)s.T * s.k + s.E - 1) / s.E;
+  if (s.cap > 0 && per > s.cap) per = s.cap;
+  const long long mt = (long long)s.E * ((per + DN_BM - 1) / DN_BM) +
+                       (long long)s.S * ((s.T + DN_BM - 1) / DN_BM);
+  const long long tiles = mt * ((s.d + DN_BN - 1) / DN_BN);
+  const int nkt = s.f / 32;   // k-tiles of the whole reduction
+  int ks = 1;
+  // split while the slices still fit in three quarters of the CUs and each
+  // slice keeps at least 8 k-tiles
+  while (ks < 4 && tiles * ks * 2 * 4 <= 3LL * kNumCUs && nkt % (ks * 2) == 0 &&
+         nkt / (ks * 2) >= 8)
+    ks *= 2;
+  return ks;
+}
 
 hipError_t launch_decode_up(const Shape& s, const void* x, const void* w_up, const void* b_up,
                             const int32_t* offsets, const int32_t* sorted_assign, void* h,
@@ -465,7 +540,7 @@ hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void
   }
   if (s.decode()) return launch_decode_up(s, x, w_up, b_up, offsets, sorted_assign, h, st);
   GemmArgs a{(const uint16_t*)x, (const uint16_t*)w_up, (const uint16_t*)bias, h, offsets,
-             sorted_assign, s.T, s.k, s.E, s.S, s.d, s.f, s.up_rows(), s.f};
+             sorted_assign, s.T, s.k, s.E, s.S, s.d, s.f, s.up_rows(), s.f, 1, nullptr, 0};
   if (s.act == MOE_SWIGLU) {
     const int NT = (s.f + UP_BN / 2 - 1) / (UP_BN / 2);
     grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_SWIGLU>
@@ -483,7 +558,8 @@ hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void
 }
 
 hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const void* b_down,
-                       const int32_t* offsets, float* y_exp, float* y_part, hipStream_t st) {
+                       const int32_t* offsets, float* y_exp, float* y_part, bool complete,
+                       hipStream_t st) {
   const void* bias = s.expert_bias() ? b_down : nullptr;
   if (s.dtype == MOE_F32) {
     const long long n = s.max_rows() * s.d;
@@ -494,11 +570,18 @@ hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const 
     return hipGetLastError();
   }
   if (s.decode()) return launch_decode_down(s, h, w_down, b_down, offsets, y_exp, y_part, st);
+  const int ks = down_ksplit(s);
+  const long long part_elems = s.max_rows() * s.d;
   GemmArgs a{(const uint16_t*)h, (const uint16_t*)w_down, (const uint16_t*)bias, y_exp, offsets,
-             nullptr, s.T, s.k, s.E, s.S, s.f, s.d, s.d, s.f};
+             nullptr, s.T, s.k, s.E, s.S, s.f, s.d, s.d, s.f, ks, y_part, part_elems};
   const int NT = (s.d + DN_BN - 1) / DN_BN;
   grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DOWN>
-      <<<grid_blocks(s, DN_BM, NT), 64 * DN_WGM * DN_WGN, 0, st>>>(a);
+      <<<grid_blocks(s, DN_BM, NT, ks), 64 * DN_WGM * DN_WGN, 0, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ks == 1 || !complete) return e;
+  const long long n = s.max_rows() * (s.d / 4);
+  part_fold_kernel<<<(int)((n + 255) / 256), 256, 0, st>>>(y_exp, y_part, offsets, s.T, s.E, s.S,
+                                                           s.d, ks - 1, part_elems);
   return hipGetLastError();
 }
 

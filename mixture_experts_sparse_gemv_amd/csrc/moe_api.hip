@@ -37,7 +37,8 @@ WsLayout ws_layout(const Shape& s) {
   w.l_aux = take(4);
   w.h = take(rows * s.f * (s.dtype == MOE_F32 ? 4 : 2));
   w.y_exp = take(rows * s.d * 4);
-  w.y_part = s.decode() ? take((size_t)kDecodeSplitK * rows * s.d * 4) : o;
+  const int nparts = s.decode() ? kDecodeSplitK : down_ksplit(s) - 1;
+  w.y_part = nparts > 0 ? take((size_t)nparts * rows * s.d * 4) : o;
   w.total = o;
   return w;
 }
@@ -182,7 +183,7 @@ moe_status moe_expert_down(const moe_problem* p, const moe_weights* w, const int
   if (!offsets || !h || !y_exp) return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(s, ws, ws_bytes, L)) != MOE_OK) return st;
   return fail_hip(launch_down(s, h, w->w_down, w->b_down, offsets, y_exp,
-                              at<float>(ws, L.y_part), stream));
+                              at<float>(ws, L.y_part), true, stream));
 }
 
 moe_status moe_expert_ffn(const moe_problem* p, const void* x, const moe_weights* w,
@@ -198,7 +199,8 @@ moe_status moe_expert_ffn(const moe_problem* p, const void* x, const moe_weights
   void* h = at<void>(ws, L.h);
   hipError_t e = launch_up(s, x, w->w_up, w->b_up, offsets, sorted_assign, h, stream);
   if (e == hipSuccess)
-    e = launch_down(s, h, w->w_down, w->b_down, offsets, y_exp, at<float>(ws, L.y_part), stream);
+    e = launch_down(s, h, w->w_down, w->b_down, offsets, y_exp, at<float>(ws, L.y_part), true,
+                    stream);
   return fail_hip(e);
 }
 
@@ -208,7 +210,7 @@ moe_status moe_combine(const moe_problem* p, const float* topk_w, const int32_t*
   moe_status st = check_problem(p, s);
   if (st != MOE_OK) return st;
   if (!topk_w || !assign_row || !offsets || !y_exp || !y) return MOE_ERR_INVALID_ARG;
-  return fail_hip(launch_combine(s, topk_w, assign_row, offsets, y_exp, y, stream));
+  return fail_hip(launch_combine(s, topk_w, assign_row, offsets, y_exp, nullptr, 0, y, stream));
 }
 
 moe_status moe_aux_stats(const moe_problem* p, const float* prob_colsum, const int32_t* counts,
@@ -253,9 +255,13 @@ moe_status moe_ffn_forward(const moe_problem* p, const moe_weights* w, const voi
     e = launch_dispatch(s, topk_idx, counts, kept, offsets, sorted_assign, assign_row, drop_mask,
                         part, at<float>(ws, L.prob_colsum), f, P, l_aux, stream);
   if (e == hipSuccess) e = launch_up(s, x, w->w_up, w->b_up, offsets, sorted_assign, h, stream);
+  // The down projection's K slices (if any) are summed by the combine.
+  float* y_part = at<float>(ws, L.y_part);
+  const int nparts = s.decode() ? 0 : down_ksplit(s) - 1;
   if (e == hipSuccess)
-    e = launch_down(s, h, w->w_down, w->b_down, offsets, y_exp, at<float>(ws, L.y_part), stream);
-  if (e == hipSuccess) e = launch_combine(s, topk_w, assign_row, offsets, y_exp, y, stream);
+    e = launch_down(s, h, w->w_down, w->b_down, offsets, y_exp, y_part, nparts == 0, stream);
+  if (e == hipSuccess)
+    e = launch_combine(s, topk_w, assign_row, offsets, y_exp, y_part, nparts, y, stream);
   return fail_hip(e);
 }
 

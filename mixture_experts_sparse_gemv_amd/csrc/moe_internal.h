@@ -14,6 +14,7 @@ constexpr int kMaxExperts = 64;       // routed experts: one wave lane per exper
 constexpr int kMaxTopK = 8;
 constexpr int kMaxSegments = 128;     // routed + shared experts
 constexpr int kDecodeMaxT = 16;       // T at or below which the streaming decode path runs
+constexpr int kNumCUs = 256;          // MI355X compute units (sizes the K split of small GEMMs)
 
 // ---------------------------------------------------------------- shape
 struct Shape {
@@ -33,6 +34,12 @@ inline int router_blocks(const Shape& s) { return (s.T + kRouterTokens - 1) / kR
 
 // Split of the reduction dimension in the decode down-projection.
 constexpr int kDecodeSplitK = 4;
+
+// K slices of the (non-decode) down projection: 1, 2 or 4.  More than one
+// when its expected tile count would leave most compute units idle; slice 0
+// is written to y_exp, slice i > 0 to y_part + (i - 1) * max_rows * d, and
+// the slices are summed in slice order (by the combine, or by a fold pass).
+int down_ksplit(const Shape& s);
 
 // ---------------------------------------------------------------- workspace
 struct WsLayout {
@@ -121,9 +128,15 @@ hipError_t launch_aux(const Shape& s, const float* colsum, const int32_t* counts
 hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void* b_up,
                      const int32_t* offsets, const int32_t* sorted_assign, void* h,
                      hipStream_t st);
+// complete = true: y_exp holds the whole result on return (K slices folded);
+// false: slices 1.. stay in y_part for the combine to add (down_ksplit(s) - 1
+// of them).
 hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const void* b_down,
-                       const int32_t* offsets, float* y_exp, float* y_part, hipStream_t st);
+                       const int32_t* offsets, float* y_exp, float* y_part, bool complete,
+                       hipStream_t st);
+// y_part/nparts: K-slice partials of y_exp still to be added (nparts = 0: none).
 hipError_t launch_combine(const Shape& s, const float* topk_w, const int32_t* assign_row,
-                          const int32_t* offsets, const float* y_exp, float* y, hipStream_t st);
+                          const int32_t* offsets, const float* y_exp, const float* y_part,
+                          int nparts, float* y, hipStream_t st);
 
 }  // namespace moe

@@ -185,3 +185,34 @@ def test_deterministic_and_no_out_of_bounds_writes():
         assert np.all(np.isfinite(yy[pad:-pad]))
         ys.append(yy[pad:-pad].copy())
     assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32)), "not bit-identical"
+
+
+@pytest.mark.parametrize("name", ["gpt2_T700", "swiglu_skew_T3000", "large_T300", "large_decode"])
+def test_stage_entry_points_equal_fused_forward(name):
+    """The per-stage entry points (router, dispatch, up, down with its K slices
+    folded, combine) give bit-identical y to the fused forward, which adds the
+    down projection's K slices inside the combine."""
+    run, inp = _inputs(name)
+    _say(f"[staged==forward] {name}")
+    g = gpu_inputs(inp)
+    p = problem_of(run)
+    T, k, E, d = run.T, run.top_k, run.num_experts, run.d_model
+    fwd = run_forward(run, g, p)
+    ws = M.workspace(p)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    idx, tw = torch.empty(T * k, **i32), torch.empty(T * k, device="cuda")
+    cnt, kept, off = torch.empty(E, **i32), torch.empty(E, **i32), torch.empty(E + 1, **i32)
+    sa, ar = torch.empty(T * k, **i32), torch.empty(T * k, **i32)
+    dm = torch.empty(T * k, dtype=torch.uint8, device="cuda")
+    w = weights_of(g)
+    M.moe_router_topk(p, g["x"], w, idx, tw, ws=ws)
+    M.moe_dispatch(p, idx, cnt, kept, off, sa, ar, dm)
+    h = torch.empty(M.max_rows(p) * run.d_ff, dtype=M.h_dtype(p), device="cuda")
+    y_exp = torch.empty(M.max_rows(p) * d, device="cuda")
+    M.moe_expert_up(p, g["x"], w, off, sa, h)
+    M.moe_expert_down(p, w, off, h, y_exp, ws)
+    y = torch.empty(T * d, device="cuda")
+    M.moe_combine(p, tw, ar, off, y_exp, y)
+    torch.cuda.synchronize()
+    ys = y.view(T, d).cpu().numpy()
+    assert np.array_equal(ys.view(np.uint32), fwd["y"].view(np.uint32)), "staged != forward"
