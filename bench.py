@@ -140,7 +140,7 @@ def main():
         M.moe_router_topk(p, g["x"], w, r["topk_idx"], r["topk_w"], None, part, ws=ws)
         rec(1)
         M.moe_dispatch(p, r["topk_idx"], r["counts"], r["kept"], r["offsets"],
-                       r["sorted_assign"], r["assign_row"], r["drop_mask"])
+                       r["sorted_assign"], r["assign_row"], r["drop_mask"], ws=ws)
         rec(2)
         M.moe_expert_up(p, g["x"], w, r["offsets"], r["sorted_assign"], h)
         rec(3)

@@ -155,7 +155,8 @@ moe_status moe_router_topk(const moe_problem* p, const void* x, const moe_weight
  *   drop_mask     [T*k]  out  1 if dropped
  * Results are exact integers (bit-identical to any correct implementation).
  * Out-of-range ids are clamped into [0, E) (the result is then unspecified).
- * ws is not used (may be NULL): the scratch of this step lives in LDS.
+ * ws: moe_workspace_size() bytes; holds the per-16-token expert counts and
+ * the per-512-token rank prefixes of the counting sort.
  */
 moe_status moe_dispatch(const moe_problem* p, const int32_t* topk_idx, int32_t* counts,
                         int32_t* kept, int32_t* offsets, int32_t* sorted_assign,

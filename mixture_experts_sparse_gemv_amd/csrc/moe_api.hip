@@ -25,6 +25,8 @@ WsLayout ws_layout(const Shape& s) {
   w.topk_idx = take(n * 4);
   w.topk_w = take(n * 4);
   w.prob_part = take((size_t)router_blocks(s) * s.E * 4);
+  w.chunk_counts = take((size_t)router_blocks(s) * s.E * 4);
+  w.sb_prefix = take((size_t)scatter_blocks(s) * s.E * 4);
   w.prob_colsum = take((size_t)s.E * 4);
   w.counts = take((size_t)s.E * 4);
   w.kept = take((size_t)s.E * 4);
@@ -135,7 +137,8 @@ moe_status moe_router_topk(const moe_problem* p, const void* x, const moe_weight
   if (!x || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(s, ws, ws_bytes, L)) != MOE_OK) return st;
   float* part = at<float>(ws, L.prob_part);
-  hipError_t e = launch_router(s, x, w->w_router, w->b_router, topk_idx, topk_w, probs, part, stream);
+  hipError_t e = launch_router(s, x, w->w_router, w->b_router, topk_idx, topk_w, probs, part,
+                               at<int32_t>(ws, L.chunk_counts), stream);
   if (e == hipSuccess && prob_colsum) e = launch_colsum(s, part, prob_colsum, stream);
   return fail_hip(e);
 }
@@ -150,11 +153,11 @@ moe_status moe_dispatch(const moe_problem* p, const int32_t* topk_idx, int32_t* 
   if (st != MOE_OK) return st;
   if (!topk_idx || !counts || !kept || !offsets || !sorted_assign || !assign_row || !drop_mask)
     return MOE_ERR_INVALID_ARG;
-  (void)ws;  // dispatch keeps its scratch in LDS
-  (void)ws_bytes;
-  (void)L;
-  return fail_hip(launch_dispatch(s, topk_idx, counts, kept, offsets, sorted_assign, assign_row,
-                                  drop_mask, nullptr, nullptr, nullptr, nullptr, nullptr, stream));
+  if ((st = check_ws(s, ws, ws_bytes, L)) != MOE_OK) return st;
+  return fail_hip(launch_dispatch(s, topk_idx, at<int32_t>(ws, L.chunk_counts), false,
+                                  at<int32_t>(ws, L.sb_prefix), counts, kept, offsets,
+                                  sorted_assign, assign_row, drop_mask, nullptr, nullptr, nullptr,
+                                  nullptr, nullptr, stream));
 }
 
 moe_status moe_expert_up(const moe_problem* p, const void* x, const moe_weights* w,
@@ -249,11 +252,13 @@ moe_status moe_ffn_forward(const moe_problem* p, const moe_weights* w, const voi
   void* h = at<void>(ws, L.h);
   float* y_exp = at<float>(ws, L.y_exp);
 
+  int32_t* chunk_counts = at<int32_t>(ws, L.chunk_counts);
   hipError_t e = launch_router(s, x, w->w_router, w->b_router, topk_idx, topk_w, r.probs, part,
-                               stream);
+                               chunk_counts, stream);
   if (e == hipSuccess)
-    e = launch_dispatch(s, topk_idx, counts, kept, offsets, sorted_assign, assign_row, drop_mask,
-                        part, at<float>(ws, L.prob_colsum), f, P, l_aux, stream);
+    e = launch_dispatch(s, topk_idx, chunk_counts, true, at<int32_t>(ws, L.sb_prefix), counts,
+                        kept, offsets, sorted_assign, assign_row, drop_mask, part,
+                        at<float>(ws, L.prob_colsum), f, P, l_aux, stream);
   if (e == hipSuccess) e = launch_up(s, x, w->w_up, w->b_up, offsets, sorted_assign, h, stream);
   // The down projection's K slices (if any) are summed by the combine.
   float* y_part = at<float>(ws, L.y_part);

@@ -31,6 +31,11 @@ struct Shape {
 // sums are the partial sums later reduced in block order).
 constexpr int kRouterTokens = 16;
 inline int router_blocks(const Shape& s) { return (s.T + kRouterTokens - 1) / kRouterTokens; }
+// Dispatch scatter blocks each rank the assignments of this many tokens
+// (a multiple of kRouterTokens: the per-chunk expert counts are summed per
+// scatter block).
+constexpr int kScatterTokens = 512;
+inline int scatter_blocks(const Shape& s) { return (s.T + kScatterTokens - 1) / kScatterTokens; }
 
 // Split of the reduction dimension in the decode down-projection.
 constexpr int kDecodeSplitK = 4;
@@ -43,7 +48,8 @@ int down_ksplit(const Shape& s);
 
 // ---------------------------------------------------------------- workspace
 struct WsLayout {
-  size_t topk_idx, topk_w, prob_part, prob_colsum, counts, kept, offsets, sorted_assign,
+  size_t topk_idx, topk_w, prob_part, chunk_counts, sb_prefix, prob_colsum, counts, kept,
+      offsets, sorted_assign,
       assign_row, drop_mask, f, P, l_aux, h, y_exp, y_part, total;
 };
 WsLayout ws_layout(const Shape& s);
@@ -113,16 +119,21 @@ __device__ __forceinline__ float gelu_f(float z) {
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; all are asynchronous on `st`.
+// Also writes each 16-token chunk's per-expert sum of probabilities
+// (prob_part) and count of selections (chunk_counts), both [chunks, E].
 hipError_t launch_router(const Shape& s, const void* x, const void* wr, const void* br,
                          int32_t* topk_idx, float* topk_w, float* probs, float* prob_part,
-                         hipStream_t st);
+                         int32_t* chunk_counts, hipStream_t st);
 hipError_t launch_colsum(const Shape& s, const float* prob_part, float* colsum, hipStream_t st);
-// Dispatch; when prob_part is non-null it also reduces the probability sums
-// into colsum and writes f, P, l_aux.
-hipError_t launch_dispatch(const Shape& s, const int32_t* topk_idx, int32_t* counts,
-                           int32_t* kept, int32_t* offsets, int32_t* sorted_assign,
-                           int32_t* assign_row, uint8_t* drop_mask, const float* prob_part,
-                           float* colsum, float* f, float* P, float* l_aux, hipStream_t st);
+// Dispatch.  counted: chunk_counts already hold the router's per-chunk
+// counts (else they are computed from topk_idx first).  sb_prefix is
+// scratch [scatter_blocks, E].  When prob_part is non-null it also reduces
+// the probability sums into colsum and writes f, P, l_aux.
+hipError_t launch_dispatch(const Shape& s, const int32_t* topk_idx, int32_t* chunk_counts,
+                           bool counted, int32_t* sb_prefix, int32_t* counts, int32_t* kept,
+                           int32_t* offsets, int32_t* sorted_assign, int32_t* assign_row,
+                           uint8_t* drop_mask, const float* prob_part, float* colsum, float* f,
+                           float* P, float* l_aux, hipStream_t st);
 hipError_t launch_aux(const Shape& s, const float* colsum, const int32_t* counts, float* f,
                       float* P, float* l_aux, hipStream_t st);
 hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void* b_up,

@@ -16,7 +16,9 @@
 // lower lane wins a tie.  Experts are ranked by logit (monotone in both
 // gates, so ranking and weights match ranking by score).  Each block also
 // writes the sum of its 16 tokens' probabilities per expert (token order);
-// these partial sums are reduced in block order for P.
+// these partial sums are reduced in block order for P.  It also writes the
+// number of selections of each expert in its 16 tokens (the dispatch's
+// per-chunk counts).
 #include "moe_internal.h"
 
 namespace moe {
@@ -54,6 +56,7 @@ struct RouterArgs {
   float* topk_w;
   float* probs;         // null if not requested
   float* prob_part;     // [blocks, E]
+  int32_t* chunk_counts;  // [blocks, E]: selections of each expert in the block's tokens
   int T, d, E, k, gating, dtype;
 };
 
@@ -61,6 +64,7 @@ template <int NE16>  // expert tiles of 16 (bf16 path); 0 = fp32 path
 __global__ __launch_bounds__(64 * RW) void router_kernel(RouterArgs a) {
   __shared__ float red[RW][RT][kMaxExperts + 1];
   __shared__ float colp[RW][kMaxExperts];
+  __shared__ int cntp[RW][kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * RT;
   const int E = a.E;
@@ -132,6 +136,7 @@ __global__ __launch_bounds__(64 * RW) void router_kernel(RouterArgs a) {
                                : ((const float*)a.br)[lane];
   const float NEG_INF = -__builtin_inff();
   float psum = 0.f;
+  int nsel = 0;   // lane e: selections of expert e by this wave's tokens
 #pragma unroll 1
   for (int i = 0; i < RT / RW; ++i) {
     const int tl = wave * (RT / RW) + i;
@@ -166,10 +171,11 @@ __global__ __launch_bounds__(64 * RW) void router_kernel(RouterArgs a) {
       float bv = key;
       int bi = lane;
       wave_argmax(bv, bi);
+      bi = bi < E ? bi : E - 1;   // only NaN logits can leave the winner outside [0, E)
       const float bs = __shfl(score, bi);
       sel_sum += bs;
       if (lane == s) { my_idx = bi; my_score = bs; }
-      if (lane == bi) key = NEG_INF;
+      if (lane == bi) { key = NEG_INF; ++nsel; }
     }
     if (lane < a.k) {
       a.topk_idx[(long long)t * a.k + lane] = my_idx;
@@ -177,12 +183,18 @@ __global__ __launch_bounds__(64 * RW) void router_kernel(RouterArgs a) {
     }
   }
   colp[wave][lane] = psum;
+  cntp[wave][lane] = nsel;
   __syncthreads();
   if (tid < E) {
     float c = colp[0][tid];
+    int n = cntp[0][tid];
 #pragma unroll
-    for (int w = 1; w < RW; ++w) c += colp[w][tid];   // wave order = token order
+    for (int w = 1; w < RW; ++w) {
+      c += colp[w][tid];   // wave order = token order
+      n += cntp[w][tid];
+    }
     a.prob_part[(long long)blockIdx.x * E + tid] = c;
+    a.chunk_counts[(long long)blockIdx.x * E + tid] = n;
   }
 }
 
@@ -207,9 +219,9 @@ __global__ __launch_bounds__(256) void colsum_kernel(const float* prob_part, int
 
 hipError_t launch_router(const Shape& s, const void* x, const void* wr, const void* br,
                          int32_t* topk_idx, float* topk_w, float* probs, float* prob_part,
-                         hipStream_t st) {
+                         int32_t* chunk_counts, hipStream_t st) {
   RouterArgs a{x, wr, s.router_bias() ? br : nullptr, topk_idx, topk_w, probs, prob_part,
-               s.T, s.d, s.E, s.k, s.gating, s.dtype};
+               chunk_counts, s.T, s.d, s.E, s.k, s.gating, s.dtype};
   const int blocks = router_blocks(s);
   if (s.dtype == MOE_F32) {
     router_kernel<0><<<blocks, 64 * RW, 0, st>>>(a);

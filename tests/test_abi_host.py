@@ -125,6 +125,8 @@ def test_stage_entry_points_reject_null_outputs():
                                None) == M.MOE_ERR_INVALID_ARG
     assert lib.moe_dispatch(byref(p), fake, fake, fake, fake, fake, fake, None, None, 0,
                             None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch(byref(p), fake, fake, fake, fake, fake, fake, fake, None, 0,
+                            None) == M.MOE_ERR_WORKSPACE
     assert lib.moe_expert_ffn(byref(p), fake, byref(w), fake, fake, None, fake, need,
                               None) == M.MOE_ERR_INVALID_ARG
     assert lib.moe_expert_down(byref(p), byref(w), fake, fake, fake, fake, need - 1,

@@ -122,7 +122,8 @@ def test_dispatch_bitexact(case, cap_mode):
                offsets=torch.empty(E + 1, **i32), sorted_assign=torch.empty(n, **i32),
                assign_row=torch.empty(n, **i32),
                drop_mask=torch.empty(n, dtype=torch.uint8, device="cuda"))
-    M.moe_dispatch(p, torch.from_numpy(idx.reshape(-1).astype(np.int32)).cuda(), **out)
+    M.moe_dispatch(p, torch.from_numpy(idx.reshape(-1).astype(np.int32)).cuda(), **out,
+                   ws=M.workspace(p))
     torch.cuda.synchronize()
     check_dispatch_bitexact({k_: v.cpu().numpy() for k_, v in out.items()}, orc, E)
 
@@ -206,7 +207,7 @@ def test_stage_entry_points_equal_fused_forward(name):
     dm = torch.empty(T * k, dtype=torch.uint8, device="cuda")
     w = weights_of(g)
     M.moe_router_topk(p, g["x"], w, idx, tw, ws=ws)
-    M.moe_dispatch(p, idx, cnt, kept, off, sa, ar, dm)
+    M.moe_dispatch(p, idx, cnt, kept, off, sa, ar, dm, ws=ws)
     h = torch.empty(M.max_rows(p) * run.d_ff, dtype=M.h_dtype(p), device="cuda")
     y_exp = torch.empty(M.max_rows(p) * d, device="cuda")
     M.moe_expert_up(p, g["x"], w, off, sa, h)
