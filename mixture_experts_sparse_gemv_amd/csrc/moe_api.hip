@@ -70,6 +70,9 @@ static moe_status check_problem(const moe_problem* p, Shape& s) {
     return MOE_ERR_UNSUPPORTED;
   if (p->dtype == MOE_BF16 && (p->d_model % 64 != 0 || p->d_ff % 64 != 0))
     return MOE_ERR_UNSUPPORTED;
+  // one expert's weight matrix must stay below 4 GiB (32-bit offsets in the kernels)
+  const long long f1 = p->activation == MOE_SWIGLU ? 2LL * p->d_ff : p->d_ff;
+  if (f1 * p->d_model * 4 >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
   s.T = p->T;
   s.d = p->d_model;
   s.f = p->d_ff;
