@@ -77,108 +77,137 @@ struct ScanArgs {
 };
 
 constexpr int PMAX = 32;   // per-thread probability partial sums prefetched
+constexpr int RMAX = 4;    // scatter-block sums a thread keeps in registers
 
-// ---- 2. one block: block prefixes, counts/kept/offsets, aux statistics
+// ---- 2. one block: block prefixes, counts/kept/offsets, aux statistics.
+// Thread (e, j) = (tid % EP, tid / EP), EP = E rounded up to a power of two,
+// J = ST / EP threads per expert.
 __global__ __launch_bounds__(ST) void dispatch_scan_kernel(ScanArgs a) {
-  __shared__ int part[SW][kMaxExperts];
+  __shared__ int sc[2][ST];
   __shared__ int tot_s[kMaxExperts];
-  __shared__ float red[ST];
-  const int tid = threadIdx.x;
+  __shared__ float wsum[SW][kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E;
-
-  // prefetch the router's per-chunk probability sums: thread (pe, pj),
-  // pe = tid % EP, sums chunks pj, pj + J, pj + 2J, ... in order
   const int EP = E <= 1 ? 1 : (E <= 2 ? 2 : (E <= 4 ? 4 : (E <= 8 ? 8 : (E <= 16 ? 16 : (E <= 32 ? 32 : 64)))));
   const int J = ST / EP;
-  const int pe = tid % EP, pj = tid / EP;
+  const int e = tid % EP, j = tid / EP;
+  const bool act = e < E;
+
+  // prefetch the router's per-chunk probability sums: chunks j, j + J, ...
   float pv[PMAX];
   int pcount = 0;
-  if (a.prob_part && pe < E) {
+  if (a.prob_part && act) {
 #pragma unroll
     for (int q = 0; q < PMAX; ++q) {
-      const int b = pj + q * J;
-      pv[q] = (b < a.nchunk) ? a.prob_part[(long long)b * E + pe] : 0.f;
+      const int b = j + q * J;
+      pv[q] = (b < a.nchunk) ? a.prob_part[(long long)b * E + e] : 0.f;
     }
     pcount = (a.nchunk + J - 1) / J;
   }
 
-  // thread (e, j) owns the contiguous range [b0, b1) of scatter blocks
-  const int e = tid & 63, j = tid >> 6;
-  const int R = (a.nsb + SW - 1) / SW;
-  const int b0 = j * R, b1 = min(a.nsb, b0 + R);
+  // phase A: sums of the scatter blocks [b0, b1) this thread owns
   constexpr int CPB = kScatterTokens / kRouterTokens;   // chunks per scatter block
+  const int R = (a.nsb + J - 1) / J;
+  const int b0 = j * R, b1 = min(a.nsb, b0 + R);
+  auto block_sum = [&](int b) {
+    const int c0 = b * CPB;
+    int v[CPB];
+#pragma unroll
+    for (int i = 0; i < CPB; ++i)   // independent loads, all in flight
+      v[i] = (c0 + i < a.nchunk) ? a.chunk_counts[(long long)(c0 + i) * E + e] : 0;
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < CPB; ++i) sum += v[i];
+    return sum;
+  };
+  int keep[RMAX];   // the first RMAX block sums stay in registers
   int acc = 0;
-  if (e < E) {
-    for (int b = b0; b < b1; ++b) {
-      const int c0 = b * CPB, c1 = min(a.nchunk, c0 + CPB);
-      int sum = 0;
-      for (int c = c0; c < c1; ++c) sum += a.chunk_counts[(long long)c * E + e];
-      a.sb_prefix[(long long)b * E + e] = sum;   // block sum; made a prefix below
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) {
+    keep[r] = (act && b0 + r < b1) ? block_sum(b0 + r) : 0;
+    acc += keep[r];
+  }
+  if (act)
+    for (int b = b0 + RMAX; b < b1; ++b) {   // the rest go through memory
+      const int sum = block_sum(b);
+      a.sb_prefix[(long long)b * E + e] = sum;
       acc += sum;
     }
-  }
-  part[j][e] = acc;
+  // phase B: exclusive scan of acc over j for each expert (Hillis-Steele)
+  int cur = 0;
+  sc[0][tid] = acc;
   __syncthreads();
-  if (tid < kMaxExperts) {
-    int run = 0;
-    for (int jj = 0; jj < SW; ++jj) {
-      const int v = part[jj][tid];
-      part[jj][tid] = run;
-      run += v;
-    }
-    tot_s[tid] = run;
+  for (int o = 1; o < J; o <<= 1) {
+    int v = sc[cur][tid];
+    if (j >= o) v += sc[cur][tid - o * EP];
+    sc[cur ^ 1][tid] = v;
+    cur ^= 1;
+    __syncthreads();
   }
-  __syncthreads();
-  if (e < E) {
-    int run = part[j][e];
-    for (int b = b0; b < b1; ++b) {
+  const int excl = sc[cur][tid] - acc;
+  if (j == J - 1 && act) tot_s[e] = sc[cur][tid];
+  // phase C: block prefixes
+  if (act) {
+    int run = excl;
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r)
+      if (b0 + r < b1) {
+        a.sb_prefix[(long long)(b0 + r) * E + e] = run;
+        run += keep[r];
+      }
+    for (int b = b0 + RMAX; b < b1; ++b) {
       const int v = a.sb_prefix[(long long)b * E + e];
       a.sb_prefix[(long long)b * E + e] = run;
       run += v;
     }
   }
-  if (tid == 0) {
-    int off = 0;
-    for (int ee = 0; ee < E; ++ee) {
-      const int c = tot_s[ee];
-      const int kk = (a.cap > 0 && c > a.cap) ? a.cap : c;
-      a.counts[ee] = c;
-      a.kept[ee] = kk;
-      a.offsets[ee] = off;
-      off += kk;
+  __syncthreads();
+  // phase D: counts, kept = min(count, capacity), offsets = exclusive scan of kept
+  if (wave == 0) {
+    const int c = lane < E ? tot_s[lane] : 0;
+    const int kk = (a.cap > 0 && c > a.cap) ? a.cap : c;
+    int incl = kk;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o);
+      if (lane >= o) incl += u;
     }
-    a.offsets[E] = off;
+    if (lane < E) {
+      a.counts[lane] = c;
+      a.kept[lane] = kk;
+      a.offsets[lane] = incl - kk;
+    }
+    if (lane == E - 1) a.offsets[E] = incl;
   }
 
-  // ---- aux statistics (f, P, L_aux) when the router's partial sums are given
+  // ---- aux statistics (f, P, L_aux) when the router's partial sums are given:
+  // per thread in chunk order, then over the wave's j in xor-butterfly order,
+  // then over the waves in order
   if (a.prob_part) {
     float v = 0.f;
-    if (pe < E) {
+    if (act) {
 #pragma unroll
       for (int q = 0; q < PMAX; ++q)
         if (q < pcount) v += pv[q];
-      for (int b = pj + PMAX * J; b < a.nchunk; b += J) v += a.prob_part[(long long)b * E + pe];
+      for (int b = j + PMAX * J; b < a.nchunk; b += J) v += a.prob_part[(long long)b * E + e];
     }
-    red[tid] = v;
+    for (int o = EP; o < 64; o <<= 1) v += __shfl_xor(v, o);
+    if (lane < EP) wsum[wave][lane] = v;
     __syncthreads();
-    // fixed tree over j: red[j*EP + e] for j = 0..J-1
-    for (int h = J / 2; h > 0; h >>= 1) {
-      if (pj < h) red[tid] += red[tid + h * EP];
-      __syncthreads();
-    }
     if (tid < E) {
-      const float cs = red[tid];
+      float cs = 0.f;
+      for (int w = 0; w < SW; ++w) cs += wsum[w][tid];
       const float fe = (float)tot_s[tid] / (float)((long long)a.T * a.k);
-      const float pe_ = cs / (float)a.T;
+      const float pe = cs / (float)a.T;
       if (a.colsum) a.colsum[tid] = cs;
       if (a.f) a.f[tid] = fe;
-      if (a.P) a.P[tid] = pe_;
-      red[ST - 1 - tid] = fe * pe_;
+      if (a.P) a.P[tid] = pe;
+      sc[0][tid] = __float_as_int(fe * pe);
     }
     __syncthreads();
     if (tid == 0 && a.l_aux) {
       float l = 0.f;
-      for (int ee = 0; ee < E; ++ee) l += red[ST - 1 - ee];
+      for (int ee = 0; ee < E; ++ee) l += __int_as_float(sc[0][ee]);
       a.l_aux[0] = (float)E * l;
     }
   }
@@ -199,26 +228,47 @@ __global__ __launch_bounds__(ST) void dispatch_scatter_kernel(ScatterArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E;
   const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  if (tid < E) {
-    kept_s[tid] = a.kept[tid];
-    off_s[tid] = a.offsets[tid];
-    run_s[tid] = a.sb_prefix[(long long)blockIdx.x * E + tid];
-  }
-  if (tid == 0) {   // start of each expert's dropped group, after all kept rows
-    int d = a.offsets[E];
-    for (int e = 0; e < E; ++e) {
-      drop_s[e] = d;
-      d += a.counts[e] - a.kept[e];
-    }
-  }
-  __syncthreads();
   const long long n = (long long)a.T * a.k;
   const long long A0 = (long long)blockIdx.x * kScatterTokens * a.k;
   const long long A1 = A0 + (long long)kScatterTokens * a.k < n ? A0 + (long long)kScatterTokens * a.k : n;
-  for (long long p0 = A0; p0 < A1; p0 += ST) {
+  // this block's expert ids, loaded before anything waits
+  constexpr int MAXP = kScatterTokens * kMaxTopK / ST;   // passes of ST assignments
+  int ids[MAXP];
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    const long long asg = A0 + (long long)p * ST + tid;
+    ids[p] = asg < A1 ? clamp_id(a.topk_idx[asg], E) : -1;
+  }
+  if (wave == 0) {   // lane e: expert e's kept count, row offset, block prefix, dropped start
+    int kp = 0, of = 0, rs = 0, dc = 0;
+    if (lane < E) {
+      kp = a.kept[lane];
+      of = a.offsets[lane];
+      rs = a.sb_prefix[(long long)blockIdx.x * E + lane];
+      dc = a.counts[lane] - kp;
+    }
+    const int offE = a.offsets[E];
+    int incl = dc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o);
+      if (lane >= o) incl += u;
+    }
+    if (lane < E) {
+      kept_s[lane] = kp;
+      off_s[lane] = of;
+      run_s[lane] = rs;
+      drop_s[lane] = offE + incl - dc;   // dropped groups follow all kept rows, by expert
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    const long long p0 = A0 + (long long)p * ST;
+    if (p0 >= A1) break;   // uniform
     const long long asg = p0 + tid;
-    const bool valid = asg < A1;
-    const int e = valid ? clamp_id(a.topk_idx[asg], E) : 0;
+    const bool valid = ids[p] >= 0;
+    const int e = valid ? ids[p] : 0;
     const Bits r = ballots(e, valid);
     const int rank_w = __popcll(lanes_with(r, e) & lower);
     wc[wave][lane] = __popcll(lanes_with(r, lane));
