@@ -163,15 +163,15 @@ def main():
         up_bytes = (touched * F1 * run.d_model * esz + T * run.d_model * esz +
                     rows * run.d_ff * 2)
         achieved = up_bytes / (up_ms * 1e-3) / 1e9
-        roof = {"kernel": "decode_up_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+        roof = {"kernel": "decode_kernel (up)", "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                "traffic": traffic_for("decode_up_kernel", name, up_bytes)}
+                "traffic": traffic_for("decode_kernel", name)}
     else:
         achieved = up_fl / (up_ms * 1e-3) / 1e12
         roof = {"kernel": "grouped_gemm_kernel (up)", "bound": "mfma",
                 "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic_for("grouped_gemm_kernel", name, None)}
+                "traffic": traffic_for("grouped_gemm_kernel", name)}
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -207,7 +207,7 @@ def main():
     print(json.dumps(out))
 
 
-def traffic_for(kernel, workload, default):
+def traffic_for(kernel, workload):
     """HBM bytes per launch measured by rocprofv3 counters (profiles/traffic.json),
     used only while the kernel's source is unchanged since the measurement."""
     path = os.path.join(ROOT, "profiles", "traffic.json")

@@ -82,10 +82,13 @@ __device__ __forceinline__ void sched_interleave() {
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int MODE>
-__global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_kernel(GemmArgs a) {
+// NST: LDS ring stages (3 or 4); OCC: waves per SIMD the register budget
+// must allow (2 lets two 4-wave blocks share a compute unit).
+template <int BM, int BN, int WGM, int WGN, int MODE, int NST = 4, int OCC = 1>
+__global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmArgs a) {
   constexpr int BK = 32;                   // k-tile depth
-  constexpr int NSTAGE = 4;                // LDS ring stages (DMA runs NSTAGE-1 tiles ahead)
+  constexpr int NSTAGE = NST;              // LDS ring stages (DMA runs NSTAGE-1 tiles ahead)
+  static_assert(NSTAGE == 3 || NSTAGE == 4, "ring depth");
   constexpr int NW = WGM * WGN;            // waves: WGM along tokens x WGN along weights
   constexpr bool SWIGLU = MODE == MODE_SWIGLU;
   constexpr bool DOWN = MODE == MODE_DOWN;
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_kernel(GemmArg
 
   // The LDS ring as distinct arrays: the compiler sees that the DMA into one
   // stage never aliases the fragment reads of another.
-  __shared__ u32x4 lds0[STAGE], lds1[STAGE], lds2[STAGE], lds3[STAGE];
+  __shared__ u32x4 lds0[STAGE], lds1[STAGE], lds2[STAGE], lds3[NSTAGE > 3 ? STAGE : 1];
   __shared__ int seg_tile[kMaxSegments + 1];
   __shared__ int sh_seg;
 
@@ -275,21 +278,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_kernel(GemmArg
   // (into stages nobody reads again) and the tail iterations are peeled.
   const int nk = kslice / BK;
   constexpr int NDMA = QWW + QWX;
-  static_assert(2 * NDMA <= 63, "vmcnt range");
-  // s_waitcnt immediate: vmcnt = 2*NDMA, expcnt and lgkmcnt = 0 (every
+  constexpr int INFLIGHT = (NSTAGE - 2) * NDMA;   // DMAs that may stay in flight
+  static_assert(INFLIGHT <= 63, "vmcnt range");
+  // s_waitcnt immediate: vmcnt = INFLIGHT, expcnt and lgkmcnt = 0 (every
   // fragment read of this tile has completed before the barrier).
-  constexpr int WAIT_IMM = ((2 * NDMA) & 15) | (((2 * NDMA) >> 4) << 14);
+  constexpr int WAIT_IMM = (INFLIGHT & 15) | ((INFLIGHT >> 4) << 14);
   u32x4 wf[2][NI], xf[2][MI];
   auto clampk = [&](int t) { return t < nk ? t : nk - 1; };
   dma(lds0, 0);
   dma(lds1, clampk(1));
-  dma(lds2, clampk(2));
+  if (NSTAGE == 4) dma(lds2, clampk(2));
   __builtin_amdgcn_s_waitcnt(WAIT_IMM);
   __builtin_amdgcn_s_barrier();
   __asm__ volatile("" ::: "memory");
   frag_load(lds0, wf[0], xf[0], 0);
   auto iteration = [&](const u32x4* cur, const u32x4* next, u32x4* far, int kt) {
-    dma(far, clampk(kt + 3));
+    dma(far, clampk(kt + NSTAGE - 1));
 #pragma unroll
     for (int s4 = 0; s4 + 1 < NSUB; ++s4) {
       frag_load(cur, wf[(s4 + 1) & 1], xf[(s4 + 1) & 1], s4 + 1);
@@ -307,15 +311,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_kernel(GemmArg
     sched_interleave<NM, SG_DS_READ, NFR, SG_VMEM_READ, 0>();
   };
   int kt = 0;
-  for (; kt + 3 < nk; kt += 4) {
-    iteration(lds0, lds1, lds3, kt);
-    iteration(lds1, lds2, lds0, kt + 1);
-    iteration(lds2, lds3, lds1, kt + 2);
-    iteration(lds3, lds0, lds2, kt + 3);
+  if constexpr (NSTAGE == 4) {
+    for (; kt + 3 < nk; kt += 4) {
+      iteration(lds0, lds1, lds3, kt);
+      iteration(lds1, lds2, lds0, kt + 1);
+      iteration(lds2, lds3, lds1, kt + 2);
+      iteration(lds3, lds0, lds2, kt + 3);
+    }
+    if (kt < nk) iteration(lds0, lds1, lds3, kt);
+    if (kt + 1 < nk) iteration(lds1, lds2, lds0, kt + 1);
+    if (kt + 2 < nk) iteration(lds2, lds3, lds1, kt + 2);
+  } else {
+    for (; kt + 2 < nk; kt += 3) {
+      iteration(lds0, lds1, lds2, kt);
+      iteration(lds1, lds2, lds0, kt + 1);
+      iteration(lds2, lds0, lds1, kt + 2);
+    }
+    if (kt < nk) iteration(lds0, lds1, lds2, kt);
+    if (kt + 1 < nk) iteration(lds1, lds2, lds0, kt + 1);
   }
-  if (kt < nk) iteration(lds0, lds1, lds3, kt);
-  if (kt + 1 < nk) iteration(lds1, lds2, lds0, kt + 1);
-  if (kt + 2 < nk) iteration(lds2, lds3, lds1, kt + 2);
 
   // ---- epilogue.  Lane holds token row (lane & 31) of each 32x32 tile and,
   // in register group g, the four consecutive weight rows 8g + 4*(lane>>5) +
@@ -334,7 +348,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void grouped_gemm_kernel(GemmArg
   constexpr int STG = 32 * PITCH;                       // staging bytes per wave
   constexpr int WPA = (int)(sizeof(lds0) / STG);        // waves per ring array
   static_assert(CPR >= 1 && CPR <= 64 && 64 % CPR == 0 && 32 % RPI == 0, "staging shape");
-  static_assert(WPA * 4 >= NW, "staging must fit in the LDS ring");
+  static_assert(WPA * NSTAGE >= NW, "staging must fit in the LDS ring");
   // Every DMA (including the clamped ones past the last tile) has landed and
   // every wave's last fragment reads are done before the ring is reused.
   __builtin_amdgcn_s_waitcnt(0);
@@ -462,8 +476,21 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* X, const flo
 #ifndef MOE_DN_WGN
 #define MOE_DN_WGN 4
 #endif
+#ifndef MOE_UP_NST
+#define MOE_UP_NST 4
+#endif
+#ifndef MOE_UP_OCC
+#define MOE_UP_OCC 1
+#endif
+#ifndef MOE_DN_NST
+#define MOE_DN_NST 4
+#endif
+#ifndef MOE_DN_OCC
+#define MOE_DN_OCC 1
+#endif
 constexpr int UP_BM = MOE_UP_BM, UP_BN = MOE_UP_BN, UP_WGM = MOE_UP_WGM, UP_WGN = MOE_UP_WGN;
 constexpr int DN_BM = MOE_DN_BM, DN_BN = MOE_DN_BN, DN_WGM = MOE_DN_WGM, DN_WGN = MOE_DN_WGN;
+constexpr int UP_NST = MOE_UP_NST, UP_OCC = MOE_UP_OCC, DN_NST = MOE_DN_NST, DN_OCC = MOE_DN_OCC;
 
 int grid_blocks(const Shape& s, int BM, int NT, int ksplit = 1) {
   const long long mt = ((long long)s.T * s.k + BM - 1) / BM + s.E +
@@ -543,15 +570,15 @@ hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void
              sorted_assign, s.T, s.k, s.E, s.S, s.d, s.f, s.up_rows(), s.f, 1, nullptr, 0};
   if (s.act == MOE_SWIGLU) {
     const int NT = (s.f + UP_BN / 2 - 1) / (UP_BN / 2);
-    grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_SWIGLU>
+    grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_SWIGLU, UP_NST, UP_OCC>
         <<<grid_blocks(s, UP_BM, NT), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
   } else {
     const int NT = (s.f + UP_BN - 1) / UP_BN;
     if (s.act == MOE_RELU)
-      grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_RELU>
+      grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_RELU, UP_NST, UP_OCC>
           <<<grid_blocks(s, UP_BM, NT), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
     else
-      grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_GELU>
+      grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_GELU, UP_NST, UP_OCC>
           <<<grid_blocks(s, UP_BM, NT), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
   }
   return hipGetLastError();
@@ -575,7 +602,7 @@ hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const 
   GemmArgs a{(const uint16_t*)h, (const uint16_t*)w_down, (const uint16_t*)bias, y_exp, offsets,
              nullptr, s.T, s.k, s.E, s.S, s.f, s.d, s.d, s.f, ks, y_part, part_elems};
   const int NT = (s.d + DN_BN - 1) / DN_BN;
-  grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DOWN>
+  grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DOWN, DN_NST, DN_OCC>
       <<<grid_blocks(s, DN_BM, NT, ks), 64 * DN_WGM * DN_WGN, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ks == 1 || !complete) return e;
