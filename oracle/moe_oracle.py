@@ -247,6 +247,38 @@ def aux_stats(idx, probs, E):
     return f, P, l_aux
 
 
+def routing_stats(counts, kept, P):
+    """Routing health indicators ([0539edu] 3.3, observability: log per step the
+    tokens each expert actually processes, the entropy of the routing
+    distribution against the uniform entropy ln N, and the variance of expert
+    utilization; its troubleshooting list judges balance by the coefficient of
+    variation of utilization; experts at zero usage are the failure to watch).
+
+    Readings: the routing distribution is the share of routing decisions per
+    expert before capacity drops, counts_e / (T*k) (the same basis as f);
+    entropy H = -sum_e s_e ln s_e with 0 ln 0 = 0, beside it the entropy of the
+    mean gate probabilities P; utilization is the tokens actually processed,
+    kept_e, with the population variance over experts and CV = std / mean
+    (0 when nothing is kept); dropped = sum_e (counts_e - kept_e); idle =
+    number of experts with kept_e = 0."""
+    counts = np.asarray(counts, dtype=np.float64)
+    kept = np.asarray(kept, dtype=np.float64)
+    P = np.asarray(P, dtype=np.float64)
+    E = counts.size
+
+    def entropy(v):
+        nz = v[v > 0]
+        return float(-np.sum(nz * np.log(nz)))
+
+    share = counts / counts.sum()
+    mean = float(kept.mean())
+    var = float(np.mean((kept - mean) ** 2))
+    cv = float(np.sqrt(var) / mean) if mean > 0 else 0.0
+    return dict(entropy=entropy(share), entropy_p=entropy(P), entropy_max=float(np.log(E)),
+                util_mean=mean, util_var=var, util_cv=cv,
+                dropped=int(np.sum(counts - kept)), idle=int(np.sum(kept == 0)))
+
+
 # ----------------------------------------------------------------------------
 # Whole forward
 # ----------------------------------------------------------------------------
@@ -290,5 +322,6 @@ def forward(x, w_router, b_router, w_up, b_up, w_down, b_down, *, top_k, num_sha
         qq = E + q
         y += expert_ffn(x[toks], w_up[qq], None if b_up is None else b_up[qq],
                         w_down[qq], None if b_down is None else b_down[qq], activation)
+    stats = routing_stats(disp["counts"], disp["kept"], P)
     return dict(logits=logits, probs=probs, idx=idx, w=w, gap=selection_gap(probs, top_k),
-                f=f, P=P, l_aux=l_aux, y=y, tokens=toks, **disp)
+                f=f, P=P, l_aux=l_aux, y=y, tokens=toks, stats=stats, **disp)

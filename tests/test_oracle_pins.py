@@ -398,3 +398,73 @@ def test_page_parameter_counts():
     idx = _random_routing(rng, 32, sf["top_k"], sf["num_experts"])
     dsp = O.dispatch(idx, sf["num_experts"], None)
     assert dsp["offsets"][-1] / (32 * sf["num_experts"]) == sf["fraction"]
+
+
+# ---------------------------------------------------------------- routing health statistics
+
+def test_routing_stats_uniform_is_maximal_and_balanced():
+    E = 8
+    st = O.routing_stats(np.full(E, 100), np.full(E, 100), np.full(E, 1.0 / E))
+    assert st["entropy"] == pytest.approx(math.log(E), rel=1e-15)
+    assert st["entropy_p"] == pytest.approx(math.log(E), rel=1e-15)
+    assert st["entropy_max"] == pytest.approx(math.log(E), rel=1e-15)
+    assert st["util_var"] == 0.0 and st["util_cv"] == 0.0
+    assert st["dropped"] == 0 and st["idle"] == 0
+
+
+def test_routing_stats_collapse_to_one_expert():
+    # all n assignments to one expert: entropy 0; kept values (n, 0, ..., 0)
+    # have mean n/E, population std n sqrt(E-1)/E, so CV = sqrt(E-1)
+    E, n = 6, 600
+    counts = np.zeros(E, dtype=np.int64)
+    counts[2] = n
+    st = O.routing_stats(counts, counts, np.eye(E)[2])
+    assert st["entropy"] == 0.0 and st["entropy_p"] == 0.0
+    assert st["util_mean"] == pytest.approx(n / E)
+    assert st["util_var"] == pytest.approx(n * n * (E - 1) / E ** 2)
+    assert st["util_cv"] == pytest.approx(math.sqrt(E - 1), rel=1e-14)
+    assert st["idle"] == E - 1 and st["dropped"] == 0
+
+
+def test_routing_stats_hand_example_and_drops():
+    # shares (1/2, 1/4, 1/4): H = ln2/2 + 2 * ln4/4 = 1.5 ln 2
+    counts = np.array([4, 2, 2])
+    kept = np.array([3, 2, 0])   # capacity 3 drops one; an expert whose kept rows were all dropped is idle
+    st = O.routing_stats(counts, kept, np.array([0.5, 0.3, 0.2]))
+    assert st["entropy"] == pytest.approx(1.5 * math.log(2.0), rel=1e-15)
+    assert st["entropy_p"] == pytest.approx(-(0.5 * math.log(0.5) + 0.3 * math.log(0.3) +
+                                             0.2 * math.log(0.2)), rel=1e-15)
+    assert st["dropped"] == 3 and st["idle"] == 1
+    m = 5.0 / 3.0
+    var = ((3 - m) ** 2 + (2 - m) ** 2 + (0 - m) ** 2) / 3.0
+    assert st["util_var"] == pytest.approx(var, rel=1e-14)
+    assert st["util_cv"] == pytest.approx(math.sqrt(var) / m, rel=1e-14)
+
+
+def test_routing_stats_invariant_under_expert_relabeling():
+    rng = np.random.default_rng(7)
+    counts = rng.integers(0, 50, size=16)
+    kept = np.minimum(counts, 30)
+    P = rng.random(16)
+    P /= P.sum()
+    perm = rng.permutation(16)
+    a = O.routing_stats(counts, kept, P)
+    b = O.routing_stats(counts[perm], kept[perm], P[perm])
+    for key in a:
+        assert a[key] == pytest.approx(b[key], rel=1e-13, abs=1e-15)
+
+
+def test_routing_stats_of_forward_match_its_dispatch():
+    rng = np.random.default_rng(3)
+    T, d, f, E, k = 40, 8, 16, 5, 2
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d))
+    w_up = rng.standard_normal((E, f, d)) * 0.1
+    w_dn = rng.standard_normal((E, d, f)) * 0.1
+    out = O.forward(x, wr, None, w_up, None, w_dn, None, top_k=k, num_shared=0,
+                    gating="softmax", activation="relu", cap=10)
+    st = out["stats"]
+    assert st["dropped"] == int(np.sum(out["drop_mask"]))
+    assert st["dropped"] == T * k - int(out["offsets"][-1])
+    share = np.bincount(out["idx"].reshape(-1), minlength=E) / (T * k)
+    assert np.allclose(share, out["f"])
