@@ -97,9 +97,33 @@ typedef struct moe_weights {
 } moe_weights;
 
 /*
+ * Routing health indicators of one forward, written to device memory by
+ * moe_routing_stats or moe_ffn_forward (0539edu 3.3: log the tokens each
+ * expert actually processes, the routing entropy against the uniform
+ * entropy ln N, and the variance of expert utilization; its troubleshooting
+ * list judges balance by the coefficient of variation of utilization and
+ * watches for experts at zero usage).
+ *   entropy      -sum_e s_e ln s_e, s_e = counts[e] / (T*k): the share of
+ *                routing decisions (before capacity drops); 0 ln 0 = 0
+ *   entropy_p    -sum_e P[e] ln P[e] of the mean gate probabilities
+ *   entropy_max  ln E (uniform routing)
+ *   util_mean    mean over experts of kept[e] (tokens actually processed)
+ *   util_var     population variance over experts of kept[e]
+ *   util_cv      sqrt(util_var) / util_mean (0 when nothing is kept)
+ *   dropped      sum_e (counts[e] - kept[e])
+ *   idle         experts with kept[e] == 0
+ */
+typedef struct moe_route_stats {
+  float entropy, entropy_p, entropy_max;
+  float util_mean, util_var, util_cv;
+  int32_t dropped, idle;
+} moe_route_stats;
+
+/*
  * Optional routing outputs of moe_ffn_forward (host struct; each device
  * pointer may be NULL, in which case the value lives only in the workspace).
- * Shapes and meaning as in moe_router_topk, moe_dispatch and moe_aux_stats.
+ * Shapes and meaning as in moe_router_topk, moe_dispatch, moe_aux_stats and
+ * moe_routing_stats.
  */
 typedef struct moe_routing {
   int32_t *topk_idx;      /* [T, k]  */
@@ -112,6 +136,7 @@ typedef struct moe_routing {
   int32_t *assign_row;    /* [T * k] */
   uint8_t *drop_mask;     /* [T * k] */
   float *f, *P, *l_aux;   /* [E], [E], [1] */
+  moe_route_stats *stats; /* [1] (computed only when non-NULL) */
 } moe_routing;
 
 /* Host only.  Capacity ceil(capacity_factor * T * k / E): the page's
@@ -203,6 +228,15 @@ moe_status moe_combine(const moe_problem* p, const float* topk_w, const int32_t*
  */
 moe_status moe_aux_stats(const moe_problem* p, const float* prob_colsum, const int32_t* counts,
                          float* f, float* P, float* l_aux, hipStream_t stream);
+
+/*
+ * Routing health indicators (see moe_route_stats) from the dispatch's
+ * counts and kept [E] (int32) and the mean gate probabilities P [E]
+ * (moe_aux_stats).  stats: one moe_route_stats in device memory.  Sums run
+ * over experts in a fixed order: the result is deterministic.
+ */
+moe_status moe_routing_stats(const moe_problem* p, const int32_t* counts, const int32_t* kept,
+                             const float* P, moe_route_stats* stats, hipStream_t stream);
 
 /*
  * The whole forward: router + top-k, dispatch, experts, combine, aux stats

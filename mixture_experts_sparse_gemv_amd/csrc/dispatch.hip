@@ -67,12 +67,49 @@ __global__ __launch_bounds__(256) void chunk_count_kernel(const int32_t* __restr
   if (lane < E) chunk_counts[(long long)c * E + lane] = cnt;
 }
 
+// Routing health indicators (moe_route_stats) computed by one wave, lane e
+// holding expert e's routed count c, kept count kp and mean probability pe
+// (lanes >= E pass zeros).  Wave sums run in a fixed xor-butterfly order.
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ void route_stats_wave(int lane, int E, int c, int kp, float pe, moe_route_stats* out) {
+  const bool on = lane < E;
+  const int total = wave_sum_i(on ? c : 0);
+  const float share = (on && total > 0) ? (float)c / (float)total : 0.f;
+  const float h = wave_sum_f(share > 0.f ? -share * logf(share) : 0.f);
+  const float hp = wave_sum_f((on && pe > 0.f) ? -pe * logf(pe) : 0.f);
+  const float mean = (float)wave_sum_i(on ? kp : 0) / (float)E;
+  const float dv = on ? (float)kp - mean : 0.f;
+  const float var = wave_sum_f(dv * dv) / (float)E;
+  const int dropped = wave_sum_i(on ? c - kp : 0);
+  const int idle = wave_sum_i((on && kp == 0) ? 1 : 0);
+  if (lane == 0) {
+    out->entropy = h;
+    out->entropy_p = hp;
+    out->entropy_max = logf((float)E);
+    out->util_mean = mean;
+    out->util_var = var;
+    out->util_cv = mean > 0.f ? sqrtf(var) / mean : 0.f;
+    out->dropped = dropped;
+    out->idle = idle;
+  }
+}
+
 struct ScanArgs {
   const int32_t* chunk_counts;   // [nchunk, E]
   int32_t* sb_prefix;            // [nsb, E] out: per scatter block exclusive prefix
   int32_t *counts, *kept, *offsets;
   const float* prob_part;        // [nchunk, E] or null (no aux statistics)
   float *colsum, *f, *P, *l_aux;
+  moe_route_stats* stats;        // or null
   int T, k, E, cap, nchunk, nsb;
 };
 
@@ -194,15 +231,20 @@ __global__ __launch_bounds__(ST) void dispatch_scan_kernel(ScanArgs a) {
     for (int o = EP; o < 64; o <<= 1) v += __shfl_xor(v, o);
     if (lane < EP) wsum[wave][lane] = v;
     __syncthreads();
+    float pe = 0.f;
     if (tid < E) {
       float cs = 0.f;
       for (int w = 0; w < SW; ++w) cs += wsum[w][tid];
       const float fe = (float)tot_s[tid] / (float)((long long)a.T * a.k);
-      const float pe = cs / (float)a.T;
+      pe = cs / (float)a.T;
       if (a.colsum) a.colsum[tid] = cs;
       if (a.f) a.f[tid] = fe;
       if (a.P) a.P[tid] = pe;
       sc[0][tid] = __float_as_int(fe * pe);
+    }
+    if (wave == 0 && a.stats) {
+      const int c = lane < E ? tot_s[lane] : 0;
+      route_stats_wave(lane, E, c, (a.cap > 0 && c > a.cap) ? a.cap : c, pe, a.stats);
     }
     __syncthreads();
     if (tid == 0 && a.l_aux) {
@@ -301,6 +343,15 @@ __global__ __launch_bounds__(ST) void dispatch_scatter_kernel(ScatterArgs a) {
   }
 }
 
+// Routing health indicators from given counts, kept and P (one wave).
+__global__ __launch_bounds__(64) void routing_stats_kernel(const int32_t* counts,
+                                                           const int32_t* kept, const float* P,
+                                                           int E, moe_route_stats* out) {
+  const int lane = threadIdx.x;
+  const bool on = lane < E;
+  route_stats_wave(lane, E, on ? counts[lane] : 0, on ? kept[lane] : 0, on ? P[lane] : 0.f, out);
+}
+
 // f, P, L_aux from given column sums and counts (one block).
 __global__ __launch_bounds__(64) void aux_kernel(const float* colsum, const int32_t* counts,
                                                  float* f, float* P, float* l_aux, int T, int k,
@@ -328,7 +379,7 @@ hipError_t launch_dispatch(const Shape& s, const int32_t* topk_idx, int32_t* chu
                            bool counted, int32_t* sb_prefix, int32_t* counts, int32_t* kept,
                            int32_t* offsets, int32_t* sorted_assign, int32_t* assign_row,
                            uint8_t* drop_mask, const float* prob_part, float* colsum, float* f,
-                           float* P, float* l_aux, hipStream_t st) {
+                           float* P, float* l_aux, moe_route_stats* stats, hipStream_t st) {
   const int nchunk = router_blocks(s), nsb = scatter_blocks(s);
   if (!counted) {
     chunk_count_kernel<<<(nchunk + 3) / 4, 256, 0, st>>>(topk_idx, chunk_counts, s.T, s.k, s.E,
@@ -337,7 +388,7 @@ hipError_t launch_dispatch(const Shape& s, const int32_t* topk_idx, int32_t* chu
     if (e != hipSuccess) return e;
   }
   ScanArgs sa{chunk_counts, sb_prefix, counts, kept, offsets, prob_part, colsum, f, P, l_aux,
-              s.T, s.k, s.E, s.cap, nchunk, nsb};
+              prob_part ? stats : nullptr, s.T, s.k, s.E, s.cap, nchunk, nsb};
   dispatch_scan_kernel<<<1, ST, 0, st>>>(sa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -350,6 +401,12 @@ hipError_t launch_dispatch(const Shape& s, const int32_t* topk_idx, int32_t* chu
 hipError_t launch_aux(const Shape& s, const float* colsum, const int32_t* counts, float* f,
                       float* P, float* l_aux, hipStream_t st) {
   aux_kernel<<<1, 64, 0, st>>>(colsum, counts, f, P, l_aux, s.T, s.k, s.E);
+  return hipGetLastError();
+}
+
+hipError_t launch_routing_stats(const Shape& s, const int32_t* counts, const int32_t* kept,
+                                const float* P, moe_route_stats* stats, hipStream_t st) {
+  routing_stats_kernel<<<1, 64, 0, st>>>(counts, kept, P, s.E, stats);
   return hipGetLastError();
 }
 

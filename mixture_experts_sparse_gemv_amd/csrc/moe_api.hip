@@ -160,7 +160,7 @@ moe_status moe_dispatch(const moe_problem* p, const int32_t* topk_idx, int32_t* 
   return fail_hip(launch_dispatch(s, topk_idx, at<int32_t>(ws, L.chunk_counts), false,
                                   at<int32_t>(ws, L.sb_prefix), counts, kept, offsets,
                                   sorted_assign, assign_row, drop_mask, nullptr, nullptr, nullptr,
-                                  nullptr, nullptr, stream));
+                                  nullptr, nullptr, nullptr, stream));
 }
 
 moe_status moe_expert_up(const moe_problem* p, const void* x, const moe_weights* w,
@@ -228,6 +228,15 @@ moe_status moe_aux_stats(const moe_problem* p, const float* prob_colsum, const i
   return fail_hip(launch_aux(s, prob_colsum, counts, f, P, l_aux, stream));
 }
 
+moe_status moe_routing_stats(const moe_problem* p, const int32_t* counts, const int32_t* kept,
+                             const float* P, moe_route_stats* stats, hipStream_t stream) {
+  Shape s;
+  moe_status st = check_problem(p, s);
+  if (st != MOE_OK) return st;
+  if (!counts || !kept || !P || !stats) return MOE_ERR_INVALID_ARG;
+  return fail_hip(launch_routing_stats(s, counts, kept, P, stats, stream));
+}
+
 moe_status moe_ffn_forward(const moe_problem* p, const moe_weights* w, const void* x, float* y,
                            const moe_routing* out, void* ws, size_t ws_bytes,
                            hipStream_t stream) {
@@ -261,7 +270,7 @@ moe_status moe_ffn_forward(const moe_problem* p, const moe_weights* w, const voi
   if (e == hipSuccess)
     e = launch_dispatch(s, topk_idx, chunk_counts, true, at<int32_t>(ws, L.sb_prefix), counts,
                         kept, offsets, sorted_assign, assign_row, drop_mask, part,
-                        at<float>(ws, L.prob_colsum), f, P, l_aux, stream);
+                        at<float>(ws, L.prob_colsum), f, P, l_aux, r.stats, stream);
   if (e == hipSuccess) e = launch_up(s, x, w->w_up, w->b_up, offsets, sorted_assign, h, stream);
   // The down projection's K slices (if any) are summed by the combine.
   float* y_part = at<float>(ws, L.y_part);

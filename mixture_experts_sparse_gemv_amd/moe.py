@@ -24,7 +24,7 @@ MOE_ROUTER_BIAS, MOE_EXPERT_BIAS = 1, 2
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_capacity", "moe_workspace_size", "moe_router_topk", "moe_dispatch",
            "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_aux_stats",
-           "moe_ffn_forward", "moe_status_string", "moe_last_hip_error")
+           "moe_routing_stats", "moe_ffn_forward", "moe_status_string", "moe_last_hip_error")
 
 
 class moe_problem(ctypes.Structure):
@@ -41,7 +41,12 @@ class moe_weights(ctypes.Structure):
 class moe_routing(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("topk_idx", "topk_w", "probs", "counts", "kept", "offsets", "sorted_assign",
-                 "assign_row", "drop_mask", "f", "P", "l_aux")]
+                 "assign_row", "drop_mask", "f", "P", "l_aux", "stats")]
+
+
+# moe_route_stats: six float32 then two int32 (32 bytes, device memory)
+ROUTE_STATS_FLOATS = ("entropy", "entropy_p", "entropy_max", "util_mean", "util_var", "util_cv")
+ROUTE_STATS_INTS = ("dropped", "idle")
 
 
 class MoeError(RuntimeError):
@@ -69,6 +74,7 @@ def _load(path=LIB_PATH):
         "moe_expert_down": (I32, [pp, pw, V, V, V, V, SZ, V]),
         "moe_combine": (I32, [pp, V, V, V, V, V, V]),
         "moe_aux_stats": (I32, [pp, V, V, V, V, V, V]),
+        "moe_routing_stats": (I32, [pp, V, V, V, V, V]),
         "moe_ffn_forward": (I32, [pp, pw, V, V, pr, V, SZ, V]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
         "moe_last_hip_error": (I32, []),
@@ -222,6 +228,29 @@ def moe_aux_stats(p, prob_colsum, counts, f, P, l_aux, stream=None):
     _check("moe_aux_stats", _lib.moe_aux_stats(
         ctypes.byref(p), _ptr(prob_colsum), _ptr(counts), _ptr(f), _ptr(P), _ptr(l_aux),
         _stream(stream)))
+
+
+def route_stats_tensor(device="cuda"):
+    """Device buffer for one moe_route_stats (8 x 4 bytes)."""
+    return torch.empty(8, dtype=torch.int32, device=device)
+
+
+def route_stats_dict(t):
+    """Decodes a moe_route_stats buffer (copied to the host)."""
+    raw = t.detach().to("cpu").contiguous()
+    fl = raw.view(torch.float32)
+    out = {n: float(fl[i]) for i, n in enumerate(ROUTE_STATS_FLOATS)}
+    out.update({n: int(raw[6 + i]) for i, n in enumerate(ROUTE_STATS_INTS)})
+    return out
+
+
+def moe_routing_stats(p, counts, kept, P, stats, stream=None):
+    _need(counts, p.num_experts, torch.int32, "counts")
+    _need(kept, p.num_experts, torch.int32, "kept")
+    _need(P, p.num_experts, torch.float32, "P")
+    _need(stats, 8, torch.int32, "stats")
+    _check("moe_routing_stats", _lib.moe_routing_stats(
+        ctypes.byref(p), _ptr(counts), _ptr(kept), _ptr(P), _ptr(stats), _stream(stream)))
 
 
 def moe_ffn_forward(p, w, x, y, ws, routing=None, stream=None):

@@ -143,7 +143,8 @@ def routing_outputs(p, device="cuda"):
                 kept=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
                 sorted_assign=torch.empty(T * k, **i32), assign_row=torch.empty(T * k, **i32),
                 drop_mask=torch.empty(T * k, dtype=torch.uint8, device=device),
-                f=torch.empty(E, **f32), P=torch.empty(E, **f32), l_aux=torch.empty(1, **f32))
+                f=torch.empty(E, **f32), P=torch.empty(E, **f32), l_aux=torch.empty(1, **f32),
+                stats=M.route_stats_tensor(device))
 
 
 def run_forward(run, g, p=None, routing=True):
@@ -153,7 +154,9 @@ def run_forward(run, g, p=None, routing=True):
     r = routing_outputs(p) if routing else None
     M.moe_ffn_forward(p, weights_of(g), g["x"], y, ws, routing=r)
     torch.cuda.synchronize()
-    out = {k: v.cpu().numpy() for k, v in (r or {}).items()}
+    out = {k: v.cpu().numpy() for k, v in (r or {}).items() if k != "stats"}
+    if r:
+        out["stats"] = M.route_stats_dict(r["stats"])
     out["y"] = y.view(run.T, run.d_model).cpu().numpy()
     return out
 
@@ -190,9 +193,22 @@ def compare_forward(run, gpu, orc, token_subset=None):
     print(f"  l_aux gpu={float(gpu['l_aux'][0]):.6f} oracle={orc['l_aux']:.6f}", flush=True)
     assert abs(float(gpu["l_aux"][0]) - orc["l_aux"]) <= tol
     assert_close(gpu["P"], orc["P"], "P", rel=1e-4, mabs=1e-5)
+    # routing health: the kernel's arithmetic on its own counts, kept and P,
+    # and the oracle's values where the routing agrees
+    check_route_stats(gpu["stats"], O.routing_stats(gpu["counts"], gpu["kept"], gpu["P"]))
     if same.all():
         np.testing.assert_allclose(gpu["f"], orc["f"], rtol=1e-6)
+        check_route_stats(gpu["stats"], orc["stats"])
     return agree
+
+
+def check_route_stats(got, ref):
+    """Routing health indicators: integers exact; float32 sums over at most 64
+    experts within 1e-5 relative (entropies and CV also 1e-6 absolute)."""
+    print(f"  stats gpu={got}", flush=True)
+    assert got["dropped"] == ref["dropped"] and got["idle"] == ref["idle"]
+    for key in ("entropy", "entropy_p", "entropy_max", "util_mean", "util_var", "util_cv"):
+        assert abs(got[key] - ref[key]) <= 1e-5 * abs(ref[key]) + 1e-6, (key, got[key], ref[key])
 
 
 def inputs_for(run):

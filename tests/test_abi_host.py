@@ -133,4 +133,5 @@ def test_stage_entry_points_reject_null_outputs():
                                None) == M.MOE_ERR_WORKSPACE
     assert lib.moe_combine(byref(p), fake, fake, fake, fake, None, None) == M.MOE_ERR_INVALID_ARG
     assert lib.moe_aux_stats(byref(p), fake, fake, fake, None, fake, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_routing_stats(byref(p), fake, fake, fake, None, None) == M.MOE_ERR_INVALID_ARG
     assert lib.moe_status_string(M.MOE_ERR_HIP) == b"MOE_ERR_HIP"

@@ -217,3 +217,24 @@ def test_stage_entry_points_equal_fused_forward(name):
     torch.cuda.synchronize()
     ys = y.view(T, d).cpu().numpy()
     assert np.array_equal(ys.view(np.uint32), fwd["y"].view(np.uint32)), "staged != forward"
+
+
+def test_routing_stats_entry_point_given_oracle_inputs():
+    from _parity import check_route_stats
+    _say("[routing_stats] synthetic counts, drops and idle experts")
+    rng = np.random.default_rng(11)
+    for E in (1, 4, 8, 64):
+        counts = rng.integers(0, 400, size=E)
+        if E > 2:
+            counts[1] = 0
+        kept = np.minimum(counts, 250)
+        Pv = rng.random(E)
+        Pv /= Pv.sum()
+        ref = O.routing_stats(counts, kept, Pv)
+        p = M.make_problem(T=int(counts.sum()) + 1, d_model=64, d_ff=64, num_experts=E, top_k=1)
+        st = M.route_stats_tensor()
+        M.moe_routing_stats(p, torch.tensor(counts, dtype=torch.int32, device="cuda"),
+                            torch.tensor(kept, dtype=torch.int32, device="cuda"),
+                            torch.tensor(Pv, dtype=torch.float32, device="cuda"), st)
+        torch.cuda.synchronize()
+        check_route_stats(M.route_stats_dict(st), ref)
