@@ -5,4 +5,5 @@ benchmark's cpu_baseline leg, never by the HIP library or its binding."""
 from . import moe_oracle
 from .moe_oracle import (router_logits, softmax, sigmoid_normalized, gate, topk_renorm,
                          selection_gap, capacity, dispatch, gelu, silu, expert_ffn,
-                         combine_rows, aux_stats, routing_stats, forward)
+                         combine_rows, aux_stats, routing_stats, forward,
+                         e4m3_values, quantize_fp8_rows, dequantize_fp8_rows)

@@ -280,6 +280,59 @@ def routing_stats(counts, kept, P):
 
 
 # ----------------------------------------------------------------------------
+# FP8 expert weights ([0539edu] 5.2: quantize expert parameters from 16 bits
+# to INT8 or FP8 to halve their memory)
+# ----------------------------------------------------------------------------
+
+FP8_MAX = 448.0
+
+
+def e4m3_values():
+    """Non-negative finite values of OCP FP8 E4M3 indexed by code 0..126 (code
+    127 is NaN; there are no infinities).  Code bits eeee mmm: exponent
+    field e with bias 7, mantissa m; e = 0 is subnormal, m/8 * 2^-6; otherwise
+    (1 + m/8) * 2^(e - 7).  The largest value, code 126, is 448."""
+    vals = []
+    for code in range(127):
+        e, m = code >> 3, code & 7
+        vals.append(m / 8.0 * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.array(vals, dtype=np.float64)
+
+
+def quantize_fp8_rows(w):
+    """Per-row (output channel) FP8 E4M3 quantization of a [rows, K] matrix.
+
+    Reading (the page names the format only): scale s = max_j |w[r, j]| / 448
+    in float32 (1 where the row is all zero); each value v = w / s in float32
+    is rounded to the nearest E4M3 value, ties to the even code, magnitudes
+    above 448 saturating to 448.  Both divisions are taken in float32, the
+    precision the kernels use, so that the codes are reproducible.
+    Returns (codes uint8 [rows, K], scales float32 [rows])."""
+    w32 = np.asarray(w, dtype=np.float32)
+    absmax = np.abs(w32).max(axis=1)
+    scales = np.where(absmax > 0, absmax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
+    v = (w32 / scales[:, None]).astype(np.float32)
+    a = np.minimum(np.abs(v).astype(np.float64), FP8_MAX)
+    vals = e4m3_values()
+    hi = np.searchsorted(vals, a, side="left")          # vals[hi] >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - vals[lo]
+    d_hi = vals[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(vals[hi] == a, hi, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    code = code | np.where(v < 0, 0x80, 0).astype(np.uint8)
+    return code, scales
+
+
+def dequantize_fp8_rows(codes, scales):
+    """w~[r, j] = value(codes[r, j]) * scales[r], exactly, in float64."""
+    vals = e4m3_values()
+    c = np.asarray(codes, dtype=np.uint8)
+    mag = vals[(c & 0x7F).astype(np.int64)]
+    return np.where(c & 0x80, -mag, mag) * np.asarray(scales, dtype=np.float64)[:, None]
+
+
+# ----------------------------------------------------------------------------
 # Whole forward
 # ----------------------------------------------------------------------------
 

@@ -468,3 +468,71 @@ def test_routing_stats_of_forward_match_its_dispatch():
     assert st["dropped"] == T * k - int(out["offsets"][-1])
     share = np.bincount(out["idx"].reshape(-1), minlength=E) / (T * k)
     assert np.allclose(share, out["f"])
+
+
+# ---------------------------------------------------------------- FP8 E4M3 expert weights
+
+def _q1(v):
+    """Code of one value with scale 1 (a row [448, v] keeps scale 448/448 = 1)."""
+    c, s = O.quantize_fp8_rows(np.array([[448.0, v]], dtype=np.float32))
+    assert s[0] == 1.0
+    return int(c[0, 1])
+
+
+def test_e4m3_table_matches_the_format_definition():
+    vals = O.e4m3_values()
+    assert vals.size == 127 and vals[0] == 0.0 and vals[-1] == 448.0
+    assert vals[1] == 2.0 ** -9 and vals[8] == 2.0 ** -6 and vals[0x38] == 1.0
+    assert np.all(np.diff(vals) > 0)          # codes are ordered by value
+    assert len(set(vals.tolist())) == 127
+    # the spacing within a binade is an eighth of its lower bound
+    assert vals[0x39] - vals[0x38] == 0.125 and vals[0x79] - vals[0x78] == 32.0
+
+
+def test_e4m3_known_codes_ties_and_saturation():
+    assert _q1(0.0) == 0x00 and _q1(1.0) == 0x38 and _q1(-1.0) == 0xB8
+    assert _q1(0.5) == 0x30 and _q1(1.125) == 0x39 and _q1(2.0 ** -9) == 0x01
+    assert _q1(2.0 ** -6) == 0x08 and _q1(-448.0) == 0xFE
+    assert _q1(1.0625) == 0x38           # tie between 1.0 (even) and 1.125
+    assert _q1(1.1875) == 0x3A           # tie between 1.125 and 1.25 (even)
+    assert _q1(1.5 * 2.0 ** -9) == 0x02  # subnormal tie goes to the even code
+    assert _q1(0.5 * 2.0 ** -9) == 0x00  # half the smallest subnormal rounds to zero
+    assert _q1(1.01 * 2.0 ** -10) == 0x01
+    assert _q1(447.0) == 0x7E and _q1(431.0) == 0x7D   # 416 and 448 are neighbours
+    # the row maximum maps to +-448 whatever its size (so magnitudes never exceed it)
+    c, s = O.quantize_fp8_rows(np.array([[1000.0, -1000.0, 500.0]], dtype=np.float32))
+    assert c[0, 0] == 0x7E and c[0, 1] == 0xFE and s[0] == np.float32(1000.0) / np.float32(448.0)
+
+
+def test_e4m3_every_finite_value_round_trips():
+    vals = O.e4m3_values()
+    row = np.concatenate([[448.0], vals, -vals[1:]]).astype(np.float32)[None, :]
+    codes, scales = O.quantize_fp8_rows(row)
+    assert scales[0] == 1.0
+    back = O.dequantize_fp8_rows(codes, scales)
+    assert np.array_equal(back, row.astype(np.float64))
+
+
+def test_fp8_rows_scale_error_bound_and_zero_row():
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((6, 300)) * 0.02).astype(np.float32)
+    w[3] = 0.0
+    codes, scales = O.quantize_fp8_rows(w)
+    assert scales[3] == 1.0 and not codes[3].any()
+    amax = np.abs(w).max(axis=1)
+    nz = amax > 0
+    assert np.array_equal(scales[nz], (amax[nz] / np.float32(448.0)).astype(np.float32))
+    # each row's largest magnitude maps to +-448
+    for r in np.flatnonzero(nz):
+        assert (int(codes[r, np.argmax(np.abs(w[r]))]) & 0x7F) == 0x7E
+    back = O.dequantize_fp8_rows(codes, scales)
+    # nearest-value rounding: error <= half a step, i.e. 2^-4 relative in the
+    # normal range, half the subnormal step 2^-10 * s below it
+    err = np.abs(back - w.astype(np.float64))
+    bound = np.maximum(np.abs(w) * 2.0 ** -4, scales[:, None].astype(np.float64) * 2.0 ** -10)
+    assert np.all(err <= bound * (1 + 1e-6))
+    # and the rounding is to the nearest representable value
+    vals = np.concatenate([-O.e4m3_values()[::-1], O.e4m3_values()[1:]])
+    v = (w[0] / scales[0]).astype(np.float64)
+    nearest = np.abs(vals[None, :] - v[:, None]).min(axis=1)
+    assert np.allclose(np.abs(back[0] / scales[0] - v), nearest, rtol=0, atol=1e-12)
