@@ -77,13 +77,24 @@ def main():
     inp = make_inputs(run)
     g = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
     del inp
+    if run.w_fp8:
+        # one-time preparation (untimed): per-row FP8 E4M3 codes and scales
+        for name_w, name_s in (("w_up", "s_up"), ("w_down", "s_down")):
+            wt = g[name_w]
+            q = torch.empty(wt.shape, dtype=torch.uint8, device=dev)
+            sc = torch.empty(wt.numel() // wt.shape[-1], dtype=torch.float32, device=dev)
+            M.moe_quantize_fp8(wt, q, sc)
+            g[name_w], g[name_s] = q, sc
+            del wt
+        torch.cuda.synchronize()
     cap = M.moe_capacity(run.T, run.top_k, run.num_experts, run.capacity_factor or 0.0)
     p = M.make_problem(T=run.T, d_model=run.d_model, d_ff=run.d_ff, num_experts=run.num_experts,
                        top_k=run.top_k, num_shared=run.num_shared, capacity=cap,
                        dtype=run.dtype, gating=run.gating, activation=run.activation,
-                       router_bias=run.router_bias != "none", expert_bias=run.expert_bias)
+                       router_bias=run.router_bias != "none", expert_bias=run.expert_bias,
+                       w_fp8=run.w_fp8)
     w = M.make_weights(g["w_router"], g["b_router"], g["w_up"], g["b_up"], g["w_down"],
-                       g["b_down"])
+                       g["b_down"], g.get("s_up"), g.get("s_down"))
     ws = M.workspace(p, dev)
     y = torch.empty(run.T * run.d_model, dtype=torch.float32, device=dev)
     E, k, T = run.num_experts, run.top_k, run.T
@@ -119,7 +130,9 @@ def main():
     step_flops = up_fl + down_fl + router_fl
     F1 = 2 * run.d_ff if run.activation == "swiglu" else run.d_ff
     esz = 4 if run.dtype == "f32" else 2
-    w_bytes_touched = touched * (F1 * run.d_model + run.d_model * run.d_ff) * esz
+    wsz = 1 if run.w_fp8 else esz   # expert weight bytes per element (scales: 4 per row)
+    w_bytes_touched = touched * ((F1 * run.d_model + run.d_model * run.d_ff) * wsz +
+                                 ((F1 + run.d_model) * 4 if run.w_fp8 else 0))
     step_bytes = (T * run.d_model * esz + E * run.d_model * esz + w_bytes_touched +
                   T * run.d_model * 4)
     decode = run.dtype == "bf16" and T <= 16
@@ -160,8 +173,8 @@ def main():
     up_ms = stage_ms["expert_up"]
 
     if decode:
-        up_bytes = (touched * F1 * run.d_model * esz + T * run.d_model * esz +
-                    rows * run.d_ff * 2)
+        up_bytes = (touched * F1 * (run.d_model * wsz + (4 if run.w_fp8 else 0)) +
+                    T * run.d_model * esz + rows * run.d_ff * 2)
         achieved = up_bytes / (up_ms * 1e-3) / 1e9
         roof = {"kernel": "decode_kernel (up)", "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),

@@ -63,7 +63,8 @@ enum {
 enum { MOE_F32 = 0, MOE_BF16 = 1 };                      /* dtype of x, weights, biases */
 enum { MOE_SOFTMAX = 0, MOE_SIGMOID_NORM = 1 };          /* gate                        */
 enum { MOE_RELU = 0, MOE_GELU = 1, MOE_SWIGLU = 2 };     /* expert activation           */
-enum { MOE_ROUTER_BIAS = 1, MOE_EXPERT_BIAS = 2 };       /* flags                       */
+enum { MOE_ROUTER_BIAS = 1, MOE_EXPERT_BIAS = 2,        /* flags                       */
+       MOE_W_FP8 = 8 };  /* expert weights as FP8 E4M3 codes with per-row scales (moe_weights) */
 
 /*
  * The problem.  T tokens (the pages' [B, L, d] input flattened to [B*L, d],
@@ -73,6 +74,9 @@ enum { MOE_ROUTER_BIAS = 1, MOE_EXPERT_BIAS = 2 };       /* flags               
  * Limits (MOE_ERR_UNSUPPORTED beyond them): E <= 64, top_k <= 8,
  * E + S <= 128, T * (top_k + S) < 2^31; for MOE_BF16, d_model and d_ff are
  * multiples of 64.  GELU is the exact erf form; SwiGLU has no biases.
+ * MOE_W_FP8 (expert weights quantized to 8 bits, 0539edu page 5.2) needs
+ * MOE_BF16, T <= 16 (the weight-streaming decode path) and d_model, d_ff
+ * multiples of 128.
  */
 typedef struct moe_problem {
   int32_t T, d_model, d_ff, num_experts, top_k, num_shared, capacity;
@@ -94,6 +98,11 @@ typedef struct moe_weights {
   const void *w_router, *b_router;
   const void *w_up, *b_up;
   const void *w_down, *b_down;
+  /* MOE_W_FP8 only: w_up and w_down hold E4M3 codes (one byte each, same
+   * shapes) and the dequantized weight of row r is code * scale[r]:
+   *   s_up [E+S, F1] float32, s_down [E+S, d] float32 (see moe_quantize_fp8).
+   * Ignored (may be NULL) otherwise. */
+  const float *s_up, *s_down;
 } moe_weights;
 
 /*
@@ -246,6 +255,20 @@ moe_status moe_routing_stats(const moe_problem* p, const int32_t* counts, const 
 moe_status moe_ffn_forward(const moe_problem* p, const moe_weights* w, const void* x, float* y,
                            const moe_routing* out, void* ws, size_t ws_bytes,
                            hipStream_t stream);
+
+/*
+ * Per-row FP8 E4M3 quantization (0539edu page 5.2: expert parameters in 8
+ * bits), a one-time preparation of weights for MOE_W_FP8.  Row r of the
+ * [rows, cols] bf16 matrix w gets scale[r] = max_j |w[r, j]| / 448 (1 for an
+ * all-zero row) and q[r, j] = the E4M3 code nearest to w[r, j] / scale[r]
+ * (float32 division; ties to the even code; magnitudes above 448 saturate).
+ * E4M3: bit 7 sign, bits 6..3 exponent (bias 7), bits 2..0 mantissa;
+ * exponent 0 is subnormal (m/8 * 2^-6); no infinities.  For w_up of shape
+ * [E+S, F1, d] pass rows = (E+S)*F1, cols = d; for w_down rows = (E+S)*d,
+ * cols = d_ff.  rows < 2^31, cols a multiple of 8.
+ */
+moe_status moe_quantize_fp8(const void* w, int64_t rows, int32_t cols, uint8_t* q, float* scale,
+                            hipStream_t stream);
 
 /* Human-readable name of a status code (static string). */
 const char* moe_status_string(moe_status s);

@@ -38,16 +38,23 @@ enum { DEC_DOWN = 3 };   // modes: MOE_RELU, MOE_GELU, MOE_SWIGLU (up) or DEC_DO
 #ifndef MOE_DECODE_STAGES
 #define MOE_DECODE_STAGES 4
 #endif
-constexpr int DR = MOE_DECODE_ROWS;     // weight rows per work item
-constexpr int NST = MOE_DECODE_STAGES;  // LDS ring stages
-constexpr int DK = 64;                  // K elements per stage: one 128-byte line per row
-constexpr int RG = DR / 16;             // MFMA row groups
-constexpr int NDMA = DR / 8;            // DMA instructions per stage (8 rows each)
-static_assert(DR % 16 == 0 && DR <= 64 && NST >= 2 && NST <= 4, "decode tiling");
+#ifndef MOE_DECODE_ROWS_F8
+#define MOE_DECODE_ROWS_F8 32
+#endif
+#ifndef MOE_DECODE_STAGES_F8
+#define MOE_DECODE_STAGES_F8 4
+#endif
+// Weight rows per work item and LDS ring stages, for bf16 and FP8 weights.
+template <bool F8> struct DecodeTile {
+  static constexpr int DR = F8 ? MOE_DECODE_ROWS_F8 : MOE_DECODE_ROWS;
+  static constexpr int NST = F8 ? MOE_DECODE_STAGES_F8 : MOE_DECODE_STAGES;
+  static_assert(DR % 16 == 0 && DR <= 64 && NST >= 2 && NST <= 4, "decode tiling");
+};
 
 struct DecodeArgs {
   const uint16_t* X;       // up: x [T, d] bf16; down: h [rows, f] fp16
-  const uint16_t* W;       // [segments][Wrows][K] bf16
+  const void* W;           // [segments][Wrows][K] bf16, or FP8 E4M3 codes
+  const float* wscale;     // FP8 only: [segments][Wrows] row scales
   const uint16_t* bias;    // up: [segments][Wrows] bf16, or null
   void* out;               // up: h [rows, f] fp16; down: y_part [nsplit][rows][d] fp32
   const int32_t* offsets;
@@ -74,11 +81,45 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int MODE>
+// Eight E4M3 codes -> eight bf16 (up) or fp16 (down) values, exactly (the
+// hardware conversions decode OCP E4M3; every E4M3 value is representable).
+template <bool TO_F16>
+__device__ __forceinline__ u32x4 e4m3x8_to_16(u32x2 c) {
+  u32x4 r = {};
+#if __HIP_DEVICE_COMPILE__   // the host pass of the kernel does not see the gfx950 builtins
+  const int w0 = (int)c[0], w1 = (int)c[1];
+  if (TO_F16) {
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true));
+  } else {
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+  }
+#endif
+  return r;
+}
+
+// F8: the weights are E4M3 codes with per-row scales (applied to the
+// accumulated sums); a stage then covers 128 K-elements (128 weight bytes
+// per row, as for bf16 with 64) and carries 256 bytes of each token row.
+template <int MODE, bool F8>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   constexpr bool DOWN = MODE == DEC_DOWN, SWIGLU = MODE == MOE_SWIGLU;
+  constexpr int DR = DecodeTile<F8>::DR;    // weight rows per work item
+  constexpr int NST = DecodeTile<F8>::NST;  // LDS ring stages
+  constexpr int RG = DR / 16;               // MFMA row groups
+  constexpr int NDMA = DR / 8;              // weight DMA instructions per stage (8 rows each)
   static_assert(!SWIGLU || RG % 2 == 0, "SwiGLU pairs MFMA row groups of gate and up rows");
-  constexpr int LR = DR + 16;   // LDS rows per stage: DR weight rows, then 16 token rows
+  constexpr int WB = F8 ? 1 : 2;         // weight bytes
+  constexpr int SK = F8 ? 128 : 64;      // K elements per stage
+  constexpr int NSUBK = SK / 32;         // MFMA k-substeps per stage
+  constexpr int XR = F8 ? 32 : 16;       // 128-byte LDS rows of token data per stage
+  constexpr int NDX = XR / 8;            // their DMA instructions
+  constexpr int LR = DR + XR;            // LDS rows per stage: weights, then token rows
   // The ring as distinct arrays ([row][8 chunks of 16 bytes] each): the
   // compiler then sees that a DMA into one stage never aliases the fragment
   // reads of another and keeps its own waits per stage.
@@ -95,7 +136,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   const int ks = DOWN ? it % a.nsplit : 0;        // K slice
   const int klen = DOWN ? a.K / a.nsplit : a.K;
   const int k0 = ks * klen;
-  const int nk = klen / DK;
+  const int nk = klen / SK;
 
   // Buffer-resource DMA: uniform bases (the expert's matrix and the token
   // rows, from column k0), per-lane 32-bit byte offsets that stay fixed over
@@ -107,43 +148,48 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     if (SWIGLU) return r < DR / 2 ? nt * (DR / 2) + r : a.f + nt * (DR / 2) + (r - DR / 2);
     return nt * DR + r;
   };
-  const uint16_t* wseg = a.W + (long long)seg * a.Wrows * a.K + k0;
+  const char* wseg = (const char*)a.W + ((long long)seg * a.Wrows * a.K + k0) * WB;
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)wseg, (short)0, (int)(((long long)a.Wrows * a.K - k0) * 2), 0x00020000);
+      (void*)wseg, (short)0, (int)(((long long)a.Wrows * a.K - k0) * WB), 0x00020000);
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.X + k0), (short)0, (int)(a.xbytes - (long long)k0 * 2), 0x00020000);
-  uint32_t soff[NDMA], xoff[2];
+  uint32_t soff[NDMA], xoff[NDX];
 #pragma unroll
   for (int q = 0; q < NDMA; ++q) {
     const int r = 8 * q + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
-    soff[q] = ((uint32_t)weight_row(r) * (uint32_t)a.K + (uint32_t)c * 8u) * 2u;
+    soff[q] = (uint32_t)weight_row(r) * (uint32_t)a.K * WB + (uint32_t)c * 16u;
   }
   // token rows: x gathered through sorted_assign (up) or h (down); rows past
-  // the segment's count repeat a valid row and their outputs are not stored
+  // the segment's count repeat a valid row and their outputs are not stored.
+  // With F8 each token row of a stage spans two LDS rows (halves of 64).
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int t = 8 * q + (lane >> 3);
+  for (int q = 0; q < NDX; ++q) {
+    const int rl = 8 * q + (lane >> 3);
+    const int t = F8 ? rl >> 1 : rl, half = F8 ? rl & 1 : 0;
     const int tt = t < rows ? t : 0;
     uint32_t brow;
     if (DOWN) brow = (uint32_t)(start + tt);
     else brow = (uint32_t)(seg < a.E ? a.sorted_assign[start + tt] / a.k : tt);
-    const int c = (lane & 7) ^ (((DR + t) >> 1) & 7);
-    xoff[q] = (brow * (uint32_t)a.K + (uint32_t)c * 8u) * 2u;
+    const int c = (lane & 7) ^ (((DR + rl) >> 1) & 7);
+    xoff[q] = (brow * (uint32_t)a.K + (uint32_t)(half * 64 + c * 8)) * 2u;
   }
-  // fragment reads: A row 16q + tl and B row DR + tl, chunk 4h + g of half h
+  // fragment reads (byte offsets in a stage): A rows 16q + tl, B token row tl;
+  // k-substep u covers K elements 32u .. 32u+31 of the stage
   const int tl = lane & 15, g = lane >> 4;
   const bool tvalid = tl < rows;
-  int fpos[RG][2], bpos[2];
+  int fpos[RG][NSUBK], bpos[NSUBK];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int u = 0; u < NSUBK; ++u) {
 #pragma unroll
     for (int q = 0; q < RG; ++q) {
       const int r = 16 * q + tl;
-      fpos[q][h] = r * 8 + ((4 * h + g) ^ ((r >> 1) & 7));
+      if (F8) fpos[q][u] = r * 128 + (((2 * u + (g >> 1)) ^ ((r >> 1) & 7)) * 16) + 8 * (g & 1);
+      else fpos[q][u] = r * 128 + (((4 * u + g) ^ ((r >> 1) & 7)) * 16);
     }
-    const int rb = DR + tl;
-    bpos[h] = rb * 8 + ((4 * h + g) ^ ((rb >> 1) & 7));
+    const int rb = F8 ? DR + 2 * tl + (u >> 1) : DR + tl;
+    const int cb = F8 ? 4 * (u & 1) + g : 4 * u + g;
+    bpos[u] = rb * 128 + ((cb ^ ((rb >> 1) & 7)) * 16);
   }
 
   typedef __attribute__((address_space(3))) void lds_void_t;
@@ -154,34 +200,38 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   for (int q = 0; q < RG; ++q) acc[q] = f32x4{};
 
   auto issue = [&](u32x4* buf, int j) {
+#if __HIP_DEVICE_COMPILE__   // (with template-dependent operands the host pass drops the kernel)
 #pragma unroll
     for (int q = 0; q < NDMA; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t*)(buf + q * 64), 16, soff[q],
-                                               j * DK * 2, 0, 2 /* nt */);
+                                               j * SK * WB, 0, 2 /* nt */);
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < NDX; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_void_t*)(buf + (DR / 8 + q) * 64), 16,
-                                               xoff[q], j * DK * 2, 0, 0);
+                                               xoff[q], j * SK * 2, 0, 0);
+#endif
   };
   auto compute = [&](const u32x4* buf) {
+    const char* b = (const char*)buf;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const u32x4 xv = buf[bpos[h]];
+    for (int u = 0; u < NSUBK; ++u) {
+      const u32x4 xv = *(const u32x4*)(b + bpos[u]);
 #pragma unroll
       for (int q = 0; q < RG; ++q) {
-        const u32x4 w = buf[fpos[q][h]];
+        u32x4 w;
+        if (F8) w = e4m3x8_to_16<DOWN>(*(const u32x2*)(b + fpos[q][u]));
+        else w = DOWN ? bf16x8_to_f16x8(*(const u32x4*)(b + fpos[q][u])) : *(const u32x4*)(b + fpos[q][u]);
         if (DOWN)
           acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              __builtin_bit_cast(f16x8, bf16x8_to_f16x8(w)), __builtin_bit_cast(f16x8, xv),
-              acc[q], 0, 0, 0);
+              __builtin_bit_cast(f16x8, w), __builtin_bit_cast(f16x8, xv), acc[q], 0, 0, 0);
         else
           acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               __builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, xv), acc[q], 0, 0, 0);
       }
     }
   };
-  // Each stage is NDMA + 2 DMA loads; they complete in issue order.
-  constexpr int PER = NDMA + 2;
+  // Each stage is NDMA + NDX DMA loads; they complete in issue order.
+  constexpr int PER = NDMA + NDX;
   auto wait_stage = [&](int ahead) {   // stages issued after the one to consume
     if (NST >= 4 && ahead >= 3) wait_vm<3 * PER>();
     else if (NST >= 3 && ahead >= 2) wait_vm<2 * PER>();
@@ -222,7 +272,15 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   }
   if (!tvalid) return;
 
-  // D[row][token]: lane holds token tl and rows 16q + 4g + 0..3 of group q.
+  // D[row][token]: lane holds token tl and rows 16q + 4g + 0..3 of group q
+  // (consecutive weight rows, so their FP8 scales are one 16-byte load).
+  if (F8) {
+#pragma unroll
+    for (int q = 0; q < RG; ++q) {
+      const f32x4 sc = *(const f32x4*)(a.wscale + (long long)seg * a.Wrows + weight_row(16 * q + 4 * g));
+      acc[q] *= sc;
+    }
+  }
   const long long orow = start + tl;
   if (DOWN) {
     float* out = (float*)a.out + ks * a.part_stride + orow * a.Wrows + nt * DR + 4 * g;
@@ -289,35 +347,48 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
 }  // namespace
 
 hipError_t launch_decode_up(const Shape& s, const void* x, const void* w_up, const void* b_up,
-                            const int32_t* offsets, const int32_t* sorted_assign, void* h,
-                            hipStream_t st) {
+                            const float* s_up, const int32_t* offsets,
+                            const int32_t* sorted_assign, void* h, hipStream_t st) {
   const int nseg = s.E + s.S;
+  const int DR = s.w_fp8() ? DecodeTile<true>::DR : DecodeTile<false>::DR;
   const int items_per_seg = s.act == MOE_SWIGLU ? s.f / (DR / 2) : s.f / DR;
   const long long items = (long long)nseg * items_per_seg;
-  DecodeArgs a{(const uint16_t*)x, (const uint16_t*)w_up,
+  DecodeArgs a{(const uint16_t*)x, w_up, s_up,
                s.expert_bias() ? (const uint16_t*)b_up : nullptr, h, offsets, sorted_assign,
                s.T, s.k, s.E, s.S, s.d, s.up_rows(), s.f, 1, items_per_seg, 0,
                (long long)s.T * s.d * 2};
-  if (s.act == MOE_SWIGLU) decode_kernel<MOE_SWIGLU><<<(int)items, 64, 0, st>>>(a);
-  else if (s.act == MOE_GELU) decode_kernel<MOE_GELU><<<(int)items, 64, 0, st>>>(a);
-  else decode_kernel<MOE_RELU><<<(int)items, 64, 0, st>>>(a);
+#define MOE_DECODE_UP(A, F)                                      \
+  decode_kernel<A, F><<<(int)items, 64, 0, st>>>(a)
+  if (s.w_fp8()) {
+    if (s.act == MOE_SWIGLU) MOE_DECODE_UP(MOE_SWIGLU, true);
+    else if (s.act == MOE_GELU) MOE_DECODE_UP(MOE_GELU, true);
+    else MOE_DECODE_UP(MOE_RELU, true);
+  } else {
+    if (s.act == MOE_SWIGLU) MOE_DECODE_UP(MOE_SWIGLU, false);
+    else if (s.act == MOE_GELU) MOE_DECODE_UP(MOE_GELU, false);
+    else MOE_DECODE_UP(MOE_RELU, false);
+  }
+#undef MOE_DECODE_UP
   return hipGetLastError();
 }
 
 hipError_t launch_decode_down(const Shape& s, const void* h, const void* w_down,
-                              const void* b_down, const int32_t* offsets, float* y_exp,
-                              float* y_part, hipStream_t st) {
+                              const void* b_down, const float* s_down, const int32_t* offsets,
+                              float* y_exp, float* y_part, hipStream_t st) {
   const int nseg = s.E + s.S;
-  // K slices of a multiple of 64 elements (f is a multiple of 64)
-  const int nsplit = (s.f % (64 * kDecodeSplitK) == 0) ? kDecodeSplitK
-                     : (s.f % 128 == 0 ? 2 : 1);
+  // K slices of a whole number of stages (64 elements; 128 for FP8 weights)
+  const int sk = s.w_fp8() ? 128 : 64;
+  const int nsplit = (s.f % (sk * kDecodeSplitK) == 0) ? kDecodeSplitK
+                     : (s.f % (2 * sk) == 0 ? 2 : 1);
+  const int DR = s.w_fp8() ? DecodeTile<true>::DR : DecodeTile<false>::DR;
   const int items_per_seg = (s.d / DR) * nsplit;
   const long long items = (long long)nseg * items_per_seg;
   const long long part_stride = s.max_rows() * s.d;
-  DecodeArgs a{(const uint16_t*)h, (const uint16_t*)w_down, nullptr, y_part, offsets, nullptr,
+  DecodeArgs a{(const uint16_t*)h, w_down, s_down, nullptr, y_part, offsets, nullptr,
                s.T, s.k, s.E, s.S, s.f, s.d, s.f, nsplit, items_per_seg, part_stride,
                s.max_rows() * s.f * 2};
-  decode_kernel<DEC_DOWN><<<(int)items, 64, 0, st>>>(a);
+  if (s.w_fp8()) decode_kernel<DEC_DOWN, true><<<(int)items, 64, 0, st>>>(a);
+  else decode_kernel<DEC_DOWN, false><<<(int)items, 64, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long n = s.max_rows() * (s.d / 4);

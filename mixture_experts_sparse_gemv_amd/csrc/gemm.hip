@@ -536,15 +536,16 @@ int down_ksplit(const Shape& s) {
 }
 
 hipError_t launch_decode_up(const Shape& s, const void* x, const void* w_up, const void* b_up,
-                            const int32_t* offsets, const int32_t* sorted_assign, void* h,
-                            hipStream_t st);
+                            const float* s_up, const int32_t* offsets,
+                            const int32_t* sorted_assign, void* h, hipStream_t st);
 hipError_t launch_decode_down(const Shape& s, const void* h, const void* w_down,
-                              const void* b_down, const int32_t* offsets, float* y_exp,
-                              float* y_part, hipStream_t st);
+                              const void* b_down, const float* s_down, const int32_t* offsets,
+                              float* y_exp, float* y_part, hipStream_t st);
 
 hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void* b_up,
-                     const int32_t* offsets, const int32_t* sorted_assign, void* h,
-                     hipStream_t st) {
+                     const float* s_up, const int32_t* offsets, const int32_t* sorted_assign,
+                     void* h, hipStream_t st) {
+  if (s.w_fp8() && !s.decode()) return hipErrorNotSupported;   // rejected by validation
   const void* bias = s.expert_bias() ? b_up : nullptr;
   if (s.dtype == MOE_F32) {
     const long long n = s.max_rows() * s.f;
@@ -565,7 +566,7 @@ hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void
                                                           s.up_rows(), s.f);
     return hipGetLastError();
   }
-  if (s.decode()) return launch_decode_up(s, x, w_up, b_up, offsets, sorted_assign, h, st);
+  if (s.decode()) return launch_decode_up(s, x, w_up, b_up, s_up, offsets, sorted_assign, h, st);
   GemmArgs a{(const uint16_t*)x, (const uint16_t*)w_up, (const uint16_t*)bias, h, offsets,
              sorted_assign, s.T, s.k, s.E, s.S, s.d, s.f, s.up_rows(), s.f, 1, nullptr, 0};
   if (s.act == MOE_SWIGLU) {
@@ -585,8 +586,9 @@ hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void
 }
 
 hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const void* b_down,
-                       const int32_t* offsets, float* y_exp, float* y_part, bool complete,
-                       hipStream_t st) {
+                       const float* s_down, const int32_t* offsets, float* y_exp, float* y_part,
+                       bool complete, hipStream_t st) {
+  if (s.w_fp8() && !s.decode()) return hipErrorNotSupported;   // rejected by validation
   const void* bias = s.expert_bias() ? b_down : nullptr;
   if (s.dtype == MOE_F32) {
     const long long n = s.max_rows() * s.d;
@@ -596,7 +598,8 @@ hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const 
         s.k, s.E, s.S, s.f, s.d, s.d, s.f);
     return hipGetLastError();
   }
-  if (s.decode()) return launch_decode_down(s, h, w_down, b_down, offsets, y_exp, y_part, st);
+  if (s.decode())
+    return launch_decode_down(s, h, w_down, b_down, s_down, offsets, y_exp, y_part, st);
   const int ks = down_ksplit(s);
   const long long part_elems = s.max_rows() * s.d;
   GemmArgs a{(const uint16_t*)h, (const uint16_t*)w_down, (const uint16_t*)bias, y_exp, offsets,

@@ -60,7 +60,7 @@ static moe_status check_problem(const moe_problem* p, Shape& s) {
   if (p->dtype != MOE_F32 && p->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (p->gating != MOE_SOFTMAX && p->gating != MOE_SIGMOID_NORM) return MOE_ERR_INVALID_ARG;
   if (p->activation < MOE_RELU || p->activation > MOE_SWIGLU) return MOE_ERR_INVALID_ARG;
-  if (p->flags & ~(MOE_ROUTER_BIAS | MOE_EXPERT_BIAS)) return MOE_ERR_INVALID_ARG;
+  if (p->flags & ~(MOE_ROUTER_BIAS | MOE_EXPERT_BIAS | MOE_W_FP8)) return MOE_ERR_INVALID_ARG;
   if (p->num_experts > kMaxExperts || p->top_k > kMaxTopK ||
       p->num_experts + p->num_shared > kMaxSegments)
     return MOE_ERR_UNSUPPORTED;
@@ -70,6 +70,10 @@ static moe_status check_problem(const moe_problem* p, Shape& s) {
     return MOE_ERR_UNSUPPORTED;
   if (p->dtype == MOE_BF16 && (p->d_model % 64 != 0 || p->d_ff % 64 != 0))
     return MOE_ERR_UNSUPPORTED;
+  if (p->flags & MOE_W_FP8) {   // FP8 expert weights: the weight-streaming decode path only
+    if (p->dtype != MOE_BF16 || p->T > kDecodeMaxT || p->d_model % 128 != 0 || p->d_ff % 128 != 0)
+      return MOE_ERR_UNSUPPORTED;
+  }
   // one expert's weight matrix must stay below 4 GiB (32-bit offsets in the kernels)
   const long long f1 = p->activation == MOE_SWIGLU ? 2LL * p->d_ff : p->d_ff;
   if (f1 * p->d_model * 4 >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
@@ -99,6 +103,7 @@ static moe_status check_weights(const Shape& s, const moe_weights* w, bool route
   if (router && (!w->w_router || (s.router_bias() && !w->b_router))) return MOE_ERR_INVALID_ARG;
   if (experts && (!w->w_up || !w->w_down)) return MOE_ERR_INVALID_ARG;
   if (experts && s.expert_bias() && (!w->b_up || !w->b_down)) return MOE_ERR_INVALID_ARG;
+  if (experts && s.w_fp8() && (!w->s_up || !w->s_down)) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
@@ -175,7 +180,7 @@ moe_status moe_expert_up(const moe_problem* p, const void* x, const moe_weights*
   (void)ws;  // the up projection needs no scratch
   (void)ws_bytes;
   (void)L;
-  return fail_hip(launch_up(s, x, w->w_up, w->b_up, offsets, sorted_assign, h, stream));
+  return fail_hip(launch_up(s, x, w->w_up, w->b_up, w->s_up, offsets, sorted_assign, h, stream));
 }
 
 moe_status moe_expert_down(const moe_problem* p, const moe_weights* w, const int32_t* offsets,
@@ -188,7 +193,7 @@ moe_status moe_expert_down(const moe_problem* p, const moe_weights* w, const int
   if ((st = check_weights(s, w, false, true)) != MOE_OK) return st;
   if (!offsets || !h || !y_exp) return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(s, ws, ws_bytes, L)) != MOE_OK) return st;
-  return fail_hip(launch_down(s, h, w->w_down, w->b_down, offsets, y_exp,
+  return fail_hip(launch_down(s, h, w->w_down, w->b_down, w->s_down, offsets, y_exp,
                               at<float>(ws, L.y_part), true, stream));
 }
 
@@ -203,9 +208,9 @@ moe_status moe_expert_ffn(const moe_problem* p, const void* x, const moe_weights
   if (!x || !offsets || !sorted_assign || !y_exp) return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(s, ws, ws_bytes, L)) != MOE_OK) return st;
   void* h = at<void>(ws, L.h);
-  hipError_t e = launch_up(s, x, w->w_up, w->b_up, offsets, sorted_assign, h, stream);
+  hipError_t e = launch_up(s, x, w->w_up, w->b_up, w->s_up, offsets, sorted_assign, h, stream);
   if (e == hipSuccess)
-    e = launch_down(s, h, w->w_down, w->b_down, offsets, y_exp, at<float>(ws, L.y_part), true,
+    e = launch_down(s, h, w->w_down, w->b_down, w->s_down, offsets, y_exp, at<float>(ws, L.y_part), true,
                     stream);
   return fail_hip(e);
 }
@@ -235,6 +240,13 @@ moe_status moe_routing_stats(const moe_problem* p, const int32_t* counts, const 
   if (st != MOE_OK) return st;
   if (!counts || !kept || !P || !stats) return MOE_ERR_INVALID_ARG;
   return fail_hip(launch_routing_stats(s, counts, kept, P, stats, stream));
+}
+
+moe_status moe_quantize_fp8(const void* w, int64_t rows, int32_t cols, uint8_t* q, float* scale,
+                            hipStream_t stream) {
+  if (!w || !q || !scale || rows <= 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
+  if (rows >= (1LL << 31) || cols % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  return fail_hip(launch_quantize_fp8(w, rows, cols, q, scale, stream));
 }
 
 moe_status moe_ffn_forward(const moe_problem* p, const moe_weights* w, const void* x, float* y,
@@ -271,12 +283,12 @@ moe_status moe_ffn_forward(const moe_problem* p, const moe_weights* w, const voi
     e = launch_dispatch(s, topk_idx, chunk_counts, true, at<int32_t>(ws, L.sb_prefix), counts,
                         kept, offsets, sorted_assign, assign_row, drop_mask, part,
                         at<float>(ws, L.prob_colsum), f, P, l_aux, r.stats, stream);
-  if (e == hipSuccess) e = launch_up(s, x, w->w_up, w->b_up, offsets, sorted_assign, h, stream);
+  if (e == hipSuccess) e = launch_up(s, x, w->w_up, w->b_up, w->s_up, offsets, sorted_assign, h, stream);
   // The down projection's K slices (if any) are summed by the combine.
   float* y_part = at<float>(ws, L.y_part);
   const int nparts = s.decode() ? 0 : down_ksplit(s) - 1;
   if (e == hipSuccess)
-    e = launch_down(s, h, w->w_down, w->b_down, offsets, y_exp, y_part, nparts == 0, stream);
+    e = launch_down(s, h, w->w_down, w->b_down, w->s_down, offsets, y_exp, y_part, nparts == 0, stream);
   if (e == hipSuccess)
     e = launch_combine(s, topk_w, assign_row, offsets, y_exp, y_part, nparts, y, stream);
   return fail_hip(e);

@@ -25,6 +25,7 @@ struct Shape {
   bool router_bias() const { return flags & MOE_ROUTER_BIAS; }
   bool expert_bias() const { return (flags & MOE_EXPERT_BIAS) && act != MOE_SWIGLU; }
   bool decode() const { return dtype == MOE_BF16 && T <= kDecodeMaxT; }
+  bool w_fp8() const { return flags & MOE_W_FP8; }
 };
 
 // Router blocks each handle this many tokens (their per-expert probability
@@ -139,16 +140,19 @@ hipError_t launch_routing_stats(const Shape& s, const int32_t* counts, const int
                                 const float* P, moe_route_stats* stats, hipStream_t st);
 hipError_t launch_aux(const Shape& s, const float* colsum, const int32_t* counts, float* f,
                       float* P, float* l_aux, hipStream_t st);
+// s_up / s_down: FP8 row scales (MOE_W_FP8), else ignored.
 hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void* b_up,
-                     const int32_t* offsets, const int32_t* sorted_assign, void* h,
-                     hipStream_t st);
+                     const float* s_up, const int32_t* offsets, const int32_t* sorted_assign,
+                     void* h, hipStream_t st);
 // complete = true: y_exp holds the whole result on return (K slices folded);
 // false: slices 1.. stay in y_part for the combine to add (down_ksplit(s) - 1
 // of them).
 hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const void* b_down,
-                       const int32_t* offsets, float* y_exp, float* y_part, bool complete,
-                       hipStream_t st);
+                       const float* s_down, const int32_t* offsets, float* y_exp, float* y_part,
+                       bool complete, hipStream_t st);
 // y_part/nparts: K-slice partials of y_exp still to be added (nparts = 0: none).
+hipError_t launch_quantize_fp8(const void* w, long long rows, int cols, uint8_t* q, float* scales,
+                               hipStream_t st);
 hipError_t launch_combine(const Shape& s, const float* topk_w, const int32_t* assign_row,
                           const int32_t* offsets, const float* y_exp, const float* y_part,
                           int nparts, float* y, hipStream_t st);

@@ -19,12 +19,13 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID_NORM = 0, 1
 MOE_RELU, MOE_GELU, MOE_SWIGLU = 0, 1, 2
-MOE_ROUTER_BIAS, MOE_EXPERT_BIAS = 1, 2
+MOE_ROUTER_BIAS, MOE_EXPERT_BIAS, MOE_W_FP8 = 1, 2, 8
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_capacity", "moe_workspace_size", "moe_router_topk", "moe_dispatch",
            "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_aux_stats",
-           "moe_routing_stats", "moe_ffn_forward", "moe_status_string", "moe_last_hip_error")
+           "moe_routing_stats", "moe_quantize_fp8", "moe_ffn_forward", "moe_status_string",
+           "moe_last_hip_error")
 
 
 class moe_problem(ctypes.Structure):
@@ -35,7 +36,7 @@ class moe_problem(ctypes.Structure):
 
 class moe_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("w_router", "b_router", "w_up", "b_up", "w_down", "b_down")]
+                ("w_router", "b_router", "w_up", "b_up", "w_down", "b_down", "s_up", "s_down")]
 
 
 class moe_routing(ctypes.Structure):
@@ -75,6 +76,7 @@ def _load(path=LIB_PATH):
         "moe_combine": (I32, [pp, V, V, V, V, V, V]),
         "moe_aux_stats": (I32, [pp, V, V, V, V, V, V]),
         "moe_routing_stats": (I32, [pp, V, V, V, V, V]),
+        "moe_quantize_fp8": (I32, [V, ctypes.c_int64, I32, V, V, V]),
         "moe_ffn_forward": (I32, [pp, pw, V, V, pr, V, SZ, V]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
         "moe_last_hip_error": (I32, []),
@@ -92,18 +94,21 @@ _lib = _load()
 
 def make_problem(T, d_model, d_ff, num_experts, top_k, num_shared=0, capacity=0,
                  dtype="bf16", gating="softmax", activation="swiglu", router_bias=False,
-                 expert_bias=False):
+                 expert_bias=False, w_fp8=False):
     return moe_problem(
         T=T, d_model=d_model, d_ff=d_ff, num_experts=num_experts, top_k=top_k,
         num_shared=num_shared, capacity=capacity or 0,
         dtype={"f32": MOE_F32, "bf16": MOE_BF16}[dtype],
         gating={"softmax": MOE_SOFTMAX, "sigmoid_norm": MOE_SIGMOID_NORM}[gating],
         activation={"relu": MOE_RELU, "gelu": MOE_GELU, "swiglu": MOE_SWIGLU}[activation],
-        flags=(MOE_ROUTER_BIAS if router_bias else 0) | (MOE_EXPERT_BIAS if expert_bias else 0))
+        flags=(MOE_ROUTER_BIAS if router_bias else 0) | (MOE_EXPERT_BIAS if expert_bias else 0) |
+        (MOE_W_FP8 if w_fp8 else 0))
 
 
-def make_weights(w_router, b_router, w_up, b_up, w_down, b_down):
-    return moe_weights(*[_ptr(t) for t in (w_router, b_router, w_up, b_up, w_down, b_down)])
+def make_weights(w_router, b_router, w_up, b_up, w_down, b_down, s_up=None, s_down=None):
+    """s_up / s_down: the FP8 row scales when w_up / w_down hold E4M3 codes."""
+    return moe_weights(*[_ptr(t) for t in (w_router, b_router, w_up, b_up, w_down, b_down,
+                                           s_up, s_down)])
 
 
 def _ptr(t):
@@ -251,6 +256,19 @@ def moe_routing_stats(p, counts, kept, P, stats, stream=None):
     _need(stats, 8, torch.int32, "stats")
     _check("moe_routing_stats", _lib.moe_routing_stats(
         ctypes.byref(p), _ptr(counts), _ptr(kept), _ptr(P), _ptr(stats), _stream(stream)))
+
+
+def moe_quantize_fp8(w, q, scale, stream=None):
+    """Per-row FP8 E4M3 codes of a bf16 tensor whose last dimension is the
+    row length: q (uint8, same shape), scale (float32, one per row)."""
+    cols = w.shape[-1]
+    rows = w.numel() // cols
+    if w.dtype != torch.bfloat16:
+        raise ValueError("w must be bfloat16")
+    _need(q, w.numel(), torch.uint8, "q")
+    _need(scale, rows, torch.float32, "scale")
+    _check("moe_quantize_fp8", _lib.moe_quantize_fp8(_ptr(w), rows, cols, _ptr(q), _ptr(scale),
+                                                     _stream(stream)))
 
 
 def moe_ffn_forward(p, w, x, y, ws, routing=None, stream=None):

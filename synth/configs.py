@@ -44,6 +44,7 @@ class Run:
     router_w_std: float = 0.02
     skew_b0: float = 0.0      # router bias of expert 0 for router_bias == "skew"
     zipf_s: float = 1.1       # exponent for router_bias == "zipf"
+    w_fp8: bool = False       # expert weights prepared as per-row FP8 E4M3 (drawn as for bf16)
     description: str = ""
 
     @property
@@ -87,6 +88,12 @@ RUNS = {
         num_shared=0, gating="softmax", activation="swiglu", router_bias="none",
         expert_bias=False, dtype="bf16", capacity_factor=None, seed=4, x_rows=8192,
         description="T=16 d=4096 f=14336 E=8 top-2 softmax SwiGLU bf16 (decode)"),
+    "large_decode_fp8": Run(
+        name="large_decode_fp8", T=16, d_model=4096, d_ff=14336, num_experts=8, top_k=2,
+        num_shared=0, gating="softmax", activation="swiglu", router_bias="none",
+        expert_bias=False, dtype="bf16", capacity_factor=None, seed=4, x_rows=8192, w_fp8=True,
+        description="T=16 d=4096 f=14336 E=8 top-2 softmax SwiGLU, bf16 activations, "
+                    "FP8 E4M3 expert weights with per-row scales (decode)"),
     "large_prefill": Run(
         name="large_prefill", T=8192, d_model=4096, d_ff=14336, num_experts=8, top_k=2,
         num_shared=0, gating="softmax", activation="swiglu", router_bias="none",

@@ -47,27 +47,57 @@ def problem_of(run, capacity=None):
         T=run.T, d_model=run.d_model, d_ff=run.d_ff, num_experts=run.num_experts,
         top_k=run.top_k, num_shared=run.num_shared, capacity=cap, dtype=run.dtype,
         gating=run.gating, activation=run.activation,
-        router_bias=run.router_bias != "none", expert_bias=run.expert_bias)
+        router_bias=run.router_bias != "none", expert_bias=run.expert_bias, w_fp8=run.w_fp8)
 
 
 def oracle_capacity(run):
     return O.capacity(run.T, run.top_k, run.num_experts, run.capacity_factor)
 
 
-def gpu_inputs(inp):
-    return {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+def gpu_inputs(inp, w_fp8=False):
+    """The inputs on the GPU; with w_fp8 the expert weights are replaced by
+    their per-row FP8 codes (moe_quantize_fp8) and scales s_up, s_down."""
+    g = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    if w_fp8:
+        for name, sname in (("w_up", "s_up"), ("w_down", "s_down")):
+            w = g[name]
+            q = torch.empty(w.shape, dtype=torch.uint8, device="cuda")
+            sc = torch.empty(w.numel() // w.shape[-1], dtype=torch.float32, device="cuda")
+            M.moe_quantize_fp8(w, q, sc)
+            g[name], g[sname] = q, sc
+            del w
+        torch.cuda.synchronize()
+    return g
 
 
 def weights_of(g):
     return M.make_weights(g["w_router"], g["b_router"], g["w_up"], g["b_up"], g["w_down"],
-                          g["b_down"])
+                          g["b_down"], g.get("s_up"), g.get("s_down"))
 
 
-def oracle_forward(run, inp, cap="run", token_subset=None):
+class LazyDeqFP8:
+    """Per-expert float64 weights of a [n, rows, K] bf16 tensor as the oracle
+    quantizes them (codes and scales from the oracle's own quantizer)."""
+
+    def __init__(self, t):
+        self.t = t
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, i):
+        w = self.t[i].to(torch.float32).numpy()
+        codes, scales = O.quantize_fp8_rows(w)
+        return O.dequantize_fp8_rows(codes, scales)
+
+
+def oracle_forward(run, inp, cap="run", token_subset=None, w_fp8=None):
+    """w_fp8 (default: run.w_fp8): expert weights as the oracle's own FP8
+    quantization of the bf16 weights, dequantized exactly."""
     c = oracle_capacity(run) if cap == "run" else cap
+    fp8 = run.w_fp8 if w_fp8 is None else w_fp8
     lazy = lambda t: None if t is None else LazyF64(t)
+    lazyw = (lambda t: LazyDeqFP8(t)) if fp8 else lazy
     return O.forward(to_f64(inp["x"]), to_f64(inp["w_router"]), to_f64(inp["b_router"]),
-                     lazy(inp["w_up"]), lazy(inp["b_up"]), lazy(inp["w_down"]),
+                     lazyw(inp["w_up"]), lazy(inp["b_up"]), lazyw(inp["w_down"]),
                      lazy(inp["b_down"]), top_k=run.top_k, num_shared=run.num_shared,
                      gating=run.gating, activation=run.activation, cap=c,
                      token_subset=token_subset)

@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol():
@@ -106,7 +106,7 @@ def test_forward_rejects_before_launch():
     assert lib.moe_ffn_forward(ctypes.byref(p), None, fake, fake, None, fake, need,
                                None) == M.MOE_ERR_INVALID_ARG
     # unknown flags / enums
-    for bad in (dict(flags=8), dict(dtype=7), dict(gating=3), dict(activation=5)):
+    for bad in (dict(flags=16), dict(dtype=7), dict(gating=3), dict(activation=5)):
         q = _problem()
         for k, v in bad.items():
             setattr(q, k, v)
@@ -135,3 +135,26 @@ def test_stage_entry_points_reject_null_outputs():
     assert lib.moe_aux_stats(byref(p), fake, fake, fake, None, fake, None) == M.MOE_ERR_INVALID_ARG
     assert lib.moe_routing_stats(byref(p), fake, fake, fake, None, None) == M.MOE_ERR_INVALID_ARG
     assert lib.moe_status_string(M.MOE_ERR_HIP) == b"MOE_ERR_HIP"
+
+
+def test_fp8_weights_validation():
+    fake = 0x1000
+    lib = M._lib
+    byref = ctypes.byref
+    # FP8 expert weights are for the decode path only (T <= 16), bf16, d and f multiples of 128
+    for kw in (dict(T=17), dict(dtype="f32"), dict(d_model=192), dict(d_ff=320)):
+        args = dict(T=16, d_model=256, d_ff=512, num_experts=8, top_k=2, w_fp8=True)
+        args.update(kw)
+        p = M.make_problem(**args)
+        n = ctypes.c_size_t(0)
+        assert lib.moe_workspace_size(byref(p), byref(n)) == M.MOE_ERR_UNSUPPORTED, kw
+    p = M.make_problem(T=16, d_model=256, d_ff=512, num_experts=8, top_k=2, w_fp8=True)
+    need = M.moe_workspace_size(p)
+    w = M.moe_weights(fake, None, fake, None, fake, None, None, None)   # scales missing
+    assert lib.moe_ffn_forward(byref(p), byref(w), fake, fake, None, fake, need,
+                               None) == M.MOE_ERR_INVALID_ARG
+    # quantizer arguments
+    assert lib.moe_quantize_fp8(None, 4, 64, fake, fake, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_fp8(fake, 0, 64, fake, fake, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_fp8(fake, 4, 60, fake, fake, None) == M.MOE_ERR_UNSUPPORTED
+    assert lib.moe_quantize_fp8(fake, 1 << 31, 64, fake, fake, None) == M.MOE_ERR_UNSUPPORTED
