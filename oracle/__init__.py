@@ -6,4 +6,5 @@ from . import moe_oracle
 from .moe_oracle import (router_logits, softmax, sigmoid_normalized, gate, topk_renorm,
                          selection_gap, capacity, dispatch, gelu, silu, expert_ffn,
                          combine_rows, aux_stats, routing_stats, forward,
-                         e4m3_values, quantize_fp8_rows, dequantize_fp8_rows)
+                         e4m3_values, quantize_fp8_rows, dequantize_fp8_rows,
+                         expert_choice_select, expert_choice_gap, forward_expert_choice)

@@ -280,6 +280,72 @@ def routing_stats(counts, kept, P):
 
 
 # ----------------------------------------------------------------------------
+# Expert-choice routing ([bojinhu] 二 2.2: each expert picks the Top-K tokens it
+# is best at; every expert's load is then exactly equal, a token can be picked
+# by several experts or by none)
+# ----------------------------------------------------------------------------
+
+
+def expert_choice_select(probs, C):
+    """Each expert e keeps the C tokens with the largest probs[t, e]; equal
+    scores go to the lower token index.  Readings: the affinity is the gate
+    probability of token-choice routing, C is the per-expert capacity.
+    Returns sel [E, C] (each expert's tokens in ascending order), row_of [T, E]
+    (row e*C + position of (t, e), -1 if e did not pick t) and token_experts
+    [T] (how many experts picked each token; 0 = an orphan token)."""
+    T, E = probs.shape
+    sel = np.empty((E, C), dtype=np.int64)
+    row_of = np.full((T, E), -1, dtype=np.int64)
+    for e in range(E):
+        order = np.lexsort((np.arange(T), -probs[:, e]))   # by score desc, then token asc
+        chosen = np.sort(order[:C])
+        sel[e] = chosen
+        row_of[chosen, e] = e * C + np.arange(C)
+    token_experts = (row_of >= 0).sum(axis=1)
+    return sel, row_of, token_experts
+
+
+def expert_choice_gap(probs, C):
+    """Per expert, the score gap between its C-th and (C+1)-th best tokens
+    (inf when C >= T): selections agree wherever this gap is clear."""
+    T, E = probs.shape
+    if C >= T:
+        return np.full(E, np.inf)
+    srt = -np.sort(-probs, axis=0)
+    return srt[C - 1] - srt[C]
+
+
+def forward_expert_choice(x, w_router, b_router, w_up, b_up, w_down, b_down, *, capacity,
+                          num_shared, gating, activation, token_subset=None):
+    """MoE-FFN forward with expert-choice routing: router -> gate -> each
+    expert takes its top-C tokens -> expert FFNs -> y[t] = sum over the
+    experts e that picked t of p[t, e] * FFN_e(x_t) (no renormalization; an
+    orphan token gets only the shared experts) + shared experts."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    logits = router_logits(x, w_router, b_router)
+    probs = gate(logits, gating)
+    sel, row_of, token_experts = expert_choice_select(probs, capacity)
+    toks = np.arange(T) if token_subset is None else np.asarray(token_subset)
+    pos = {int(t): i for i, t in enumerate(toks)}
+    y = np.zeros((len(toks), d), dtype=np.float64)
+    for e in range(E):
+        tt = np.array([t for t in sel[e] if int(t) in pos], dtype=np.int64)
+        if tt.size == 0:
+            continue
+        out = expert_ffn(x[tt], w_up[e], None if b_up is None else b_up[e],
+                         w_down[e], None if b_down is None else b_down[e], activation)
+        for i, t in enumerate(tt):
+            y[pos[int(t)]] += probs[t, e] * out[i]
+    for q in range(num_shared):
+        qq = E + q
+        y += expert_ffn(x[toks], w_up[qq], None if b_up is None else b_up[qq],
+                        w_down[qq], None if b_down is None else b_down[qq], activation)
+    return dict(logits=logits, probs=probs, sel=sel, row_of=row_of, token_experts=token_experts,
+                gap=expert_choice_gap(probs, capacity), y=y, tokens=toks)
+
+
+# ----------------------------------------------------------------------------
 # FP8 expert weights ([0539edu] 5.2: quantize expert parameters from 16 bits
 # to INT8 or FP8 to halve their memory)
 # ----------------------------------------------------------------------------

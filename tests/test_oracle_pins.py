@@ -536,3 +536,72 @@ def test_fp8_rows_scale_error_bound_and_zero_row():
     v = (w[0] / scales[0]).astype(np.float64)
     nearest = np.abs(vals[None, :] - v[:, None]).min(axis=1)
     assert np.allclose(np.abs(back[0] / scales[0] - v), nearest, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- expert-choice routing
+
+def test_expert_choice_hand_example():
+    # 4 tokens, 2 experts, C = 2.  Expert 0 scores (.5, .2, .5, .1): tie at .5
+    # -> tokens 0 and 2; expert 1 scores (.5, .8, .5, .9) -> tokens 3 and 1.
+    probs = np.array([[0.5, 0.5], [0.2, 0.8], [0.5, 0.5], [0.1, 0.9]])
+    sel, row_of, te = O.expert_choice_select(probs, 2)
+    assert sel.tolist() == [[0, 2], [1, 3]]
+    assert row_of.tolist() == [[0, -1], [-1, 2], [1, -1], [-1, 3]]
+    assert te.tolist() == [1, 1, 1, 1]
+    # ties go to the lower token index
+    sel, _, te = O.expert_choice_select(np.array([[0.3, 0.7]] * 5), 3)
+    assert sel.tolist() == [[0, 1, 2], [0, 1, 2]] and te.tolist() == [2, 2, 2, 0, 0]
+
+
+def test_expert_choice_bruteforce_and_balance():
+    rng = np.random.default_rng(4)
+    for T, E, C in [(9, 3, 4), (20, 5, 7), (6, 4, 6)]:
+        probs = np.round(rng.random((T, E)), 1)   # many ties
+        sel, row_of, te = O.expert_choice_select(probs, C)
+        for e in range(E):
+            ranked = sorted(range(T), key=lambda t: (-probs[t, e], t))[:C]
+            assert sel[e].tolist() == sorted(ranked)
+            assert np.array_equal(np.flatnonzero(row_of[:, e] >= 0), sel[e])
+            assert np.array_equal(row_of[sel[e], e], e * C + np.arange(C))
+        assert te.sum() == E * C                   # exactly C tokens per expert
+        assert np.array_equal(te, (row_of >= 0).sum(1))
+
+
+def test_expert_choice_capacity_T_is_the_probability_mixture():
+    # every expert takes every token: y = sum_e p[t,e] FFN_e(x_t), the dense
+    # soft mixture, which equals token choice with k = E
+    rng = np.random.default_rng(8)
+    T, d, f, E = 6, 5, 7, 3
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d))
+    w_up = rng.standard_normal((E, f, d)) * 0.3
+    w_dn = rng.standard_normal((E, d, f)) * 0.3
+    ec = O.forward_expert_choice(x, wr, None, w_up, None, w_dn, None, capacity=T, num_shared=0,
+                                 gating="softmax", activation="relu")
+    tc = O.forward(x, wr, None, w_up, None, w_dn, None, top_k=E, num_shared=0,
+                   gating="softmax", activation="relu")
+    assert np.allclose(ec["y"], tc["y"], rtol=1e-12, atol=1e-13)
+    assert np.all(ec["token_experts"] == E)
+
+
+def test_expert_choice_orphans_get_only_shared_experts():
+    rng = np.random.default_rng(9)
+    T, d, f, E, S = 10, 4, 6, 2, 1
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d))
+    w_up = rng.standard_normal((E + S, f, d)) * 0.3
+    w_dn = rng.standard_normal((E + S, d, f)) * 0.3
+    out = O.forward_expert_choice(x, wr, None, w_up, None, w_dn, None, capacity=2, num_shared=S,
+                                  gating="softmax", activation="gelu")
+    orphans = np.flatnonzero(out["token_experts"] == 0)
+    assert orphans.size >= T - 2 * E
+    shared = O.expert_ffn(x[orphans], w_up[E], None, w_dn[E], None, "gelu")
+    assert np.allclose(out["y"][orphans], shared, rtol=1e-13, atol=1e-14)
+    # a picked token: its experts' weighted outputs plus the shared expert
+    t = int(np.flatnonzero(out["token_experts"] > 0)[0])
+    ref = O.expert_ffn(x[[t]], w_up[E], None, w_dn[E], None, "gelu")[0]
+    for e in range(E):
+        if out["row_of"][t, e] >= 0:
+            ref = ref + out["probs"][t, e] * O.expert_ffn(x[[t]], w_up[e], None, w_dn[e], None,
+                                                          "gelu")[0]
+    assert np.allclose(out["y"][t], ref, rtol=1e-12, atol=1e-14)
