@@ -92,21 +92,28 @@ def main():
                        top_k=run.top_k, num_shared=run.num_shared, capacity=cap,
                        dtype=run.dtype, gating=run.gating, activation=run.activation,
                        router_bias=run.router_bias != "none", expert_bias=run.expert_bias,
-                       w_fp8=run.w_fp8)
+                       w_fp8=run.w_fp8, expert_choice=run.expert_choice)
     w = M.make_weights(g["w_router"], g["b_router"], g["w_up"], g["b_up"], g["w_down"],
                        g["b_down"], g.get("s_up"), g.get("s_down"))
     ws = M.workspace(p, dev)
     y = torch.empty(run.T * run.d_model, dtype=torch.float32, device=dev)
     E, k, T = run.num_experts, run.top_k, run.T
     i32 = dict(dtype=torch.int32, device=dev)
-    r = dict(topk_idx=torch.empty(T * k, **i32), topk_w=torch.empty(T * k, dtype=torch.float32,
-                                                                      device=dev),
-             counts=torch.empty(E, **i32), kept=torch.empty(E, **i32),
-             offsets=torch.empty(E + 1, **i32), sorted_assign=torch.empty(T * k, **i32),
-             assign_row=torch.empty(T * k, **i32),
-             drop_mask=torch.empty(T * k, dtype=torch.uint8, device=dev),
-             f=torch.empty(E, device=dev), P=torch.empty(E, device=dev),
-             l_aux=torch.empty(1, device=dev))
+    if run.expert_choice:   # experts pick their tokens: E*cap rows, [T, E] rows and weights
+        r = dict(probs=torch.empty(T * E, dtype=torch.float32, device=dev),
+                 counts=torch.empty(E, **i32), kept=torch.empty(E, **i32),
+                 offsets=torch.empty(E + 1, **i32), sorted_assign=torch.empty(E * cap, **i32),
+                 assign_row=torch.empty(T * E, **i32), f=torch.empty(E, device=dev),
+                 P=torch.empty(E, device=dev), l_aux=torch.empty(1, device=dev))
+    else:
+        r = dict(topk_idx=torch.empty(T * k, **i32),
+                 topk_w=torch.empty(T * k, dtype=torch.float32, device=dev),
+                 counts=torch.empty(E, **i32), kept=torch.empty(E, **i32),
+                 offsets=torch.empty(E + 1, **i32), sorted_assign=torch.empty(T * k, **i32),
+                 assign_row=torch.empty(T * k, **i32),
+                 drop_mask=torch.empty(T * k, dtype=torch.uint8, device=dev),
+                 f=torch.empty(E, device=dev), P=torch.empty(E, device=dev),
+                 l_aux=torch.empty(1, device=dev))
     print(f"bench: {name} T={T} d={run.d_model} f={run.d_ff} E={E} k={k} S={run.num_shared} "
           f"cap={cap} warmup={a.warmup} steps={a.steps}", file=sys.stderr, flush=True)
 
@@ -150,16 +157,23 @@ def main():
     def staged(evs=None):
         rec = (lambda i: evs[i].record(stream)) if evs else (lambda i: None)
         rec(0)
-        M.moe_router_topk(p, g["x"], w, r["topk_idx"], r["topk_w"], None, part, ws=ws)
-        rec(1)
-        M.moe_dispatch(p, r["topk_idx"], r["counts"], r["kept"], r["offsets"],
-                       r["sorted_assign"], r["assign_row"], r["drop_mask"], ws=ws)
+        if run.expert_choice:
+            M.moe_router_topk(p, g["x"], w, None, None, r["probs"], part, ws=ws)
+            rec(1)
+            M.moe_expert_choice(p, r["probs"], r["offsets"], r["sorted_assign"], r["assign_row"],
+                                ws=ws)
+        else:
+            M.moe_router_topk(p, g["x"], w, r["topk_idx"], r["topk_w"], None, part, ws=ws)
+            rec(1)
+            M.moe_dispatch(p, r["topk_idx"], r["counts"], r["kept"], r["offsets"],
+                           r["sorted_assign"], r["assign_row"], r["drop_mask"], ws=ws)
         rec(2)
         M.moe_expert_up(p, g["x"], w, r["offsets"], r["sorted_assign"], h)
         rec(3)
         M.moe_expert_down(p, w, r["offsets"], h, y_exp, ws)
         rec(4)
-        M.moe_combine(p, r["topk_w"], r["assign_row"], r["offsets"], y_exp, y)
+        M.moe_combine(p, r["probs"] if run.expert_choice else r["topk_w"], r["assign_row"],
+                      r["offsets"], y_exp, y)
         rec(5)
 
     for _ in range(a.warmup):
@@ -255,6 +269,8 @@ def cpu_baseline(run, cap, seconds):
         threads = os.cpu_count()
     inp = make_inputs(run)
     f64 = lambda t: None if t is None else _Lazy(t)
+    # FP8 expert weights: the oracle's own quantization, dequantized exactly
+    f64w = (lambda t: _LazyFP8(t, O)) if run.w_fp8 else f64
     x, wr = to_f64(inp["x"]), to_f64(inp["w_router"])
     br = None if inp["b_router"] is None else to_f64(inp["b_router"])
     ocap = O.capacity(run.T, run.top_k, run.num_experts, run.capacity_factor)
@@ -264,9 +280,15 @@ def cpu_baseline(run, cap, seconds):
     n_tok = run.T if sub is None else len(sub)
     reps, t0 = 0, time.perf_counter()
     while True:
-        O.forward(x, wr, br, f64(inp["w_up"]), f64(inp["b_up"]), f64(inp["w_down"]),
-                  f64(inp["b_down"]), top_k=run.top_k, num_shared=run.num_shared,
-                  gating=run.gating, activation=run.activation, cap=ocap, token_subset=sub)
+        if run.expert_choice:
+            O.forward_expert_choice(x, wr, br, f64w(inp["w_up"]), f64(inp["b_up"]),
+                                    f64w(inp["w_down"]), f64(inp["b_down"]), capacity=ocap,
+                                    num_shared=run.num_shared, gating=run.gating,
+                                    activation=run.activation, token_subset=sub)
+        else:
+            O.forward(x, wr, br, f64w(inp["w_up"]), f64(inp["b_up"]), f64w(inp["w_down"]),
+                      f64(inp["b_down"]), top_k=run.top_k, num_shared=run.num_shared,
+                      gating=run.gating, activation=run.activation, cap=ocap, token_subset=sub)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 50:
@@ -284,6 +306,16 @@ class _Lazy:
 
     def __getitem__(self, i):
         return self.t[i].to(__import__("torch").float64).numpy()
+
+
+class _LazyFP8(_Lazy):
+    def __init__(self, t, oracle):
+        super().__init__(t)
+        self.O = oracle
+
+    def __getitem__(self, i):
+        codes, scales = self.O.quantize_fp8_rows(self.t[i].to(__import__("torch").float32).numpy())
+        return self.O.dequantize_fp8_rows(codes, scales)
 
 
 if __name__ == "__main__":

@@ -64,7 +64,8 @@ enum { MOE_F32 = 0, MOE_BF16 = 1 };                      /* dtype of x, weights,
 enum { MOE_SOFTMAX = 0, MOE_SIGMOID_NORM = 1 };          /* gate                        */
 enum { MOE_RELU = 0, MOE_GELU = 1, MOE_SWIGLU = 2 };     /* expert activation           */
 enum { MOE_ROUTER_BIAS = 1, MOE_EXPERT_BIAS = 2,        /* flags                       */
-       MOE_W_FP8 = 8 };  /* expert weights as FP8 E4M3 codes with per-row scales (moe_weights) */
+       MOE_W_FP8 = 8,           /* expert weights as FP8 E4M3 codes with per-row scales (moe_weights) */
+       MOE_EXPERT_CHOICE = 16 };/* expert-choice routing (see moe_expert_choice)                  */
 
 /*
  * The problem.  T tokens (the pages' [B, L, d] input flattened to [B*L, d],
@@ -77,6 +78,15 @@ enum { MOE_ROUTER_BIAS = 1, MOE_EXPERT_BIAS = 2,        /* flags                
  * MOE_W_FP8 (expert weights quantized to 8 bits, 0539edu page 5.2) needs
  * MOE_BF16, T <= 16 (the weight-streaming decode path) and d_model, d_ff
  * multiples of 128.
+ * MOE_EXPERT_CHOICE ("MoE架构解析" 二 2.2: experts choose their tokens): every
+ * expert takes exactly `capacity` tokens (1 <= capacity <= T, else
+ * MOE_ERR_INVALID_ARG; T <= 16384); top_k is not used for routing.  The
+ * routed rows are then E * capacity and, in every entry point below:
+ * sorted_assign holds token ids (E * capacity of them, expert by expert, each
+ * expert's tokens ascending), assign_row is the [T, E] row of each (token,
+ * expert) pair (-1 where the expert did not take the token), the combine
+ * weights are probs [T, E], and counts = kept = capacity.  moe_dispatch does
+ * not apply (moe_expert_choice replaces it).
  */
 typedef struct moe_problem {
   int32_t T, d_model, d_ff, num_experts, top_k, num_shared, capacity;
@@ -146,6 +156,7 @@ typedef struct moe_routing {
   uint8_t *drop_mask;     /* [T * k] */
   float *f, *P, *l_aux;   /* [E], [E], [1] */
   moe_route_stats *stats; /* [1] (computed only when non-NULL) */
+  int32_t *token_experts; /* [T] expert choice only: experts that took each token (0 = orphan) */
 } moe_routing;
 
 /* Host only.  Capacity ceil(capacity_factor * T * k / E): the page's
@@ -167,6 +178,7 @@ moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
  *                            sigmoid: sigma values; both give the same weights)
  *   probs       [T, E]  out, nullable: softmax p, or sigma / sum_e sigma
  *   prob_colsum [E]     out, nullable: sum over tokens of probs (fixed order)
+ * With MOE_EXPERT_CHOICE probs is required and topk_idx, topk_w are ignored.
  */
 moe_status moe_router_topk(const moe_problem* p, const void* x, const moe_weights* w,
                            int32_t* topk_idx, float* topk_w, float* probs,
@@ -244,6 +256,24 @@ moe_status moe_aux_stats(const moe_problem* p, const float* prob_colsum, const i
  * (moe_aux_stats).  stats: one moe_route_stats in device memory.  Sums run
  * over experts in a fixed order: the result is deterministic.
  */
+/*
+ * Expert-choice routing ("MoE架构解析" 二 2.2: each expert picks the tokens it
+ * scores highest, which balances the load exactly; a token may be picked by
+ * several experts or by none).  Problem flag MOE_EXPERT_CHOICE.
+ *   probs         [T, E] in   gate probabilities (moe_router_topk's probs)
+ *   offsets       [E+1]  out  e * capacity
+ *   sorted_assign [E * capacity] out  expert e's tokens in ascending order at
+ *                              rows e*capacity .. (e+1)*capacity - 1: the
+ *                              capacity tokens with the largest probs[t, e],
+ *                              equal scores going to the lower token index
+ *   row_of        [T, E] out  row of (t, e), or -1 if e did not take t
+ *   token_experts [T]    out  number of experts that took t (may be NULL)
+ * Integer results, exact given probs.  ws: moe_workspace_size() bytes.
+ */
+moe_status moe_expert_choice(const moe_problem* p, const float* probs, int32_t* offsets,
+                             int32_t* sorted_assign, int32_t* row_of, int32_t* token_experts,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
 moe_status moe_routing_stats(const moe_problem* p, const int32_t* counts, const int32_t* kept,
                              const float* P, moe_route_stats* stats, hipStream_t stream);
 

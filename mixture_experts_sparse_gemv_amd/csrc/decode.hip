@@ -192,7 +192,6 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     bpos[u] = rb * 128 + ((cb ^ ((rb >> 1) & 7)) * 16);
   }
 
-  typedef __attribute__((address_space(3))) void lds_void_t;
   // called with indices that are constants after unrolling
   auto slot = [&](int i) -> u32x4* { return i == 0 ? ring0 : i == 1 ? ring1 : i == 2 ? ring2 : ring3; };
   f32x4 acc[RG];
@@ -201,6 +200,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 
   auto issue = [&](u32x4* buf, int j) {
 #if __HIP_DEVICE_COMPILE__   // (with template-dependent operands the host pass drops the kernel)
+    typedef __attribute__((address_space(3))) void lds_void_t;
 #pragma unroll
     for (int q = 0; q < NDMA; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t*)(buf + q * 64), 16, soff[q],
@@ -355,7 +355,7 @@ hipError_t launch_decode_up(const Shape& s, const void* x, const void* w_up, con
   const long long items = (long long)nseg * items_per_seg;
   DecodeArgs a{(const uint16_t*)x, w_up, s_up,
                s.expert_bias() ? (const uint16_t*)b_up : nullptr, h, offsets, sorted_assign,
-               s.T, s.k, s.E, s.S, s.d, s.up_rows(), s.f, 1, items_per_seg, 0,
+               s.T, s.tok_div(), s.E, s.S, s.d, s.up_rows(), s.f, 1, items_per_seg, 0,
                (long long)s.T * s.d * 2};
 #define MOE_DECODE_UP(A, F)                                      \
   decode_kernel<A, F><<<(int)items, 64, 0, st>>>(a)
@@ -385,7 +385,7 @@ hipError_t launch_decode_down(const Shape& s, const void* h, const void* w_down,
   const long long items = (long long)nseg * items_per_seg;
   const long long part_stride = s.max_rows() * s.d;
   DecodeArgs a{(const uint16_t*)h, w_down, s_down, nullptr, y_part, offsets, nullptr,
-               s.T, s.k, s.E, s.S, s.f, s.d, s.f, nsplit, items_per_seg, part_stride,
+               s.T, s.tok_div(), s.E, s.S, s.f, s.d, s.f, nsplit, items_per_seg, part_stride,
                s.max_rows() * s.f * 2};
   if (s.w_fp8()) decode_kernel<DEC_DOWN, true><<<(int)items, 64, 0, st>>>(a);
   else decode_kernel<DEC_DOWN, false><<<(int)items, 64, 0, st>>>(a);

@@ -354,12 +354,12 @@ __global__ __launch_bounds__(64) void routing_stats_kernel(const int32_t* counts
 
 // f, P, L_aux from given column sums and counts (one block).
 __global__ __launch_bounds__(64) void aux_kernel(const float* colsum, const int32_t* counts,
-                                                 float* f, float* P, float* l_aux, int T, int k,
-                                                 int E) {
+                                                 float* f, float* P, float* l_aux, int T,
+                                                 long long total, int E) {
   __shared__ float prod[kMaxExperts];
   const int e = threadIdx.x;
   if (e < E) {
-    const float fe = (float)counts[e] / (float)((long long)T * k);
+    const float fe = (float)counts[e] / (float)total;   // share of the routing decisions
     const float pe = colsum[e] / (float)T;
     f[e] = fe;
     P[e] = pe;
@@ -400,7 +400,7 @@ hipError_t launch_dispatch(const Shape& s, const int32_t* topk_idx, int32_t* chu
 
 hipError_t launch_aux(const Shape& s, const float* colsum, const int32_t* counts, float* f,
                       float* P, float* l_aux, hipStream_t st) {
-  aux_kernel<<<1, 64, 0, st>>>(colsum, counts, f, P, l_aux, s.T, s.k, s.E);
+  aux_kernel<<<1, 64, 0, st>>>(colsum, counts, f, P, l_aux, s.T, s.routed_rows(), s.E);
   return hipGetLastError();
 }
 

@@ -493,7 +493,7 @@ constexpr int DN_BM = MOE_DN_BM, DN_BN = MOE_DN_BN, DN_WGM = MOE_DN_WGM, DN_WGN 
 constexpr int UP_NST = MOE_UP_NST, UP_OCC = MOE_UP_OCC, DN_NST = MOE_DN_NST, DN_OCC = MOE_DN_OCC;
 
 int grid_blocks(const Shape& s, int BM, int NT, int ksplit = 1) {
-  const long long mt = ((long long)s.T * s.k + BM - 1) / BM + s.E +
+  const long long mt = (s.routed_rows() + BM - 1) / BM + s.E +
                        (long long)s.S * ((s.T + BM - 1) / BM);
   const long long g = NT * mt * ksplit;
   return (int)((g + 7) / 8 * 8);
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(256) void part_fold_kernel(float* __restrict__ y_ex
 int down_ksplit(const Shape& s) {
   if (s.dtype != MOE_BF16 || s.decode()) return 1;
   // expected tiles with evenly routed experts (capacity-limited)
-  long long per = ((long long)s.T * s.k + s.E - 1) / s.E;
+  long long per = (s.routed_rows() + s.E - 1) / s.E;
   if (s.cap > 0 && per > s.cap) per = s.cap;
   const long long mt = (long long)s.E * ((per + DN_BM - 1) / DN_BM) +
                        (long long)s.S * ((s.T + DN_BM - 1) / DN_BM);
@@ -556,19 +556,19 @@ hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void
     float* O = (float*)h;
     if (s.act == MOE_RELU)
       gemm_f32_kernel<MODE_RELU><<<blocks, 256, 0, st>>>(X, W, B, O, offsets, sorted_assign, s.T,
-                                                        s.k, s.E, s.S, s.d, s.f, s.up_rows(), s.f);
+                                                        s.tok_div(), s.E, s.S, s.d, s.f, s.up_rows(), s.f);
     else if (s.act == MOE_GELU)
       gemm_f32_kernel<MODE_GELU><<<blocks, 256, 0, st>>>(X, W, B, O, offsets, sorted_assign, s.T,
-                                                        s.k, s.E, s.S, s.d, s.f, s.up_rows(), s.f);
+                                                        s.tok_div(), s.E, s.S, s.d, s.f, s.up_rows(), s.f);
     else
       gemm_f32_kernel<MODE_SWIGLU><<<blocks, 256, 0, st>>>(X, W, B, O, offsets, sorted_assign,
-                                                          s.T, s.k, s.E, s.S, s.d, s.f,
+                                                          s.T, s.tok_div(), s.E, s.S, s.d, s.f,
                                                           s.up_rows(), s.f);
     return hipGetLastError();
   }
   if (s.decode()) return launch_decode_up(s, x, w_up, b_up, s_up, offsets, sorted_assign, h, st);
   GemmArgs a{(const uint16_t*)x, (const uint16_t*)w_up, (const uint16_t*)bias, h, offsets,
-             sorted_assign, s.T, s.k, s.E, s.S, s.d, s.f, s.up_rows(), s.f, 1, nullptr, 0};
+             sorted_assign, s.T, s.tok_div(), s.E, s.S, s.d, s.f, s.up_rows(), s.f, 1, nullptr, 0};
   if (s.act == MOE_SWIGLU) {
     const int NT = (s.f + UP_BN / 2 - 1) / (UP_BN / 2);
     grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_SWIGLU, UP_NST, UP_OCC>
@@ -595,7 +595,7 @@ hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const 
     const int blocks = (int)((n + 255) / 256);
     gemm_f32_kernel<MODE_DOWN><<<blocks, 256, 0, st>>>(
         (const float*)h, (const float*)w_down, (const float*)bias, y_exp, offsets, nullptr, s.T,
-        s.k, s.E, s.S, s.f, s.d, s.d, s.f);
+        s.tok_div(), s.E, s.S, s.f, s.d, s.d, s.f);
     return hipGetLastError();
   }
   if (s.decode())
@@ -603,7 +603,7 @@ hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const 
   const int ks = down_ksplit(s);
   const long long part_elems = s.max_rows() * s.d;
   GemmArgs a{(const uint16_t*)h, (const uint16_t*)w_down, (const uint16_t*)bias, y_exp, offsets,
-             nullptr, s.T, s.k, s.E, s.S, s.f, s.d, s.d, s.f, ks, y_part, part_elems};
+             nullptr, s.T, s.tok_div(), s.E, s.S, s.f, s.d, s.d, s.f, ks, y_part, part_elems};
   const int NT = (s.d + DN_BN - 1) / DN_BN;
   grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DOWN, DN_NST, DN_OCC>
       <<<grid_blocks(s, DN_BM, NT, ks), 64 * DN_WGM * DN_WGN, 0, st>>>(a);

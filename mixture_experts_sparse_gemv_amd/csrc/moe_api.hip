@@ -22,8 +22,14 @@ WsLayout ws_layout(const Shape& s) {
   };
   const size_t n = (size_t)s.T * s.k;
   const size_t rows = (size_t)s.max_rows();
+  // expert choice: sorted_assign holds the E*cap token ids, assign_row the
+  // [T, E] row of each (token, expert) pair, probs the gate probabilities
+  const size_t na = s.ec() ? (size_t)s.routed_rows() : n;
+  const size_t nr = s.ec() ? (size_t)s.T * s.E : n;
   w.topk_idx = take(n * 4);
   w.topk_w = take(n * 4);
+  w.probs = s.ec() ? take((size_t)s.T * s.E * 4) : o;
+  w.token_experts = s.ec() ? take((size_t)s.T * 4) : o;
   w.prob_part = take((size_t)router_blocks(s) * s.E * 4);
   w.chunk_counts = take((size_t)router_blocks(s) * s.E * 4);
   w.sb_prefix = take((size_t)scatter_blocks(s) * s.E * 4);
@@ -31,8 +37,8 @@ WsLayout ws_layout(const Shape& s) {
   w.counts = take((size_t)s.E * 4);
   w.kept = take((size_t)s.E * 4);
   w.offsets = take((size_t)(s.E + 1) * 4);
-  w.sorted_assign = take(n * 4);
-  w.assign_row = take(n * 4);
+  w.sorted_assign = take(na * 4);
+  w.assign_row = take(nr * 4);
   w.drop_mask = take(n);
   w.f = take((size_t)s.E * 4);
   w.P = take((size_t)s.E * 4);
@@ -60,11 +66,20 @@ static moe_status check_problem(const moe_problem* p, Shape& s) {
   if (p->dtype != MOE_F32 && p->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (p->gating != MOE_SOFTMAX && p->gating != MOE_SIGMOID_NORM) return MOE_ERR_INVALID_ARG;
   if (p->activation < MOE_RELU || p->activation > MOE_SWIGLU) return MOE_ERR_INVALID_ARG;
-  if (p->flags & ~(MOE_ROUTER_BIAS | MOE_EXPERT_BIAS | MOE_W_FP8)) return MOE_ERR_INVALID_ARG;
+  if (p->flags & ~(MOE_ROUTER_BIAS | MOE_EXPERT_BIAS | MOE_W_FP8 | MOE_EXPERT_CHOICE))
+    return MOE_ERR_INVALID_ARG;
+  if (p->flags & MOE_EXPERT_CHOICE) {   // every expert takes exactly `capacity` tokens
+    if (p->capacity < 1 || p->capacity > p->T) return MOE_ERR_INVALID_ARG;
+    if (p->T > kEcMaxT || (long long)p->num_experts * p->capacity >= (1LL << 31))
+      return MOE_ERR_UNSUPPORTED;
+  }
   if (p->num_experts > kMaxExperts || p->top_k > kMaxTopK ||
       p->num_experts + p->num_shared > kMaxSegments)
     return MOE_ERR_UNSUPPORTED;
-  const long long rows = (long long)p->T * (p->top_k + p->num_shared);
+  const long long routed = (p->flags & MOE_EXPERT_CHOICE)
+                               ? (long long)p->num_experts * p->capacity
+                               : (long long)p->T * p->top_k;
+  const long long rows = routed + (long long)p->T * p->num_shared;
   if (rows >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   if ((long long)rows * p->d_ff >= (1LL << 40) || (long long)rows * p->d_model >= (1LL << 40))
     return MOE_ERR_UNSUPPORTED;
@@ -142,7 +157,9 @@ moe_status moe_router_topk(const moe_problem* p, const void* x, const moe_weight
   moe_status st = check_problem(p, s);
   if (st != MOE_OK) return st;
   if ((st = check_weights(s, w, true, false)) != MOE_OK) return st;
-  if (!x || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!x) return MOE_ERR_INVALID_ARG;
+  if (s.ec() ? !probs : (!topk_idx || !topk_w)) return MOE_ERR_INVALID_ARG;
+  if (s.ec()) topk_idx = nullptr, topk_w = nullptr;   // expert choice uses the probabilities only
   if ((st = check_ws(s, ws, ws_bytes, L)) != MOE_OK) return st;
   float* part = at<float>(ws, L.prob_part);
   hipError_t e = launch_router(s, x, w->w_router, w->b_router, topk_idx, topk_w, probs, part,
@@ -159,6 +176,7 @@ moe_status moe_dispatch(const moe_problem* p, const int32_t* topk_idx, int32_t* 
   WsLayout L;
   moe_status st = check_problem(p, s);
   if (st != MOE_OK) return st;
+  if (s.ec()) return MOE_ERR_INVALID_ARG;   // expert choice dispatches with moe_expert_choice
   if (!topk_idx || !counts || !kept || !offsets || !sorted_assign || !assign_row || !drop_mask)
     return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(s, ws, ws_bytes, L)) != MOE_OK) return st;
@@ -221,6 +239,8 @@ moe_status moe_combine(const moe_problem* p, const float* topk_w, const int32_t*
   moe_status st = check_problem(p, s);
   if (st != MOE_OK) return st;
   if (!topk_w || !assign_row || !offsets || !y_exp || !y) return MOE_ERR_INVALID_ARG;
+  if (s.ec())   // topk_w = probs [T, E], assign_row = row of each (token, expert) [T, E]
+    return fail_hip(launch_combine_ec(s, topk_w, assign_row, offsets, y_exp, nullptr, 0, y, stream));
   return fail_hip(launch_combine(s, topk_w, assign_row, offsets, y_exp, nullptr, 0, y, stream));
 }
 
@@ -231,6 +251,22 @@ moe_status moe_aux_stats(const moe_problem* p, const float* prob_colsum, const i
   if (st != MOE_OK) return st;
   if (!prob_colsum || !counts || !f || !P || !l_aux) return MOE_ERR_INVALID_ARG;
   return fail_hip(launch_aux(s, prob_colsum, counts, f, P, l_aux, stream));
+}
+
+moe_status moe_expert_choice(const moe_problem* p, const float* probs, int32_t* offsets,
+                             int32_t* sorted_assign, int32_t* row_of, int32_t* token_experts,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  WsLayout L;
+  moe_status st = check_problem(p, s);
+  if (st != MOE_OK) return st;
+  if (!s.ec()) return MOE_ERR_INVALID_ARG;
+  if (!probs || !offsets || !sorted_assign || !row_of) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(s, ws, ws_bytes, L)) != MOE_OK) return st;
+  hipError_t e = launch_expert_choice(s, probs, sorted_assign, row_of, at<int32_t>(ws, L.counts),
+                                      at<int32_t>(ws, L.kept), offsets, nullptr, stream);
+  if (e == hipSuccess && token_experts) e = launch_token_experts(s, row_of, token_experts, stream);
+  return fail_hip(e);
 }
 
 moe_status moe_routing_stats(const moe_problem* p, const int32_t* counts, const int32_t* kept,
@@ -277,20 +313,39 @@ moe_status moe_ffn_forward(const moe_problem* p, const moe_weights* w, const voi
   float* y_exp = at<float>(ws, L.y_exp);
 
   int32_t* chunk_counts = at<int32_t>(ws, L.chunk_counts);
-  hipError_t e = launch_router(s, x, w->w_router, w->b_router, topk_idx, topk_w, r.probs, part,
-                               chunk_counts, stream);
+  hipError_t e;
+  if (s.ec()) {
+    // expert choice: probabilities -> each expert's top-cap tokens -> f, P, L_aux
+    float* probs = r.probs ? r.probs : at<float>(ws, L.probs);
+    float* colsum = at<float>(ws, L.prob_colsum);
+    e = launch_router(s, x, w->w_router, w->b_router, nullptr, nullptr, probs, part, chunk_counts,
+                      stream);
+    if (e == hipSuccess)
+      e = launch_expert_choice(s, probs, sorted_assign, assign_row, counts, kept, offsets, colsum,
+                               stream);
+    if (e == hipSuccess) e = launch_aux(s, colsum, counts, f, P, l_aux, stream);
+    if (e == hipSuccess && r.token_experts)
+      e = launch_token_experts(s, assign_row, r.token_experts, stream);
+    if (e == hipSuccess && r.stats) e = launch_routing_stats(s, counts, kept, P, r.stats, stream);
+    topk_w = probs;   // the combine weights
+  } else {
+    e = launch_router(s, x, w->w_router, w->b_router, topk_idx, topk_w, r.probs, part,
+                      chunk_counts, stream);
+    if (e == hipSuccess)
+      e = launch_dispatch(s, topk_idx, chunk_counts, true, at<int32_t>(ws, L.sb_prefix), counts,
+                          kept, offsets, sorted_assign, assign_row, drop_mask, part,
+                          at<float>(ws, L.prob_colsum), f, P, l_aux, r.stats, stream);
+  }
   if (e == hipSuccess)
-    e = launch_dispatch(s, topk_idx, chunk_counts, true, at<int32_t>(ws, L.sb_prefix), counts,
-                        kept, offsets, sorted_assign, assign_row, drop_mask, part,
-                        at<float>(ws, L.prob_colsum), f, P, l_aux, r.stats, stream);
-  if (e == hipSuccess) e = launch_up(s, x, w->w_up, w->b_up, w->s_up, offsets, sorted_assign, h, stream);
+    e = launch_up(s, x, w->w_up, w->b_up, w->s_up, offsets, sorted_assign, h, stream);
   // The down projection's K slices (if any) are summed by the combine.
   float* y_part = at<float>(ws, L.y_part);
   const int nparts = s.decode() ? 0 : down_ksplit(s) - 1;
   if (e == hipSuccess)
     e = launch_down(s, h, w->w_down, w->b_down, w->s_down, offsets, y_exp, y_part, nparts == 0, stream);
   if (e == hipSuccess)
-    e = launch_combine(s, topk_w, assign_row, offsets, y_exp, y_part, nparts, y, stream);
+    e = s.ec() ? launch_combine_ec(s, topk_w, assign_row, offsets, y_exp, y_part, nparts, y, stream)
+               : launch_combine(s, topk_w, assign_row, offsets, y_exp, y_part, nparts, y, stream);
   return fail_hip(e);
 }
 

@@ -14,6 +14,7 @@ constexpr int kMaxExperts = 64;       // routed experts: one wave lane per exper
 constexpr int kMaxTopK = 8;
 constexpr int kMaxSegments = 128;     // routed + shared experts
 constexpr int kDecodeMaxT = 16;       // T at or below which the streaming decode path runs
+constexpr int kEcMaxT = 16384;        // expert-choice selection keeps a column of T scores in LDS
 constexpr int kNumCUs = 256;          // MI355X compute units (sizes the K split of small GEMMs)
 
 // ---------------------------------------------------------------- shape
@@ -21,7 +22,13 @@ struct Shape {
   int T, d, f, E, k, S, cap;   // cap <= 0: unlimited
   int dtype, gating, act, flags;
   int up_rows() const { return act == MOE_SWIGLU ? 2 * f : f; }
-  long long max_rows() const { return (long long)T * k + (long long)S * T; }
+  // expert-choice routing: every expert takes exactly cap tokens
+  bool ec() const { return flags & MOE_EXPERT_CHOICE; }
+  // rows of the routed experts' segments, and what a sorted_assign entry is
+  // divided by to give its token (assignment ids t*k+s; token ids for ec)
+  long long routed_rows() const { return ec() ? (long long)E * cap : (long long)T * k; }
+  int tok_div() const { return ec() ? 1 : k; }
+  long long max_rows() const { return routed_rows() + (long long)S * T; }
   bool router_bias() const { return flags & MOE_ROUTER_BIAS; }
   bool expert_bias() const { return (flags & MOE_EXPERT_BIAS) && act != MOE_SWIGLU; }
   bool decode() const { return dtype == MOE_BF16 && T <= kDecodeMaxT; }
@@ -49,8 +56,8 @@ int down_ksplit(const Shape& s);
 
 // ---------------------------------------------------------------- workspace
 struct WsLayout {
-  size_t topk_idx, topk_w, prob_part, chunk_counts, sb_prefix, prob_colsum, counts, kept,
-      offsets, sorted_assign,
+  size_t topk_idx, topk_w, probs, token_experts, prob_part, chunk_counts, sb_prefix,
+      prob_colsum, counts, kept, offsets, sorted_assign,
       assign_row, drop_mask, f, P, l_aux, h, y_exp, y_part, total;
 };
 WsLayout ws_layout(const Shape& s);
@@ -140,6 +147,19 @@ hipError_t launch_routing_stats(const Shape& s, const int32_t* counts, const int
                                 const float* P, moe_route_stats* stats, hipStream_t st);
 hipError_t launch_aux(const Shape& s, const float* colsum, const int32_t* counts, float* f,
                       float* P, float* l_aux, hipStream_t st);
+// Expert choice: each expert's top-cap tokens by probs[:, e] (ties to the lower
+// token), in ascending token order: sorted_assign[e*cap + i] = token,
+// row_of[t*E + e] = row or -1; counts = kept = cap, offsets[e] = e*cap; colsum
+// = column sums of probs (fixed order).  token_experts[t] = experts that took t.
+hipError_t launch_expert_choice(const Shape& s, const float* probs, int32_t* sorted_assign,
+                                int32_t* row_of, int32_t* counts, int32_t* kept,
+                                int32_t* offsets, float* colsum, hipStream_t st);
+hipError_t launch_token_experts(const Shape& s, const int32_t* row_of, int32_t* token_experts,
+                                hipStream_t st);
+// y[t] = sum over experts e with row_of[t*E+e] >= 0 of probs[t*E+e] * y_exp row + shared rows.
+hipError_t launch_combine_ec(const Shape& s, const float* probs, const int32_t* row_of,
+                             const int32_t* offsets, const float* y_exp, const float* y_part,
+                             int nparts, float* y, hipStream_t st);
 // s_up / s_down: FP8 row scales (MOE_W_FP8), else ignored.
 hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void* b_up,
                      const float* s_up, const int32_t* offsets, const int32_t* sorted_assign,

@@ -177,7 +177,7 @@ __global__ __launch_bounds__(64 * RW) void router_kernel(RouterArgs a) {
       if (lane == s) { my_idx = bi; my_score = bs; }
       if (lane == bi) { key = NEG_INF; ++nsel; }
     }
-    if (lane < a.k) {
+    if (lane < a.k && a.topk_idx) {   // (expert-choice routing uses the probabilities only)
       a.topk_idx[(long long)t * a.k + lane] = my_idx;
       a.topk_w[(long long)t * a.k + lane] = my_score / sel_sum;
     }

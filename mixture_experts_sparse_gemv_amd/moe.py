@@ -19,13 +19,13 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID_NORM = 0, 1
 MOE_RELU, MOE_GELU, MOE_SWIGLU = 0, 1, 2
-MOE_ROUTER_BIAS, MOE_EXPERT_BIAS, MOE_W_FP8 = 1, 2, 8
+MOE_ROUTER_BIAS, MOE_EXPERT_BIAS, MOE_W_FP8, MOE_EXPERT_CHOICE = 1, 2, 8, 16
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_capacity", "moe_workspace_size", "moe_router_topk", "moe_dispatch",
            "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_aux_stats",
-           "moe_routing_stats", "moe_quantize_fp8", "moe_ffn_forward", "moe_status_string",
-           "moe_last_hip_error")
+           "moe_routing_stats", "moe_quantize_fp8", "moe_expert_choice", "moe_ffn_forward",
+           "moe_status_string", "moe_last_hip_error")
 
 
 class moe_problem(ctypes.Structure):
@@ -42,7 +42,7 @@ class moe_weights(ctypes.Structure):
 class moe_routing(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("topk_idx", "topk_w", "probs", "counts", "kept", "offsets", "sorted_assign",
-                 "assign_row", "drop_mask", "f", "P", "l_aux", "stats")]
+                 "assign_row", "drop_mask", "f", "P", "l_aux", "stats", "token_experts")]
 
 
 # moe_route_stats: six float32 then two int32 (32 bytes, device memory)
@@ -77,6 +77,7 @@ def _load(path=LIB_PATH):
         "moe_aux_stats": (I32, [pp, V, V, V, V, V, V]),
         "moe_routing_stats": (I32, [pp, V, V, V, V, V]),
         "moe_quantize_fp8": (I32, [V, ctypes.c_int64, I32, V, V, V]),
+        "moe_expert_choice": (I32, [pp, V, V, V, V, V, V, SZ, V]),
         "moe_ffn_forward": (I32, [pp, pw, V, V, pr, V, SZ, V]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
         "moe_last_hip_error": (I32, []),
@@ -94,7 +95,7 @@ _lib = _load()
 
 def make_problem(T, d_model, d_ff, num_experts, top_k, num_shared=0, capacity=0,
                  dtype="bf16", gating="softmax", activation="swiglu", router_bias=False,
-                 expert_bias=False, w_fp8=False):
+                 expert_bias=False, w_fp8=False, expert_choice=False):
     return moe_problem(
         T=T, d_model=d_model, d_ff=d_ff, num_experts=num_experts, top_k=top_k,
         num_shared=num_shared, capacity=capacity or 0,
@@ -102,7 +103,7 @@ def make_problem(T, d_model, d_ff, num_experts, top_k, num_shared=0, capacity=0,
         gating={"softmax": MOE_SOFTMAX, "sigmoid_norm": MOE_SIGMOID_NORM}[gating],
         activation={"relu": MOE_RELU, "gelu": MOE_GELU, "swiglu": MOE_SWIGLU}[activation],
         flags=(MOE_ROUTER_BIAS if router_bias else 0) | (MOE_EXPERT_BIAS if expert_bias else 0) |
-        (MOE_W_FP8 if w_fp8 else 0))
+        (MOE_W_FP8 if w_fp8 else 0) | (MOE_EXPERT_CHOICE if expert_choice else 0))
 
 
 def make_weights(w_router, b_router, w_up, b_up, w_down, b_down, s_up=None, s_down=None):
@@ -149,8 +150,15 @@ def h_dtype(p):
     return torch.float16 if p.dtype == MOE_BF16 else torch.float32
 
 
+def routed_rows(p):
+    """Rows of the routed experts: T*k assignments, or E*capacity (expert choice)."""
+    if p.flags & MOE_EXPERT_CHOICE:
+        return p.num_experts * p.capacity
+    return p.T * p.top_k
+
+
 def max_rows(p):
-    return p.T * p.top_k + p.num_shared * p.T
+    return routed_rows(p) + p.num_shared * p.T
 
 
 # ---------------------------------------------------------------- entry points
@@ -223,6 +231,7 @@ def moe_expert_down(p, w, offsets, h, y_exp, ws, stream=None):
 
 
 def moe_combine(p, topk_w, assign_row, offsets, y_exp, y, stream=None):
+    """Expert choice: topk_w = probs [T, E], assign_row = row_of [T, E]."""
     _need(y, p.T * p.d_model, torch.float32, "y")
     _check("moe_combine", _lib.moe_combine(
         ctypes.byref(p), _ptr(topk_w), _ptr(assign_row), _ptr(offsets), _ptr(y_exp), _ptr(y),
@@ -247,6 +256,20 @@ def route_stats_dict(t):
     out = {n: float(fl[i]) for i, n in enumerate(ROUTE_STATS_FLOATS)}
     out.update({n: int(raw[6 + i]) for i, n in enumerate(ROUTE_STATS_INTS)})
     return out
+
+
+def moe_expert_choice(p, probs, offsets, sorted_assign, row_of, token_experts=None, ws=None,
+                      stream=None):
+    T, E = p.T, p.num_experts
+    _need(probs, T * E, torch.float32, "probs")
+    _need(offsets, E + 1, torch.int32, "offsets")
+    _need(sorted_assign, E * p.capacity, torch.int32, "sorted_assign")
+    _need(row_of, T * E, torch.int32, "row_of")
+    _need(token_experts, T, torch.int32, "token_experts")
+    wp, wb = _ws(ws)
+    _check("moe_expert_choice", _lib.moe_expert_choice(
+        ctypes.byref(p), _ptr(probs), _ptr(offsets), _ptr(sorted_assign), _ptr(row_of),
+        _ptr(token_experts), wp, wb, _stream(stream)))
 
 
 def moe_routing_stats(p, counts, kept, P, stats, stream=None):

@@ -45,6 +45,7 @@ class Run:
     skew_b0: float = 0.0      # router bias of expert 0 for router_bias == "skew"
     zipf_s: float = 1.1       # exponent for router_bias == "zipf"
     w_fp8: bool = False       # expert weights prepared as per-row FP8 E4M3 (drawn as for bf16)
+    expert_choice: bool = False   # experts pick their tokens; capacity from capacity_factor
     description: str = ""
 
     @property
@@ -83,6 +84,12 @@ RUNS = {
         expert_bias=False, dtype="bf16", capacity_factor=None, seed=3,
         skew_b0=C3_SKEW_B0,
         description="T=16384 d=512 f=1408 E=4 top-1 softmax SwiGLU bf16, ~50% to expert 0"),
+    "gpt2_ec": Run(
+        name="gpt2_ec", T=4096, d_model=768, d_ff=3072, num_experts=8, top_k=2, num_shared=0,
+        gating="softmax", activation="gelu", router_bias="learned", expert_bias=True,
+        dtype="bf16", capacity_factor=1.0, seed=2, expert_choice=True,
+        description="T=4096 (8x512) d=768 f=3072 E=8 softmax GELU bf16, expert choice: each "
+                    "expert takes T*2/E = 1024 tokens"),
     "large_decode": Run(
         name="large_decode", T=16, d_model=4096, d_ff=14336, num_experts=8, top_k=2,
         num_shared=0, gating="softmax", activation="swiglu", router_bias="none",

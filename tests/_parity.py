@@ -47,7 +47,8 @@ def problem_of(run, capacity=None):
         T=run.T, d_model=run.d_model, d_ff=run.d_ff, num_experts=run.num_experts,
         top_k=run.top_k, num_shared=run.num_shared, capacity=cap, dtype=run.dtype,
         gating=run.gating, activation=run.activation,
-        router_bias=run.router_bias != "none", expert_bias=run.expert_bias, w_fp8=run.w_fp8)
+        router_bias=run.router_bias != "none", expert_bias=run.expert_bias, w_fp8=run.w_fp8,
+        expert_choice=run.expert_choice)
 
 
 def oracle_capacity(run):
@@ -96,6 +97,12 @@ def oracle_forward(run, inp, cap="run", token_subset=None, w_fp8=None):
     fp8 = run.w_fp8 if w_fp8 is None else w_fp8
     lazy = lambda t: None if t is None else LazyF64(t)
     lazyw = (lambda t: LazyDeqFP8(t)) if fp8 else lazy
+    if run.expert_choice:
+        return O.forward_expert_choice(
+            to_f64(inp["x"]), to_f64(inp["w_router"]), to_f64(inp["b_router"]),
+            lazyw(inp["w_up"]), lazy(inp["b_up"]), lazyw(inp["w_down"]), lazy(inp["b_down"]),
+            capacity=c, num_shared=run.num_shared, gating=run.gating,
+            activation=run.activation, token_subset=token_subset)
     return O.forward(to_f64(inp["x"]), to_f64(inp["w_router"]), to_f64(inp["b_router"]),
                      lazyw(inp["w_up"]), lazy(inp["b_up"]), lazyw(inp["w_down"]),
                      lazy(inp["b_down"]), top_k=run.top_k, num_shared=run.num_shared,
@@ -168,6 +175,14 @@ def routing_outputs(p, device="cuda"):
     T, k, E = p.T, p.top_k, p.num_experts
     i32 = dict(dtype=torch.int32, device=device)
     f32 = dict(dtype=torch.float32, device=device)
+    if p.flags & M.MOE_EXPERT_CHOICE:
+        n = E * p.capacity
+        return dict(probs=torch.empty(T * E, **f32), counts=torch.empty(E, **i32),
+                    kept=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+                    sorted_assign=torch.empty(n, **i32), assign_row=torch.empty(T * E, **i32),
+                    f=torch.empty(E, **f32), P=torch.empty(E, **f32),
+                    l_aux=torch.empty(1, **f32), stats=M.route_stats_tensor(device),
+                    token_experts=torch.empty(T, **i32))
     return dict(topk_idx=torch.empty(T * k, **i32), topk_w=torch.empty(T * k, **f32),
                 probs=torch.empty(T * E, **f32), counts=torch.empty(E, **i32),
                 kept=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
@@ -243,3 +258,40 @@ def check_route_stats(got, ref):
 
 def inputs_for(run):
     return make_inputs(run)
+
+
+def compare_forward_ec(run, gpu, orc):
+    """Expert-choice forward against the oracle.  Selection: experts whose
+    C-th and (C+1)-th best scores differ by more than GAP pick exactly the
+    oracle's tokens; elsewhere every picked token scores within GAP of the
+    oracle's C-th best.  y is compared on the tokens picked by the same set
+    of experts."""
+    T, E = run.T, run.num_experts
+    C = oracle_capacity(run)
+    probs = orc["probs"]
+    assert_close(gpu["probs"].reshape(T, E), probs, "probs")
+    assert np.array_equal(gpu["offsets"], np.arange(E + 1) * C)
+    assert np.all(gpu["counts"] == C) and np.all(gpu["kept"] == C)
+    gsel = gpu["sorted_assign"].reshape(E, C)
+    kth = -np.sort(-probs, axis=0)[C - 1]
+    for e in range(E):
+        assert np.all(np.diff(gsel[e]) > 0), "tokens of an expert not ascending"
+        if orc["gap"][e] > GAP:
+            assert np.array_equal(gsel[e], orc["sel"][e]), f"expert {e} picked other tokens"
+        else:
+            assert np.all(probs[gsel[e], e] >= kth[e] - GAP)
+    row_of = gpu["assign_row"].reshape(T, E)
+    for e in range(E):   # row_of is consistent with the GPU's own selection
+        assert np.array_equal(np.flatnonzero(row_of[:, e] >= 0), gsel[e])
+        assert np.array_equal(row_of[gsel[e], e], e * C + np.arange(C))
+    assert np.array_equal(gpu["token_experts"], (row_of >= 0).sum(1))
+    agree = np.all((row_of >= 0) == (orc["row_of"] >= 0), axis=1)
+    n_dis = int((~agree).sum())
+    assert n_dis <= max(2, int(0.002 * T)), f"{n_dis} tokens picked by other experts"
+    toks = orc["tokens"]
+    mask = agree[toks]
+    assert_close(gpu["y"][toks][mask], orc["y"][mask], "y")
+    np.testing.assert_allclose(gpu["f"], np.full(E, 1.0 / E), rtol=1e-6)
+    assert_close(gpu["P"], probs.mean(0), "P", rel=1e-4, mabs=1e-5)
+    check_route_stats(gpu["stats"], O.routing_stats(gpu["counts"], gpu["kept"], gpu["P"]))
+    return agree
