@@ -103,26 +103,27 @@ __device__ __forceinline__ float silu_f(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + fast_exp(-z));
 }
 
-// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, 7.1.26
-// (rational approximation in t = 1/(1 + p|x|) times exp(-x^2); absolute
-// error at most 1.5e-7).
-__device__ __forceinline__ float erf_as(float x) {
-  const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
-  float poly = fmaf(1.061405429f, t, -1.453152027f);
-  poly = fmaf(poly, t, 1.421413741f);
-  poly = fmaf(poly, t, -0.284496736f);
-  poly = fmaf(poly, t, 0.254829592f);
-  poly *= t;
-  const float e = fast_exp(-ax * ax);
-  const float r = fmaf(-poly, e, 1.0f);
-  return copysignf(r, x);
-}
-
-// GELU in the exact erf form: 0.5 z (1 + erf(z / sqrt 2)).
+// GELU in the exact erf form, 0.5 z (1 + erf(z / sqrt 2)), with erf from
+// Abramowitz & Stegun, Handbook of Mathematical Functions, 7.1.28: for u >= 0,
+// erf(u) = 1 - (1 + a1 u + a2 u^2 + ... + a6 u^6)^-16, absolute error at most
+// 3e-7 (no exponential: six fma, four squarings, one reciprocal; the power
+// overflows to inf for large u, where the reciprocal gives erf = 1).  With
+// r = 1 - erf(|z|/sqrt 2): GELU(z) = z - z r / 2 for z >= 0, z r / 2 below.
 __device__ __forceinline__ float gelu_f(float z) {
+  const float u = fabsf(z) * 0.70710678118654752f;
+  float p = fmaf(4.30638e-5f, u, 2.765672e-4f);
+  p = fmaf(p, u, 1.520143e-4f);
+  p = fmaf(p, u, 9.2705272e-3f);
+  p = fmaf(p, u, 4.22820123e-2f);
+  p = fmaf(p, u, 7.05230784e-2f);
+  p = fmaf(p, u, 1.0f);
+  p *= p;
+  p *= p;
+  p *= p;
+  p *= p;
+  const float r = __builtin_amdgcn_rcpf(p);
   const float hz = 0.5f * z;
-  return fmaf(hz, erf_as(z * 0.70710678118654752f), hz);
+  return z >= 0.0f ? fmaf(-hz, r, z) : hz * r;
 }
 
 // ---------------------------------------------------------------- launchers
