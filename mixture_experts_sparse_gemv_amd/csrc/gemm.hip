@@ -25,6 +25,11 @@
 // of one expert weight stay within one XCD's L2.
 #include "moe_internal.h"
 
+// Persistent launch: one block per compute unit, each looping over its tiles.
+#ifndef MOE_PERSISTENT
+#define MOE_PERSISTENT 1
+#endif
+
 namespace moe {
 namespace {
 
@@ -143,8 +148,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   const int total = tiles * nsplit;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int per = (total + 7) >> 3;
+#if MOE_PERSISTENT
+  // persistent blocks: XCD xcd's blocks walk its tile range in steps of their count
+  const int nslots = gridDim.x >> 3;
+  for (int it = slot; it < per; it += nslots) {
+  const int LL = xcd * per + it;
+  if (LL >= total) break;                  // uniform over the block
+  __syncthreads();                         // the previous tile's LDS reads are done
+#else
   const int LL = xcd * per + slot;
   if (slot >= per || LL >= total) return;  // uniform over the block
+#endif
   const int ks = LL / tiles;               // K slice
   const int L = LL - ks * tiles;
   if (tid < nseg && seg_tile[tid] * NT <= L && L < seg_tile[tid + 1] * NT) sh_seg = tid;
@@ -404,6 +418,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
         *(u32x4*)(obase + ((long long)(row_start + m) * a.Nout + col) * ES) = val;
     }
   }
+#if MOE_PERSISTENT
+  }
+#endif
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -495,7 +512,8 @@ constexpr int UP_NST = MOE_UP_NST, UP_OCC = MOE_UP_OCC, DN_NST = MOE_DN_NST, DN_
 int grid_blocks(const Shape& s, int BM, int NT, int ksplit = 1) {
   const long long mt = (s.routed_rows() + BM - 1) / BM + s.E +
                        (long long)s.S * ((s.T + BM - 1) / BM);
-  const long long g = NT * mt * ksplit;
+  long long g = NT * mt * ksplit;
+  if (MOE_PERSISTENT && g > kNumCUs) g = kNumCUs;   // one block per CU, looping over tiles
   return (int)((g + 7) / 8 * 8);
 }
 
