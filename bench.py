@@ -36,7 +36,76 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (for counter scaling)")
+    ap.add_argument("--record-traffic", nargs=6,
+                    metavar=("KERNEL", "WORKLOAD", "NAME", "SOURCE", "FETCH_DIR", "WRITE_DIR"),
+                    help="host only: write the traffic entry KERNEL:WORKLOAD of "
+                         "profiles/traffic.json from two rocprofv3 --pmc output folders "
+                         "(FETCH_SIZE, WRITE_SIZE), averaging the dispatches whose name "
+                         "contains NAME; SOURCE = the kernel's file under csrc/")
+    ap.add_argument("--calibration", nargs=3, metavar=("MIB", "FETCH_DIR", "WRITE_DIR"),
+                    help="with --record-traffic: the --pmc folders of a "
+                         "--copy-calibration-mb MIB run, giving the counter scales")
     return ap.parse_args()
+
+
+def _counter_rows(folder, counter):
+    import csv
+    import glob
+    paths = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    rows = []
+    for path in paths:
+        with open(path) as fh:
+            rows += [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
+    return rows
+
+
+def record_traffic(a):
+    """HBM bytes per launch of one kernel = FETCH_SIZE * fetch_scale + WRITE_SIZE *
+    write_scale, where the scales make the counters of a plain device copy of
+    known size read its true byte counts.  Writes profiles/traffic.json."""
+    kernel, workload, name, source, fdir, wdir = a.record_traffic
+    if not a.calibration:
+        raise SystemExit("--record-traffic needs --calibration MIB FETCH_DIR WRITE_DIR")
+    mib, cfdir, cwdir = int(a.calibration[0]), a.calibration[1], a.calibration[2]
+    nbytes = mib * (1 << 20)
+
+    def copy_kib(folder, counter):
+        rows = [r for r in _counter_rows(folder, counter) if "copyBuffer" in r["Kernel_Name"]]
+        return max(float(r["Counter_Value"]) for r in rows)   # the big copy
+
+    def kernel_kib(folder, counter):
+        vals = [float(r["Counter_Value"]) for r in _counter_rows(folder, counter)
+                if name in r["Kernel_Name"]]
+        if not vals:
+            raise SystemExit(f"no dispatch of '{name}' in {folder}")
+        return sum(vals) / len(vals), len(vals)
+
+    cf, cw = copy_kib(cfdir, "FETCH_SIZE"), copy_kib(cwdir, "WRITE_SIZE")
+    fs, ws = nbytes / (cf * 1024), nbytes / (cw * 1024)
+    fk, nf = kernel_kib(fdir, "FETCH_SIZE")
+    wk, nw = kernel_kib(wdir, "WRITE_SIZE")
+    src = os.path.join(ROOT, "mixture_experts_sparse_gemv_amd", "csrc", source)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    db = json.load(open(path)) if os.path.exists(path) else {}
+    db["_about"] = ("HBM bytes per launch = FETCH_SIZE * fetch_scale + WRITE_SIZE * write_scale "
+                    "(rocprofv3 --pmc, KiB per dispatch); the scales make a plain device copy's "
+                    "counters read the bytes it moves. Valid while the kernel source file hashes "
+                    "to source_sha256.")
+    db["calibration"] = {"copy_bytes_each_way": nbytes, "fetch_kib": cf, "write_kib": cw,
+                         "fetch_scale": fs, "write_scale": ws}
+    db[f"{kernel}:{workload}"] = {
+        "source": source,
+        "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+        "dispatch_name": name, "dispatches": [nf, nw],
+        "fetch_kib": fk, "write_kib": wk,
+        "bytes_per_launch": int(round(fk * 1024 * fs + wk * 1024 * ws)),
+    }
+    with open(path, "w") as fh:
+        json.dump(db, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(db[f"{kernel}:{workload}"]))
 
 
 def expert_flops(run, kept_rows):
@@ -48,6 +117,9 @@ def expert_flops(run, kept_rows):
 
 def main():
     a = parse()
+    if a.record_traffic:
+        record_traffic(a)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {a.gpus}); the layer runs on a "
               f"single MI355X with all experts resident, so there is no multi-GPU step.",
