@@ -1,8 +1,8 @@
-"""Plain float64 CPU oracle of the MoE-FFN forward.
+"""Plain float64 CPU oracle of the MoE-FFN forward and backward.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
 benchmark's cpu_baseline leg, never by the HIP library or its binding."""
-from . import moe_oracle
+from . import moe_backward, moe_oracle
 from .moe_oracle import (router_logits, softmax, sigmoid_normalized, gate, topk_renorm,
                          selection_gap, capacity, dispatch, gelu, silu, expert_ffn,
                          combine_rows, aux_stats, routing_stats, forward,
