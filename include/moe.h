@@ -1,6 +1,6 @@
 /*
- * libmoe_mi355x — forward pass of one Mixture-of-Experts FFN layer on one
- * AMD MI355X (gfx950), as a C ABI.
+ * libmoe_mi355x — forward and backward pass of one Mixture-of-Experts FFN
+ * layer on one AMD MI355X (gfx950), as a C ABI.
  *
  * The layer (pages cited by title and section):
  *   router      logits = Wr x + br, one output per expert
@@ -299,6 +299,53 @@ moe_status moe_ffn_forward(const moe_problem* p, const moe_weights* w, const voi
  */
 moe_status moe_quantize_fp8(const void* w, int64_t rows, int32_t cols, uint8_t* q, float* scale,
                             hipStream_t stream);
+
+/*
+ * Backward pass of the layer for training: the gradients of
+ *     L = <dy, y> + alpha * L_aux
+ * (the load-balancing loss added to the task loss before one backward:
+ * 0539edu page 4.3; kamacoder 七, total loss), dy being the gradient of the
+ * task loss with respect to y.  Top-k selection, capacity drops and the
+ * counts f_e are piecewise constant and pass no gradient; a dropped slot
+ * sends none to its expert or gate weight; the router receives gradient
+ * through the renormalized top-k weights and through P_e.
+ *
+ * Limits: dtype MOE_BF16, token-choice routing (no MOE_EXPERT_CHOICE), bf16
+ * expert weights (no MOE_W_FP8); otherwise MOE_ERR_UNSUPPORTED.  Also
+ * unsupported when a transposed gradient operand would reach 4 GiB
+ * (F1 or d_model times the padded row count, times 2 bytes).
+ *
+ * The expert activations are recomputed (not stored by the forward).
+ *   x, w     the forward's input and weights
+ *   dy       [T, d] float32 in
+ *   alpha    weight of L_aux in the objective
+ *   fwd      routing of the forward pass of the same x and weights (what
+ *            moe_ffn_forward wrote into its moe_routing): topk_idx, topk_w,
+ *            counts, offsets, sorted_assign, assign_row are required
+ *   g        gradient outputs (host struct of device pointers, all float32,
+ *            overwritten):
+ *              dx        [T, d]               required
+ *              dw_router [E, d]               required
+ *              db_router [E]                  may be NULL
+ *              dw_up     [E+S, F1, d]         required (F1 = 2 d_ff for SwiGLU)
+ *              db_up     [E+S, d_ff]          required with MOE_EXPERT_BIAS (not SwiGLU), else ignored
+ *              dw_down   [E+S, d, d_ff]       required
+ *              db_down   [E+S, d]             as db_up
+ *              d_topk_w  [T, k]               may be NULL: gradient of the slot weights (0 if dropped)
+ *              d_logits  [T, E]               may be NULL: gradient of the router logits
+ *   ws       moe_backward_workspace_size() bytes (256-byte aligned)
+ * Deterministic: every sum runs in a fixed order.
+ */
+typedef struct moe_grads {
+  float *dx, *dw_router, *db_router, *dw_up, *db_up, *dw_down, *db_down, *d_topk_w, *d_logits;
+} moe_grads;
+
+/* Host only.  Workspace bytes of moe_ffn_backward for this problem. */
+moe_status moe_backward_workspace_size(const moe_problem* p, size_t* bytes);
+
+moe_status moe_ffn_backward(const moe_problem* p, const moe_weights* w, const void* x,
+                            const float* dy, float alpha, const moe_routing* fwd,
+                            const moe_grads* g, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Human-readable name of a status code (static string). */
 const char* moe_status_string(moe_status s);

@@ -1,0 +1,596 @@
+// Backward pass of the MoE-FFN layer (bf16 problems, token-choice routing).
+//
+// Objective: L = <dy, y> + alpha * L_aux — the task loss and the load-balancing
+// loss merged before one backward ("MoE混合专家模型…" 4.3; "手撕一个极简
+// MoE-FFN" 七).  Top-k selection, capacity drops and the counts f_e are
+// piecewise constant and pass no gradient; a dropped slot sends none to its
+// expert or gate weight; shared experts have weight 1.
+//
+// The expert activations are recomputed from the routing the forward pass
+// returns, instead of being stored by it:
+//   Z  = x_rows W1^T + b1                 grouped GEMM, fp32 [rows, F1]
+//   G  = dy_rows W2                        grouped GEMM against W2 transposed
+//   per row: h = act(Z), dw = <h, G> + <b2, dy> (the gate weight's gradient),
+//            dZ = act'(Z) * (w G)  (SwiGLU: [w G u silu'(g); w G silu(g)])
+//   dX_rows = dZ W1                        grouped GEMM against W1 transposed
+//   dW2_e = (w dy)_e^T H_e, dW1_e = dZ_e^T x_e   per-expert GEMMs reducing
+//            over the expert's rows (operands transposed, rows zero-padded)
+//   db2_e, db1_e = sums over the expert's rows
+//   router: dw -> renormalized top-k -> softmax / normalized sigmoid (+ the
+//            aux term alpha E f_e / T on every p[t, e]) -> dlogits;
+//            dx += dlogits Wr, dWr = dlogits^T x, dbr = column sums
+//   dx[t] = router part + sum over kept slots and shared experts of dX rows.
+// Every sum runs in a fixed order: results are deterministic.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+// Row segments: routed rows [0, offsets[E]) by expert, then the S shared
+// experts' T rows each.  Token and gate weight of a row.
+__device__ __forceinline__ void row_info(int r, const int32_t* offsets, const int32_t* sorted_assign,
+                                         const float* topk_w, int T, int k, int E, int& seg,
+                                         int& tok, float& wgt, int& assign) {
+  const int off_E = offsets[E];
+  if (r < off_E) {
+    int lo = 0, hi = E;   // last e with offsets[e] <= r
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (offsets[mid] <= r) lo = mid; else hi = mid;
+    }
+    seg = lo;
+    assign = sorted_assign[r];
+    tok = assign / k;
+    wgt = topk_w[assign];
+  } else {
+    const int q = (r - off_E) / T;
+    seg = E + q;
+    tok = (r - off_E) - q * T;
+    wgt = 1.0f;
+    assign = -1;
+  }
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// ---------------------------------------------------------------- elementwise
+__global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict__ src,
+                                                        uint16_t* __restrict__ dst, long long n4) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4 v = *(const f32x4*)(src + 4 * i);
+  u32x2 o;
+  o[0] = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+  o[1] = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+  *(u32x2*)(dst + 4 * i) = o;
+}
+
+// dst[m][c][r] = src[m][r][c] for nmat matrices of R x C bf16 (R, C multiples of 64).
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ src,
+                                                        uint16_t* __restrict__ dst, int R, int C) {
+  __shared__ uint16_t tile[64][64 + 2];
+  const long long mat = (long long)blockIdx.z * R * C;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tid = threadIdx.x;
+  // read 64 rows x 64 columns: 8 threads per row, 8 columns each
+  for (int rr = tid / 8; rr < 64; rr += 32) {
+    const u32x4 v = *(const u32x4*)(src + mat + (long long)(r0 + rr) * C + c0 + (tid % 8) * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tile[rr][(tid % 8) * 8 + 2 * i] = (uint16_t)(v[i] & 0xffffu);
+      tile[rr][(tid % 8) * 8 + 2 * i + 1] = (uint16_t)(v[i] >> 16);
+    }
+  }
+  __syncthreads();
+  for (int cc = tid / 8; cc < 64; cc += 32) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = (tid % 8) * 8 + 2 * i;
+      v[i] = (uint32_t)tile[rr][cc] | ((uint32_t)tile[rr + 1][cc] << 16);
+    }
+    *(u32x4*)(dst + mat + (long long)(c0 + cc) * R + r0 + (tid % 8) * 8) = v;
+  }
+}
+
+// Padded column start of every segment for the weight-gradient operands:
+// poff[seg] = sum of wgrad_pad(rows) of the segments before it.
+__global__ __launch_bounds__(64) void wgrad_offsets_kernel(const int32_t* __restrict__ offsets,
+                                                           int T, int E, int S,
+                                                           int32_t* __restrict__ poff) {
+  if (threadIdx.x != 0) return;
+  int acc = 0;
+  for (int seg = 0; seg < E + S; ++seg) {
+    poff[seg] = acc;
+    const int rows = seg < E ? offsets[seg + 1] - offsets[seg] : T;
+    acc += rows <= 0 ? 32 : (rows + 31) / 32 * 32;
+  }
+  poff[E + S] = acc;
+}
+
+// out[c][poff[seg] + i] = scale(row) * src[srow(row)][c] for the segment's
+// rows i (bf16), 0 in the padding.  SRC32: fp32 source (else bf16); GATHER:
+// source row = the row's token (else the row itself); SCALE: times the row's
+// gate weight.  Block = 32 padded rows x 64 columns.
+template <bool SRC32, bool GATHER, bool SCALE>
+__global__ __launch_bounds__(256) void seg_transpose_kernel(
+    const void* __restrict__ src, int C, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_assign, const float* __restrict__ topk_w,
+    const int32_t* __restrict__ poff, int T, int k, int E, int S, uint16_t* __restrict__ out,
+    int ldk) {
+  __shared__ uint16_t tile[32][64 + 2];
+  __shared__ int sh_seg;
+  const int p0 = blockIdx.x * 32, c0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  const int nseg = E + S;
+  if (p0 >= poff[nseg]) return;   // beyond the used columns (uniform)
+  if (tid < nseg && poff[tid] <= p0 && p0 < poff[tid + 1]) sh_seg = tid;
+  __syncthreads();
+  const int seg = sh_seg;
+  const int rows = seg < E ? offsets[seg + 1] - offsets[seg] : T;
+  const int base = seg < E ? offsets[seg] : offsets[E] + (seg - E) * T;
+  {
+    const int ri = tid / 8, cq = (tid % 8) * 8;
+    const int i = p0 - poff[seg] + ri;
+    float v[8];
+    if (i < rows) {
+      const int r = base + i;
+      int srow = r;
+      float sc = 1.0f;
+      if (seg < E) {
+        const int a = sorted_assign[r];
+        if (GATHER) srow = a / k;
+        if (SCALE) sc = topk_w[a];
+      } else if (GATHER) {
+        srow = i;
+      }
+      if (SRC32) {
+        const float* sp = (const float*)src + (long long)srow * C + c0 + cq;
+        const f32x4 a0 = *(const f32x4*)sp, a1 = *(const f32x4*)(sp + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = a0[j] * sc, v[4 + j] = a1[j] * sc;
+      } else {
+        const u32x4 a = *(const u32x4*)((const uint16_t*)src + (long long)srow * C + c0 + cq);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[2 * j] = __uint_as_float(a[j] << 16) * sc;
+          v[2 * j + 1] = __uint_as_float(a[j] & 0xffff0000u) * sc;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[ri][cq + j] = f32_to_bf16_rne(v[j]);
+  }
+  __syncthreads();
+  // write 64 output rows (columns of the source) x 32 padded rows: 4 threads per row
+  const int cc = tid / 4, part = (tid % 4) * 8;
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = (uint32_t)tile[part + 2 * j][cc] | ((uint32_t)tile[part + 2 * j + 1][cc] << 16);
+  *(u32x4*)(out + (long long)(c0 + cc) * ldk + p0 + part) = o;
+}
+
+// db[seg][c] = sum over the segment's padded columns of M[c][.] (bf16), in
+// column order per lane, then a fixed butterfly.  One wave per (seg, c).
+__global__ __launch_bounds__(256) void seg_rowsum_kernel(const uint16_t* __restrict__ M, int C,
+                                                         int ldk, const int32_t* __restrict__ poff,
+                                                         int nseg, float* __restrict__ db) {
+  const long long wid = ((long long)blockIdx.x * 256 + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (wid >= (long long)nseg * C) return;
+  const int seg = (int)(wid / C), c = (int)(wid % C);
+  const int lo = poff[seg], hi = poff[seg + 1];
+  const uint16_t* row = M + (long long)c * ldk;
+  float s = 0.0f;
+  for (int i = lo + lane * 8; i < hi; i += 512) {
+    const u32x4 v = *(const u32x4*)(row + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += __uint_as_float(v[j] << 16) + __uint_as_float(v[j] & 0xffff0000u);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) db[(long long)seg * C + c] = s;
+}
+
+// ---------------------------------------------------------------- activation backward
+// GELU'(z) = Phi(z) + z phi(z), Phi from the erf approximation of the
+// forward (Abramowitz & Stegun 7.1.28), phi(z) = exp(-z^2/2) / sqrt(2 pi).
+__device__ __forceinline__ float gelu_grad_f(float z) {
+  const float u = fabsf(z) * 0.70710678118654752f;
+  float p = fmaf(4.30638e-5f, u, 2.765672e-4f);
+  p = fmaf(p, u, 1.520143e-4f);
+  p = fmaf(p, u, 9.2705272e-3f);
+  p = fmaf(p, u, 4.22820123e-2f);
+  p = fmaf(p, u, 7.05230784e-2f);
+  p = fmaf(p, u, 1.0f);
+  p *= p;
+  p *= p;
+  p *= p;
+  p *= p;
+  const float r = __builtin_amdgcn_rcpf(p);   // 1 - erf(|z| / sqrt 2)
+  const float cdf = z >= 0.0f ? 1.0f - 0.5f * r : 0.5f * r;
+  const float pdf = 0.3989422804014327f * fast_exp(-0.5f * z * z);
+  return fmaf(z, pdf, cdf);
+}
+
+// One block per row.  Writes Hb (bf16 act(Z)), dZ (bf16) and, for routed
+// rows, dwslot[assignment] = <h, G> + <b2_e, dy_t>.
+template <int ACT>
+__global__ __launch_bounds__(256) void act_backward_kernel(
+    const float* __restrict__ Z, const float* __restrict__ G, const float* __restrict__ dy,
+    const uint16_t* __restrict__ b_down, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_assign, const float* __restrict__ topk_w, int T, int k,
+    int E, int S, int d, int f, uint16_t* __restrict__ Hb, uint16_t* __restrict__ dZ,
+    float* __restrict__ dwslot) {
+  __shared__ float wsum[4];
+  const int r = blockIdx.x;
+  if (r >= offsets[E] + S * T) return;
+  int seg, tok, assign;
+  float wgt;
+  row_info(r, offsets, sorted_assign, topk_w, T, k, E, seg, tok, wgt, assign);
+  const int F1 = ACT == MOE_SWIGLU ? 2 * f : f;
+  const float* zr = Z + (long long)r * F1;
+  const float* gr = G + (long long)r * f;
+  uint16_t* hr = Hb + (long long)r * f;
+  uint16_t* dzr = dZ + (long long)r * F1;
+  float dot = 0.0f;
+  for (int j = threadIdx.x * 4; j < f; j += 1024) {
+    const f32x4 z = *(const f32x4*)(zr + j);
+    const f32x4 g = *(const f32x4*)(gr + j);
+    float h[4], dz[4], du[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float wg = wgt * g[q];
+      if (ACT == MOE_RELU) {
+        h[q] = fmaxf(z[q], 0.0f);
+        dz[q] = z[q] > 0.0f ? wg : 0.0f;
+      } else if (ACT == MOE_GELU) {
+        h[q] = gelu_f(z[q]);
+        dz[q] = wg * gelu_grad_f(z[q]);
+      } else {
+        const float u = zr[f + j + q];
+        const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp(-z[q]));
+        const float si = z[q] * sg;
+        h[q] = si * u;
+        dz[q] = wg * u * sg * fmaf(z[q], 1.0f - sg, 1.0f);
+        du[q] = wg * si;
+      }
+      dot = fmaf(h[q], g[q], dot);
+    }
+    u32x2 ho, zo;
+    ho[0] = (uint32_t)f32_to_bf16_rne(h[0]) | ((uint32_t)f32_to_bf16_rne(h[1]) << 16);
+    ho[1] = (uint32_t)f32_to_bf16_rne(h[2]) | ((uint32_t)f32_to_bf16_rne(h[3]) << 16);
+    zo[0] = (uint32_t)f32_to_bf16_rne(dz[0]) | ((uint32_t)f32_to_bf16_rne(dz[1]) << 16);
+    zo[1] = (uint32_t)f32_to_bf16_rne(dz[2]) | ((uint32_t)f32_to_bf16_rne(dz[3]) << 16);
+    *(u32x2*)(hr + j) = ho;
+    *(u32x2*)(dzr + j) = zo;
+    if (ACT == MOE_SWIGLU) {
+      u32x2 uo;
+      uo[0] = (uint32_t)f32_to_bf16_rne(du[0]) | ((uint32_t)f32_to_bf16_rne(du[1]) << 16);
+      uo[1] = (uint32_t)f32_to_bf16_rne(du[2]) | ((uint32_t)f32_to_bf16_rne(du[3]) << 16);
+      *(u32x2*)(dzr + f + j) = uo;
+    }
+  }
+  if (assign < 0) return;   // shared rows have no gate weight (uniform over the block)
+  if (b_down) {
+    const float* dyr = dy + (long long)tok * d;
+    const uint16_t* br = b_down + (long long)seg * d;
+    for (int j = threadIdx.x; j < d; j += 256) dot = fmaf(bf16_to_f32(br[j]), dyr[j], dot);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = dot;
+  __syncthreads();
+  if (threadIdx.x == 0) dwslot[assign] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+}
+
+// ---------------------------------------------------------------- router backward
+// One wave per token: recompute the logits (lane e = expert e), the keys
+// (softmax p, or sigma for the normalized sigmoid), then
+//   dkey[e_s] += (dw_s - sum_s' w_s' dw_s') / S   (renormalized top-k)
+//   dp[e]      = alpha E f_e / T                    (aux loss through P)
+//   softmax:  dl = p (dkey + dp - sum p (dkey + dp))
+//   sigmoid:  dl = (dkey + (dp - sum p dp) / sum sigma) sigma (1 - sigma)
+// and dx_router[t] = sum_e dl_e Wr[e, :].
+__global__ __launch_bounds__(256) void router_backward_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const uint16_t* __restrict__ br, const int32_t* __restrict__ topk_idx,
+    const int32_t* __restrict__ assign_row, const float* __restrict__ dwslot,
+    const int32_t* __restrict__ counts, float alpha, int T, int d, int E, int k, int gating,
+    float* __restrict__ dlogits, float* __restrict__ d_topk_w, float* __restrict__ dxr) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;   // per wave
+  const uint16_t* xr = x + (long long)t * d;
+  const bool act = lane < E;
+  const uint16_t* wrow = wr + (long long)(act ? lane : 0) * d;
+  float l = 0.0f;
+  for (int j = 0; j < d; j += 8) {
+    const u32x4 xv = *(const u32x4*)(xr + j);
+    const u32x4 wv = *(const u32x4*)(wrow + j);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      l = fmaf(__uint_as_float(xv[q] << 16), __uint_as_float(wv[q] << 16), l);
+      l = fmaf(__uint_as_float(xv[q] & 0xffff0000u), __uint_as_float(wv[q] & 0xffff0000u), l);
+    }
+  }
+  if (br && act) l += bf16_to_f32(br[lane]);
+  float key, p, sig = 0.0f, tot = 1.0f;
+  if (gating == MOE_SOFTMAX) {
+    float m = act ? l : -INFINITY;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    const float ex = act ? fast_exp(l - m) : 0.0f;
+    float sum = ex;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+    p = ex / sum;
+    key = p;
+  } else {
+    sig = act ? 1.0f / (1.0f + fast_exp(-l)) : 0.0f;
+    tot = sig;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
+    p = sig / tot;
+    key = sig;
+  }
+  // renormalized top-k
+  float S = 0.0f, inner = 0.0f, dws[kMaxTopK], ks_[kMaxTopK];
+  int es[kMaxTopK];
+#pragma unroll
+  for (int s = 0; s < kMaxTopK; ++s) {
+    es[s] = 0;
+    dws[s] = 0.0f;
+    ks_[s] = 0.0f;
+    if (s < k) {
+      es[s] = topk_idx[(long long)t * k + s];
+      dws[s] = assign_row[(long long)t * k + s] >= 0 ? dwslot[(long long)t * k + s] : 0.0f;
+    }
+    ks_[s] = __shfl(key, es[s]);
+    if (s < k) S += ks_[s];
+  }
+#pragma unroll
+  for (int s = 0; s < kMaxTopK; ++s)
+    if (s < k) inner = fmaf(ks_[s] / S, dws[s], inner);
+  float dkey = 0.0f;
+#pragma unroll
+  for (int s = 0; s < kMaxTopK; ++s)
+    if (s < k && es[s] == lane) dkey += (dws[s] - inner) / S;
+  const float dp = act ? alpha * (float)E * ((float)counts[act ? lane : 0] / ((float)T * k)) / T : 0.0f;
+  float dl;
+  if (gating == MOE_SOFTMAX) {
+    const float g = dkey + dp;
+    float pg = act ? p * g : 0.0f;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) pg += __shfl_xor(pg, o);
+    dl = act ? p * (g - pg) : 0.0f;
+  } else {
+    float pd = act ? p * dp : 0.0f;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) pd += __shfl_xor(pd, o);
+    const float ds = dkey + (dp - pd) / tot;
+    dl = act ? ds * sig * (1.0f - sig) : 0.0f;
+  }
+  if (act) dlogits[(long long)t * E + lane] = dl;
+  if (d_topk_w && lane < k) {
+    float v = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) v = s == lane ? dws[s] : v;
+    d_topk_w[(long long)t * k + lane] = v;
+  }
+  // dx_router[t, j] = sum_e dl_e Wr[e, j]; lane covers 8 columns per 512
+  for (int j0 = 0; j0 < d; j0 += 512) {
+    const int j = j0 + lane * 8;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int e = 0; e < E; ++e) {
+      const float de = __shfl(dl, e);
+      if (j < d) {
+        const u32x4 wv = *(const u32x4*)(wr + (long long)e * d + j);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = fmaf(de, __uint_as_float(wv[q] << 16), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(de, __uint_as_float(wv[q] & 0xffff0000u), acc[2 * q + 1]);
+        }
+      }
+    }
+    if (j < d) {
+      float* o = dxr + (long long)t * d + j;
+      *(f32x4*)o = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      *(f32x4*)(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    }
+  }
+}
+
+// Partial router weight gradient over a slice of kRwTok tokens:
+// part[slice][e][j] = sum over the slice's tokens (in order) of dl[t, e] x[t, j];
+// bpart[slice][e] likewise of dl[t, e] (blocks of column chunk 0).  Block =
+// 64 columns x 4 expert groups.
+constexpr int kRwTok = 256;
+__global__ __launch_bounds__(256) void router_wgrad_part_kernel(
+    const float* __restrict__ dl, const uint16_t* __restrict__ x, int T, int d, int E,
+    float* __restrict__ part, float* __restrict__ bpart) {
+  __shared__ float sdl[kRwTok][kMaxExperts + 1];
+  const int j = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int eg = threadIdx.x >> 6;   // experts eg, eg+4, ...
+  const int t0 = blockIdx.y * kRwTok;
+  const int nt = min(kRwTok, T - t0);
+  for (int i = threadIdx.x; i < nt * E; i += 256) sdl[i / E][i % E] = dl[(long long)t0 * E + i];
+  __syncthreads();
+  float acc[kMaxExperts / 4];
+#pragma unroll
+  for (int q = 0; q < kMaxExperts / 4; ++q) acc[q] = 0.0f;
+  const int ne = (E - eg + 3) / 4;
+  for (int tt = 0; tt < nt; ++tt) {
+    const float xv = bf16_to_f32(x[(long long)(t0 + tt) * d + j]);
+#pragma unroll
+    for (int q = 0; q < kMaxExperts / 4; ++q)
+      if (q < ne) acc[q] = fmaf(sdl[tt][eg + 4 * q], xv, acc[q]);
+  }
+#pragma unroll
+  for (int q = 0; q < kMaxExperts / 4; ++q)
+    if (q < ne) part[((long long)blockIdx.y * E + eg + 4 * q) * d + j] = acc[q];
+  if (blockIdx.x == 0 && threadIdx.x < E) {
+    float b = 0.0f;
+    for (int tt = 0; tt < nt; ++tt) b += sdl[tt][threadIdx.x];
+    bpart[(long long)blockIdx.y * E + threadIdx.x] = b;
+  }
+}
+
+// dWr[e][j] = sum over slices (in order) of part; dbr likewise.
+__global__ __launch_bounds__(256) void router_wgrad_sum_kernel(const float* __restrict__ part,
+                                                               const float* __restrict__ bpart,
+                                                               int nslices, int E, int d,
+                                                               float* __restrict__ dwr,
+                                                               float* __restrict__ dbr) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long n = (long long)E * d;
+  if (i < n) {
+    float s = 0.0f;
+    for (int q = 0; q < nslices; ++q) s += part[(long long)q * n + i];
+    dwr[i] = s;
+  }
+  if (dbr && i < E) {
+    float s = 0.0f;
+    for (int q = 0; q < nslices; ++q) s += bpart[(long long)q * E + i];
+    dbr[i] = s;
+  }
+}
+
+// dx[t] = dx_router[t] + sum over kept slots (slot order) of the dX row (+ its
+// K-slice parts) + sum over shared experts of their rows.  One thread per 4
+// columns.
+__global__ __launch_bounds__(256) void dx_gather_kernel(
+    const float* __restrict__ dxr, const float* __restrict__ dxrows,
+    const float* __restrict__ parts, int nparts, long long part_elems,
+    const int32_t* __restrict__ assign_row, const int32_t* __restrict__ offsets, int T, int d,
+    int k, int E, int S, float* __restrict__ dx) {
+  const int dv = d / 4;
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (long long)T * dv) return;
+  const int t = (int)(gid / dv);
+  const int c = (int)(gid % dv) * 4;
+  auto row = [&](long long r) {
+    f32x4 v = *(const f32x4*)(dxrows + r * d + c);
+    for (int p = 0; p < nparts; ++p) v += *(const f32x4*)(parts + p * part_elems + r * d + c);
+    return v;
+  };
+  f32x4 acc = *(const f32x4*)(dxr + (long long)t * d + c);
+  for (int s = 0; s < k; ++s) {
+    const int r = assign_row[(long long)t * k + s];
+    if (r >= 0) acc += row(r);
+  }
+  const long long base = offsets[E];
+  for (int q = 0; q < S; ++q) acc += row(base + (long long)q * T + t);
+  *(f32x4*)(dx + (long long)t * d + c) = acc;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_cast_bf16(const float* src, uint16_t* dst, long long n, hipStream_t st) {
+  const long long n4 = n / 4;
+  cast_bf16_kernel<<<(int)((n4 + 255) / 256), 256, 0, st>>>(src, dst, n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const void* src, void* dst, int nmat, int R, int C, hipStream_t st) {
+  transpose_kernel<<<dim3(C / 64, R / 64, nmat), 256, 0, st>>>((const uint16_t*)src,
+                                                               (uint16_t*)dst, R, C);
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad_offsets(const Shape& s, const int32_t* offsets, int32_t* poff,
+                                hipStream_t st) {
+  wgrad_offsets_kernel<<<1, 64, 0, st>>>(offsets, s.T, s.E, s.S, poff);
+  return hipGetLastError();
+}
+
+// kind: 0 = fp32 rows gathered by token and scaled by the gate weight (dy);
+// 1 = bf16 rows as they are (H, dZ); 2 = bf16 rows gathered by token (x).
+hipError_t launch_seg_transpose(const Shape& s, int kind, const void* src, int C,
+                                const int32_t* offsets, const int32_t* sorted_assign,
+                                const float* topk_w, const int32_t* poff, uint16_t* out, int ldk,
+                                hipStream_t st) {
+  const dim3 grid(ldk / 32, C / 64);
+  if (kind == 0)
+    seg_transpose_kernel<true, true, true><<<grid, 256, 0, st>>>(
+        src, C, offsets, sorted_assign, topk_w, poff, s.T, s.k, s.E, s.S, out, ldk);
+  else if (kind == 1)
+    seg_transpose_kernel<false, false, false><<<grid, 256, 0, st>>>(
+        src, C, offsets, sorted_assign, topk_w, poff, s.T, s.k, s.E, s.S, out, ldk);
+  else
+    seg_transpose_kernel<false, true, false><<<grid, 256, 0, st>>>(
+        src, C, offsets, sorted_assign, topk_w, poff, s.T, s.k, s.E, s.S, out, ldk);
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_rowsum(const Shape& s, const uint16_t* M, int C, int ldk,
+                             const int32_t* poff, float* db, hipStream_t st) {
+  const long long waves = (long long)(s.E + s.S) * C;
+  seg_rowsum_kernel<<<(int)((waves * 64 + 255) / 256), 256, 0, st>>>(M, C, ldk, poff, s.E + s.S,
+                                                                      db);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_backward(const Shape& s, const float* Z, const float* G, const float* dy,
+                               const void* b_down, const int32_t* offsets,
+                               const int32_t* sorted_assign, const float* topk_w, uint16_t* Hb,
+                               uint16_t* dZ, float* dwslot, hipStream_t st) {
+  const int blocks = (int)s.max_rows();
+  const uint16_t* b2 = (const uint16_t*)b_down;
+#define MOE_ACT_BWD(A)                                                                          \
+  act_backward_kernel<A><<<blocks, 256, 0, st>>>(Z, G, dy, b2, offsets, sorted_assign, topk_w, \
+                                                 s.T, s.k, s.E, s.S, s.d, s.f, Hb, dZ, dwslot)
+  if (s.act == MOE_RELU) MOE_ACT_BWD(MOE_RELU);
+  else if (s.act == MOE_GELU) MOE_ACT_BWD(MOE_GELU);
+  else MOE_ACT_BWD(MOE_SWIGLU);
+#undef MOE_ACT_BWD
+  return hipGetLastError();
+}
+
+hipError_t launch_router_backward(const Shape& s, const void* x, const void* wr, const void* br,
+                                  const int32_t* topk_idx, const int32_t* assign_row,
+                                  const float* dwslot, const int32_t* counts, float alpha,
+                                  float* dlogits, float* d_topk_w, float* dxr, hipStream_t st) {
+  router_backward_kernel<<<(s.T + 3) / 4, 256, 0, st>>>(
+      (const uint16_t*)x, (const uint16_t*)wr, (const uint16_t*)br, topk_idx, assign_row, dwslot,
+      counts, alpha, s.T, s.d, s.E, s.k, s.gating, dlogits, d_topk_w, dxr);
+  return hipGetLastError();
+}
+
+int router_wgrad_slices(const Shape& s) { return (s.T + kRwTok - 1) / kRwTok; }
+
+hipError_t launch_router_wgrad(const Shape& s, const float* dlogits, const void* x, float* part,
+                               float* bpart, float* dwr, float* dbr, hipStream_t st) {
+  const int ns = router_wgrad_slices(s);
+  router_wgrad_part_kernel<<<dim3(s.d / 64, ns), 256, 0, st>>>(dlogits, (const uint16_t*)x, s.T,
+                                                               s.d, s.E, part, bpart);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long n = (long long)s.E * s.d;
+  router_wgrad_sum_kernel<<<(int)((n + 255) / 256), 256, 0, st>>>(part, bpart, ns, s.E, s.d, dwr,
+                                                                  dbr);
+  return hipGetLastError();
+}
+
+hipError_t launch_dx_gather(const Shape& s, const float* dxr, const float* dxrows,
+                            const float* parts, int nparts, long long part_elems,
+                            const int32_t* assign_row, const int32_t* offsets, float* dx,
+                            hipStream_t st) {
+  const long long n = (long long)s.T * (s.d / 4);
+  dx_gather_kernel<<<(int)((n + 255) / 256), 256, 0, st>>>(dxr, dxrows, parts, nparts, part_elems,
+                                                           assign_row, offsets, s.T, s.d, s.k, s.E,
+                                                           s.S, dx);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -33,7 +33,16 @@
 namespace moe {
 namespace {
 
-enum { MODE_RELU = 0, MODE_GELU = 1, MODE_SWIGLU = 2, MODE_DOWN = 3 };
+// Up projection with activation (RELU/GELU/SWIGLU, fp16 h out), down
+// projection (DOWN: fp16 h times W2 converted to fp16, fp32 out).  The
+// backward pass adds: LIN, gathered token rows times bf16 weights with an
+// optional bias and fp32 out (no activation); DXB, like DOWN with bf16 rows
+// and weights; WGRAD, the per-expert weight gradient, whose reduction runs
+// over the expert's rows (see wgrad_* below).
+enum {
+  MODE_RELU = 0, MODE_GELU = 1, MODE_SWIGLU = 2, MODE_DOWN = 3, MODE_LIN = 4, MODE_DXB = 5,
+  MODE_WGRAD = 6
+};
 
 struct GemmArgs {
   const uint16_t* X;       // up: x [T, K] bf16; down: h [rows, K] fp16
@@ -43,11 +52,23 @@ struct GemmArgs {
   const int32_t* offsets;  // [E + 1]
   const int32_t* sorted_assign;
   int T, k, E, S, K, Nout, Wrows, f;
-  // down only: K slices; slice i > 0 writes to out2 + (i - 1) * part_elems
+  // DOWN / DXB: K slices; slice i > 0 writes to out2 + (i - 1) * part_elems
   int ksplit;
   float* out2;
   long long part_elems;
+  // WGRAD: out[seg] = A_seg B_seg^T, [M, Nout] fp32, with A = X [M, K] and
+  // B = W [Nout, K] (row stride K); segment seg reduces over its padded row
+  // range of the columns (wgrad_pad / wgrad_poff)
+  int M;
 };
+
+// Weight-gradient layout: segment seg's rows occupy columns poff .. poff+pad
+// of the transposed operands, pad = rows rounded up to a multiple of 32 (at
+// least 32; the padding is zero), so every segment has a whole, non-empty
+// number of 32-deep k-tiles.
+__host__ __device__ __forceinline__ int wgrad_pad(int rows) {
+  return rows <= 0 ? 32 : (rows + 31) / 32 * 32;
+}
 
 // Per-segment row count and first row.
 __device__ __forceinline__ void segment_rows(const GemmArgs& a, int seg, int off_E, int& rows,
@@ -96,7 +117,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   static_assert(NSTAGE == 3 || NSTAGE == 4, "ring depth");
   constexpr int NW = WGM * WGN;            // waves: WGM along tokens x WGN along weights
   constexpr bool SWIGLU = MODE == MODE_SWIGLU;
-  constexpr bool DOWN = MODE == MODE_DOWN;
+  constexpr bool GATHER = MODE <= MODE_SWIGLU || MODE == MODE_LIN;   // token rows via sorted_assign
+  constexpr bool CVT16 = MODE == MODE_DOWN;      // fp16 rows: W converted bf16 -> fp16
+  constexpr bool OUT32 = MODE >= MODE_DOWN;      // fp32 output (else fp16 h)
+  constexpr bool KSPLIT = MODE == MODE_DOWN || MODE == MODE_DXB;
+  constexpr bool WG = MODE == MODE_WGRAD;
   constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile: token rows x weight rows
   constexpr int MI = WM / 32, NI = WN / 32;
   constexpr int NOUT_TILE = SWIGLU ? BN / 2 : BN;
@@ -124,12 +149,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   const int NT = (a.Nout + NOUT_TILE - 1) / NOUT_TILE;
   const int off_E = a.offsets[a.E];
 
-  // ---- tile schedule: prefix sum of m-tiles per segment (wave 0, 2 segments per lane)
+  // ---- tile schedule: prefix sum of m-tiles per segment (wave 0, 2 segments
+  // per lane).  WGRAD: every segment has the same M tiles; the prefix is that
+  // of the padded row counts (the segment's k range), kept in seg_kpos.
+  __shared__ int seg_kpos[WG ? kMaxSegments + 1 : 1];
   if (wave == 0) {
     int c0 = 0, c1 = 0, r, st;
     const int s0 = 2 * lane, s1 = 2 * lane + 1;
-    if (s0 < nseg) { segment_rows(a, s0, off_E, r, st); c0 = (r + BM - 1) / BM; }
-    if (s1 < nseg) { segment_rows(a, s1, off_E, r, st); c1 = (r + BM - 1) / BM; }
+    if (s0 < nseg) { segment_rows(a, s0, off_E, r, st); c0 = WG ? wgrad_pad(r) : (r + BM - 1) / BM; }
+    if (s1 < nseg) { segment_rows(a, s1, off_E, r, st); c1 = WG ? wgrad_pad(r) : (r + BM - 1) / BM; }
     int v = c0 + c1, incl = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -137,13 +165,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
       if (lane >= o) incl += u;
     }
     const int excl = incl - v;
-    if (s0 < nseg) seg_tile[s0] = excl;
-    if (s1 < nseg) seg_tile[s1] = excl + c0;
-    if (lane == 63) seg_tile[nseg] = incl;
+    if (WG) {
+      const int mtw = (a.M + BM - 1) / BM;
+      if (s0 < nseg) seg_kpos[s0] = excl;
+      if (s1 < nseg) seg_kpos[s1] = excl + c0;
+      if (lane == 63) seg_kpos[nseg] = incl;
+      if (s0 < nseg) seg_tile[s0] = s0 * mtw;
+      if (s1 < nseg) seg_tile[s1] = s1 * mtw;
+      if (lane == 63) seg_tile[nseg] = nseg * mtw;
+    } else {
+      if (s0 < nseg) seg_tile[s0] = excl;
+      if (s1 < nseg) seg_tile[s1] = excl + c0;
+      if (lane == 63) seg_tile[nseg] = incl;
+    }
   }
   __syncthreads();
   // Tiles per K slice; with several slices the slice is the slowest index.
-  const int nsplit = DOWN ? a.ksplit : 1;
+  const int nsplit = KSPLIT ? a.ksplit : 1;
   const int tiles = seg_tile[nseg] * NT;
   const int total = tiles * nsplit;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -169,6 +207,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   const int nt = local / mtiles, mt = local % mtiles;
   int seg_rows, row_start;
   segment_rows(a, seg, off_E, seg_rows, row_start);
+  if (WG) {   // output rows of this segment's gradient; no gather, no row offset
+    seg_rows = a.M;
+    row_start = seg * a.M;
+  }
 
   // ---- LDS layout.  Row r of a tile (W rows first, then token rows) holds
   // its ROWCH chunks of 16 bytes at chunk positions kc ^ ((r / RPB) % ROWCH).
@@ -184,11 +226,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   // Wave w issues the W instructions q = w*QWW + j and the token-row
   // instructions q = BN/RI + w*QWX + j.
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int kslice = a.K / nsplit;         // K elements of this block's slice
+  // K elements of this block's slice; WGRAD: the segment's padded row range
+  const int kslice = WG ? seg_kpos[seg + 1] - seg_kpos[seg] : a.K / nsplit;
   const char* xbase;
-  if (DOWN) xbase = (const char*)(a.X + (long long)row_start * a.K + (long long)ks * kslice);
-  else xbase = (const char*)a.X;
-  const char* wbase = (const char*)(a.W + (long long)seg * a.Wrows * a.K + (long long)ks * kslice);
+  const char* wbase;
+  if (WG) {
+    xbase = (const char*)(a.X + seg_kpos[seg]);
+    wbase = (const char*)(a.W + seg_kpos[seg]);
+  } else {
+    if (GATHER) xbase = (const char*)a.X;
+    else xbase = (const char*)(a.X + (long long)row_start * a.K + (long long)ks * kslice);
+    wbase = (const char*)(a.W + (long long)seg * a.Wrows * a.K + (long long)ks * kslice);
+  }
   auto kc_dma = [&](int q) { return (lane % ROWCH) ^ ((4 * q + lane / 16) % ROWCH); };
   uint32_t woff[QWW], xoff[QWX];   // byte offsets of this lane's source chunks
 #pragma unroll
@@ -214,7 +263,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
     const int m = mt * BM + rr;
     const int mm = m < seg_rows ? m : seg_rows - 1;
     uint32_t row;
-    if (DOWN) row = (uint32_t)mm;
+    if (!GATHER) row = (uint32_t)mm;
     else row = seg < a.E ? (uint32_t)(a.sorted_assign[row_start + mm] / a.k) : (uint32_t)mm;
     xoff[j] = (row * (uint32_t)a.K + (uint32_t)kc_dma(q) * 8u) * 2u;
   }
@@ -268,10 +317,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       // the down projection's W2 tile is bf16 in LDS: fp16 for the fp16 MFMA
-      const u32x4 w = DOWN ? bf16x8_to_f16x8(wf[j]) : wf[j];
+      const u32x4 w = CVT16 ? bf16x8_to_f16x8(wf[j]) : wf[j];
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
-        if (DOWN)
+        if (CVT16)
           acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
               __builtin_bit_cast(f16x8, w), __builtin_bit_cast(f16x8, xf[i]), acc[j][i], 0, 0, 0);
         else
@@ -355,8 +404,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   // the staging writes and reads free of bank conflicts.
   constexpr int NJ = SWIGLU ? NI / 2 : NI;
   constexpr int WNOUT = NJ * 32;                       // output columns of a wave
-  constexpr int ES = DOWN ? 4 : 2;                      // output element bytes
-  constexpr int PITCH = WNOUT * ES + (DOWN ? 16 : 8);   // staging row pitch, bytes
+  constexpr int ES = OUT32 ? 4 : 2;                     // output element bytes
+  constexpr int PITCH = WNOUT * ES + (OUT32 ? 16 : 8);  // staging row pitch, bytes
   constexpr int CPR = WNOUT * ES / 16;                  // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;                         // rows per store instruction
   constexpr int STG = 32 * PITCH;                       // staging bytes per wave
@@ -394,7 +443,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
           v[3] += __uint_as_float(b[1] & 0xffff0000u);
         }
         char* dst = stg + (lane & 31) * PITCH + nloc * ES;
-        if (DOWN) {
+        if (OUT32) {
           *(f32x4*)dst = f32x4{v[0], v[1], v[2], v[3]};
         } else {
 #pragma unroll
@@ -535,15 +584,16 @@ __global__ __launch_bounds__(256) void part_fold_kernel(float* __restrict__ y_ex
 
 }  // namespace
 
-int down_ksplit(const Shape& s) {
-  if (s.dtype != MOE_BF16 || s.decode()) return 1;
+// K slices of a down-style grouped GEMM (K = reduction length, N = output
+// columns) over the routed and shared row segments.
+static int gemm_ksplit(const Shape& s, int K, int N) {
   // expected tiles with evenly routed experts (capacity-limited)
   long long per = (s.routed_rows() + s.E - 1) / s.E;
   if (s.cap > 0 && per > s.cap) per = s.cap;
   const long long mt = (long long)s.E * ((per + DN_BM - 1) / DN_BM) +
                        (long long)s.S * ((s.T + DN_BM - 1) / DN_BM);
-  const long long tiles = mt * ((s.d + DN_BN - 1) / DN_BN);
-  const int nkt = s.f / 32;   // k-tiles of the whole reduction
+  const long long tiles = mt * ((N + DN_BN - 1) / DN_BN);
+  const int nkt = K / 32;     // k-tiles of the whole reduction
   int ks = 1;
   // split while the slices still fit in three quarters of the CUs and each
   // slice keeps at least 8 k-tiles
@@ -552,6 +602,13 @@ int down_ksplit(const Shape& s) {
     ks *= 2;
   return ks;
 }
+
+int down_ksplit(const Shape& s) {
+  if (s.dtype != MOE_BF16 || s.decode()) return 1;
+  return gemm_ksplit(s, s.f, s.d);
+}
+
+int bwd_dx_ksplit(const Shape& s) { return gemm_ksplit(s, s.up_rows(), s.d); }
 
 hipError_t launch_decode_up(const Shape& s, const void* x, const void* w_up, const void* b_up,
                             const float* s_up, const int32_t* offsets,
@@ -586,7 +643,7 @@ hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void
   }
   if (s.decode()) return launch_decode_up(s, x, w_up, b_up, s_up, offsets, sorted_assign, h, st);
   GemmArgs a{(const uint16_t*)x, (const uint16_t*)w_up, (const uint16_t*)bias, h, offsets,
-             sorted_assign, s.T, s.tok_div(), s.E, s.S, s.d, s.f, s.up_rows(), s.f, 1, nullptr, 0};
+             sorted_assign, s.T, s.tok_div(), s.E, s.S, s.d, s.f, s.up_rows(), s.f, 1, nullptr, 0, 0};
   if (s.act == MOE_SWIGLU) {
     const int NT = (s.f + UP_BN / 2 - 1) / (UP_BN / 2);
     grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_SWIGLU, UP_NST, UP_OCC>
@@ -621,7 +678,7 @@ hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const 
   const int ks = down_ksplit(s);
   const long long part_elems = s.max_rows() * s.d;
   GemmArgs a{(const uint16_t*)h, (const uint16_t*)w_down, (const uint16_t*)bias, y_exp, offsets,
-             nullptr, s.T, s.tok_div(), s.E, s.S, s.f, s.d, s.d, s.f, ks, y_part, part_elems};
+             nullptr, s.T, s.tok_div(), s.E, s.S, s.f, s.d, s.d, s.f, ks, y_part, part_elems, 0};
   const int NT = (s.d + DN_BN - 1) / DN_BN;
   grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DOWN, DN_NST, DN_OCC>
       <<<grid_blocks(s, DN_BM, NT, ks), 64 * DN_WGM * DN_WGN, 0, st>>>(a);
@@ -630,6 +687,49 @@ hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const 
   const long long n = s.max_rows() * (s.d / 4);
   part_fold_kernel<<<(int)((n + 255) / 256), 256, 0, st>>>(y_exp, y_part, offsets, s.T, s.E, s.S,
                                                            s.d, ks - 1, part_elems);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- backward GEMMs
+// out[r, n] = sum_j X[token of r, j] W_seg[n, j] (+ bias_seg[n]) for n < Wrows,
+// over the routed and shared row segments; fp32 out [rows, Wrows].
+hipError_t launch_bwd_lin(const Shape& s, const void* X, const void* W, const void* bias,
+                          int Wrows, int K, float* out, const int32_t* offsets,
+                          const int32_t* sorted_assign, hipStream_t st) {
+  GemmArgs a{(const uint16_t*)X, (const uint16_t*)W, (const uint16_t*)bias, out, offsets,
+             sorted_assign, s.T, s.tok_div(), s.E, s.S, K, Wrows, Wrows, s.f, 1, nullptr, 0, 0};
+  const int NT = (Wrows + DN_BN - 1) / DN_BN;
+  grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_LIN, DN_NST, DN_OCC>
+      <<<grid_blocks(s, DN_BM, NT), 64 * DN_WGM * DN_WGN, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+// out[r, n] = sum_j X[r, j] W_seg[n, j] for the rows X [rows, K] (bf16) and
+// W [segments][N][K]; K slices as in the down projection (slice i > 0 into
+// out2 + (i - 1) * part_elems).
+hipError_t launch_bwd_dx(const Shape& s, const void* X, const void* W, int K, int N, float* out,
+                         float* out2, long long part_elems, int ksplit, const int32_t* offsets,
+                         hipStream_t st) {
+  GemmArgs a{(const uint16_t*)X, (const uint16_t*)W, nullptr, out, offsets, nullptr, s.T,
+             s.tok_div(), s.E, s.S, K, N, N, s.f, ksplit, out2, part_elems, 0};
+  const int NT = (N + DN_BN - 1) / DN_BN;
+  grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DXB, DN_NST, DN_OCC>
+      <<<grid_blocks(s, DN_BM, NT, ksplit), 64 * DN_WGM * DN_WGN, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+// out[seg] = A_seg B_seg^T: A [M, ldk] and B [N, ldk] bf16, segment seg
+// reducing over its padded row range; fp32 out [segments][M][N].
+hipError_t launch_bwd_wgrad(const Shape& s, const void* A, const void* B, int M, int N, int ldk,
+                            float* out, const int32_t* offsets, hipStream_t st) {
+  GemmArgs a{(const uint16_t*)A, (const uint16_t*)B, nullptr, out, offsets, nullptr, s.T,
+             s.tok_div(), s.E, s.S, ldk, N, N, s.f, 1, nullptr, 0, M};
+  const long long tiles = (long long)(s.E + s.S) * ((M + DN_BM - 1) / DN_BM) *
+                          ((N + DN_BN - 1) / DN_BN);
+  long long g = MOE_PERSISTENT && tiles > kNumCUs ? kNumCUs : tiles;
+  g = (g + 7) / 8 * 8;
+  grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_WGRAD, DN_NST, DN_OCC>
+      <<<(int)g, 64 * DN_WGM * DN_WGN, 0, st>>>(a);
   return hipGetLastError();
 }
 

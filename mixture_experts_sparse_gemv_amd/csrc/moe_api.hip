@@ -51,6 +51,41 @@ WsLayout ws_layout(const Shape& s) {
   return w;
 }
 
+BwdLayout bwd_layout(const Shape& s) {
+  BwdLayout b{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  const size_t rows = (size_t)s.max_rows();
+  const size_t F1 = (size_t)s.up_rows(), nseg = (size_t)(s.E + s.S);
+  const size_t ldk = (size_t)wgrad_ldk(s);
+  const int ks = bwd_dx_ksplit(s);
+  b.dyb = take((size_t)s.T * s.d * 2);
+  b.w1t = take(nseg * F1 * s.d * 2);
+  b.w2t = take(nseg * s.d * s.f * 2);
+  b.Z = take(rows * F1 * 4);
+  b.G = take(rows * s.f * 4);
+  b.Hb = take(rows * s.f * 2);
+  b.dZ = take(rows * F1 * 2);
+  b.dxrows = take(rows * s.d * 4);
+  b.dxparts = ks > 1 ? take((size_t)(ks - 1) * rows * s.d * 4) : o;
+  b.A2 = take((size_t)s.d * ldk * 2);
+  b.B2 = take((size_t)s.f * ldk * 2);
+  b.A1 = take(F1 * ldk * 2);
+  b.B1 = take((size_t)s.d * ldk * 2);
+  b.dwslot = take((size_t)s.T * s.k * 4);
+  b.dlogits = take((size_t)s.T * s.E * 4);
+  b.dxr = take((size_t)s.T * s.d * 4);
+  b.rw_part = take((size_t)router_wgrad_slices(s) * s.E * s.d * 4);
+  b.rb_part = take((size_t)router_wgrad_slices(s) * s.E * 4);
+  b.poff = take((nseg + 1) * 4);
+  b.total = o;
+  return b;
+}
+
 static moe_status fail_hip(hipError_t e) {
   if (e == hipSuccess) return MOE_OK;
   g_last_hip_error = (int32_t)e;
@@ -346,6 +381,117 @@ moe_status moe_ffn_forward(const moe_problem* p, const moe_weights* w, const voi
   if (e == hipSuccess)
     e = s.ec() ? launch_combine_ec(s, topk_w, assign_row, offsets, y_exp, y_part, nparts, y, stream)
                : launch_combine(s, topk_w, assign_row, offsets, y_exp, y_part, nparts, y, stream);
+  return fail_hip(e);
+}
+
+// Backward limits beyond check_problem's.
+static moe_status check_backward(const Shape& s) {
+  if (s.dtype != MOE_BF16 || s.ec() || s.w_fp8()) return MOE_ERR_UNSUPPORTED;
+  const long long ldk = wgrad_ldk(s);
+  // transposed operands [F1 or d, ldk] bf16 are addressed with 32-bit offsets
+  if ((long long)s.up_rows() * ldk * 2 >= (1LL << 32) || (long long)s.d * ldk * 2 >= (1LL << 32) ||
+      (long long)s.f * ldk * 2 >= (1LL << 32))
+    return MOE_ERR_UNSUPPORTED;
+  // token rows (x, dy) and the largest row segment are addressed likewise
+  if ((long long)s.T * s.d * 4 >= (1LL << 32) || s.max_rows() * (long long)s.up_rows() * 2 >= (1LL << 32))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status moe_backward_workspace_size(const moe_problem* p, size_t* bytes) {
+  Shape s;
+  moe_status st = check_problem(p, s);
+  if (st != MOE_OK) return st;
+  if ((st = check_backward(s)) != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = bwd_layout(s).total;
+  return MOE_OK;
+}
+
+moe_status moe_ffn_backward(const moe_problem* p, const moe_weights* w, const void* x,
+                            const float* dy, float alpha, const moe_routing* fwd,
+                            const moe_grads* g, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  moe_status st = check_problem(p, s);
+  if (st != MOE_OK) return st;
+  if ((st = check_backward(s)) != MOE_OK) return st;
+  if ((st = check_weights(s, w, true, true)) != MOE_OK) return st;
+  if (!x || !dy || !fwd || !g || !isfinite(alpha)) return MOE_ERR_INVALID_ARG;
+  if (!fwd->topk_idx || !fwd->topk_w || !fwd->counts || !fwd->offsets || !fwd->sorted_assign ||
+      !fwd->assign_row)
+    return MOE_ERR_INVALID_ARG;
+  if (!g->dx || !g->dw_router || !g->dw_up || !g->dw_down) return MOE_ERR_INVALID_ARG;
+  if (s.expert_bias() && (!g->db_up || !g->db_down)) return MOE_ERR_INVALID_ARG;
+  const BwdLayout B = bwd_layout(s);
+  if (!ws || ws_bytes < B.total) return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)ws & 255) != 0) return MOE_ERR_INVALID_ARG;
+
+  const int F1 = s.up_rows(), nseg = s.E + s.S, ldk = wgrad_ldk(s);
+  const int ks = bwd_dx_ksplit(s);
+  const long long part_elems = s.max_rows() * s.d;
+  const int32_t* offsets = fwd->offsets;
+  const int32_t* sa = fwd->sorted_assign;
+  const float* topk_w = fwd->topk_w;
+  uint16_t* dyb = at<uint16_t>(ws, B.dyb);
+  uint16_t* w1t = at<uint16_t>(ws, B.w1t);
+  uint16_t* w2t = at<uint16_t>(ws, B.w2t);
+  float* Z = at<float>(ws, B.Z);
+  float* G = at<float>(ws, B.G);
+  uint16_t* Hb = at<uint16_t>(ws, B.Hb);
+  uint16_t* dZ = at<uint16_t>(ws, B.dZ);
+  float* dxrows = at<float>(ws, B.dxrows);
+  float* dxparts = at<float>(ws, B.dxparts);
+  uint16_t* A2 = at<uint16_t>(ws, B.A2);
+  uint16_t* B2 = at<uint16_t>(ws, B.B2);
+  uint16_t* A1 = at<uint16_t>(ws, B.A1);
+  uint16_t* B1 = at<uint16_t>(ws, B.B1);
+  float* dwslot = at<float>(ws, B.dwslot);
+  float* dlogits = g->d_logits ? g->d_logits : at<float>(ws, B.dlogits);
+  float* dxr = at<float>(ws, B.dxr);
+  int32_t* poff = at<int32_t>(ws, B.poff);
+  const void* b_up = s.expert_bias() ? w->b_up : nullptr;
+  const void* b_down = s.expert_bias() ? w->b_down : nullptr;
+
+  // operands in the layouts the grouped GEMM reads: bf16 dy, W1^T and W2^T
+  hipError_t e = launch_cast_bf16(dy, dyb, (long long)s.T * s.d, stream);
+  if (e == hipSuccess) e = launch_transpose(w->w_up, w1t, nseg, F1, s.d, stream);
+  if (e == hipSuccess) e = launch_transpose(w->w_down, w2t, nseg, s.d, s.f, stream);
+  // recomputed pre-activations, and G = dy_rows W2
+  if (e == hipSuccess)
+    e = launch_bwd_lin(s, x, w->w_up, b_up, F1, s.d, Z, offsets, sa, stream);
+  if (e == hipSuccess) e = launch_bwd_lin(s, dyb, w2t, nullptr, s.f, s.d, G, offsets, sa, stream);
+  // h, dZ and the gate weights' gradient
+  if (e == hipSuccess)
+    e = launch_act_backward(s, Z, G, dy, b_down, offsets, sa, topk_w, Hb, dZ, dwslot, stream);
+  // dX rows = dZ W1
+  if (e == hipSuccess)
+    e = launch_bwd_dx(s, dZ, w1t, F1, s.d, dxrows, dxparts, part_elems, ks, offsets, stream);
+  // weight gradients: transposed, zero-padded operands per segment
+  if (e == hipSuccess) e = launch_wgrad_offsets(s, offsets, poff, stream);
+  if (e == hipSuccess)
+    e = launch_seg_transpose(s, 0, dy, s.d, offsets, sa, topk_w, poff, A2, ldk, stream);
+  if (e == hipSuccess)
+    e = launch_seg_transpose(s, 1, Hb, s.f, offsets, sa, topk_w, poff, B2, ldk, stream);
+  if (e == hipSuccess)
+    e = launch_seg_transpose(s, 1, dZ, F1, offsets, sa, topk_w, poff, A1, ldk, stream);
+  if (e == hipSuccess)
+    e = launch_seg_transpose(s, 2, x, s.d, offsets, sa, topk_w, poff, B1, ldk, stream);
+  if (e == hipSuccess) e = launch_bwd_wgrad(s, A2, B2, s.d, s.f, ldk, g->dw_down, offsets, stream);
+  if (e == hipSuccess) e = launch_bwd_wgrad(s, A1, B1, F1, s.d, ldk, g->dw_up, offsets, stream);
+  if (e == hipSuccess && s.expert_bias()) e = launch_seg_rowsum(s, A2, s.d, ldk, poff, g->db_down, stream);
+  if (e == hipSuccess && s.expert_bias()) e = launch_seg_rowsum(s, A1, F1, ldk, poff, g->db_up, stream);
+  // router
+  if (e == hipSuccess)
+    e = launch_router_backward(s, x, w->w_router, s.router_bias() ? w->b_router : nullptr,
+                               fwd->topk_idx, fwd->assign_row, dwslot, fwd->counts, alpha,
+                               dlogits, g->d_topk_w, dxr, stream);
+  if (e == hipSuccess)
+    e = launch_router_wgrad(s, dlogits, x, at<float>(ws, B.rw_part), at<float>(ws, B.rb_part),
+                            g->dw_router, g->db_router, stream);
+  // dx = router part + the rows of every kept slot and shared expert
+  if (e == hipSuccess)
+    e = launch_dx_gather(s, dxr, dxrows, dxparts, ks - 1, part_elems, fwd->assign_row, offsets,
+                         g->dx, stream);
   return fail_hip(e);
 }
 

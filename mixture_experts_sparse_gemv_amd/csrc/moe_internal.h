@@ -178,4 +178,53 @@ hipError_t launch_combine(const Shape& s, const float* topk_w, const int32_t* as
                           const int32_t* offsets, const float* y_exp, const float* y_part,
                           int nparts, float* y, hipStream_t st);
 
+// ---------------------------------------------------------------- backward
+// K slices of the dX GEMM (reduction over F1, d outputs), as down_ksplit.
+int bwd_dx_ksplit(const Shape& s);
+// Row stride of the transposed weight-gradient operands: every segment's
+// rows padded to a multiple of 32 (at least 32) fit.
+inline int wgrad_ldk(const Shape& s) {
+  return (int)(((s.max_rows() + 31) / 32) * 32 + 32LL * (s.E + s.S));
+}
+int router_wgrad_slices(const Shape& s);
+struct BwdLayout {
+  size_t dyb, w1t, w2t, Z, G, Hb, dZ, dxrows, dxparts, A2, B2, A1, B1, dwslot, dlogits, dxr,
+      rw_part, rb_part, poff, total;
+};
+BwdLayout bwd_layout(const Shape& s);
+
+hipError_t launch_cast_bf16(const float* src, uint16_t* dst, long long n, hipStream_t st);
+// dst[m] = src[m]^T for nmat bf16 matrices of R x C (multiples of 64).
+hipError_t launch_transpose(const void* src, void* dst, int nmat, int R, int C, hipStream_t st);
+hipError_t launch_bwd_lin(const Shape& s, const void* X, const void* W, const void* bias,
+                          int Wrows, int K, float* out, const int32_t* offsets,
+                          const int32_t* sorted_assign, hipStream_t st);
+hipError_t launch_bwd_dx(const Shape& s, const void* X, const void* W, int K, int N, float* out,
+                         float* out2, long long part_elems, int ksplit, const int32_t* offsets,
+                         hipStream_t st);
+hipError_t launch_bwd_wgrad(const Shape& s, const void* A, const void* B, int M, int N, int ldk,
+                            float* out, const int32_t* offsets, hipStream_t st);
+hipError_t launch_act_backward(const Shape& s, const float* Z, const float* G, const float* dy,
+                               const void* b_down, const int32_t* offsets,
+                               const int32_t* sorted_assign, const float* topk_w, uint16_t* Hb,
+                               uint16_t* dZ, float* dwslot, hipStream_t st);
+hipError_t launch_wgrad_offsets(const Shape& s, const int32_t* offsets, int32_t* poff,
+                                hipStream_t st);
+hipError_t launch_seg_transpose(const Shape& s, int kind, const void* src, int C,
+                                const int32_t* offsets, const int32_t* sorted_assign,
+                                const float* topk_w, const int32_t* poff, uint16_t* out, int ldk,
+                                hipStream_t st);
+hipError_t launch_seg_rowsum(const Shape& s, const uint16_t* M, int C, int ldk,
+                             const int32_t* poff, float* db, hipStream_t st);
+hipError_t launch_router_backward(const Shape& s, const void* x, const void* wr, const void* br,
+                                  const int32_t* topk_idx, const int32_t* assign_row,
+                                  const float* dwslot, const int32_t* counts, float alpha,
+                                  float* dlogits, float* d_topk_w, float* dxr, hipStream_t st);
+hipError_t launch_router_wgrad(const Shape& s, const float* dlogits, const void* x, float* part,
+                               float* bpart, float* dwr, float* dbr, hipStream_t st);
+hipError_t launch_dx_gather(const Shape& s, const float* dxr, const float* dxrows,
+                            const float* parts, int nparts, long long part_elems,
+                            const int32_t* assign_row, const int32_t* offsets, float* dx,
+                            hipStream_t st);
+
 }  // namespace moe

@@ -25,7 +25,8 @@ MOE_ROUTER_BIAS, MOE_EXPERT_BIAS, MOE_W_FP8, MOE_EXPERT_CHOICE = 1, 2, 8, 16
 EXPORTS = ("moe_capacity", "moe_workspace_size", "moe_router_topk", "moe_dispatch",
            "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_aux_stats",
            "moe_routing_stats", "moe_quantize_fp8", "moe_expert_choice", "moe_ffn_forward",
-           "moe_status_string", "moe_last_hip_error")
+           "moe_backward_workspace_size", "moe_ffn_backward", "moe_status_string",
+           "moe_last_hip_error")
 
 
 class moe_problem(ctypes.Structure):
@@ -43,6 +44,12 @@ class moe_routing(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("topk_idx", "topk_w", "probs", "counts", "kept", "offsets", "sorted_assign",
                  "assign_row", "drop_mask", "f", "P", "l_aux", "stats", "token_experts")]
+
+
+class moe_grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("dx", "dw_router", "db_router", "dw_up", "db_up", "dw_down", "db_down",
+                 "d_topk_w", "d_logits")]
 
 
 # moe_route_stats: six float32 then two int32 (32 bytes, device memory)
@@ -64,7 +71,7 @@ def _load(path=LIB_PATH):
         raise ImportError(f"{path} is not built; run __graft_entry__.build()")
     lib = ctypes.CDLL(path)
     P, V, I32, SZ = ctypes.POINTER, ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
-    pp, pw, pr = P(moe_problem), P(moe_weights), P(moe_routing)
+    pp, pw, pr, pg = P(moe_problem), P(moe_weights), P(moe_routing), P(moe_grads)
     sig = {
         "moe_capacity": (I32, [I32, I32, I32, ctypes.c_float]),
         "moe_workspace_size": (I32, [pp, P(SZ)]),
@@ -79,6 +86,8 @@ def _load(path=LIB_PATH):
         "moe_quantize_fp8": (I32, [V, ctypes.c_int64, I32, V, V, V]),
         "moe_expert_choice": (I32, [pp, V, V, V, V, V, V, SZ, V]),
         "moe_ffn_forward": (I32, [pp, pw, V, V, pr, V, SZ, V]),
+        "moe_backward_workspace_size": (I32, [pp, P(SZ)]),
+        "moe_ffn_backward": (I32, [pp, pw, V, V, ctypes.c_float, pr, pg, V, SZ, V]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
         "moe_last_hip_error": (I32, []),
     }
@@ -304,3 +313,42 @@ def moe_ffn_forward(p, w, x, y, ws, routing=None, stream=None):
     _check("moe_ffn_forward", _lib.moe_ffn_forward(
         ctypes.byref(p), ctypes.byref(w), _ptr(x), _ptr(y),
         ctypes.byref(r) if r is not None else None, wp, wb, _stream(stream)))
+
+
+def moe_backward_workspace_size(p):
+    n = ctypes.c_size_t(0)
+    _check("moe_backward_workspace_size",
+           _lib.moe_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def backward_workspace(p, device="cuda"):
+    return torch.empty(moe_backward_workspace_size(p), dtype=torch.uint8, device=device)
+
+
+GRAD_FIELDS = ("dx", "dw_router", "db_router", "dw_up", "db_up", "dw_down", "db_down",
+               "d_topk_w", "d_logits")
+
+
+def moe_ffn_backward(p, w, x, dy, alpha, routing, grads, ws, stream=None):
+    """routing: dict of the forward's routing tensors (moe_routing field
+    names; topk_idx, topk_w, counts, offsets, sorted_assign, assign_row
+    required).  grads: dict of float32 output tensors named as moe_grads'
+    fields (dx, dw_router, dw_up, dw_down required)."""
+    _need(dy, p.T * p.d_model, torch.float32, "dy")
+    F1 = 2 * p.d_ff if p.activation == MOE_SWIGLU else p.d_ff
+    nseg = p.num_experts + p.num_shared
+    sizes = dict(dx=p.T * p.d_model, dw_router=p.num_experts * p.d_model,
+                 db_router=p.num_experts, dw_up=nseg * F1 * p.d_model, db_up=nseg * p.d_ff,
+                 dw_down=nseg * p.d_model * p.d_ff, db_down=nseg * p.d_model,
+                 d_topk_w=p.T * p.top_k, d_logits=p.T * p.num_experts)
+    for k, v in grads.items():
+        if k not in sizes:
+            raise ValueError(f"unknown gradient {k}")
+        _need(v, sizes[k], torch.float32, k)
+    r = moe_routing(**{k: _ptr(v) for k, v in routing.items()})
+    g = moe_grads(**{k: _ptr(v) for k, v in grads.items()})
+    wp, wb = _ws(ws)
+    _check("moe_ffn_backward", _lib.moe_ffn_backward(
+        ctypes.byref(p), ctypes.byref(w), _ptr(x), _ptr(dy), float(alpha), ctypes.byref(r),
+        ctypes.byref(g), wp, wb, _stream(stream)))

@@ -163,8 +163,8 @@ def backward(x, w_router, b_router, w_up, b_up, w_down, b_down, dy, *, alpha, to
     disp = dispatch(idx, E, cap)
 
     dx = np.zeros_like(x)
-    dw_up = np.zeros_like(w_up)
-    dw_down = np.zeros_like(w_down)
+    dw_up = np.zeros(w_up.shape)        # weights may be per-expert lazy views
+    dw_down = np.zeros(w_down.shape)
     db_up = np.zeros((w_up.shape[0], w_up.shape[1]))
     db_down = np.zeros((w_down.shape[0], w_down.shape[1]))
     dw = np.zeros((T, k))

@@ -16,6 +16,8 @@ Every draw is fp32; bf16 runs round each tensor to bf16 (round to nearest
 even) right after drawing it.  Both the oracle and the kernels read these
 same bytes (the oracle upcasts bf16 exactly).
 
+make_grad_output draws the upstream gradient of the backward pass.
+
 This module performs no step of the method: no router product, no gate, no
 routing, no FFN.  The weights follow the nn.Linear [out, in] layout.
 """
@@ -76,6 +78,15 @@ def make_inputs(run: Run) -> Dict[str, torch.Tensor]:
             b_down[q] = draw((d,), run.w_std)
     return dict(x=x, w_router=w_router, b_router=b_router, w_up=w_up, b_up=b_up,
                 w_down=w_down, b_down=b_down)
+
+
+def make_grad_output(run: Run) -> torch.Tensor:
+    """Upstream gradient dy [T, d_model] for the backward pass: float32
+    N(0, 1), from its own CPU generator seeded with run.seed + 1000 (so the
+    forward inputs above are unchanged)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(run.seed + 1000)
+    return torch.randn((run.T, run.d_model), generator=g, dtype=torch.float32)
 
 
 def to_f64(t):
