@@ -33,6 +33,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default=None, help="workload name (default: gpt2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="pass_", choices=("forward", "backward"), default="forward",
+                    help="backward: time moe_ffn_backward (gradients of the task loss plus "
+                         "alpha * L_aux) instead of the forward")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (for counter scaling)")
@@ -189,6 +192,10 @@ def main():
     print(f"bench: {name} T={T} d={run.d_model} f={run.d_ff} E={E} k={k} S={run.num_shared} "
           f"cap={cap} warmup={a.warmup} steps={a.steps}", file=sys.stderr, flush=True)
 
+    if a.pass_ == "backward":
+        bench_backward(a, name, run, p, w, g, ws, y, r)
+        return
+
     # ---- headline: K whole forward calls
     for _ in range(a.warmup):
         M.moe_ffn_forward(p, w, g["x"], y, ws, routing=r)
@@ -304,6 +311,117 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+ALPHA = 0.01   # weight of L_aux in the training objective (the pages' usual value)
+
+
+def bench_backward(a, name, run, p, w, g, ws, y, r):
+    """One step = one moe_ffn_backward call over resident inputs: x, weights,
+    the upstream gradient dy and the routing of one (untimed) forward call."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_sparse_gemv_amd import moe as M
+    from synth import make_grad_output
+    if run.dtype != "bf16" or run.w_fp8 or run.expert_choice:
+        print(f"the backward pass supports bf16 token-choice problems; {name} is not one",
+              file=sys.stderr)
+        sys.exit(2)
+    dev = g["x"].device
+    T, E, k, S, d, f = run.T, run.num_experts, run.top_k, run.num_shared, run.d_model, run.d_ff
+    F1 = 2 * f if run.activation == "swiglu" else f
+    M.moe_ffn_forward(p, w, g["x"], y, ws, routing=r)
+    dy = make_grad_output(run).to(dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    grads = dict(dx=torch.empty(T * d, **f32), dw_router=torch.empty(E * d, **f32),
+                 dw_up=torch.empty((E + S) * F1 * d, **f32),
+                 dw_down=torch.empty((E + S) * d * f, **f32))
+    if run.router_bias != "none":
+        grads["db_router"] = torch.empty(E, **f32)
+    if run.expert_bias:
+        grads["db_up"] = torch.empty((E + S) * f, **f32)
+        grads["db_down"] = torch.empty((E + S) * d, **f32)
+    bws = M.backward_workspace(p, dev)
+    torch.cuda.synchronize()
+    rows = int(r["offsets"][E].item()) + S * T
+    for _ in range(a.warmup):
+        M.moe_ffn_backward(p, w, g["x"], dy, ALPHA, r, grads, bws)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(a.steps):
+        M.moe_ffn_backward(p, w, g["x"], dy, ALPHA, r, grads, bws)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(a.steps)]
+    step_s = float(np.median(per)) * 1e-3
+    up_fl, dn_fl = expert_flops(run, rows)
+    # dX and dW of both projections (twice the forward's expert flops), plus the
+    # router's dlogits Wr and dlogits^T x; the recomputed pre-activations are not counted
+    bwd_flops = 2.0 * (up_fl + dn_fl) + 4.0 * T * E * d
+    achieved = bwd_flops / step_s / 1e12
+    cpu = None if a.no_cpu_baseline else cpu_baseline_backward(run, a.cpu_seconds)
+    out = {
+        "metric": "MoE-FFN backward tokens/s + TFLOP/s (% bf16 MFMA peak), 1 MI355X",
+        "value": round(T / step_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(step_s * 1e3, 5),
+        "wall_ms_per_step": round((t1 - t0) * 1e3 / a.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the workload, random weights, "
+                "dy ~ N(0, 1))",
+        "config": {"workload": run.description + ", backward", "name": name, "T": T,
+                   "d_model": d, "d_ff": f, "num_experts": E, "top_k": k, "num_shared": S,
+                   "alpha": ALPHA, "rows": rows, "parallelism": "single GPU"},
+        "step_tflops": round(achieved, 2),
+        "step_pct_bf16_peak": round(100 * achieved / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"kernel": "moe_ffn_backward (whole pass)", "bound": "mfma",
+                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline_backward(run, seconds):
+    """The backward oracle on the first n <= 512 tokens of the workload (a
+    batch of its own, same capacity factor), repeated for about `seconds`."""
+    import oracle.moe_backward as OB
+    from oracle import moe_oracle as O
+    from synth import make_grad_output, make_inputs, scaled, to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    n = min(run.T, 512)
+    sub = scaled(run, T=n)
+    inp, dy = make_inputs(sub), make_grad_output(sub).double().numpy()
+    f64 = lambda t: None if t is None else _Lazy(t)
+    cap = O.capacity(n, run.top_k, run.num_experts, run.capacity_factor)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        OB.backward(to_f64(inp["x"]), to_f64(inp["w_router"]), to_f64(inp["b_router"]),
+                    f64(inp["w_up"]), f64(inp["b_up"]), f64(inp["w_down"]), f64(inp["b_down"]),
+                    dy, alpha=ALPHA, top_k=run.top_k, num_shared=run.num_shared,
+                    gating=run.gating, activation=run.activation, cap=cap)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    sample = f"oracle backward of a {n}-token batch of the workload, x{reps} repetitions in {el:.1f} s"
+    return {"value": round(n * reps / el, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "sample": sample}
 
 
 def traffic_for(kernel, workload):

@@ -294,155 +294,188 @@ __global__ __launch_bounds__(256) void act_backward_kernel(
 }
 
 // ---------------------------------------------------------------- router backward
-// One wave per token: recompute the logits (lane e = expert e), the keys
-// (softmax p, or sigma for the normalized sigmoid), then
+// One wave per RBT tokens; for each token, lane e holds the logit of expert e
+// (from the router kernel) and computes the keys (softmax p, or sigma for the
+// normalized sigmoid), then
 //   dkey[e_s] += (dw_s - sum_s' w_s' dw_s') / S   (renormalized top-k)
 //   dp[e]      = alpha E f_e / T                    (aux loss through P)
 //   softmax:  dl = p (dkey + dp - sum p (dkey + dp))
 //   sigmoid:  dl = (dkey + (dp - sum p dp) / sum sigma) sigma (1 - sigma)
-// and dx_router[t] = sum_e dl_e Wr[e, :].
+// and dx_router[t] = sum_e dl_e Wr[e, :] (each Wr load serves RBT tokens).
+constexpr int RBT = 4;
 __global__ __launch_bounds__(256) void router_backward_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-    const uint16_t* __restrict__ br, const int32_t* __restrict__ topk_idx,
-    const int32_t* __restrict__ assign_row, const float* __restrict__ dwslot,
-    const int32_t* __restrict__ counts, float alpha, int T, int d, int E, int k, int gating,
-    float* __restrict__ dlogits, float* __restrict__ d_topk_w, float* __restrict__ dxr) {
+    const float* __restrict__ logits, const uint16_t* __restrict__ wr,
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ assign_row,
+    const float* __restrict__ dwslot, const int32_t* __restrict__ counts, float alpha, int T,
+    int d, int E, int k, int gating, float* __restrict__ dlogits, float* __restrict__ d_topk_w,
+    float* __restrict__ dxr) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;   // per wave
-  const uint16_t* xr = x + (long long)t * d;
+  const int tb = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RBT;
+  if (tb >= T) return;   // per wave
   const bool act = lane < E;
-  const uint16_t* wrow = wr + (long long)(act ? lane : 0) * d;
-  float l = 0.0f;
-  for (int j = 0; j < d; j += 8) {
-    const u32x4 xv = *(const u32x4*)(xr + j);
-    const u32x4 wv = *(const u32x4*)(wrow + j);
+  const float dp = act ? alpha * (float)E * ((float)counts[act ? lane : 0] / ((float)T * k)) / T
+                       : 0.0f;
+  float dls[RBT];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      l = fmaf(__uint_as_float(xv[q] << 16), __uint_as_float(wv[q] << 16), l);
-      l = fmaf(__uint_as_float(xv[q] & 0xffff0000u), __uint_as_float(wv[q] & 0xffff0000u), l);
+  for (int i = 0; i < RBT; ++i) {
+    const int t = tb + i;
+    dls[i] = 0.0f;
+    if (t >= T) continue;   // uniform over the wave
+    const float l = act ? logits[(long long)t * E + lane] : 0.0f;
+    float key, p, sig = 0.0f, tot = 1.0f;
+    if (gating == MOE_SOFTMAX) {
+      float m = act ? l : -INFINITY;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      const float ex = act ? fast_exp(l - m) : 0.0f;
+      float sum = ex;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+      p = ex / sum;
+      key = p;
+    } else {
+      sig = act ? 1.0f / (1.0f + fast_exp(-l)) : 0.0f;
+      tot = sig;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
+      p = sig / tot;
+      key = sig;
     }
-  }
-  if (br && act) l += bf16_to_f32(br[lane]);
-  float key, p, sig = 0.0f, tot = 1.0f;
-  if (gating == MOE_SOFTMAX) {
-    float m = act ? l : -INFINITY;
+    // renormalized top-k
+    float S = 0.0f, inner = 0.0f, dws[kMaxTopK], ks_[kMaxTopK];
+    int es[kMaxTopK];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    const float ex = act ? fast_exp(l - m) : 0.0f;
-    float sum = ex;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
-    p = ex / sum;
-    key = p;
-  } else {
-    sig = act ? 1.0f / (1.0f + fast_exp(-l)) : 0.0f;
-    tot = sig;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
-    p = sig / tot;
-    key = sig;
-  }
-  // renormalized top-k
-  float S = 0.0f, inner = 0.0f, dws[kMaxTopK], ks_[kMaxTopK];
-  int es[kMaxTopK];
-#pragma unroll
-  for (int s = 0; s < kMaxTopK; ++s) {
-    es[s] = 0;
-    dws[s] = 0.0f;
-    ks_[s] = 0.0f;
-    if (s < k) {
-      es[s] = topk_idx[(long long)t * k + s];
-      dws[s] = assign_row[(long long)t * k + s] >= 0 ? dwslot[(long long)t * k + s] : 0.0f;
+    for (int s = 0; s < kMaxTopK; ++s) {
+      es[s] = 0;
+      dws[s] = 0.0f;
+      if (s < k) {
+        es[s] = topk_idx[(long long)t * k + s];
+        dws[s] = assign_row[(long long)t * k + s] >= 0 ? dwslot[(long long)t * k + s] : 0.0f;
+      }
+      ks_[s] = __shfl(key, es[s]);
+      if (s < k) S += ks_[s];
     }
-    ks_[s] = __shfl(key, es[s]);
-    if (s < k) S += ks_[s];
-  }
 #pragma unroll
-  for (int s = 0; s < kMaxTopK; ++s)
-    if (s < k) inner = fmaf(ks_[s] / S, dws[s], inner);
-  float dkey = 0.0f;
+    for (int s = 0; s < kMaxTopK; ++s)
+      if (s < k) inner = fmaf(ks_[s] / S, dws[s], inner);
+    float dkey = 0.0f;
 #pragma unroll
-  for (int s = 0; s < kMaxTopK; ++s)
-    if (s < k && es[s] == lane) dkey += (dws[s] - inner) / S;
-  const float dp = act ? alpha * (float)E * ((float)counts[act ? lane : 0] / ((float)T * k)) / T : 0.0f;
-  float dl;
-  if (gating == MOE_SOFTMAX) {
-    const float g = dkey + dp;
-    float pg = act ? p * g : 0.0f;
+    for (int s = 0; s < kMaxTopK; ++s)
+      if (s < k && es[s] == lane) dkey += (dws[s] - inner) / S;
+    float dl;
+    if (gating == MOE_SOFTMAX) {
+      const float g = dkey + dp;
+      float pg = act ? p * g : 0.0f;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) pg += __shfl_xor(pg, o);
-    dl = act ? p * (g - pg) : 0.0f;
-  } else {
-    float pd = act ? p * dp : 0.0f;
+      for (int o = 32; o >= 1; o >>= 1) pg += __shfl_xor(pg, o);
+      dl = act ? p * (g - pg) : 0.0f;
+    } else {
+      float pd = act ? p * dp : 0.0f;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) pd += __shfl_xor(pd, o);
-    const float ds = dkey + (dp - pd) / tot;
-    dl = act ? ds * sig * (1.0f - sig) : 0.0f;
-  }
-  if (act) dlogits[(long long)t * E + lane] = dl;
-  if (d_topk_w && lane < k) {
-    float v = 0.0f;
+      for (int o = 32; o >= 1; o >>= 1) pd += __shfl_xor(pd, o);
+      const float ds = dkey + (dp - pd) / tot;
+      dl = act ? ds * sig * (1.0f - sig) : 0.0f;
+    }
+    dls[i] = dl;
+    if (act) dlogits[(long long)t * E + lane] = dl;
+    if (d_topk_w && lane < k) {
+      float v = 0.0f;
 #pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s) v = s == lane ? dws[s] : v;
-    d_topk_w[(long long)t * k + lane] = v;
+      for (int s = 0; s < kMaxTopK; ++s) v = s == lane ? dws[s] : v;
+      d_topk_w[(long long)t * k + lane] = v;
+    }
   }
   // dx_router[t, j] = sum_e dl_e Wr[e, j]; lane covers 8 columns per 512
   for (int j0 = 0; j0 < d; j0 += 512) {
     const int j = j0 + lane * 8;
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float acc[RBT][8];
+#pragma unroll
+    for (int i = 0; i < RBT; ++i)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[i][q] = 0.0f;
     for (int e = 0; e < E; ++e) {
-      const float de = __shfl(dl, e);
+      float de[RBT];
+#pragma unroll
+      for (int i = 0; i < RBT; ++i) de[i] = __shfl(dls[i], e);
       if (j < d) {
         const u32x4 wv = *(const u32x4*)(wr + (long long)e * d + j);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          acc[2 * q] = fmaf(de, __uint_as_float(wv[q] << 16), acc[2 * q]);
-          acc[2 * q + 1] = fmaf(de, __uint_as_float(wv[q] & 0xffff0000u), acc[2 * q + 1]);
+          const float w0 = __uint_as_float(wv[q] << 16), w1 = __uint_as_float(wv[q] & 0xffff0000u);
+#pragma unroll
+          for (int i = 0; i < RBT; ++i) {
+            acc[i][2 * q] = fmaf(de[i], w0, acc[i][2 * q]);
+            acc[i][2 * q + 1] = fmaf(de[i], w1, acc[i][2 * q + 1]);
+          }
         }
       }
     }
     if (j < d) {
-      float* o = dxr + (long long)t * d + j;
-      *(f32x4*)o = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      *(f32x4*)(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+#pragma unroll
+      for (int i = 0; i < RBT; ++i) {
+        if (tb + i >= T) break;
+        float* o = dxr + (long long)(tb + i) * d + j;
+        *(f32x4*)o = f32x4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+        *(f32x4*)(o + 4) = f32x4{acc[i][4], acc[i][5], acc[i][6], acc[i][7]};
+      }
     }
   }
 }
 
-// Partial router weight gradient over a slice of kRwTok tokens:
-// part[slice][e][j] = sum over the slice's tokens (in order) of dl[t, e] x[t, j];
-// bpart[slice][e] likewise of dl[t, e] (blocks of column chunk 0).  Block =
-// 64 columns x 4 expert groups.
-constexpr int kRwTok = 256;
+// Partial router weight gradient over a slice of `tpb` tokens (a multiple of
+// 64): part[slice][e][j] = sum over the slice's tokens (in order) of
+// dl[t, e] x[t, j]; bpart[slice][e] likewise of dl[t, e] (blocks of column
+// chunk 0).  Block = 256 columns; the slice moves through LDS 64 tokens at a
+// time (x by 16-byte loads, dl as [64][EB]); thread = one column, EB
+// accumulators (E <= EB).
+template <int EB>
 __global__ __launch_bounds__(256) void router_wgrad_part_kernel(
-    const float* __restrict__ dl, const uint16_t* __restrict__ x, int T, int d, int E,
+    const float* __restrict__ dl, const uint16_t* __restrict__ x, int T, int d, int E, int tpb,
     float* __restrict__ part, float* __restrict__ bpart) {
-  __shared__ float sdl[kRwTok][kMaxExperts + 1];
-  const int j = blockIdx.x * 64 + (threadIdx.x & 63);
-  const int eg = threadIdx.x >> 6;   // experts eg, eg+4, ...
-  const int t0 = blockIdx.y * kRwTok;
-  const int nt = min(kRwTok, T - t0);
-  for (int i = threadIdx.x; i < nt * E; i += 256) sdl[i / E][i % E] = dl[(long long)t0 * E + i];
-  __syncthreads();
-  float acc[kMaxExperts / 4];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[64][256 + 8];
+  __shared__ __attribute__((aligned(16))) float sdl[64][EB];
+  const int tid = threadIdx.x;
+  const int c0 = blockIdx.x * 256, j = c0 + tid;
+  const int ts = blockIdx.y * tpb, te = min(T, ts + tpb);
+  float acc[EB];
 #pragma unroll
-  for (int q = 0; q < kMaxExperts / 4; ++q) acc[q] = 0.0f;
-  const int ne = (E - eg + 3) / 4;
-  for (int tt = 0; tt < nt; ++tt) {
-    const float xv = bf16_to_f32(x[(long long)(t0 + tt) * d + j]);
+  for (int e = 0; e < EB; ++e) acc[e] = 0.0f;
+  float bsum = 0.0f;
+  for (int t0 = ts; t0 < te; t0 += 64) {
+    __syncthreads();   // the previous tile's reads are done
 #pragma unroll
-    for (int q = 0; q < kMaxExperts / 4; ++q)
-      if (q < ne) acc[q] = fmaf(sdl[tt][eg + 4 * q], xv, acc[q]);
+    for (int i = 0; i < 8; ++i) {
+      const int q = tid + 256 * i;          // 16-byte chunk: row q / 32, columns (q % 32) * 8
+      const int rr = q >> 5, cc = (q & 31) * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (t0 + rr < te && c0 + cc < d) v = *(const u32x4*)(x + (long long)(t0 + rr) * d + c0 + cc);
+      *(u32x4*)&xs[rr][cc] = v;
+    }
+    for (int i = tid; i < 64 * EB; i += 256) {
+      const int rr = i / EB, e = i % EB;
+      sdl[rr][e] = (e < E && t0 + rr < te) ? dl[(long long)(t0 + rr) * E + e] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int rr = 0; rr < 64; ++rr) {
+      const float xv = bf16_to_f32(xs[rr][tid]);
+#pragma unroll
+      for (int e = 0; e < EB; e += 4) {
+        const f32x4 dv = *(const f32x4*)&sdl[rr][e];
+        acc[e] = fmaf(dv[0], xv, acc[e]);
+        acc[e + 1] = fmaf(dv[1], xv, acc[e + 1]);
+        acc[e + 2] = fmaf(dv[2], xv, acc[e + 2]);
+        acc[e + 3] = fmaf(dv[3], xv, acc[e + 3]);
+      }
+      if (blockIdx.x == 0 && tid < E) bsum += sdl[rr][tid];
+    }
   }
+  if (j < d) {
 #pragma unroll
-  for (int q = 0; q < kMaxExperts / 4; ++q)
-    if (q < ne) part[((long long)blockIdx.y * E + eg + 4 * q) * d + j] = acc[q];
-  if (blockIdx.x == 0 && threadIdx.x < E) {
-    float b = 0.0f;
-    for (int tt = 0; tt < nt; ++tt) b += sdl[tt][threadIdx.x];
-    bpart[(long long)blockIdx.y * E + threadIdx.x] = b;
+    for (int e = 0; e < EB; ++e)
+      if (e < E) part[((long long)blockIdx.y * E + e) * d + j] = acc[e];
   }
+  if (blockIdx.x == 0 && tid < E) bpart[(long long)blockIdx.y * E + tid] = bsum;
 }
 
 // dWr[e][j] = sum over slices (in order) of part; dbr likewise.
@@ -557,23 +590,45 @@ hipError_t launch_act_backward(const Shape& s, const float* Z, const float* G, c
   return hipGetLastError();
 }
 
-hipError_t launch_router_backward(const Shape& s, const void* x, const void* wr, const void* br,
+hipError_t launch_router_backward(const Shape& s, const float* logits, const void* wr,
                                   const int32_t* topk_idx, const int32_t* assign_row,
                                   const float* dwslot, const int32_t* counts, float alpha,
                                   float* dlogits, float* d_topk_w, float* dxr, hipStream_t st) {
-  router_backward_kernel<<<(s.T + 3) / 4, 256, 0, st>>>(
-      (const uint16_t*)x, (const uint16_t*)wr, (const uint16_t*)br, topk_idx, assign_row, dwslot,
-      counts, alpha, s.T, s.d, s.E, s.k, s.gating, dlogits, d_topk_w, dxr);
+  const int per_block = 4 * RBT;
+  router_backward_kernel<<<(s.T + per_block - 1) / per_block, 256, 0, st>>>(
+      logits, (const uint16_t*)wr, topk_idx, assign_row, dwslot, counts, alpha, s.T, s.d, s.E,
+      s.k, s.gating, dlogits, d_topk_w, dxr);
   return hipGetLastError();
 }
 
-int router_wgrad_slices(const Shape& s) { return (s.T + kRwTok - 1) / kRwTok; }
+// Token slice per block of the router weight gradient: a multiple of 64,
+// about 512 blocks in all.
+static int router_wgrad_tpb(const Shape& s) {
+  const int cchunks = (s.d + 255) / 256;
+  const int want = 512 / cchunks > 1 ? 512 / cchunks : 1;     // slices wanted
+  int tpb = (s.T + want - 1) / want;
+  tpb = (tpb + 63) / 64 * 64;
+  return tpb < 64 ? 64 : tpb;
+}
+
+int router_wgrad_slices(const Shape& s) {
+  const int tpb = router_wgrad_tpb(s);
+  return (s.T + tpb - 1) / tpb;
+}
 
 hipError_t launch_router_wgrad(const Shape& s, const float* dlogits, const void* x, float* part,
                                float* bpart, float* dwr, float* dbr, hipStream_t st) {
-  const int ns = router_wgrad_slices(s);
-  router_wgrad_part_kernel<<<dim3(s.d / 64, ns), 256, 0, st>>>(dlogits, (const uint16_t*)x, s.T,
-                                                               s.d, s.E, part, bpart);
+  const int tpb = router_wgrad_tpb(s), ns = router_wgrad_slices(s);
+  const dim3 grid((s.d + 255) / 256, ns);
+  const uint16_t* xb = (const uint16_t*)x;
+  if (s.E <= 8)
+    router_wgrad_part_kernel<8><<<grid, 256, 0, st>>>(dlogits, xb, s.T, s.d, s.E, tpb, part, bpart);
+  else if (s.E <= 16)
+    router_wgrad_part_kernel<16><<<grid, 256, 0, st>>>(dlogits, xb, s.T, s.d, s.E, tpb, part, bpart);
+  else if (s.E <= 32)
+    router_wgrad_part_kernel<32><<<grid, 256, 0, st>>>(dlogits, xb, s.T, s.d, s.E, tpb, part, bpart);
+  else
+    router_wgrad_part_kernel<64><<<grid, 256, 0, st>>>(dlogits, xb, s.T, s.d, s.E, tpb, part, bpart);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long n = (long long)s.E * s.d;

@@ -82,6 +82,9 @@ BwdLayout bwd_layout(const Shape& s) {
   b.rw_part = take((size_t)router_wgrad_slices(s) * s.E * s.d * 4);
   b.rb_part = take((size_t)router_wgrad_slices(s) * s.E * 4);
   b.poff = take((nseg + 1) * 4);
+  b.logits = take((size_t)s.T * s.E * 4);
+  b.prob_part = take((size_t)router_blocks(s) * s.E * 4);
+  b.chunk_counts = take((size_t)router_blocks(s) * s.E * 4);
   b.total = o;
   return b;
 }
@@ -480,11 +483,14 @@ moe_status moe_ffn_backward(const moe_problem* p, const moe_weights* w, const vo
   if (e == hipSuccess) e = launch_bwd_wgrad(s, A1, B1, F1, s.d, ldk, g->dw_up, offsets, stream);
   if (e == hipSuccess && s.expert_bias()) e = launch_seg_rowsum(s, A2, s.d, ldk, poff, g->db_down, stream);
   if (e == hipSuccess && s.expert_bias()) e = launch_seg_rowsum(s, A1, F1, ldk, poff, g->db_up, stream);
-  // router
+  // router: the logits again (router kernel, no top-k output), then its backward
+  float* logits = at<float>(ws, B.logits);
   if (e == hipSuccess)
-    e = launch_router_backward(s, x, w->w_router, s.router_bias() ? w->b_router : nullptr,
-                               fwd->topk_idx, fwd->assign_row, dwslot, fwd->counts, alpha,
-                               dlogits, g->d_topk_w, dxr, stream);
+    e = launch_router(s, x, w->w_router, w->b_router, nullptr, nullptr, nullptr,
+                      at<float>(ws, B.prob_part), at<int32_t>(ws, B.chunk_counts), stream, logits);
+  if (e == hipSuccess)
+    e = launch_router_backward(s, logits, w->w_router, fwd->topk_idx, fwd->assign_row, dwslot,
+                               fwd->counts, alpha, dlogits, g->d_topk_w, dxr, stream);
   if (e == hipSuccess)
     e = launch_router_wgrad(s, dlogits, x, at<float>(ws, B.rw_part), at<float>(ws, B.rb_part),
                             g->dw_router, g->db_router, stream);

@@ -129,10 +129,12 @@ __device__ __forceinline__ float gelu_f(float z) {
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; all are asynchronous on `st`.
 // Also writes each 16-token chunk's per-expert sum of probabilities
-// (prob_part) and count of selections (chunk_counts), both [chunks, E].
+// (prob_part) and count of selections (chunk_counts), both [chunks, E], and,
+// when `logits` is non-null, the logits (with bias) [T, E].  topk_idx null:
+// no top-k output.
 hipError_t launch_router(const Shape& s, const void* x, const void* wr, const void* br,
                          int32_t* topk_idx, float* topk_w, float* probs, float* prob_part,
-                         int32_t* chunk_counts, hipStream_t st);
+                         int32_t* chunk_counts, hipStream_t st, float* logits = nullptr);
 hipError_t launch_colsum(const Shape& s, const float* prob_part, float* colsum, hipStream_t st);
 // Dispatch.  counted: chunk_counts already hold the router's per-chunk
 // counts (else they are computed from topk_idx first).  sb_prefix is
@@ -189,7 +191,7 @@ inline int wgrad_ldk(const Shape& s) {
 int router_wgrad_slices(const Shape& s);
 struct BwdLayout {
   size_t dyb, w1t, w2t, Z, G, Hb, dZ, dxrows, dxparts, A2, B2, A1, B1, dwslot, dlogits, dxr,
-      rw_part, rb_part, poff, total;
+      rw_part, rb_part, poff, logits, prob_part, chunk_counts, total;
 };
 BwdLayout bwd_layout(const Shape& s);
 
@@ -216,7 +218,8 @@ hipError_t launch_seg_transpose(const Shape& s, int kind, const void* src, int C
                                 hipStream_t st);
 hipError_t launch_seg_rowsum(const Shape& s, const uint16_t* M, int C, int ldk,
                              const int32_t* poff, float* db, hipStream_t st);
-hipError_t launch_router_backward(const Shape& s, const void* x, const void* wr, const void* br,
+// logits: [T, E] as launch_router writes them.
+hipError_t launch_router_backward(const Shape& s, const float* logits, const void* wr,
                                   const int32_t* topk_idx, const int32_t* assign_row,
                                   const float* dwslot, const int32_t* counts, float alpha,
                                   float* dlogits, float* d_topk_w, float* dxr, hipStream_t st);

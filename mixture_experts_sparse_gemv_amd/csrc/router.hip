@@ -57,6 +57,7 @@ struct RouterArgs {
   float* probs;         // null if not requested
   float* prob_part;     // [blocks, E]
   int32_t* chunk_counts;  // [blocks, E]: selections of each expert in the block's tokens
+  float* logits;        // [T, E] logits incl. bias, or null (the backward pass recomputes them)
   int T, d, E, k, gating, dtype;
 };
 
@@ -148,6 +149,7 @@ __global__ __launch_bounds__(64 * RW) void router_kernel(RouterArgs a) {
 #pragma unroll
       for (int w = 1; w < RW; ++w) z += red[w][tl][lane];   // fixed order
       l = z + bias;
+      if (a.logits) a.logits[(long long)t * E + lane] = l;
     }
     float score, denom;
     if (a.gating == MOE_SOFTMAX) {
@@ -219,9 +221,9 @@ __global__ __launch_bounds__(256) void colsum_kernel(const float* prob_part, int
 
 hipError_t launch_router(const Shape& s, const void* x, const void* wr, const void* br,
                          int32_t* topk_idx, float* topk_w, float* probs, float* prob_part,
-                         int32_t* chunk_counts, hipStream_t st) {
+                         int32_t* chunk_counts, hipStream_t st, float* logits) {
   RouterArgs a{x, wr, s.router_bias() ? br : nullptr, topk_idx, topk_w, probs, prob_part,
-               chunk_counts, s.T, s.d, s.E, s.k, s.gating, s.dtype};
+               chunk_counts, logits, s.T, s.d, s.E, s.k, s.gating, s.dtype};
   const int blocks = router_blocks(s);
   if (s.dtype == MOE_F32) {
     router_kernel<0><<<blocks, 64 * RW, 0, st>>>(a);
