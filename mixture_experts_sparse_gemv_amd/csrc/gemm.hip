@@ -10,13 +10,14 @@
 //
 // Dense contractions, so they run on the matrix cores: bf16 MFMA 32x32x16
 // for the up projection, fp16 MFMA 32x32x16 for the down projection (h is
-// fp16; each bf16 W2 tile is converted to fp16 while it is staged into LDS).
-// Accumulation is fp32.  Block = 4 waves in a 2x2 grid; block tile BM token
-// rows x BN weight rows x BK=64; tiles are double-buffered in LDS with an XOR
-// swizzle of the 16-byte chunks that keeps fragment reads conflict-free.  The MFMA "A" operand is the
-// weight tile and "B" the token tile, so each lane's accumulator holds four
-// consecutive output columns of one token row: the epilogue stores 8-byte
-// (fp16 x4) or 16-byte (fp32 x4) vectors.
+// fp16; each bf16 W2 fragment is converted to fp16 in registers after its
+// LDS read).  Accumulation is fp32.  Block = 8 waves (WGM x WGN grid); block
+// tile BM token rows x BN weight rows (256 x 256) x BK = 32, in a 4-stage
+// LDS ring filled by direct global-to-LDS DMA three k-tiles ahead, with an
+// XOR swizzle of the 16-byte chunks that keeps fragment reads conflict-free.
+// The MFMA "A" operand is the weight tile and "B" the token tile, so each
+// lane's accumulator holds four consecutive output columns of one token row;
+// the epilogue stages each wave's rows in LDS and stores whole row segments.
 //
 // The tile schedule is computed on the device from offsets[] (no host sync):
 // every block derives the per-segment m-tile counts, their prefix sum, and its
@@ -558,11 +559,12 @@ constexpr int UP_BM = MOE_UP_BM, UP_BN = MOE_UP_BN, UP_WGM = MOE_UP_WGM, UP_WGN 
 constexpr int DN_BM = MOE_DN_BM, DN_BN = MOE_DN_BN, DN_WGM = MOE_DN_WGM, DN_WGN = MOE_DN_WGN;
 constexpr int UP_NST = MOE_UP_NST, UP_OCC = MOE_UP_OCC, DN_NST = MOE_DN_NST, DN_OCC = MOE_DN_OCC;
 
-int grid_blocks(const Shape& s, int BM, int NT, int ksplit = 1) {
+int grid_blocks(const Shape& s, int BM, int NT, int ksplit = 1, int occ = 1) {
   const long long mt = (s.routed_rows() + BM - 1) / BM + s.E +
                        (long long)s.S * ((s.T + BM - 1) / BM);
   long long g = NT * mt * ksplit;
-  if (MOE_PERSISTENT && g > kNumCUs) g = kNumCUs;   // one block per CU, looping over tiles
+  // persistent: `occ` resident blocks per CU, each looping over tiles
+  if (MOE_PERSISTENT && g > (long long)kNumCUs * occ) g = (long long)kNumCUs * occ;
   return (int)((g + 7) / 8 * 8);
 }
 
@@ -647,15 +649,15 @@ hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void
   if (s.act == MOE_SWIGLU) {
     const int NT = (s.f + UP_BN / 2 - 1) / (UP_BN / 2);
     grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_SWIGLU, UP_NST, UP_OCC>
-        <<<grid_blocks(s, UP_BM, NT), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
+        <<<grid_blocks(s, UP_BM, NT, 1, UP_OCC), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
   } else {
     const int NT = (s.f + UP_BN - 1) / UP_BN;
     if (s.act == MOE_RELU)
       grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_RELU, UP_NST, UP_OCC>
-          <<<grid_blocks(s, UP_BM, NT), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
+          <<<grid_blocks(s, UP_BM, NT, 1, UP_OCC), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
     else
       grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_GELU, UP_NST, UP_OCC>
-          <<<grid_blocks(s, UP_BM, NT), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
+          <<<grid_blocks(s, UP_BM, NT, 1, UP_OCC), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
   }
   return hipGetLastError();
 }
@@ -681,7 +683,7 @@ hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const 
              nullptr, s.T, s.tok_div(), s.E, s.S, s.f, s.d, s.d, s.f, ks, y_part, part_elems, 0};
   const int NT = (s.d + DN_BN - 1) / DN_BN;
   grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DOWN, DN_NST, DN_OCC>
-      <<<grid_blocks(s, DN_BM, NT, ks), 64 * DN_WGM * DN_WGN, 0, st>>>(a);
+      <<<grid_blocks(s, DN_BM, NT, ks, DN_OCC), 64 * DN_WGM * DN_WGN, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ks == 1 || !complete) return e;
   const long long n = s.max_rows() * (s.d / 4);
