@@ -51,6 +51,17 @@ def parse():
     return ap.parse_args()
 
 
+def source_digest(path):
+    """sha256 of a kernel source with its comments and whitespace removed:
+    recorded counters stay valid across comment-only edits and become
+    invalid when the code changes."""
+    import re
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256("".join(text.split()).encode()).hexdigest()
+
+
 def _counter_rows(folder, counter):
     import csv
     import glob
@@ -94,13 +105,13 @@ def record_traffic(a):
     db = json.load(open(path)) if os.path.exists(path) else {}
     db["_about"] = ("HBM bytes per launch = FETCH_SIZE * fetch_scale + WRITE_SIZE * write_scale "
                     "(rocprofv3 --pmc, KiB per dispatch); the scales make a plain device copy's "
-                    "counters read the bytes it moves. Valid while the kernel source file hashes "
-                    "to source_sha256.")
+                    "counters read the bytes it moves. Valid while the kernel source file (comments and whitespace "
+                    "removed) hashes to source_sha256.")
     db["calibration"] = {"copy_bytes_each_way": nbytes, "fetch_kib": cf, "write_kib": cw,
                          "fetch_scale": fs, "write_scale": ws}
     db[f"{kernel}:{workload}"] = {
         "source": source,
-        "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+        "source_sha256": source_digest(src),
         "dispatch_name": name, "dispatches": [nf, nw],
         "fetch_kib": fk, "write_kib": wk,
         "bytes_per_launch": int(round(fk * 1024 * fs + wk * 1024 * ws)),
@@ -437,8 +448,7 @@ def traffic_for(kernel, workload):
         if not ent:
             return None
         src = os.path.join(ROOT, "mixture_experts_sparse_gemv_amd", "csrc", ent["source"])
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if digest != ent["source_sha256"]:
+        if source_digest(src) != ent["source_sha256"]:
             return None
         return ent["bytes_per_launch"]
     except Exception:
