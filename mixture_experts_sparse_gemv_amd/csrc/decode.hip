@@ -16,8 +16,11 @@
 // buffer_load ... lds (one 128-byte line of one row per 8 lanes, so every
 // instruction consumes whole lines; non-temporal, since nothing re-reads
 // them), through a ring of NST stages of 64 K-elements, NST-1 stages in
-// flight.  Each stage also carries the 64 K-elements of the 16 token rows
-// (x gathered through sorted_assign, or h), the MFMA "B" operand.
+// flight.  The 16 token rows (x gathered through sorted_assign, or h) are
+// the MFMA "B" operand: each stage also carries their K range in LDS, or,
+// for the FP8 up projection, loads it straight into registers (16 bytes per
+// lane and k-substep, beside the weight DMA; the rows stay in L2), which
+// halves the wave's LDS ring and lets twice as many waves share a unit.
 // LDS rows are XOR-swizzled in 16-byte chunks ((row/2) % 8) so the fragment
 // reads are free of bank conflicts.
 //
@@ -42,7 +45,11 @@ enum { DEC_DOWN = 3 };   // modes: MOE_RELU, MOE_GELU, MOE_SWIGLU (up) or DEC_DO
 #define MOE_DECODE_ROWS_F8 32
 #endif
 #ifndef MOE_DECODE_STAGES_F8
-#define MOE_DECODE_STAGES_F8 4
+#define MOE_DECODE_STAGES_F8 3
+#endif
+// token rows in registers: 0 never, 1 for the FP8 up projection, 2 always
+#ifndef MOE_DECODE_XREG
+#define MOE_DECODE_XREG 1
 #endif
 // Weight rows per work item and LDS ring stages, for bf16 and FP8 weights.
 template <bool F8> struct DecodeTile {
@@ -117,7 +124,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   constexpr int WB = F8 ? 1 : 2;         // weight bytes
   constexpr int SK = F8 ? 128 : 64;      // K elements per stage
   constexpr int NSUBK = SK / 32;         // MFMA k-substeps per stage
-  constexpr int XR = F8 ? 32 : 16;       // 128-byte LDS rows of token data per stage
+  // token rows in registers (XREG) or as XR 128-byte LDS rows per stage
+  constexpr bool XREG = MOE_DECODE_XREG == 2 || (MOE_DECODE_XREG == 1 && F8 && !DOWN);
+  constexpr int XR = XREG ? 0 : (F8 ? 32 : 16);
   constexpr int NDX = XR / 8;            // their DMA instructions
   constexpr int LR = DR + XR;            // LDS rows per stage: weights, then token rows
   // The ring as distinct arrays ([row][8 chunks of 16 bytes] each): the
@@ -153,7 +162,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       (void*)wseg, (short)0, (int)(((long long)a.Wrows * a.K - k0) * WB), 0x00020000);
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.X + k0), (short)0, (int)(a.xbytes - (long long)k0 * 2), 0x00020000);
-  uint32_t soff[NDMA], xoff[NDX];
+  uint32_t soff[NDMA], xoff[NDX > 0 ? NDX : 1];
 #pragma unroll
   for (int q = 0; q < NDMA; ++q) {
     const int r = 8 * q + (lane >> 3);
@@ -178,6 +187,15 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   // k-substep u covers K elements 32u .. 32u+31 of the stage
   const int tl = lane & 15, g = lane >> 4;
   const bool tvalid = tl < rows;
+  // XREG: the lane's token row (K elements 32u + 8g .. +7 of substep u)
+  uint32_t xroff = 0;
+  if (XREG) {
+    const int tt = tvalid ? tl : 0;
+    uint32_t brow;
+    if (DOWN) brow = (uint32_t)(start + tt);
+    else brow = (uint32_t)(seg < a.E ? a.sorted_assign[start + tt] / a.k : tt);
+    xroff = (brow * (uint32_t)a.K + (uint32_t)(8 * g)) * 2u;
+  }
   int fpos[RG][NSUBK], bpos[NSUBK];
 #pragma unroll
   for (int u = 0; u < NSUBK; ++u) {
@@ -197,8 +215,10 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   f32x4 acc[RG];
 #pragma unroll
   for (int q = 0; q < RG; ++q) acc[q] = f32x4{};
+  // XREG: token fragments of the stages in flight, one set per ring slot
+  u32x4 xr[XREG ? NST : 1][NSUBK];
 
-  auto issue = [&](u32x4* buf, int j) {
+  auto issue = [&](u32x4* buf, u32x4 (&xs)[NSUBK], int j) {
 #if __HIP_DEVICE_COMPILE__   // (with template-dependent operands the host pass drops the kernel)
     typedef __attribute__((address_space(3))) void lds_void_t;
 #pragma unroll
@@ -209,13 +229,19 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     for (int q = 0; q < NDX; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_void_t*)(buf + (DR / 8 + q) * 64), 16,
                                                xoff[q], j * SK * 2, 0, 0);
+    if (XREG) {
+#pragma unroll
+      for (int u = 0; u < NSUBK; ++u)
+        xs[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              xres, xroff + u * 64, j * SK * 2, 0));
+    }
 #endif
   };
-  auto compute = [&](const u32x4* buf) {
+  auto compute = [&](const u32x4* buf, const u32x4 (&xs)[NSUBK]) {
     const char* b = (const char*)buf;
 #pragma unroll
     for (int u = 0; u < NSUBK; ++u) {
-      const u32x4 xv = *(const u32x4*)(b + bpos[u]);
+      const u32x4 xv = XREG ? xs[u] : *(const u32x4*)(b + bpos[u]);
 #pragma unroll
       for (int q = 0; q < RG; ++q) {
         u32x4 w;
@@ -230,8 +256,10 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       }
     }
   };
-  // Each stage is NDMA + NDX DMA loads; they complete in issue order.
-  constexpr int PER = NDMA + NDX;
+  // Each stage is NDMA + NDX DMA loads (+ NSUBK token loads with XREG); they
+  // complete in issue order.
+  constexpr int PER = NDMA + NDX + (XREG ? NSUBK : 0);
+  auto xslot = [&](int i) -> u32x4(&)[NSUBK] { return xr[XREG ? i : 0]; };
   auto wait_stage = [&](int ahead) {   // stages issued after the one to consume
     if (NST >= 4 && ahead >= 3) wait_vm<3 * PER>();
     else if (NST >= 3 && ahead >= 2) wait_vm<2 * PER>();
@@ -242,7 +270,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 
 #pragma unroll
   for (int j = 0; j < NST - 1; ++j)
-    if (j < nk) issue(slot(j), j);
+    if (j < nk) issue(slot(j), xslot(j), j);
   // Stage j lives in ring slot j % NST (loops unrolled over the slots).
   // Steady state: every step issues stage j + NST - 1 and waits for stage j
   // with NST - 1 stages still in flight.
@@ -251,10 +279,10 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int sl = 0; sl < NST; ++sl) {
       __asm__ volatile("" ::: "memory");   // slot (j-1) % NST has been read
-      issue(slot((sl + NST - 1) % NST), j0 + sl + NST - 1);
+      issue(slot((sl + NST - 1) % NST), xslot((sl + NST - 1) % NST), j0 + sl + NST - 1);
       wait_vm<(NST - 1) * PER>();
       __asm__ volatile("" ::: "memory");
-      compute(slot(sl));
+      compute(slot(sl), xslot(sl));
     }
   }
   // the last (fewer than 2 NST - 1) stages
@@ -264,9 +292,10 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       const int j = j0 + sl;
       if (j < nk) {
         __asm__ volatile("" ::: "memory");
-        if (j + NST - 1 < nk) issue(slot((sl + NST - 1) % NST), j + NST - 1);
+        if (j + NST - 1 < nk)
+          issue(slot((sl + NST - 1) % NST), xslot((sl + NST - 1) % NST), j + NST - 1);
         wait_stage(min(NST - 1, nk - 1 - j));
-        compute(slot(sl));
+        compute(slot(sl), xslot(sl));
       }
     }
   }
