@@ -40,7 +40,7 @@ import math
 import numpy as np
 from scipy.special import erf
 
-from .moe_oracle import dispatch, expert_ffn, gate, router_logits, silu
+from .moe_oracle import dispatch, gate, router_logits, silu
 
 
 def gelu_grad(z):
@@ -211,3 +211,125 @@ def backward(x, w_router, b_router, w_up, b_up, w_down, b_down, dy, *, alpha, to
                 db_up=db_up if b_up is not None else None, dw_down=dw_down,
                 db_down=db_down if b_down is not None else None, dw=dw, dlogits=dlogits,
                 idx=idx, w=w, probs=probs, **disp)
+
+
+# ----------------------------------------------------------------------------
+# Single gradient entries, for checks at sizes where the whole backward is
+# too large for the host: each follows the same chain rule as `backward`,
+# restricted to what one entry depends on.
+# ----------------------------------------------------------------------------
+
+
+def gate_keys(logits, gating):
+    """(p, keys): the gate probabilities and the values the top-k ranks and
+    renormalizes (p for softmax, sigma for the normalized sigmoid)."""
+    probs = gate(logits, gating)
+    keys = probs if gating == "softmax" else 1.0 / (1.0 + np.exp(-logits))
+    return probs, keys
+
+
+def router_backward_token(t, x, w_router, b_router, *, alpha, top_k, gating, idx, counts, dw):
+    """Router part of token t's gradients for given slot-weight gradients
+    dw [k]: the renormalized top-k, the gate and the aux term
+    ([0539edu] 2.1, 2.3).  Returns dlogits [E] and dx_router = dlogits Wr."""
+    T = x.shape[0]
+    E = w_router.shape[0]
+    logits = router_logits(x[t:t + 1], w_router, b_router)
+    probs, keys = gate_keys(logits, gating)
+    dkey = topk_renorm_backward(keys, idx[t:t + 1], np.asarray(dw, dtype=np.float64)[None, :])
+    f = np.asarray(counts, dtype=np.float64) / (T * top_k)
+    dp = (alpha * E * f / T)[None, :]
+    if gating == "softmax":
+        dl = softmax_backward(probs, dkey + dp)
+    else:
+        dl = sigmoid_normalized_backward(logits, dkey, dp)
+    return dict(dlogits=dl[0], dx_router=(dl @ w_router)[0])
+
+
+def backward_token(t, x, w_router, b_router, w_up, b_up, w_down, b_down, dy, *, alpha, top_k,
+                   num_shared, gating, activation, idx, kept_slots, counts):
+    """Gradients belonging to token t: dx[t], the slot weights' gradient
+    dw[t, :] and dlogits[t, :].  idx [T, k] is the selection, kept_slots[s]
+    whether slot s of token t survived the capacity, counts [E] the routed
+    counts over the whole batch (they fix f_e).  Also returns dw_scale[s] =
+    sum_j |dy[t, j] out_s[j]|, the magnitude behind the sum dw[s] =
+    <dy[t], out_s> (what a rounding of dy scales with)."""
+    E = w_router.shape[0]
+    k = top_k
+    xt = x[t:t + 1]
+    _, keys = gate_keys(router_logits(xt, w_router, b_router), gating)
+    sel = keys[0, idx[t]]
+    w = sel / sel.sum()
+    dx = np.zeros(x.shape[1])
+    dw = np.zeros(k)
+    dw_scale = np.zeros(k)
+    for s in range(k):
+        if not kept_slots[s]:
+            continue
+        e = int(idx[t, s])
+        g = expert_ffn_backward(xt, w_up[e], None if b_up is None else b_up[e], w_down[e],
+                                None if b_down is None else b_down[e], activation,
+                                w[s] * dy[t:t + 1])
+        dx += g["dx"][0]
+        dw[s] = float(np.dot(dy[t], g["out"][0]))
+        dw_scale[s] = float(np.sum(np.abs(dy[t] * g["out"][0])))
+    for q in range(num_shared):
+        qq = E + q
+        g = expert_ffn_backward(xt, w_up[qq], None if b_up is None else b_up[qq], w_down[qq],
+                                None if b_down is None else b_down[qq], activation, dy[t:t + 1])
+        dx += g["dx"][0]
+    r = router_backward_token(t, x, w_router, b_router, alpha=alpha, top_k=k, gating=gating,
+                              idx=idx, counts=counts, dw=dw)
+    return dict(dx=dx + r["dx_router"], dw=dw, dw_scale=dw_scale, dlogits=r["dlogits"])
+
+
+def _segment_rows(seg, E, T, k, disp, topk_weights):
+    """(tokens, gate weights) of the rows of segment seg: an expert's kept
+    assignments in dispatch order, or every token with weight 1 (shared)."""
+    if seg < E:
+        lo, hi = int(disp["offsets"][seg]), int(disp["offsets"][seg + 1])
+        a = np.asarray(disp["sorted_assign"][lo:hi], dtype=np.int64)
+        return a // k, topk_weights[a // k, a % k]
+    return np.arange(T), np.ones(T)
+
+
+def _preact_column(x_rows, w_up_e, b_up_e, n):
+    z = x_rows @ w_up_e[n]
+    return z + b_up_e[n] if b_up_e is not None else z
+
+
+def backward_weight_entries(seg, n, x, w_up, b_up, w_down, b_down, dy, *, activation, top_k,
+                            disp, topk_weights):
+    """Row n of dW1[seg] (with db1[seg][n]) and column n of dW2[seg] (with
+    nothing else), for segment seg (expert, or E + q for shared expert q).
+    For SwiGLU, row n < f of W1 is a gate row and row f + n the matching up
+    row; column n of W2 multiplies h[:, n].  disp: the dispatch of the
+    selection; topk_weights [T, k] the renormalized gate weights."""
+    T, d = x.shape
+    E = len(disp["offsets"]) - 1
+    toks, wts = _segment_rows(seg, E, T, top_k, disp, topk_weights)
+    xr, dyr = x[toks], dy[toks]
+    w_up_e, w_down_e = w_up[seg], w_down[seg]
+    b_up_e = None if b_up is None else b_up[seg]
+    f = w_down_e.shape[1]
+    col = n if n < f else n - f                  # h column this W1 row feeds
+    # G[r] = (W2_e^T dy_r)[col]: the unweighted gradient reaching h[r, col]
+    G = dyr @ w_down_e[:, col]
+    dh = wts * G
+    if activation == "swiglu":
+        g = _preact_column(xr, w_up_e, b_up_e, col)
+        u = _preact_column(xr, w_up_e, b_up_e, f + col)
+        h = silu(g) * u
+        dz = dh * u * silu_grad(g) if n < f else dh * silu(g)
+    else:
+        z = _preact_column(xr, w_up_e, b_up_e, col)
+        if activation == "relu":
+            h = np.maximum(z, 0.0)
+            dz = dh * (z > 0.0)
+        else:
+            h = 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))
+            dz = dh * gelu_grad(z)
+    dw_up_row = dz @ xr                          # dW1[seg][n, :] = sum_r dz_r x_r
+    db_up = float(dz.sum())
+    dw_down_col = (wts[:, None] * dyr).T @ h     # dW2[seg][:, col] = sum_r (w_r dy_r) h_r[col]
+    return dict(dw_up_row=dw_up_row, db_up=db_up, dw_down_col=dw_down_col, col=col)

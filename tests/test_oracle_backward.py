@@ -8,6 +8,8 @@
    with the oracle's selection held fixed.
 3. Invariants: dropped slots get zero gate gradient; an expert with no kept
    rows gets zero weight gradients; alpha enters linearly.
+4. The single-entry functions (a token's gradients, a row of dW1, a column
+   of dW2) reproduce the full backward entry by entry.
 """
 import numpy as np
 import pytest
@@ -174,3 +176,52 @@ def test_activation_derivatives_closed_forms():
     assert B.gelu_grad(np.array([0.0]))[0] == 0.5 and B.silu_grad(np.array([0.0]))[0] == 0.5
     assert abs(B.gelu_grad(np.array([8.0]))[0] - 1) < 1e-12
     assert abs(B.silu_grad(np.array([-40.0]))[0]) < 1e-15
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_single_entries_match_full_backward(case):
+    """The per-token and per-weight-row entry functions (used for checks at
+    full sizes) reproduce the full backward oracle entry by entry."""
+    p, dy, kw = make(case)
+    args = (p["x"], p["w_router"], p["b_router"], p["w_up"], p["b_up"], p["w_down"], p["b_down"], dy)
+    g = B.backward(*args, alpha=ALPHA, **kw)
+    kept = g["assign_row"].reshape(T, K) >= 0
+    for t in range(T):
+        tok = B.backward_token(t, *args, alpha=ALPHA, top_k=K, num_shared=kw["num_shared"],
+                               gating=kw["gating"], activation=kw["activation"], idx=g["idx"],
+                               kept_slots=kept[t], counts=g["counts"])
+        np.testing.assert_allclose(tok["dx"], g["dx"][t], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(tok["dw"], g["dw"][t], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(tok["dlogits"], g["dlogits"][t], rtol=1e-12, atol=1e-13)
+    F1 = p["w_up"].shape[1]
+    for seg in range(E + kw["num_shared"]):
+        for n in range(F1):
+            ent = B.backward_weight_entries(seg, n, p["x"], p["w_up"], p["b_up"], p["w_down"],
+                                            p["b_down"], dy, activation=kw["activation"],
+                                            top_k=K, disp=g, topk_weights=g["w"])
+            np.testing.assert_allclose(ent["dw_up_row"], g["dw_up"][seg][n], rtol=1e-12, atol=1e-13)
+            if p["b_up"] is not None:
+                np.testing.assert_allclose(ent["db_up"], g["db_up"][seg][n], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(ent["dw_down_col"], g["dw_down"][seg][:, ent["col"]],
+                                       rtol=1e-12, atol=1e-13)
+
+
+def test_router_backward_token_is_linear_in_dw():
+    """router_backward_token at the oracle's own dw gives the full backward's
+    logit gradients; it is affine in dw (the aux term is the constant)."""
+    p, dy, kw = make("swiglu_sigmoid_shared_drops")
+    g = B.backward(p["x"], p["w_router"], p["b_router"], p["w_up"], p["b_up"], p["w_down"],
+                   p["b_down"], dy, alpha=ALPHA, **kw)
+    for t in range(T):
+        r = B.router_backward_token(t, p["x"], p["w_router"], p["b_router"], alpha=ALPHA, top_k=K,
+                                    gating=kw["gating"], idx=g["idx"], counts=g["counts"],
+                                    dw=g["dw"][t])
+        np.testing.assert_allclose(r["dlogits"], g["dlogits"][t], rtol=1e-12, atol=1e-13)
+        r0 = B.router_backward_token(t, p["x"], p["w_router"], p["b_router"], alpha=ALPHA, top_k=K,
+                                     gating=kw["gating"], idx=g["idx"], counts=g["counts"],
+                                     dw=np.zeros(K))
+        r2 = B.router_backward_token(t, p["x"], p["w_router"], p["b_router"], alpha=ALPHA, top_k=K,
+                                     gating=kw["gating"], idx=g["idx"], counts=g["counts"],
+                                     dw=2 * g["dw"][t])
+        np.testing.assert_allclose(r2["dlogits"] - r0["dlogits"], 2 * (r["dlogits"] - r0["dlogits"]),
+                                   rtol=1e-10, atol=1e-13)
