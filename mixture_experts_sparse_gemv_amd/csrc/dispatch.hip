@@ -2,21 +2,15 @@
 // statistics (0539edu 2.3; kamacoder 七).
 //
 // Dispatch is a stable counting sort of the T*k assignments a = t*k + s by
-// expert, in three kernels with no inter-block waiting:
+// expert, in two kernels with no inter-block waiting:
 //   1. per-chunk expert counts: chunk c = tokens 16c .. 16c+15 (the router
 //      kernel writes them in the fused forward; chunk_count_kernel otherwise);
-//   2. dispatch_scan_kernel (one block): sums the chunk counts of each
-//      scatter block (512 tokens), turns them into per-block exclusive
-//      prefixes per expert, and writes counts, kept = min(count, capacity),
-//      offsets (exclusive scan of kept); with the router's per-block
-//      probability sums it also reduces them in a fixed order and writes
-//      colsum, f, P and L_aux;
-//   3. dispatch_scatter_kernel (one block per 512 tokens): ranks each of its
-//      assignments within its expert — the block's prefix, plus the counts
-//      of earlier waves of the block, plus the lanes below it in its wave
-//      holding the same expert (six bit-plane ballots) — and scatters:
-//      rank < kept gives row offsets[e] + rank, otherwise the assignment is
-//      dropped and goes after all kept rows, grouped by expert.
+//   2. dispatch_kernel (one block per 512 tokens): from the chunk counts
+//      each block forms the expert totals (so kept = min(count, capacity)
+//      and the row offsets, an exclusive scan of kept) and its own base
+//      ranks, then ranks and scatters its assignments; block 0 writes
+//      counts, kept and offsets and, with the router's per-chunk probability
+//      sums, reduces them in a fixed order to colsum, f, P and L_aux.
 // Ranks are the token order within each expert, so an expert keeps its C
 // lowest-token assignments, bit-exactly and independently of scheduling.
 #include "moe_internal.h"
@@ -103,173 +97,88 @@ __device__ void route_stats_wave(int lane, int E, int c, int kp, float pe, moe_r
   }
 }
 
-struct ScanArgs {
+struct DispatchArgs {
+  const int32_t* topk_idx;
   const int32_t* chunk_counts;   // [nchunk, E]
-  int32_t* sb_prefix;            // [nsb, E] out: per scatter block exclusive prefix
   int32_t *counts, *kept, *offsets;
+  int32_t *sorted_assign, *assign_row;
+  uint8_t* drop_mask;
   const float* prob_part;        // [nchunk, E] or null (no aux statistics)
   float *colsum, *f, *P, *l_aux;
   moe_route_stats* stats;        // or null
-  int T, k, E, cap, nchunk, nsb;
+  int T, k, E, cap, nchunk;
 };
 
 constexpr int PMAX = 32;   // per-thread probability partial sums prefetched
-constexpr int RMAX = 4;    // scatter-block sums a thread keeps in registers
 
-// ---- 2. one block: block prefixes, counts/kept/offsets, aux statistics.
-// Thread (e, j) = (tid % EP, tid / EP), EP = E rounded up to a power of two,
-// J = ST / EP threads per expert.
-__global__ __launch_bounds__(ST) void dispatch_scan_kernel(ScanArgs a) {
-  __shared__ int sc[2][ST];
-  __shared__ int tot_s[kMaxExperts];
-  __shared__ float wsum[SW][kMaxExperts];
+// Aux statistics (block 0): colsum, f, P, L_aux and the routing health
+// indicators from the router's per-chunk probability sums and the routed
+// counts tot_s.  Sums run per thread in chunk order, over the wave's j in
+// xor-butterfly order, then over the waves in order.  Thread (e, j) as in
+// dispatch_kernel.
+__device__ void aux_block(const DispatchArgs& a, const int* tot_s, int e, int j, int EP, int J,
+                          float (*wsum)[kMaxExperts], int* scratch) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E;
-  const int EP = E <= 1 ? 1 : (E <= 2 ? 2 : (E <= 4 ? 4 : (E <= 8 ? 8 : (E <= 16 ? 16 : (E <= 32 ? 32 : 64)))));
-  const int J = ST / EP;
-  const int e = tid % EP, j = tid / EP;
   const bool act = e < E;
-
-  // prefetch the router's per-chunk probability sums: chunks j, j + J, ...
-  float pv[PMAX];
-  int pcount = 0;
-  if (a.prob_part && act) {
+  float v = 0.f;
+  if (act) {
+    float pv[PMAX];
 #pragma unroll
-    for (int q = 0; q < PMAX; ++q) {
+    for (int q = 0; q < PMAX; ++q) {   // independent loads, all in flight
       const int b = j + q * J;
       pv[q] = (b < a.nchunk) ? a.prob_part[(long long)b * E + e] : 0.f;
     }
-    pcount = (a.nchunk + J - 1) / J;
+#pragma unroll
+    for (int q = 0; q < PMAX; ++q) v += pv[q];
+    for (int b = j + PMAX * J; b < a.nchunk; b += J) v += a.prob_part[(long long)b * E + e];
   }
-
-  // phase A: sums of the scatter blocks [b0, b1) this thread owns
-  constexpr int CPB = kScatterTokens / kRouterTokens;   // chunks per scatter block
-  const int R = (a.nsb + J - 1) / J;
-  const int b0 = j * R, b1 = min(a.nsb, b0 + R);
-  auto block_sum = [&](int b) {
-    const int c0 = b * CPB;
-    int v[CPB];
-#pragma unroll
-    for (int i = 0; i < CPB; ++i)   // independent loads, all in flight
-      v[i] = (c0 + i < a.nchunk) ? a.chunk_counts[(long long)(c0 + i) * E + e] : 0;
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < CPB; ++i) sum += v[i];
-    return sum;
-  };
-  int keep[RMAX];   // the first RMAX block sums stay in registers
-  int acc = 0;
-#pragma unroll
-  for (int r = 0; r < RMAX; ++r) {
-    keep[r] = (act && b0 + r < b1) ? block_sum(b0 + r) : 0;
-    acc += keep[r];
-  }
-  if (act)
-    for (int b = b0 + RMAX; b < b1; ++b) {   // the rest go through memory
-      const int sum = block_sum(b);
-      a.sb_prefix[(long long)b * E + e] = sum;
-      acc += sum;
-    }
-  // phase B: exclusive scan of acc over j for each expert (Hillis-Steele)
-  int cur = 0;
-  sc[0][tid] = acc;
+  for (int o = EP; o < 64; o <<= 1) v += __shfl_xor(v, o);
+  if (lane < EP) wsum[wave][lane] = v;
   __syncthreads();
-  for (int o = 1; o < J; o <<= 1) {
-    int v = sc[cur][tid];
-    if (j >= o) v += sc[cur][tid - o * EP];
-    sc[cur ^ 1][tid] = v;
-    cur ^= 1;
-    __syncthreads();
+  float pe = 0.f;
+  if (tid < E) {
+    float cs = 0.f;
+    for (int w = 0; w < SW; ++w) cs += wsum[w][tid];
+    const float fe = (float)tot_s[tid] / (float)((long long)a.T * a.k);
+    pe = cs / (float)a.T;
+    if (a.colsum) a.colsum[tid] = cs;
+    if (a.f) a.f[tid] = fe;
+    if (a.P) a.P[tid] = pe;
+    scratch[tid] = __float_as_int(fe * pe);
   }
-  const int excl = sc[cur][tid] - acc;
-  if (j == J - 1 && act) tot_s[e] = sc[cur][tid];
-  // phase C: block prefixes
-  if (act) {
-    int run = excl;
-#pragma unroll
-    for (int r = 0; r < RMAX; ++r)
-      if (b0 + r < b1) {
-        a.sb_prefix[(long long)(b0 + r) * E + e] = run;
-        run += keep[r];
-      }
-    for (int b = b0 + RMAX; b < b1; ++b) {
-      const int v = a.sb_prefix[(long long)b * E + e];
-      a.sb_prefix[(long long)b * E + e] = run;
-      run += v;
-    }
-  }
-  __syncthreads();
-  // phase D: counts, kept = min(count, capacity), offsets = exclusive scan of kept
-  if (wave == 0) {
+  if (wave == 0 && a.stats) {
     const int c = lane < E ? tot_s[lane] : 0;
-    const int kk = (a.cap > 0 && c > a.cap) ? a.cap : c;
-    int incl = kk;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_up(incl, o);
-      if (lane >= o) incl += u;
-    }
-    if (lane < E) {
-      a.counts[lane] = c;
-      a.kept[lane] = kk;
-      a.offsets[lane] = incl - kk;
-    }
-    if (lane == E - 1) a.offsets[E] = incl;
+    route_stats_wave(lane, E, c, (a.cap > 0 && c > a.cap) ? a.cap : c, pe, a.stats);
   }
-
-  // ---- aux statistics (f, P, L_aux) when the router's partial sums are given:
-  // per thread in chunk order, then over the wave's j in xor-butterfly order,
-  // then over the waves in order
-  if (a.prob_part) {
-    float v = 0.f;
-    if (act) {
-#pragma unroll
-      for (int q = 0; q < PMAX; ++q)
-        if (q < pcount) v += pv[q];
-      for (int b = j + PMAX * J; b < a.nchunk; b += J) v += a.prob_part[(long long)b * E + e];
-    }
-    for (int o = EP; o < 64; o <<= 1) v += __shfl_xor(v, o);
-    if (lane < EP) wsum[wave][lane] = v;
-    __syncthreads();
-    float pe = 0.f;
-    if (tid < E) {
-      float cs = 0.f;
-      for (int w = 0; w < SW; ++w) cs += wsum[w][tid];
-      const float fe = (float)tot_s[tid] / (float)((long long)a.T * a.k);
-      pe = cs / (float)a.T;
-      if (a.colsum) a.colsum[tid] = cs;
-      if (a.f) a.f[tid] = fe;
-      if (a.P) a.P[tid] = pe;
-      sc[0][tid] = __float_as_int(fe * pe);
-    }
-    if (wave == 0 && a.stats) {
-      const int c = lane < E ? tot_s[lane] : 0;
-      route_stats_wave(lane, E, c, (a.cap > 0 && c > a.cap) ? a.cap : c, pe, a.stats);
-    }
-    __syncthreads();
-    if (tid == 0 && a.l_aux) {
-      float l = 0.f;
-      for (int ee = 0; ee < E; ++ee) l += __int_as_float(sc[0][ee]);
-      a.l_aux[0] = (float)E * l;
-    }
+  __syncthreads();
+  if (tid == 0 && a.l_aux) {
+    float l = 0.f;
+    for (int ee = 0; ee < E; ++ee) l += __int_as_float(scratch[ee]);
+    a.l_aux[0] = (float)E * l;
   }
 }
 
-struct ScatterArgs {
-  const int32_t* topk_idx;
-  const int32_t *sb_prefix, *counts, *kept, *offsets;
-  int32_t *sorted_assign, *assign_row;
-  uint8_t* drop_mask;
-  int T, k, E;
-};
-
-// ---- 3. ranks and scatter, one block per kScatterTokens tokens
-__global__ __launch_bounds__(ST) void dispatch_scatter_kernel(ScatterArgs a) {
+// ---- 2. one block per kScatterTokens tokens.  Each block sums the chunk
+// counts itself: over all chunks (the expert totals, hence kept = min(total,
+// capacity) and the row offsets) and over the chunks before its tokens (its
+// base ranks).  It then ranks each of its assignments within its expert —
+// base rank, plus the counts of earlier waves and passes of the block, plus
+// the lanes below it in its wave holding the same expert (six bit-plane
+// ballots) — and scatters: rank < kept gives row offsets[e] + rank,
+// otherwise the assignment is dropped and goes after all kept rows, grouped
+// by expert.  Block 0 also writes counts, kept and offsets and, given the
+// router's probability sums, the aux statistics.
+// Thread (e, j) = (tid % EP, tid / EP) while summing, EP = E rounded up to a
+// power of two, J = ST / EP threads per expert.
+__global__ __launch_bounds__(ST) void dispatch_kernel(DispatchArgs a) {
+  __shared__ int sp[ST], stot[ST];
   __shared__ int kept_s[kMaxExperts], off_s[kMaxExperts], drop_s[kMaxExperts], run_s[kMaxExperts];
+  __shared__ int tot_s[kMaxExperts];
   __shared__ int wc[SW][kMaxExperts];
+  __shared__ float wsum[SW][kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E;
-  const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const long long n = (long long)a.T * a.k;
   const long long A0 = (long long)blockIdx.x * kScatterTokens * a.k;
   const long long A1 = A0 + (long long)kScatterTokens * a.k < n ? A0 + (long long)kScatterTokens * a.k : n;
@@ -281,38 +190,86 @@ __global__ __launch_bounds__(ST) void dispatch_scatter_kernel(ScatterArgs a) {
     const long long asg = A0 + (long long)p * ST + tid;
     ids[p] = asg < A1 ? clamp_id(a.topk_idx[asg], E) : -1;
   }
-  if (wave == 0) {   // lane e: expert e's kept count, row offset, block prefix, dropped start
-    int kp = 0, of = 0, rs = 0, dc = 0;
-    if (lane < E) {
-      kp = a.kept[lane];
-      of = a.offsets[lane];
-      rs = a.sb_prefix[(long long)blockIdx.x * E + lane];
-      dc = a.counts[lane] - kp;
+
+  // expert totals and this block's base ranks from the chunk counts
+  const int EP = E <= 1 ? 1 : (E <= 2 ? 2 : (E <= 4 ? 4 : (E <= 8 ? 8 : (E <= 16 ? 16 : (E <= 32 ? 32 : 64)))));
+  const int J = ST / EP;
+  const int e = tid % EP, j = tid / EP;
+  const int cb = blockIdx.x * (kScatterTokens / kRouterTokens);   // chunks before this block
+  int pre = 0, tot = 0;
+  if (e < E) {
+    constexpr int U = 8;
+    int c = j;
+    for (; c + (U - 1) * J < a.nchunk; c += U * J) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = a.chunk_counts[(long long)(c + u * J) * E + e];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        tot += v[u];
+        if (c + u * J < cb) pre += v[u];
+      }
     }
-    const int offE = a.offsets[E];
-    int incl = dc;
+    for (; c < a.nchunk; c += J) {
+      const int v = a.chunk_counts[(long long)c * E + e];
+      tot += v;
+      if (c < cb) pre += v;
+    }
+  }
+  sp[tid] = pre;
+  stot[tid] = tot;
+  __syncthreads();
+  for (int o = J >> 1; o >= 1; o >>= 1) {   // integer sums: exact in any order
+    if (j < o) {
+      sp[tid] += sp[tid + o * EP];
+      stot[tid] += stot[tid + o * EP];
+    }
+    __syncthreads();
+  }
+  if (wave == 0) {   // lane e: kept count, row offset, base rank, dropped start
+    const int c = lane < E ? stot[lane] : 0;
+    const int kp = (a.cap > 0 && c > a.cap) ? a.cap : c;
+    int incl = kp;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int u = __shfl_up(incl, o);
       if (lane >= o) incl += u;
     }
-    if (lane < E) {
-      kept_s[lane] = kp;
-      off_s[lane] = of;
-      run_s[lane] = rs;
-      drop_s[lane] = offE + incl - dc;   // dropped groups follow all kept rows, by expert
+    const int offE = __shfl(incl, 63);
+    const int dc = c - kp;
+    int dincl = dc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(dincl, o);
+      if (lane >= o) dincl += u;
     }
+    if (lane < E) {
+      tot_s[lane] = c;
+      kept_s[lane] = kp;
+      off_s[lane] = incl - kp;
+      run_s[lane] = sp[lane];
+      drop_s[lane] = offE + dincl - dc;   // dropped groups follow all kept rows, by expert
+      if (blockIdx.x == 0) {
+        a.counts[lane] = c;
+        a.kept[lane] = kp;
+        a.offsets[lane] = incl - kp;
+      }
+    }
+    if (blockIdx.x == 0 && lane == 0) a.offsets[E] = offE;
   }
   __syncthreads();
+  if (blockIdx.x == 0 && a.prob_part) aux_block(a, tot_s, e, j, EP, J, wsum, sp);
+
+  const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int p = 0; p < MAXP; ++p) {
     const long long p0 = A0 + (long long)p * ST;
     if (p0 >= A1) break;   // uniform
     const long long asg = p0 + tid;
     const bool valid = ids[p] >= 0;
-    const int e = valid ? ids[p] : 0;
-    const Bits r = ballots(e, valid);
-    const int rank_w = __popcll(lanes_with(r, e) & lower);
+    const int ee = valid ? ids[p] : 0;
+    const Bits r = ballots(ee, valid);
+    const int rank_w = __popcll(lanes_with(r, ee) & lower);
     wc[wave][lane] = __popcll(lanes_with(r, lane));
     __syncthreads();
     if (tid < E) {   // per-wave base ranks: earlier blocks and passes, then earlier waves
@@ -326,14 +283,14 @@ __global__ __launch_bounds__(ST) void dispatch_scatter_kernel(ScatterArgs a) {
     }
     __syncthreads();
     if (valid) {
-      const int rank = wc[wave][e] + rank_w;
+      const int rank = wc[wave][ee] + rank_w;
       int row;
-      if (rank < kept_s[e]) {
-        row = off_s[e] + rank;
+      if (rank < kept_s[ee]) {
+        row = off_s[ee] + rank;
         a.assign_row[asg] = row;
         if (a.drop_mask) a.drop_mask[asg] = 0;
       } else {
-        row = drop_s[e] + (rank - kept_s[e]);
+        row = drop_s[ee] + (rank - kept_s[ee]);
         a.assign_row[asg] = -1;
         if (a.drop_mask) a.drop_mask[asg] = 1;
       }
@@ -376,10 +333,10 @@ __global__ __launch_bounds__(64) void aux_kernel(const float* colsum, const int3
 }  // namespace
 
 hipError_t launch_dispatch(const Shape& s, const int32_t* topk_idx, int32_t* chunk_counts,
-                           bool counted, int32_t* sb_prefix, int32_t* counts, int32_t* kept,
-                           int32_t* offsets, int32_t* sorted_assign, int32_t* assign_row,
-                           uint8_t* drop_mask, const float* prob_part, float* colsum, float* f,
-                           float* P, float* l_aux, moe_route_stats* stats, hipStream_t st) {
+                           bool counted, int32_t* counts, int32_t* kept, int32_t* offsets,
+                           int32_t* sorted_assign, int32_t* assign_row, uint8_t* drop_mask,
+                           const float* prob_part, float* colsum, float* f, float* P,
+                           float* l_aux, moe_route_stats* stats, hipStream_t st) {
   const int nchunk = router_blocks(s), nsb = scatter_blocks(s);
   if (!counted) {
     chunk_count_kernel<<<(nchunk + 3) / 4, 256, 0, st>>>(topk_idx, chunk_counts, s.T, s.k, s.E,
@@ -387,14 +344,10 @@ hipError_t launch_dispatch(const Shape& s, const int32_t* topk_idx, int32_t* chu
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  ScanArgs sa{chunk_counts, sb_prefix, counts, kept, offsets, prob_part, colsum, f, P, l_aux,
-              prob_part ? stats : nullptr, s.T, s.k, s.E, s.cap, nchunk, nsb};
-  dispatch_scan_kernel<<<1, ST, 0, st>>>(sa);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  ScatterArgs ca{topk_idx, sb_prefix, counts, kept, offsets, sorted_assign, assign_row, drop_mask,
-                 s.T, s.k, s.E};
-  dispatch_scatter_kernel<<<nsb, ST, 0, st>>>(ca);
+  DispatchArgs da{topk_idx, chunk_counts, counts, kept, offsets, sorted_assign, assign_row,
+                  drop_mask, prob_part, colsum, f, P, l_aux, prob_part ? stats : nullptr,
+                  s.T, s.k, s.E, s.cap, nchunk};
+  dispatch_kernel<<<nsb, ST, 0, st>>>(da);
   return hipGetLastError();
 }
 

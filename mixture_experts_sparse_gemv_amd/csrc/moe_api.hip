@@ -32,7 +32,6 @@ WsLayout ws_layout(const Shape& s) {
   w.token_experts = s.ec() ? take((size_t)s.T * 4) : o;
   w.prob_part = take((size_t)router_blocks(s) * s.E * 4);
   w.chunk_counts = take((size_t)router_blocks(s) * s.E * 4);
-  w.sb_prefix = take((size_t)scatter_blocks(s) * s.E * 4);
   w.prob_colsum = take((size_t)s.E * 4);
   w.counts = take((size_t)s.E * 4);
   w.kept = take((size_t)s.E * 4);
@@ -218,8 +217,8 @@ moe_status moe_dispatch(const moe_problem* p, const int32_t* topk_idx, int32_t* 
   if (!topk_idx || !counts || !kept || !offsets || !sorted_assign || !assign_row || !drop_mask)
     return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(s, ws, ws_bytes, L)) != MOE_OK) return st;
-  return fail_hip(launch_dispatch(s, topk_idx, at<int32_t>(ws, L.chunk_counts), false,
-                                  at<int32_t>(ws, L.sb_prefix), counts, kept, offsets,
+  return fail_hip(launch_dispatch(s, topk_idx, at<int32_t>(ws, L.chunk_counts), false, counts,
+                                  kept, offsets,
                                   sorted_assign, assign_row, drop_mask, nullptr, nullptr, nullptr,
                                   nullptr, nullptr, nullptr, stream));
 }
@@ -370,7 +369,7 @@ moe_status moe_ffn_forward(const moe_problem* p, const moe_weights* w, const voi
     e = launch_router(s, x, w->w_router, w->b_router, topk_idx, topk_w, r.probs, part,
                       chunk_counts, stream);
     if (e == hipSuccess)
-      e = launch_dispatch(s, topk_idx, chunk_counts, true, at<int32_t>(ws, L.sb_prefix), counts,
+      e = launch_dispatch(s, topk_idx, chunk_counts, true, counts,
                           kept, offsets, sorted_assign, assign_row, drop_mask, part,
                           at<float>(ws, L.prob_colsum), f, P, l_aux, r.stats, stream);
   }

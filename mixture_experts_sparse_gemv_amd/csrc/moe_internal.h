@@ -56,8 +56,7 @@ int down_ksplit(const Shape& s);
 
 // ---------------------------------------------------------------- workspace
 struct WsLayout {
-  size_t topk_idx, topk_w, probs, token_experts, prob_part, chunk_counts, sb_prefix,
-      prob_colsum, counts, kept, offsets, sorted_assign,
+  size_t topk_idx, topk_w, probs, token_experts, prob_part, chunk_counts, prob_colsum, counts, kept, offsets, sorted_assign,
       assign_row, drop_mask, f, P, l_aux, h, y_exp, y_part, total;
 };
 WsLayout ws_layout(const Shape& s);
@@ -137,15 +136,14 @@ hipError_t launch_router(const Shape& s, const void* x, const void* wr, const vo
                          int32_t* chunk_counts, hipStream_t st, float* logits = nullptr);
 hipError_t launch_colsum(const Shape& s, const float* prob_part, float* colsum, hipStream_t st);
 // Dispatch.  counted: chunk_counts already hold the router's per-chunk
-// counts (else they are computed from topk_idx first).  sb_prefix is
-// scratch [scatter_blocks, E].  When prob_part is non-null it also reduces
-// the probability sums into colsum and writes f, P, l_aux (and the routing
-// health indicators when stats is non-null).
+// counts (else they are computed from topk_idx first).  When prob_part is
+// non-null it also reduces the probability sums into colsum and writes f, P,
+// l_aux (and the routing health indicators when stats is non-null).
 hipError_t launch_dispatch(const Shape& s, const int32_t* topk_idx, int32_t* chunk_counts,
-                           bool counted, int32_t* sb_prefix, int32_t* counts, int32_t* kept,
-                           int32_t* offsets, int32_t* sorted_assign, int32_t* assign_row,
-                           uint8_t* drop_mask, const float* prob_part, float* colsum, float* f,
-                           float* P, float* l_aux, moe_route_stats* stats, hipStream_t st);
+                           bool counted, int32_t* counts, int32_t* kept, int32_t* offsets,
+                           int32_t* sorted_assign, int32_t* assign_row, uint8_t* drop_mask,
+                           const float* prob_part, float* colsum, float* f, float* P,
+                           float* l_aux, moe_route_stats* stats, hipStream_t st);
 hipError_t launch_routing_stats(const Shape& s, const int32_t* counts, const int32_t* kept,
                                 const float* P, moe_route_stats* stats, hipStream_t st);
 hipError_t launch_aux(const Shape& s, const float* colsum, const int32_t* counts, float* f,
