@@ -33,6 +33,13 @@ CASES = {
     "decode_T16_d1024": (scaled(RUNS["large_decode"], d_model=1024, d_ff=2048), 0.01),
     "relu_T333": (scaled(RUNS["gpt2"], T=333, d_model=256, d_ff=512, activation="relu",
                          capacity_factor=1.0), 0.05),
+    # edge cases: one token; one expert; every expert selected; capacity 1
+    "one_token": (scaled(RUNS["gpt2"], T=1, d_model=256, d_ff=512), 0.1),
+    "single_expert": (scaled(RUNS["swiglu_skew"], T=100, d_model=256, d_ff=256, num_experts=1),
+                      0.1),
+    "all_experts": (scaled(RUNS["gpt2"], T=200, d_model=256, d_ff=256, top_k=8), 0.1),
+    "capacity_one": (scaled(RUNS["gpt2"], T=300, d_model=256, d_ff=256, capacity_factor=0.01),
+                     0.1),
 }
 
 
