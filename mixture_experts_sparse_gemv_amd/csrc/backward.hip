@@ -10,8 +10,10 @@
 // returns, instead of being stored by it:
 //   Z  = x_rows W1^T + b1                 grouped GEMM, fp32 [rows, F1]
 //   G  = dy_rows W2                        grouped GEMM against W2 transposed
-//   per row: h = act(Z), dw = <h, G> + <b2, dy> (the gate weight's gradient),
-//            dZ = act'(Z) * (w G)  (SwiGLU: [w G u silu'(g); w G silu(g)])
+//   per tile of 32 rows x 64 columns of h: h = act(Z), dZ = act'(Z) * (w G)
+//            (SwiGLU: [w G u silu'(g); w G silu(g)]), written row-major and
+//            transposed, and the partial sums of <h, G>; the gate weight's
+//            gradient dw = (sum of the partials) + <b2, dy>
 //   dX_rows = dZ W1                        grouped GEMM against W1 transposed
 //   dW2_e = (w dy)_e^T H_e, dW1_e = dZ_e^T x_e   per-expert GEMMs reducing
 //            over the expert's rows (operands transposed, rows zero-padded)
@@ -113,11 +115,10 @@ __global__ __launch_bounds__(64) void wgrad_offsets_kernel(const int32_t* __rest
   poff[E + S] = acc;
 }
 
-// out[c][poff[seg] + i] = scale(row) * src[srow(row)][c] for the segment's
-// rows i (bf16), 0 in the padding.  SRC32: fp32 source (else bf16); GATHER:
-// source row = the row's token (else the row itself); SCALE: times the row's
-// gate weight.  Block = 32 padded rows x 64 columns.
-template <bool SRC32, bool GATHER, bool SCALE>
+// out[c][poff[seg] + i] = scale(row) * src[token(row)][c] for the segment's
+// rows i (bf16), 0 in the padding.  SRC32: fp32 source (else bf16); SCALE:
+// times the row's gate weight.  Block = 32 padded rows x 64 columns.
+template <bool SRC32, bool SCALE>
 __global__ __launch_bounds__(256) void seg_transpose_kernel(
     const void* __restrict__ src, int C, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_assign, const float* __restrict__ topk_w,
@@ -140,14 +141,12 @@ __global__ __launch_bounds__(256) void seg_transpose_kernel(
     float v[8];
     if (i < rows) {
       const int r = base + i;
-      int srow = r;
+      int srow = i;   // shared expert: row i is token i
       float sc = 1.0f;
       if (seg < E) {
         const int a = sorted_assign[r];
-        if (GATHER) srow = a / k;
+        srow = a / k;
         if (SCALE) sc = topk_w[a];
-      } else if (GATHER) {
-        srow = i;
       }
       if (SRC32) {
         const float* sp = (const float*)src + (long long)srow * C + c0 + cq;
@@ -222,75 +221,132 @@ __device__ __forceinline__ float gelu_grad_f(float z) {
   return fmaf(z, pdf, cdf);
 }
 
-// One block per row.  Writes Hb (bf16 act(Z)), dZ (bf16) and, for routed
-// rows, dwslot[assignment] = <h, G> + <b2_e, dy_t>.
+// One block per 32 padded rows of one segment (the weight-gradient layout
+// of wgrad_offsets_kernel) and 64 columns c of h.  For each row it forms
+// h = act(Z), dZ = act'(Z) w G (SwiGLU: the gate and the up column) and the
+// partial sum <h, G> over its 64 columns; it writes dZ row-major (the dX
+// product's operand) and both transposed weight-gradient operands, dZ^T
+// into A1 [F1][ldk] and h^T into B2 [f][ldk] (zero in the padding rows), so
+// no separate transposes are needed.  dwpart[row][c / 64] holds the partial
+// sums of routed rows; slot_grad_kernel adds them in column order.
+constexpr int AB_C = 64;   // columns of h per block
 template <int ACT>
 __global__ __launch_bounds__(256) void act_backward_kernel(
-    const float* __restrict__ Z, const float* __restrict__ G, const float* __restrict__ dy,
-    const uint16_t* __restrict__ b_down, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_assign, const float* __restrict__ topk_w, int T, int k,
-    int E, int S, int d, int f, uint16_t* __restrict__ Hb, uint16_t* __restrict__ dZ,
-    float* __restrict__ dwslot) {
-  __shared__ float wsum[4];
-  const int r = blockIdx.x;
-  if (r >= offsets[E] + S * T) return;
-  int seg, tok, assign;
-  float wgt;
-  row_info(r, offsets, sorted_assign, topk_w, T, k, E, seg, tok, wgt, assign);
-  const int F1 = ACT == MOE_SWIGLU ? 2 * f : f;
-  const float* zr = Z + (long long)r * F1;
-  const float* gr = G + (long long)r * f;
-  uint16_t* hr = Hb + (long long)r * f;
-  uint16_t* dzr = dZ + (long long)r * F1;
-  float dot = 0.0f;
-  for (int j = threadIdx.x * 4; j < f; j += 1024) {
-    const f32x4 z = *(const f32x4*)(zr + j);
-    const f32x4 g = *(const f32x4*)(gr + j);
-    float h[4], dz[4], du[4];
+    const float* __restrict__ Z, const float* __restrict__ G, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_assign, const float* __restrict__ topk_w,
+    const int32_t* __restrict__ poff, int T, int E, int S, int f, int ldk,
+    uint16_t* __restrict__ dZ, uint16_t* __restrict__ A1, uint16_t* __restrict__ B2,
+    float* __restrict__ dwpart, int nparts) {
+  constexpr bool SWIGLU = ACT == MOE_SWIGLU;
+  __shared__ uint16_t th[32][AB_C + 2], tz[32][AB_C + 2], tu[SWIGLU ? 32 : 1][AB_C + 2];
+  __shared__ int sh_seg;
+  const int p0 = blockIdx.x * 32, c0 = blockIdx.y * AB_C;
+  const int tid = threadIdx.x;
+  const int nseg = E + S;
+  if (p0 >= poff[nseg]) return;   // beyond the used columns (uniform)
+  if (tid < nseg && poff[tid] <= p0 && p0 < poff[tid + 1]) sh_seg = tid;
+  __syncthreads();
+  const int seg = sh_seg;
+  const int rows = seg < E ? offsets[seg + 1] - offsets[seg] : T;
+  const int base = seg < E ? offsets[seg] : offsets[E] + (seg - E) * T;
+  const int F1 = SWIGLU ? 2 * f : f;
+  const int ri = tid >> 3, cq = (tid & 7) * 8;   // row of the tile, first of 8 columns
+  const int i = p0 - poff[seg] + ri;
+  const bool valid = i < rows;
+  const long long r = base + i;
+  float h[8], dz[8], du[8], dot = 0.0f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float wg = wgt * g[q];
+  for (int q = 0; q < 8; ++q) h[q] = dz[q] = du[q] = 0.0f;
+  if (valid) {
+    const float wgt = seg < E ? topk_w[sorted_assign[r]] : 1.0f;
+    const float* zr = Z + r * F1 + c0 + cq;
+    const float* gr = G + r * f + c0 + cq;
+    const f32x4 z0 = *(const f32x4*)zr, z1 = *(const f32x4*)(zr + 4);
+    const f32x4 g0 = *(const f32x4*)gr, g1 = *(const f32x4*)(gr + 4);
+    f32x4 u0 = {}, u1 = {};
+    if (SWIGLU) u0 = *(const f32x4*)(zr + f), u1 = *(const f32x4*)(zr + f + 4);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float z = q < 4 ? z0[q] : z1[q - 4];
+      const float g = q < 4 ? g0[q] : g1[q - 4];
+      const float wg = wgt * g;
       if (ACT == MOE_RELU) {
-        h[q] = fmaxf(z[q], 0.0f);
-        dz[q] = z[q] > 0.0f ? wg : 0.0f;
+        h[q] = fmaxf(z, 0.0f);
+        dz[q] = z > 0.0f ? wg : 0.0f;
       } else if (ACT == MOE_GELU) {
-        h[q] = gelu_f(z[q]);
-        dz[q] = wg * gelu_grad_f(z[q]);
+        h[q] = gelu_f(z);
+        dz[q] = wg * gelu_grad_f(z);
       } else {
-        const float u = zr[f + j + q];
-        const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp(-z[q]));
-        const float si = z[q] * sg;
+        const float u = q < 4 ? u0[q] : u1[q - 4];
+        const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp(-z));
+        const float si = z * sg;
         h[q] = si * u;
-        dz[q] = wg * u * sg * fmaf(z[q], 1.0f - sg, 1.0f);
+        dz[q] = wg * u * sg * fmaf(z, 1.0f - sg, 1.0f);
         du[q] = wg * si;
       }
-      dot = fmaf(h[q], g[q], dot);
+      dot = fmaf(h[q], g, dot);
     }
-    u32x2 ho, zo;
-    ho[0] = (uint32_t)f32_to_bf16_rne(h[0]) | ((uint32_t)f32_to_bf16_rne(h[1]) << 16);
-    ho[1] = (uint32_t)f32_to_bf16_rne(h[2]) | ((uint32_t)f32_to_bf16_rne(h[3]) << 16);
-    zo[0] = (uint32_t)f32_to_bf16_rne(dz[0]) | ((uint32_t)f32_to_bf16_rne(dz[1]) << 16);
-    zo[1] = (uint32_t)f32_to_bf16_rne(dz[2]) | ((uint32_t)f32_to_bf16_rne(dz[3]) << 16);
-    *(u32x2*)(hr + j) = ho;
-    *(u32x2*)(dzr + j) = zo;
-    if (ACT == MOE_SWIGLU) {
-      u32x2 uo;
-      uo[0] = (uint32_t)f32_to_bf16_rne(du[0]) | ((uint32_t)f32_to_bf16_rne(du[1]) << 16);
-      uo[1] = (uint32_t)f32_to_bf16_rne(du[2]) | ((uint32_t)f32_to_bf16_rne(du[3]) << 16);
-      *(u32x2*)(dzr + f + j) = uo;
-    }
-  }
-  if (assign < 0) return;   // shared rows have no gate weight (uniform over the block)
-  if (b_down) {
-    const float* dyr = dy + (long long)tok * d;
-    const uint16_t* br = b_down + (long long)seg * d;
-    for (int j = threadIdx.x; j < d; j += 256) dot = fmaf(bf16_to_f32(br[j]), dyr[j], dot);
-  }
+    u32x4 zo, uo;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
-  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = dot;
+    for (int q = 0; q < 4; ++q) {
+      zo[q] = (uint32_t)f32_to_bf16_rne(dz[2 * q]) | ((uint32_t)f32_to_bf16_rne(dz[2 * q + 1]) << 16);
+      uo[q] = (uint32_t)f32_to_bf16_rne(du[2 * q]) | ((uint32_t)f32_to_bf16_rne(du[2 * q + 1]) << 16);
+    }
+    *(u32x4*)(dZ + r * F1 + c0 + cq) = zo;
+    if (SWIGLU) *(u32x4*)(dZ + r * F1 + f + c0 + cq) = uo;
+  }
+  // the row's partial <h, G>: its 8 threads are consecutive lanes
+  dot += __shfl_xor(dot, 1);
+  dot += __shfl_xor(dot, 2);
+  dot += __shfl_xor(dot, 4);
+  if (valid && seg < E && (tid & 7) == 0) dwpart[r * nparts + blockIdx.y] = dot;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    th[ri][cq + q] = f32_to_bf16_rne(h[q]);
+    tz[ri][cq + q] = f32_to_bf16_rne(dz[q]);
+    if (SWIGLU) tu[ri][cq + q] = f32_to_bf16_rne(du[q]);
+  }
   __syncthreads();
-  if (threadIdx.x == 0) dwslot[assign] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  // transposed: 64 output rows (columns of h) x 32 padded rows, 4 threads per row
+  const int cc = tid >> 2, part = (tid & 3) * 8;
+  u32x4 vh, vz, vu;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    vh[q] = (uint32_t)th[part + 2 * q][cc] | ((uint32_t)th[part + 2 * q + 1][cc] << 16);
+    vz[q] = (uint32_t)tz[part + 2 * q][cc] | ((uint32_t)tz[part + 2 * q + 1][cc] << 16);
+    if (SWIGLU) vu[q] = (uint32_t)tu[part + 2 * q][cc] | ((uint32_t)tu[part + 2 * q + 1][cc] << 16);
+  }
+  *(u32x4*)(B2 + (long long)(c0 + cc) * ldk + p0 + part) = vh;
+  *(u32x4*)(A1 + (long long)(c0 + cc) * ldk + p0 + part) = vz;
+  if (SWIGLU) *(u32x4*)(A1 + (long long)(f + c0 + cc) * ldk + p0 + part) = vu;
+}
+
+// dwslot[t*k + s] = <h, G> + <b2_e, dy_t> for a kept slot (0 if dropped):
+// one wave per token; for each slot the lanes split the column partials of
+// its row (dwpart[row][.]) and the d products of the bias term, then a fixed
+// butterfly adds them.
+__global__ __launch_bounds__(256) void slot_grad_kernel(
+    const int32_t* __restrict__ assign_row, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ dwpart, int nparts, const uint16_t* __restrict__ b_down,
+    const float* __restrict__ dy, int T, int k, int d, float* __restrict__ dwslot) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;   // per wave
+  for (int s = 0; s < k; ++s) {
+    const int row = assign_row[(long long)t * k + s];
+    float v = 0.0f;
+    if (row >= 0) {   // uniform over the wave
+      for (int c = lane; c < nparts; c += 64) v += dwpart[(long long)row * nparts + c];
+      if (b_down) {
+        const uint16_t* br = b_down + (long long)topk_idx[(long long)t * k + s] * d;
+        const float* dyr = dy + (long long)t * d;
+        for (int j = lane; j < d; j += 64) v = fmaf(bf16_to_f32(br[j]), dyr[j], v);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) dwslot[(long long)t * k + s] = v;
+  }
 }
 
 // ---------------------------------------------------------------- router backward
@@ -478,23 +534,25 @@ __global__ __launch_bounds__(256) void router_wgrad_part_kernel(
   if (blockIdx.x == 0 && tid < E) bpart[(long long)blockIdx.y * E + tid] = bsum;
 }
 
-// dWr[e][j] = sum over slices (in order) of part; dbr likewise.
-__global__ __launch_bounds__(256) void router_wgrad_sum_kernel(const float* __restrict__ part,
-                                                               const float* __restrict__ bpart,
-                                                               int nslices, int E, int d,
-                                                               float* __restrict__ dwr,
-                                                               float* __restrict__ dbr) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long n = (long long)E * d;
-  if (i < n) {
-    float s = 0.0f;
-    for (int q = 0; q < nslices; ++q) s += part[(long long)q * n + i];
-    dwr[i] = s;
-  }
-  if (dbr && i < E) {
-    float s = 0.0f;
-    for (int q = 0; q < nslices; ++q) s += bpart[(long long)q * E + i];
-    dbr[i] = s;
+// out[i] = sum over the nslices slices of part[slice * n + i], i < n: thread
+// (o, q) of a block sums slices q, q + 16, ... of output o (in order), then
+// the 16 group sums are added in group order.  16 outputs per block.
+__global__ __launch_bounds__(256) void slice_sum_kernel(const float* __restrict__ part,
+                                                        int nslices, long long n,
+                                                        float* __restrict__ out) {
+  __shared__ float acc[16][17];
+  const int o = threadIdx.x & 15, q = threadIdx.x >> 4;
+  const long long i = (long long)blockIdx.x * 16 + o;
+  float v = 0.0f;
+  if (i < n)
+    for (int sl = q; sl < nslices; sl += 16) v += part[(long long)sl * n + i];
+  acc[q][o] = v;
+  __syncthreads();
+  if (q == 0 && i < n) {
+    float t = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) t += acc[g][o];
+    out[i] = t;
   }
 }
 
@@ -547,21 +605,18 @@ hipError_t launch_wgrad_offsets(const Shape& s, const int32_t* offsets, int32_t*
   return hipGetLastError();
 }
 
-// kind: 0 = fp32 rows gathered by token and scaled by the gate weight (dy);
-// 1 = bf16 rows as they are (H, dZ); 2 = bf16 rows gathered by token (x).
+// kind 0: fp32 rows gathered by token and scaled by the gate weight (dy);
+// kind 1: bf16 rows gathered by token (x).
 hipError_t launch_seg_transpose(const Shape& s, int kind, const void* src, int C,
                                 const int32_t* offsets, const int32_t* sorted_assign,
                                 const float* topk_w, const int32_t* poff, uint16_t* out, int ldk,
                                 hipStream_t st) {
   const dim3 grid(ldk / 32, C / 64);
   if (kind == 0)
-    seg_transpose_kernel<true, true, true><<<grid, 256, 0, st>>>(
-        src, C, offsets, sorted_assign, topk_w, poff, s.T, s.k, s.E, s.S, out, ldk);
-  else if (kind == 1)
-    seg_transpose_kernel<false, false, false><<<grid, 256, 0, st>>>(
+    seg_transpose_kernel<true, true><<<grid, 256, 0, st>>>(
         src, C, offsets, sorted_assign, topk_w, poff, s.T, s.k, s.E, s.S, out, ldk);
   else
-    seg_transpose_kernel<false, true, false><<<grid, 256, 0, st>>>(
+    seg_transpose_kernel<false, false><<<grid, 256, 0, st>>>(
         src, C, offsets, sorted_assign, topk_w, poff, s.T, s.k, s.E, s.S, out, ldk);
   return hipGetLastError();
 }
@@ -576,19 +631,29 @@ hipError_t launch_seg_rowsum(const Shape& s, const uint16_t* M, int C, int ldk,
 
 hipError_t launch_act_backward(const Shape& s, const float* Z, const float* G, const float* dy,
                                const void* b_down, const int32_t* offsets,
-                               const int32_t* sorted_assign, const float* topk_w, uint16_t* Hb,
-                               uint16_t* dZ, float* dwslot, hipStream_t st) {
-  const int blocks = (int)s.max_rows();
+                               const int32_t* sorted_assign, const float* topk_w,
+                               const int32_t* poff, const int32_t* assign_row,
+                               const int32_t* topk_idx, int ldk, uint16_t* dZ, uint16_t* A1,
+                               uint16_t* B2, float* dwpart, float* dwslot, hipStream_t st) {
+  const dim3 grid(ldk / 32, s.f / AB_C);
+  const int nparts = s.f / AB_C;
   const uint16_t* b2 = (const uint16_t*)b_down;
 #define MOE_ACT_BWD(A)                                                                          \
-  act_backward_kernel<A><<<blocks, 256, 0, st>>>(Z, G, dy, b2, offsets, sorted_assign, topk_w, \
-                                                 s.T, s.k, s.E, s.S, s.d, s.f, Hb, dZ, dwslot)
+  act_backward_kernel<A><<<grid, 256, 0, st>>>(Z, G, offsets, sorted_assign, topk_w, poff,    \
+                                               s.T, s.E, s.S, s.f, ldk, dZ, A1, B2, dwpart,    \
+                                               nparts)
   if (s.act == MOE_RELU) MOE_ACT_BWD(MOE_RELU);
   else if (s.act == MOE_GELU) MOE_ACT_BWD(MOE_GELU);
   else MOE_ACT_BWD(MOE_SWIGLU);
 #undef MOE_ACT_BWD
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  slot_grad_kernel<<<(s.T + 3) / 4, 256, 0, st>>>(assign_row, topk_idx, dwpart, nparts, b2, dy,
+                                                  s.T, s.k, s.d, dwslot);
   return hipGetLastError();
 }
+
+int act_backward_parts(const Shape& s) { return s.f / AB_C; }
 
 hipError_t launch_router_backward(const Shape& s, const float* logits, const void* wr,
                                   const int32_t* topk_idx, const int32_t* assign_row,
@@ -632,8 +697,10 @@ hipError_t launch_router_wgrad(const Shape& s, const float* dlogits, const void*
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long n = (long long)s.E * s.d;
-  router_wgrad_sum_kernel<<<(int)((n + 255) / 256), 256, 0, st>>>(part, bpart, ns, s.E, s.d, dwr,
-                                                                  dbr);
+  slice_sum_kernel<<<(int)((n + 15) / 16), 256, 0, st>>>(part, ns, n, dwr);
+  e = hipGetLastError();
+  if (e != hipSuccess || !dbr) return e;
+  slice_sum_kernel<<<(s.E + 15) / 16, 256, 0, st>>>(bpart, ns, s.E, dbr);
   return hipGetLastError();
 }
 

@@ -67,7 +67,6 @@ BwdLayout bwd_layout(const Shape& s) {
   b.w2t = take(nseg * s.d * s.f * 2);
   b.Z = take(rows * F1 * 4);
   b.G = take(rows * s.f * 4);
-  b.Hb = take(rows * s.f * 2);
   b.dZ = take(rows * F1 * 2);
   b.dxrows = take(rows * s.d * 4);
   b.dxparts = ks > 1 ? take((size_t)(ks - 1) * rows * s.d * 4) : o;
@@ -75,6 +74,7 @@ BwdLayout bwd_layout(const Shape& s) {
   b.B2 = take((size_t)s.f * ldk * 2);
   b.A1 = take(F1 * ldk * 2);
   b.B1 = take((size_t)s.d * ldk * 2);
+  b.dwpart = take((size_t)act_backward_parts(s) * (size_t)s.routed_rows() * 4);
   b.dwslot = take((size_t)s.T * s.k * 4);
   b.dlogits = take((size_t)s.T * s.E * 4);
   b.dxr = take((size_t)s.T * s.d * 4);
@@ -439,7 +439,6 @@ moe_status moe_ffn_backward(const moe_problem* p, const moe_weights* w, const vo
   uint16_t* w2t = at<uint16_t>(ws, B.w2t);
   float* Z = at<float>(ws, B.Z);
   float* G = at<float>(ws, B.G);
-  uint16_t* Hb = at<uint16_t>(ws, B.Hb);
   uint16_t* dZ = at<uint16_t>(ws, B.dZ);
   float* dxrows = at<float>(ws, B.dxrows);
   float* dxparts = at<float>(ws, B.dxparts);
@@ -447,6 +446,7 @@ moe_status moe_ffn_backward(const moe_problem* p, const moe_weights* w, const vo
   uint16_t* B2 = at<uint16_t>(ws, B.B2);
   uint16_t* A1 = at<uint16_t>(ws, B.A1);
   uint16_t* B1 = at<uint16_t>(ws, B.B1);
+  float* dwpart = at<float>(ws, B.dwpart);
   float* dwslot = at<float>(ws, B.dwslot);
   float* dlogits = g->d_logits ? g->d_logits : at<float>(ws, B.dlogits);
   float* dxr = at<float>(ws, B.dxr);
@@ -462,22 +462,20 @@ moe_status moe_ffn_backward(const moe_problem* p, const moe_weights* w, const vo
   if (e == hipSuccess)
     e = launch_bwd_lin(s, x, w->w_up, b_up, F1, s.d, Z, offsets, sa, stream);
   if (e == hipSuccess) e = launch_bwd_lin(s, dyb, w2t, nullptr, s.f, s.d, G, offsets, sa, stream);
-  // h, dZ and the gate weights' gradient
+  // the weight gradients' transposed operands are zero-padded per segment
+  if (e == hipSuccess) e = launch_wgrad_offsets(s, offsets, poff, stream);
+  // h, dZ (row-major, and transposed into A1), h^T into B2, and the column
+  // partials of the gate weights' gradient
   if (e == hipSuccess)
-    e = launch_act_backward(s, Z, G, dy, b_down, offsets, sa, topk_w, Hb, dZ, dwslot, stream);
+    e = launch_act_backward(s, Z, G, dy, b_down, offsets, sa, topk_w, poff, fwd->assign_row,
+                            fwd->topk_idx, ldk, dZ, A1, B2, dwpart, dwslot, stream);
   // dX rows = dZ W1
   if (e == hipSuccess)
     e = launch_bwd_dx(s, dZ, w1t, F1, s.d, dxrows, dxparts, part_elems, ks, offsets, stream);
-  // weight gradients: transposed, zero-padded operands per segment
-  if (e == hipSuccess) e = launch_wgrad_offsets(s, offsets, poff, stream);
   if (e == hipSuccess)
     e = launch_seg_transpose(s, 0, dy, s.d, offsets, sa, topk_w, poff, A2, ldk, stream);
   if (e == hipSuccess)
-    e = launch_seg_transpose(s, 1, Hb, s.f, offsets, sa, topk_w, poff, B2, ldk, stream);
-  if (e == hipSuccess)
-    e = launch_seg_transpose(s, 1, dZ, F1, offsets, sa, topk_w, poff, A1, ldk, stream);
-  if (e == hipSuccess)
-    e = launch_seg_transpose(s, 2, x, s.d, offsets, sa, topk_w, poff, B1, ldk, stream);
+    e = launch_seg_transpose(s, 1, x, s.d, offsets, sa, topk_w, poff, B1, ldk, stream);
   if (e == hipSuccess) e = launch_bwd_wgrad(s, A2, B2, s.d, s.f, ldk, g->dw_down, offsets, stream);
   if (e == hipSuccess) e = launch_bwd_wgrad(s, A1, B1, F1, s.d, ldk, g->dw_up, offsets, stream);
   if (e == hipSuccess && s.expert_bias()) e = launch_seg_rowsum(s, A2, s.d, ldk, poff, g->db_down, stream);

@@ -188,7 +188,7 @@ inline int wgrad_ldk(const Shape& s) {
 }
 int router_wgrad_slices(const Shape& s);
 struct BwdLayout {
-  size_t dyb, w1t, w2t, Z, G, Hb, dZ, dxrows, dxparts, A2, B2, A1, B1, dwslot, dlogits, dxr,
+  size_t dyb, w1t, w2t, Z, G, dZ, dxrows, dxparts, A2, B2, A1, B1, dwpart, dwslot, dlogits, dxr,
       rw_part, rb_part, poff, logits, prob_part, chunk_counts, total;
 };
 BwdLayout bwd_layout(const Shape& s);
@@ -204,10 +204,17 @@ hipError_t launch_bwd_dx(const Shape& s, const void* X, const void* W, int K, in
                          hipStream_t st);
 hipError_t launch_bwd_wgrad(const Shape& s, const void* A, const void* B, int M, int N, int ldk,
                             float* out, const int32_t* offsets, hipStream_t st);
+// h, dZ and the transposed weight-gradient operands (A1 = dZ^T, B2 = h^T,
+// [F1 or f][ldk], zero-padded per segment as poff says), and the slot
+// weights' gradient dwslot[a] = <h, G> + <b2_e, dy_t> (0 if dropped), summed
+// from per-row column partials dwpart [T*k][act_backward_parts(s)].
 hipError_t launch_act_backward(const Shape& s, const float* Z, const float* G, const float* dy,
                                const void* b_down, const int32_t* offsets,
-                               const int32_t* sorted_assign, const float* topk_w, uint16_t* Hb,
-                               uint16_t* dZ, float* dwslot, hipStream_t st);
+                               const int32_t* sorted_assign, const float* topk_w,
+                               const int32_t* poff, const int32_t* assign_row,
+                               const int32_t* topk_idx, int ldk, uint16_t* dZ, uint16_t* A1,
+                               uint16_t* B2, float* dwpart, float* dwslot, hipStream_t st);
+int act_backward_parts(const Shape& s);
 hipError_t launch_wgrad_offsets(const Shape& s, const int32_t* offsets, int32_t* poff,
                                 hipStream_t st);
 hipError_t launch_seg_transpose(const Shape& s, int kind, const void* src, int C,
@@ -216,7 +223,8 @@ hipError_t launch_seg_transpose(const Shape& s, int kind, const void* src, int C
                                 hipStream_t st);
 hipError_t launch_seg_rowsum(const Shape& s, const uint16_t* M, int C, int ldk,
                              const int32_t* poff, float* db, hipStream_t st);
-// logits: [T, E] as launch_router writes them.
+// logits: [T, E] as launch_router writes them; dwslot as launch_act_backward
+// writes it.
 hipError_t launch_router_backward(const Shape& s, const float* logits, const void* wr,
                                   const int32_t* topk_idx, const int32_t* assign_row,
                                   const float* dwslot, const int32_t* counts, float alpha,
