@@ -33,6 +33,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default=None, help="workload name (default: gpt2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the forward captured in a HIP graph (graph_ms_per_step)")
     ap.add_argument("--pass", dest="pass_", choices=("forward", "backward"), default="forward",
                     help="backward: time moe_ffn_backward (gradients of the task loss plus "
                          "alpha * L_aux) instead of the forward")
@@ -218,6 +220,25 @@ def main():
     t1 = time.perf_counter()
     step_s = (t1 - t0) / a.steps
 
+    graph_ms = None
+    if a.graph:   # the same step captured once and replayed
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=side):
+                M.moe_ffn_forward(p, w, g["x"], y, ws, routing=r)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for _ in range(a.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        for _ in range(a.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - g0) / a.steps * 1e3
+
     kept = int(r["offsets"][E].item())
     rows = kept + run.num_shared * T
     counts = r["counts"].cpu().numpy()
@@ -318,6 +339,7 @@ def main():
         "step_gbps": round(step_gbps, 1),
         "step_pct_hbm": round(100 * step_gbps / PEAK_HBM_GBPS, 2),
         "stage_ms": {n: round(v, 5) for n, v in stage_ms.items()},
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
         "roofline": roof,
         "cpu_baseline": cpu,
     }
