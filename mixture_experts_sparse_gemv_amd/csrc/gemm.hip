@@ -26,11 +26,6 @@
 // of one expert weight stay within one XCD's L2.
 #include "moe_internal.h"
 
-// Persistent launch: one block per compute unit, each looping over its tiles.
-#ifndef MOE_PERSISTENT
-#define MOE_PERSISTENT 1
-#endif
-
 namespace moe {
 namespace {
 
@@ -109,13 +104,17 @@ __device__ __forceinline__ void sched_interleave() {
   }
 }
 
-// NST: LDS ring stages (3 or 4); OCC: waves per SIMD the register budget
-// must allow (2 lets two 4-wave blocks share a compute unit).
-template <int BM, int BN, int WGM, int WGN, int MODE, int NST = 4, int OCC = 1>
+// Coordinates of one block tile: K slice, segment, n-tile and m-tile, and the
+// segment's row count and first row.
+struct TileCoord {
+  int ks, seg, nt, mt, rows, start;
+};
+
+// OCC: waves per SIMD the register budget must allow.
+template <int BM, int BN, int WGM, int WGN, int MODE, int OCC = 1>
 __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmArgs a) {
   constexpr int BK = 32;                   // k-tile depth
-  constexpr int NSTAGE = NST;              // LDS ring stages (DMA runs NSTAGE-1 tiles ahead)
-  static_assert(NSTAGE == 3 || NSTAGE == 4, "ring depth");
+  constexpr int NSTAGE = 4;                // LDS ring stages (DMA runs NSTAGE-1 tiles ahead)
   constexpr int NW = WGM * WGN;            // waves: WGM along tokens x WGN along weights
   constexpr bool SWIGLU = MODE == MODE_SWIGLU;
   constexpr bool GATHER = MODE <= MODE_SWIGLU || MODE == MODE_LIN;   // token rows via sorted_assign
@@ -123,6 +122,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   constexpr bool OUT32 = MODE >= MODE_DOWN;      // fp32 output (else fp16 h)
   constexpr bool KSPLIT = MODE == MODE_DOWN || MODE == MODE_DXB;
   constexpr bool WG = MODE == MODE_WGRAD;
+  constexpr bool BIAS = !SWIGLU && !WG;         // an optional per-column bias
   constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile: token rows x weight rows
   constexpr int MI = WM / 32, NI = WN / 32;
   constexpr int NOUT_TILE = SWIGLU ? BN / 2 : BN;
@@ -140,9 +140,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
 
   // The LDS ring as distinct arrays: the compiler sees that the DMA into one
   // stage never aliases the fragment reads of another.
-  __shared__ u32x4 lds0[STAGE], lds1[STAGE], lds2[STAGE], lds3[NSTAGE > 3 ? STAGE : 1];
+  __shared__ u32x4 lds0[STAGE], lds1[STAGE], lds2[STAGE], lds3[STAGE];
   __shared__ int seg_tile[kMaxSegments + 1];
-  __shared__ int sh_seg;
+  __shared__ int seg_nrows[kMaxSegments], seg_row0[kMaxSegments];
+  __shared__ int sh_seg[2];
+  __shared__ uint32_t sh_bias[BIAS ? BN / 2 : 1];   // the tile's bias columns, bf16 pairs
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WGM, wn = wave / WGM;
@@ -151,14 +153,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   const int off_E = a.offsets[a.E];
 
   // ---- tile schedule: prefix sum of m-tiles per segment (wave 0, 2 segments
-  // per lane).  WGRAD: every segment has the same M tiles; the prefix is that
-  // of the padded row counts (the segment's k range), kept in seg_kpos.
+  // per lane), with each segment's row count and first row.  WGRAD: every
+  // segment has the same M tiles; the prefix is that of the padded row counts
+  // (the segment's k range), kept in seg_kpos.
   __shared__ int seg_kpos[WG ? kMaxSegments + 1 : 1];
   if (wave == 0) {
     int c0 = 0, c1 = 0, r, st;
     const int s0 = 2 * lane, s1 = 2 * lane + 1;
-    if (s0 < nseg) { segment_rows(a, s0, off_E, r, st); c0 = WG ? wgrad_pad(r) : (r + BM - 1) / BM; }
-    if (s1 < nseg) { segment_rows(a, s1, off_E, r, st); c1 = WG ? wgrad_pad(r) : (r + BM - 1) / BM; }
+    if (s0 < nseg) {
+      segment_rows(a, s0, off_E, r, st);
+      c0 = WG ? wgrad_pad(r) : (r + BM - 1) / BM;
+      seg_nrows[s0] = r;
+      seg_row0[s0] = st;
+    }
+    if (s1 < nseg) {
+      segment_rows(a, s1, off_E, r, st);
+      c1 = WG ? wgrad_pad(r) : (r + BM - 1) / BM;
+      seg_nrows[s1] = r;
+      seg_row0[s1] = st;
+    }
     int v = c0 + c1, incl = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -185,33 +198,35 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   const int nsplit = KSPLIT ? a.ksplit : 1;
   const int tiles = seg_tile[nseg] * NT;
   const int total = tiles * nsplit;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  // Persistent blocks, one per compute unit: the blocks of XCD xcd (block b
+  // runs on XCD b % 8) walk that XCD's contiguous range of tiles in steps of
+  // their count, so the tiles of one expert weight stay within one L2.
+  const int xcd = blockIdx.x & 7, nslots = gridDim.x >> 3;
   const int per = (total + 7) >> 3;
-#if MOE_PERSISTENT
-  // persistent blocks: XCD xcd's blocks walk its tile range in steps of their count
-  const int nslots = gridDim.x >> 3;
-  for (int it = slot; it < per; it += nslots) {
-  const int LL = xcd * per + it;
-  if (LL >= total) break;                  // uniform over the block
-  __syncthreads();                         // the previous tile's LDS reads are done
-#else
-  const int LL = xcd * per + slot;
-  if (slot >= per || LL >= total) return;  // uniform over the block
-#endif
-  const int ks = LL / tiles;               // K slice
-  const int L = LL - ks * tiles;
-  if (tid < nseg && seg_tile[tid] * NT <= L && L < seg_tile[tid + 1] * NT) sh_seg = tid;
-  __syncthreads();
-  const int seg = sh_seg;
-  const int mtiles = seg_tile[seg + 1] - seg_tile[seg];
-  const int local = L - seg_tile[seg] * NT;
-  const int nt = local / mtiles, mt = local % mtiles;
-  int seg_rows, row_start;
-  segment_rows(a, seg, off_E, seg_rows, row_start);
-  if (WG) {   // output rows of this segment's gradient; no gather, no row offset
-    seg_rows = a.M;
-    row_start = seg * a.M;
-  }
+  int it = blockIdx.x >> 3;
+  auto tile_at = [&](int i) { return i < per && xcd * per + i < total ? xcd * per + i : -1; };
+  // The thread of the segment that holds tile LL records it in sh_seg[b].
+  auto locate = [&](int LL, int b) {
+    const int L = LL % tiles;
+    if (tid < nseg && seg_tile[tid] * NT <= L && L < seg_tile[tid + 1] * NT) sh_seg[b] = tid;
+  };
+  auto coords = [&](int LL, int b) {
+    TileCoord c;
+    c.seg = __builtin_amdgcn_readfirstlane(sh_seg[b]);
+    c.ks = LL / tiles;
+    const int local = LL - c.ks * tiles - seg_tile[c.seg] * NT;
+    const int mtiles = seg_tile[c.seg + 1] - seg_tile[c.seg];
+    c.nt = local / mtiles;
+    c.mt = local % mtiles;
+    if (WG) {   // output rows of this segment's gradient; no gather, no row offset
+      c.rows = a.M;
+      c.start = c.seg * a.M;
+    } else {
+      c.rows = seg_nrows[c.seg];
+      c.start = seg_row0[c.seg];
+    }
+    return c;
+  };
 
   // ---- LDS layout.  Row r of a tile (W rows first, then token rows) holds
   // its ROWCH chunks of 16 bytes at chunk positions kc ^ ((r / RPB) % ROWCH).
@@ -227,47 +242,68 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   // Wave w issues the W instructions q = w*QWW + j and the token-row
   // instructions q = BN/RI + w*QWX + j.
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  // K elements of this block's slice; WGRAD: the segment's padded row range
-  const int kslice = WG ? seg_kpos[seg + 1] - seg_kpos[seg] : a.K / nsplit;
+  auto kc_dma = [&](int q) { return (lane % ROWCH) ^ ((4 * q + lane / 16) % ROWCH); };
+  // Source rows of this lane's token-row chunks: gathered tiles load their
+  // sorted_assign entries (the token's assignment) ahead of the tile.
+  int srow[QWX];
+  auto row_loads = [&](const TileCoord& c) {
+#pragma unroll
+    for (int j = 0; j < QWX; ++j) {
+      const int q = BN / RI + wave * QWX + j;
+      const int m = c.mt * BM + RI * q + lane / ROWCH - BN;
+      const int mm = m < c.rows ? m : c.rows - 1;
+      if (GATHER && c.seg < a.E) srow[j] = a.sorted_assign[c.start + mm];
+      else srow[j] = mm;
+    }
+  };
+  // K elements of the tile's slice (WGRAD: the segment's padded row range),
+  // source bases and this lane's byte offsets of its source chunks.
+  int kslice;
   const char* xbase;
   const char* wbase;
-  if (WG) {
-    xbase = (const char*)(a.X + seg_kpos[seg]);
-    wbase = (const char*)(a.W + seg_kpos[seg]);
-  } else {
-    if (GATHER) xbase = (const char*)a.X;
-    else xbase = (const char*)(a.X + (long long)row_start * a.K + (long long)ks * kslice);
-    wbase = (const char*)(a.W + (long long)seg * a.Wrows * a.K + (long long)ks * kslice);
-  }
-  auto kc_dma = [&](int q) { return (lane % ROWCH) ^ ((4 * q + lane / 16) % ROWCH); };
-  uint32_t woff[QWW], xoff[QWX];   // byte offsets of this lane's source chunks
-#pragma unroll
-  for (int j = 0; j < QWW; ++j) {
-    const int q = wave * QWW + j;
-    const int rho = RI * q + lane / ROWCH;
-    int wr;
-    if (SWIGLU) {
-      const int half = BN / 2;
-      const int nn = nt * half + (rho < half ? rho : rho - half);
-      const int nc = nn < a.f ? nn : a.f - 1;
-      wr = rho < half ? nc : a.f + nc;
+  uint32_t woff[QWW], xoff[QWX];
+  auto setup = [&](const TileCoord& c) {
+    kslice = WG ? seg_kpos[c.seg + 1] - seg_kpos[c.seg] : a.K / nsplit;
+    if (WG) {
+      xbase = (const char*)(a.X + seg_kpos[c.seg]);
+      wbase = (const char*)(a.W + seg_kpos[c.seg]);
     } else {
-      const int nn = nt * BN + rho;
-      wr = nn < a.Wrows ? nn : a.Wrows - 1;
+      if (GATHER) xbase = (const char*)a.X;
+      else xbase = (const char*)(a.X + (long long)c.start * a.K + (long long)c.ks * kslice);
+      wbase = (const char*)(a.W + (long long)c.seg * a.Wrows * a.K + (long long)c.ks * kslice);
     }
-    woff[j] = ((uint32_t)wr * (uint32_t)a.K + (uint32_t)kc_dma(q) * 8u) * 2u;
-  }
 #pragma unroll
-  for (int j = 0; j < QWX; ++j) {
-    const int q = BN / RI + wave * QWX + j;
-    const int rr = RI * q + lane / ROWCH - BN;
-    const int m = mt * BM + rr;
-    const int mm = m < seg_rows ? m : seg_rows - 1;
-    uint32_t row;
-    if (!GATHER) row = (uint32_t)mm;
-    else row = seg < a.E ? (uint32_t)(a.sorted_assign[row_start + mm] / a.k) : (uint32_t)mm;
-    xoff[j] = (row * (uint32_t)a.K + (uint32_t)kc_dma(q) * 8u) * 2u;
-  }
+    for (int j = 0; j < QWW; ++j) {
+      const int q = wave * QWW + j;
+      const int rho = RI * q + lane / ROWCH;
+      int wr;
+      if (SWIGLU) {
+        const int half = BN / 2;
+        const int nn = c.nt * half + (rho < half ? rho : rho - half);
+        const int nc = nn < a.f ? nn : a.f - 1;
+        wr = rho < half ? nc : a.f + nc;
+      } else {
+        const int nn = c.nt * BN + rho;
+        wr = nn < a.Wrows ? nn : a.Wrows - 1;
+      }
+      woff[j] = ((uint32_t)wr * (uint32_t)a.K + (uint32_t)kc_dma(q) * 8u) * 2u;
+    }
+#pragma unroll
+    for (int j = 0; j < QWX; ++j) {
+      const int q = BN / RI + wave * QWX + j;
+      const uint32_t row = (GATHER && c.seg < a.E) ? (uint32_t)(srow[j] / a.k) : (uint32_t)srow[j];
+      xoff[j] = (row * (uint32_t)a.K + (uint32_t)kc_dma(q) * 8u) * 2u;
+    }
+  };
+  // The bias columns of a tile (K slice 0 only), two per thread of the first
+  // BN / 2, loaded a tile ahead and moved into sh_bias before the epilogue.
+  uint32_t bias_reg = 0;
+  auto bias_load = [&](const TileCoord& c) {
+    if (BIAS && a.bias && c.ks == 0 && tid < BN / 2) {
+      const int col = c.nt * BN + 2 * tid;
+      bias_reg = col < a.Nout ? *(const uint32_t*)(a.bias + (long long)c.seg * a.Wrows + col) : 0u;
+    }
+  };
   // Fragment rows are 32-aligned bases plus lane & 31, so the swizzle term
   // depends on the lane only: one per-lane offset per k-substep.
   int fro[NSUB];
@@ -309,73 +345,111 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
     for (int i = 0; i < MI; ++i) xf[i] = buf[xrb[i] + fro[s4]];
   };
 
-  f32x16 acc[NI][MI];
-#pragma unroll
-  for (int j = 0; j < NI; ++j)
-#pragma unroll
-    for (int i = 0; i < MI; ++i) acc[j][i] = f32x16{};
-  auto mfmas = [&](const u32x4(&wf)[NI], const u32x4(&xf)[MI]) {
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      // the down projection's W2 tile is bf16 in LDS: fp16 for the fp16 MFMA
-      const u32x4 w = CVT16 ? bf16x8_to_f16x8(wf[j]) : wf[j];
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        if (CVT16)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              __builtin_bit_cast(f16x8, w), __builtin_bit_cast(f16x8, xf[i]), acc[j][i], 0, 0, 0);
-        else
-          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, xf[i]), acc[j][i], 0, 0, 0);
-      }
-    }
-  };
-
-  // ---- main loop over k-tiles with an NSTAGE ring in LDS.  Iteration kt
-  // issues the DMA of tile kt+3 into the stage of tile kt-1 (all its reads
-  // finished before the previous barrier), computes tile kt, then waits until
-  // tile kt+1 has landed (the DMAs of tiles kt+2 and kt+3 may stay in
-  // flight: vmcnt(2 * DMAs per tile)) and crosses the barrier.  The last
-  // k-substep's MFMAs run after the barrier, under the fragment reads of the
-  // next tile, so the matrix pipe does not drain at tile boundaries.  The
-  // loop body is straight-line: DMAs past the last tile are clamped to it
-  // (into stages nobody reads again) and the tail iterations are peeled.
-  const int nk = kslice / BK;
   constexpr int NDMA = QWW + QWX;
   constexpr int INFLIGHT = (NSTAGE - 2) * NDMA;   // DMAs that may stay in flight
   static_assert(INFLIGHT <= 63, "vmcnt range");
   // s_waitcnt immediate: vmcnt = INFLIGHT, expcnt and lgkmcnt = 0 (every
   // fragment read of this tile has completed before the barrier).
   constexpr int WAIT_IMM = (INFLIGHT & 15) | ((INFLIGHT >> 4) << 14);
-  u32x4 wf[2][NI], xf[2][MI];
-  auto clampk = [&](int t) { return t < nk ? t : nk - 1; };
+  // A barrier after this wave's LDS operations have completed, with no wait
+  // for its global loads and stores in flight (s_waitcnt lgkmcnt(0) only:
+  // vmcnt 63, expcnt 7).
+  auto lds_barrier = [&]() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+  };
+
+  // ---- tile pipeline.  During a tile's epilogue (which stages its output in
+  // ring stages 1 to 3), once its first 32-row slab is out, the block's next
+  // tile issues the DMA of its first k-tile into stage 0 and loads its bias
+  // columns, and the gathered source rows of the tile after that are
+  // fetched.  Tile segments are located two tiles ahead (after a tile's main
+  // loop, when no load is in flight), in sh_seg slots that alternate.  Loads
+  // complete in order, so the wait for stage 0 at the top of a tile covers
+  // the bias and row loads too.
+  int LL = tile_at(it);
+  if (LL < 0) return;   // uniform over the block
+  int LL1 = tile_at(it + nslots);
+  locate(LL, 0);
+  if (LL1 >= 0) locate(LL1, 1);
+  __syncthreads();
+  TileCoord cur = coords(LL, 0);
+  row_loads(cur);
+  setup(cur);
   dma(lds0, 0);
-  dma(lds1, clampk(1));
-  if (NSTAGE == 4) dma(lds2, clampk(2));
-  __builtin_amdgcn_s_waitcnt(WAIT_IMM);
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-  frag_load(lds0, wf[0], xf[0], 0);
-  auto iteration = [&](const u32x4* cur, const u32x4* next, u32x4* far, int kt) {
-    dma(far, clampk(kt + NSTAGE - 1));
-#pragma unroll
-    for (int s4 = 0; s4 + 1 < NSUB; ++s4) {
-      frag_load(cur, wf[(s4 + 1) & 1], xf[(s4 + 1) & 1], s4 + 1);
-      mfmas(wf[s4 & 1], xf[s4 & 1]);
-    }
-    // substep 0: the DMA interleaved with its MFMAs and the next fragments
-    sched_interleave<NM, SG_VMEM_READ, NDMA, SG_DS_READ, NFR>();
-#pragma unroll
-    for (int s4 = 1; s4 + 1 < NSUB; ++s4) sched_interleave<NM, SG_DS_READ, NFR, SG_VMEM_READ, 0>();
+  if (LL1 >= 0) row_loads(coords(LL1, 1));
+  bias_load(cur);
+  lds_barrier();     // sh_seg has been read everywhere before it is rewritten
+  int b = 0;         // sh_seg slot of this tile and of the tile two ahead
+  for (;;) {
+    const bool more = LL1 >= 0;   // uniform over the block
+    const int LL2 = more ? tile_at(it + 2 * nslots) : -1;
+    const int nk = kslice / BK;
+    auto clampk = [&](int t) { return t < nk ? t : nk - 1; };
+    dma(lds1, clampk(1));
+    dma(lds2, clampk(2));
+    // stage 0 has landed; the DMAs of stages 1 and 2 may stay in flight
     __builtin_amdgcn_s_waitcnt(WAIT_IMM);
     __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");   // no LDS read moves above the barrier
-    frag_load(next, wf[0], xf[0], 0);
-    mfmas(wf[(NSUB - 1) & 1], xf[(NSUB - 1) & 1]);
-    sched_interleave<NM, SG_DS_READ, NFR, SG_VMEM_READ, 0>();
-  };
-  int kt = 0;
-  if constexpr (NSTAGE == 4) {
+    __asm__ volatile("" ::: "memory");
+
+    u32x4 wf[2][NI], xf[2][MI];
+    frag_load(lds0, wf[0], xf[0], 0);
+    f32x16 acc[NI][MI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int i = 0; i < MI; ++i) acc[j][i] = f32x16{};
+    auto mfmas = [&](const u32x4(&wf)[NI], const u32x4(&xf)[MI]) {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        // the down projection's W2 tile is bf16 in LDS: fp16 for the fp16 MFMA
+        const u32x4 w = CVT16 ? bf16x8_to_f16x8(wf[j]) : wf[j];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          if (CVT16)
+            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(f16x8, w), __builtin_bit_cast(f16x8, xf[i]), acc[j][i], 0, 0,
+                0);
+          else
+            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, xf[i]), acc[j][i], 0,
+                0, 0);
+        }
+      }
+    };
+
+    // ---- main loop over k-tiles with an NSTAGE ring in LDS.  Iteration kt
+    // issues the DMA of tile kt+3 into the stage of tile kt-1 (all its reads
+    // finished before the previous barrier), computes tile kt, then waits
+    // until tile kt+1 has landed (the DMAs of tiles kt+2 and kt+3 may stay in
+    // flight: vmcnt(2 * DMAs per tile)) and crosses the barrier.  The last
+    // k-substep's MFMAs run after the barrier, under the fragment reads of the
+    // next tile, so the matrix pipe does not drain at tile boundaries.  The
+    // loop body is straight-line: DMAs past the last tile are clamped to it
+    // (into stages nobody reads again) and the tail iterations are peeled.
+    auto iteration = [&](const u32x4* cur_st, const u32x4* next_st, u32x4* far, int kt) {
+      dma(far, clampk(kt + NSTAGE - 1));
+#pragma unroll
+      for (int s4 = 0; s4 + 1 < NSUB; ++s4) {
+        frag_load(cur_st, wf[(s4 + 1) & 1], xf[(s4 + 1) & 1], s4 + 1);
+        mfmas(wf[s4 & 1], xf[s4 & 1]);
+      }
+      // substep 0: the DMA interleaved with its MFMAs and the next fragments
+      sched_interleave<NM, SG_VMEM_READ, NDMA, SG_DS_READ, NFR>();
+#pragma unroll
+      for (int s4 = 1; s4 + 1 < NSUB; ++s4)
+        sched_interleave<NM, SG_DS_READ, NFR, SG_VMEM_READ, 0>();
+      __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");   // no LDS read moves above the barrier
+      frag_load(next_st, wf[0], xf[0], 0);
+      mfmas(wf[(NSUB - 1) & 1], xf[(NSUB - 1) & 1]);
+      sched_interleave<NM, SG_DS_READ, NFR, SG_VMEM_READ, 0>();
+    };
+    int kt = 0;
     for (; kt + 3 < nk; kt += 4) {
       iteration(lds0, lds1, lds3, kt);
       iteration(lds1, lds2, lds0, kt + 1);
@@ -385,92 +459,101 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
     if (kt < nk) iteration(lds0, lds1, lds3, kt);
     if (kt + 1 < nk) iteration(lds1, lds2, lds0, kt + 1);
     if (kt + 2 < nk) iteration(lds2, lds3, lds1, kt + 2);
-  } else {
-    for (; kt + 2 < nk; kt += 3) {
-      iteration(lds0, lds1, lds2, kt);
-      iteration(lds1, lds2, lds0, kt + 1);
-      iteration(lds2, lds0, lds1, kt + 2);
-    }
-    if (kt < nk) iteration(lds0, lds1, lds2, kt);
-    if (kt + 1 < nk) iteration(lds1, lds2, lds0, kt + 1);
-  }
 
-  // ---- epilogue.  Lane holds token row (lane & 31) of each 32x32 tile and,
-  // in register group g, the four consecutive weight rows 8g + 4*(lane>>5) +
-  // 0..3.  Stored directly, one instruction would touch 32 rows with 16-32
-  // bytes each; instead each wave stages one 32-row slab of its output (after
-  // bias and activation, in the output type) in a padded LDS region and
-  // writes it back as whole 16-byte chunks of rows, CPR lanes per row, so a
-  // store instruction covers RPI rows of contiguous bytes.  The padding keeps
-  // the staging writes and reads free of bank conflicts.
-  constexpr int NJ = SWIGLU ? NI / 2 : NI;
-  constexpr int WNOUT = NJ * 32;                       // output columns of a wave
-  constexpr int ES = OUT32 ? 4 : 2;                     // output element bytes
-  constexpr int PITCH = WNOUT * ES + (OUT32 ? 16 : 8);  // staging row pitch, bytes
-  constexpr int CPR = WNOUT * ES / 16;                  // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;                         // rows per store instruction
-  constexpr int STG = 32 * PITCH;                       // staging bytes per wave
-  constexpr int WPA = (int)(sizeof(lds0) / STG);        // waves per ring array
-  static_assert(CPR >= 1 && CPR <= 64 && 64 % CPR == 0 && 32 % RPI == 0, "staging shape");
-  static_assert(WPA * NSTAGE >= NW, "staging must fit in the LDS ring");
-  // Every DMA (including the clamped ones past the last tile) has landed and
-  // every wave's last fragment reads are done before the ring is reused.
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-  const int wa = wv / WPA;
-  char* stg = (char*)(wa == 0 ? lds0 : wa == 1 ? lds1 : wa == 2 ? lds2 : lds3) + (wv % WPA) * STG;
-  const int colw = SWIGLU ? nt * (BN / 2) + wn * (BN / 2 / WGN) : nt * BN + wn * WN;
-  char* obase = ks == 0 ? (char*)a.out : (char*)(a.out2 + (long long)(ks - 1) * a.part_elems);
+    // Every DMA (including the clamped ones past the last tile) has landed and
+    // every wave's last fragment reads are done before the ring is reused;
+    // the tile's bias columns are in sh_bias, the segment of the tile two
+    // ahead in sh_seg.
+    if (BIAS && a.bias && cur.ks == 0 && tid < BN / 2) sh_bias[tid] = bias_reg;
+    if (LL2 >= 0) locate(LL2, b);
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    // ---- epilogue.  Lane holds token row (lane & 31) of each 32x32 tile
+    // and, in register group g, the four consecutive weight rows 8g +
+    // 4*(lane>>5) + 0..3.  Stored directly, one instruction would touch 32
+    // rows with 16-32 bytes each; instead each wave stages one 32-row slab of
+    // its output (after bias and activation, in the output type) in a padded
+    // LDS region of ring stages 1 to 3 and writes it back as whole 16-byte
+    // chunks of rows, CPR lanes per row, so a store instruction covers RPI
+    // rows of contiguous bytes.  The padding keeps the staging writes and
+    // reads free of bank conflicts.
+    constexpr int NJ = SWIGLU ? NI / 2 : NI;
+    constexpr int WNOUT = NJ * 32;                       // output columns of a wave
+    constexpr int ES = OUT32 ? 4 : 2;                     // output element bytes
+    constexpr int PITCH = WNOUT * ES + (OUT32 ? 16 : 8);  // staging row pitch, bytes
+    constexpr int CPR = WNOUT * ES / 16;                  // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;                         // rows per store instruction
+    constexpr int STG = 32 * PITCH;                       // staging bytes per wave
+    constexpr int WPA = (int)(sizeof(lds0) / STG);        // waves per ring stage
+    static_assert(CPR >= 1 && CPR <= 64 && 64 % CPR == 0 && 32 % RPI == 0, "staging shape");
+    static_assert(WPA * (NSTAGE - 1) >= NW, "staging must fit in ring stages 1 to 3");
+    const int wa = wv / WPA;
+    char* stg = (char*)(wa == 0 ? lds1 : wa == 1 ? lds2 : lds3) + (wv % WPA) * STG;
+    const int colw = SWIGLU ? cur.nt * (BN / 2) + wn * (BN / 2 / WGN) : cur.nt * BN + wn * WN;
+    char* obase =
+        cur.ks == 0 ? (char*)a.out : (char*)(a.out2 + (long long)(cur.ks - 1) * a.part_elems);
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
+    for (int i = 0; i < MI; ++i) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
+      for (int j = 0; j < NJ; ++j) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int nloc = j * 32 + 8 * g + 4 * (lane >> 5);
-        const int col = colw + nloc;
-        float v[4];
+        for (int g = 0; g < 4; ++g) {
+          const int nloc = j * 32 + 8 * g + 4 * (lane >> 5);
+          const int col = colw + nloc;
+          float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc[j][i][4 * g + r];
-        if (SWIGLU) {
+          for (int r = 0; r < 4; ++r) v[r] = acc[j][i][4 * g + r];
+          if (SWIGLU) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = silu_f(v[r]) * acc[j + NI / 2][i][4 * g + r];
-        } else if (a.bias && ks == 0 && col < a.Nout) {
-          const u32x2 b = *(const u32x2*)(a.bias + (long long)seg * a.Wrows + col);
-          v[0] += __uint_as_float(b[0] << 16);
-          v[1] += __uint_as_float(b[0] & 0xffff0000u);
-          v[2] += __uint_as_float(b[1] << 16);
-          v[3] += __uint_as_float(b[1] & 0xffff0000u);
-        }
-        char* dst = stg + (lane & 31) * PITCH + nloc * ES;
-        if (OUT32) {
-          *(f32x4*)dst = f32x4{v[0], v[1], v[2], v[3]};
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if (MODE == MODE_RELU) v[r] = fmaxf(v[r], 0.0f);
-            if (MODE == MODE_GELU) v[r] = gelu_f(v[r]);
+            for (int r = 0; r < 4; ++r) v[r] = silu_f(v[r]) * acc[j + NI / 2][i][4 * g + r];
+          } else if (BIAS && a.bias && cur.ks == 0) {
+            const u32x2 bb = *(const u32x2*)(sh_bias + (wn * WN + nloc) / 2);
+            v[0] += __uint_as_float(bb[0] << 16);
+            v[1] += __uint_as_float(bb[0] & 0xffff0000u);
+            v[2] += __uint_as_float(bb[1] << 16);
+            v[3] += __uint_as_float(bb[1] & 0xffff0000u);
           }
-          *(f16x4*)dst = f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+          char* dst = stg + (lane & 31) * PITCH + nloc * ES;
+          if (OUT32) {
+            *(f32x4*)dst = f32x4{v[0], v[1], v[2], v[3]};
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if (MODE == MODE_RELU) v[r] = fmaxf(v[r], 0.0f);
+              if (MODE == MODE_GELU) v[r] = gelu_f(v[r]);
+            }
+            *(f16x4*)dst = f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+          }
         }
       }
-    }
-    // LDS operations of one wave complete in order: the reads below see the
-    // writes above, and the next slab's writes follow these reads.
+      // LDS operations of one wave complete in order: the reads below see the
+      // writes above, and the next slab's writes follow these reads.
 #pragma unroll
-    for (int q = 0; q < 32 / RPI; ++q) {
-      const int r = q * RPI + lane / CPR, c = lane % CPR;
-      const u32x4 val = *(const u32x4*)(stg + r * PITCH + c * 16);
-      const int m = mt * BM + wm * WM + i * 32 + r;
-      const int col = colw + c * (16 / ES);
-      if (m < seg_rows && col < a.Nout)
-        *(u32x4*)(obase + ((long long)(row_start + m) * a.Nout + col) * ES) = val;
+      for (int q = 0; q < 32 / RPI; ++q) {
+        const int r = q * RPI + lane / CPR, c = lane % CPR;
+        const u32x4 val = *(const u32x4*)(stg + r * PITCH + c * 16);
+        const int m = cur.mt * BM + wm * WM + i * 32 + r;
+        const int col = colw + c * (16 / ES);
+        if (m < cur.rows && col < a.Nout)
+          *(u32x4*)(obase + ((long long)(cur.start + m) * a.Nout + col) * ES) = val;
+      }
+      if (i == 0 && more) {   // the next tile's first k-tile and bias, the row loads of the one after
+        const TileCoord nx = coords(LL1, b ^ 1);
+        setup(nx);
+        dma(lds0, 0);
+        bias_load(nx);
+        if (LL2 >= 0) row_loads(coords(LL2, b));
+      }
     }
+    if (!more) break;
+    cur = coords(LL1, b ^ 1);
+    it += nslots;
+    LL1 = LL2;
+    b ^= 1;
+    lds_barrier();   // every wave's staging reads are done before stages 1 and 2 refill
   }
-#if MOE_PERSISTENT
-  }
-#endif
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -543,28 +626,22 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* X, const flo
 #ifndef MOE_DN_WGN
 #define MOE_DN_WGN 4
 #endif
-#ifndef MOE_UP_NST
-#define MOE_UP_NST 4
-#endif
 #ifndef MOE_UP_OCC
 #define MOE_UP_OCC 1
-#endif
-#ifndef MOE_DN_NST
-#define MOE_DN_NST 4
 #endif
 #ifndef MOE_DN_OCC
 #define MOE_DN_OCC 1
 #endif
 constexpr int UP_BM = MOE_UP_BM, UP_BN = MOE_UP_BN, UP_WGM = MOE_UP_WGM, UP_WGN = MOE_UP_WGN;
 constexpr int DN_BM = MOE_DN_BM, DN_BN = MOE_DN_BN, DN_WGM = MOE_DN_WGM, DN_WGN = MOE_DN_WGN;
-constexpr int UP_NST = MOE_UP_NST, UP_OCC = MOE_UP_OCC, DN_NST = MOE_DN_NST, DN_OCC = MOE_DN_OCC;
+constexpr int UP_OCC = MOE_UP_OCC, DN_OCC = MOE_DN_OCC;
 
 int grid_blocks(const Shape& s, int BM, int NT, int ksplit = 1, int occ = 1) {
   const long long mt = (s.routed_rows() + BM - 1) / BM + s.E +
                        (long long)s.S * ((s.T + BM - 1) / BM);
   long long g = NT * mt * ksplit;
   // persistent: `occ` resident blocks per CU, each looping over tiles
-  if (MOE_PERSISTENT && g > (long long)kNumCUs * occ) g = (long long)kNumCUs * occ;
+  if (g > (long long)kNumCUs * occ) g = (long long)kNumCUs * occ;
   return (int)((g + 7) / 8 * 8);
 }
 
@@ -648,15 +725,15 @@ hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void
              sorted_assign, s.T, s.tok_div(), s.E, s.S, s.d, s.f, s.up_rows(), s.f, 1, nullptr, 0, 0};
   if (s.act == MOE_SWIGLU) {
     const int NT = (s.f + UP_BN / 2 - 1) / (UP_BN / 2);
-    grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_SWIGLU, UP_NST, UP_OCC>
+    grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_SWIGLU, UP_OCC>
         <<<grid_blocks(s, UP_BM, NT, 1, UP_OCC), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
   } else {
     const int NT = (s.f + UP_BN - 1) / UP_BN;
     if (s.act == MOE_RELU)
-      grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_RELU, UP_NST, UP_OCC>
+      grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_RELU, UP_OCC>
           <<<grid_blocks(s, UP_BM, NT, 1, UP_OCC), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
     else
-      grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_GELU, UP_NST, UP_OCC>
+      grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_GELU, UP_OCC>
           <<<grid_blocks(s, UP_BM, NT, 1, UP_OCC), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
   }
   return hipGetLastError();
@@ -682,7 +759,7 @@ hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const 
   GemmArgs a{(const uint16_t*)h, (const uint16_t*)w_down, (const uint16_t*)bias, y_exp, offsets,
              nullptr, s.T, s.tok_div(), s.E, s.S, s.f, s.d, s.d, s.f, ks, y_part, part_elems, 0};
   const int NT = (s.d + DN_BN - 1) / DN_BN;
-  grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DOWN, DN_NST, DN_OCC>
+  grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DOWN, DN_OCC>
       <<<grid_blocks(s, DN_BM, NT, ks, DN_OCC), 64 * DN_WGM * DN_WGN, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ks == 1 || !complete) return e;
@@ -701,7 +778,7 @@ hipError_t launch_bwd_lin(const Shape& s, const void* X, const void* W, const vo
   GemmArgs a{(const uint16_t*)X, (const uint16_t*)W, (const uint16_t*)bias, out, offsets,
              sorted_assign, s.T, s.tok_div(), s.E, s.S, K, Wrows, Wrows, s.f, 1, nullptr, 0, 0};
   const int NT = (Wrows + DN_BN - 1) / DN_BN;
-  grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_LIN, DN_NST, DN_OCC>
+  grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_LIN, DN_OCC>
       <<<grid_blocks(s, DN_BM, NT), 64 * DN_WGM * DN_WGN, 0, st>>>(a);
   return hipGetLastError();
 }
@@ -715,7 +792,7 @@ hipError_t launch_bwd_dx(const Shape& s, const void* X, const void* W, int K, in
   GemmArgs a{(const uint16_t*)X, (const uint16_t*)W, nullptr, out, offsets, nullptr, s.T,
              s.tok_div(), s.E, s.S, K, N, N, s.f, ksplit, out2, part_elems, 0};
   const int NT = (N + DN_BN - 1) / DN_BN;
-  grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DXB, DN_NST, DN_OCC>
+  grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DXB, DN_OCC>
       <<<grid_blocks(s, DN_BM, NT, ksplit), 64 * DN_WGM * DN_WGN, 0, st>>>(a);
   return hipGetLastError();
 }
@@ -728,9 +805,9 @@ hipError_t launch_bwd_wgrad(const Shape& s, const void* A, const void* B, int M,
              s.tok_div(), s.E, s.S, ldk, N, N, s.f, 1, nullptr, 0, M};
   const long long tiles = (long long)(s.E + s.S) * ((M + DN_BM - 1) / DN_BM) *
                           ((N + DN_BN - 1) / DN_BN);
-  long long g = MOE_PERSISTENT && tiles > kNumCUs ? kNumCUs : tiles;
+  long long g = tiles > kNumCUs ? kNumCUs : tiles;
   g = (g + 7) / 8 * 8;
-  grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_WGRAD, DN_NST, DN_OCC>
+  grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_WGRAD, DN_OCC>
       <<<(int)g, 64 * DN_WGM * DN_WGN, 0, st>>>(a);
   return hipGetLastError();
 }
