@@ -196,6 +196,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     else brow = (uint32_t)(seg < a.E ? a.sorted_assign[start + tt] / a.k : tt);
     xroff = (brow * (uint32_t)a.K + (uint32_t)(8 * g)) * 2u;
   }
+  (void)xroff;   // read by the device pass only
   int fpos[RG][NSUBK], bpos[NSUBK];
 #pragma unroll
   for (int u = 0; u < NSUBK; ++u) {

@@ -144,6 +144,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   __shared__ int seg_tile[kMaxSegments + 1];
   __shared__ int seg_nrows[kMaxSegments], seg_row0[kMaxSegments];
   __shared__ int sh_seg[2];
+  __shared__ int sh_range[2];   // WGRAD: the tile range of this block's XCD
   __shared__ uint32_t sh_bias[BIAS ? BN / 2 : 1];   // the tile's bias columns, bf16 pairs
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -201,10 +202,46 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   // Persistent blocks, one per compute unit: the blocks of XCD xcd (block b
   // runs on XCD b % 8) walk that XCD's contiguous range of tiles in steps of
   // their count, so the tiles of one expert weight stay within one L2.
+  // WGRAD tiles differ in length (a segment's k range is its padded row
+  // count: a shared expert's is every token), so there the XCD ranges split
+  // the cumulative k-tiles instead of the tile count: XCD x takes the tiles
+  // whose midpoints fall in its eighth of the k-tiles.
   const int xcd = blockIdx.x & 7, nslots = gridDim.x >> 3;
-  const int per = (total + 7) >> 3;
   int it = blockIdx.x >> 3;
-  auto tile_at = [&](int i) { return i < per && xcd * per + i < total ? xcd * per + i : -1; };
+  int wg_first = 0, wg_end = 0;
+  if (WG) {
+    if (wave == 0) {
+      const long long Ts = tiles / nseg;                          // tiles per segment
+      const long long W = (long long)(seg_kpos[nseg] / 32) * Ts;  // k-tiles of all tiles
+      const long long G = 8;
+      // tiles j of segment s with midpoint below x W / 8, for x = this XCD
+      // and the next: 8 w (2j + 1) < 2 x W - 16 C, where w is the segment's
+      // k-tiles per tile and C the k-tiles of all tiles before it
+      for (int e = 0; e < 2; ++e) {
+        const long long X0 = 2 * (long long)(xcd + e) * W;
+        long long cnt = 0;
+        for (int sg = lane; sg < nseg; sg += 64) {
+          const long long w = (seg_kpos[sg + 1] - seg_kpos[sg]) / 32;
+          const long long X = X0 - 2 * G * ((long long)(seg_kpos[sg] / 32) * Ts);
+          const long long c = X >= 1 ? ((X - 1) / (G * w) + 1) / 2 : 0;
+          cnt += c < Ts ? c : Ts;
+        }
+        int ci = (int)cnt;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) ci += __shfl_xor(ci, o);
+        if (lane == 0) sh_range[e] = ci;
+      }
+    }
+    __syncthreads();
+    wg_first = sh_range[0];
+    wg_end = sh_range[1];
+  }
+  const int per = (total + 7) >> 3;
+  auto tile_at = [&](int i) {
+    if (WG) return wg_first + i < wg_end ? wg_first + i : -1;
+    return i < per && xcd * per + i < total ? xcd * per + i : -1;
+  };
+  const int step = nslots;
   // The thread of the segment that holds tile LL records it in sh_seg[b].
   auto locate = [&](int LL, int b) {
     const int L = LL % tiles;
@@ -371,7 +408,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   // the bias and row loads too.
   int LL = tile_at(it);
   if (LL < 0) return;   // uniform over the block
-  int LL1 = tile_at(it + nslots);
+  int LL1 = tile_at(it + step);
   locate(LL, 0);
   if (LL1 >= 0) locate(LL1, 1);
   __syncthreads();
@@ -385,7 +422,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   int b = 0;         // sh_seg slot of this tile and of the tile two ahead
   for (;;) {
     const bool more = LL1 >= 0;   // uniform over the block
-    const int LL2 = more ? tile_at(it + 2 * nslots) : -1;
+    const int LL2 = more ? tile_at(it + 2 * step) : -1;
     const int nk = kslice / BK;
     auto clampk = [&](int t) { return t < nk ? t : nk - 1; };
     dma(lds1, clampk(1));
@@ -549,7 +586,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
     }
     if (!more) break;
     cur = coords(LL1, b ^ 1);
-    it += nslots;
+    it += step;
     LL1 = LL2;
     b ^= 1;
     lds_barrier();   // every wave's staging reads are done before stages 1 and 2 refill
