@@ -148,7 +148,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   __shared__ uint32_t sh_bias[BIAS ? BN / 2 : 1];   // the tile's bias columns, bf16 pairs
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % WGM, wn = wave / WGM;
+  // Wave w sits on SIMD w % 4 and takes token-row block wm = w / WGN: the
+  // two waves sharing a SIMD take different row blocks (w and w + 4), so on
+  // a tile whose valid rows end in its first half every SIMD has one wave's
+  // MFMAs to do (the waves past the last valid row skip their main loop).
+  const int wm = wave / WGN, wn = wave % WGN;
   const int nseg = a.E + a.S;
   const int NT = (a.Nout + NOUT_TILE - 1) / NOUT_TILE;
   const int off_E = a.offsets[a.E];
@@ -433,7 +437,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
     __asm__ volatile("" ::: "memory");
 
     u32x4 wf[2][NI], xf[2][MI];
-    frag_load(lds0, wf[0], xf[0], 0);
+    // this wave's token rows hold valid rows of the tile (uniform per wave)
+    const bool wact = cur.mt * BM + wm * WM < cur.rows;
     f32x16 acc[NI][MI];
 #pragma unroll
     for (int j = 0; j < NI; ++j)
@@ -486,16 +491,38 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
       mfmas(wf[(NSUB - 1) & 1], xf[(NSUB - 1) & 1]);
       sched_interleave<NM, SG_DS_READ, NFR, SG_VMEM_READ, 0>();
     };
-    int kt = 0;
-    for (; kt + 3 < nk; kt += 4) {
-      iteration(lds0, lds1, lds3, kt);
-      iteration(lds1, lds2, lds0, kt + 1);
-      iteration(lds2, lds3, lds1, kt + 2);
-      iteration(lds3, lds0, lds2, kt + 3);
+    // A wave without valid rows only issues its DMA share and keeps the
+    // block's barriers.
+    auto idle = [&](u32x4* far, int kt) {
+      dma(far, clampk(kt + NSTAGE - 1));
+      __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+    };
+    if (wact) {
+      frag_load(lds0, wf[0], xf[0], 0);
+      int kt = 0;
+      for (; kt + 3 < nk; kt += 4) {
+        iteration(lds0, lds1, lds3, kt);
+        iteration(lds1, lds2, lds0, kt + 1);
+        iteration(lds2, lds3, lds1, kt + 2);
+        iteration(lds3, lds0, lds2, kt + 3);
+      }
+      if (kt < nk) iteration(lds0, lds1, lds3, kt);
+      if (kt + 1 < nk) iteration(lds1, lds2, lds0, kt + 1);
+      if (kt + 2 < nk) iteration(lds2, lds3, lds1, kt + 2);
+    } else {
+      int kt = 0;
+      for (; kt + 3 < nk; kt += 4) {
+        idle(lds3, kt);
+        idle(lds0, kt + 1);
+        idle(lds1, kt + 2);
+        idle(lds2, kt + 3);
+      }
+      if (kt < nk) idle(lds3, kt);
+      if (kt + 1 < nk) idle(lds0, kt + 1);
+      if (kt + 2 < nk) idle(lds1, kt + 2);
     }
-    if (kt < nk) iteration(lds0, lds1, lds3, kt);
-    if (kt + 1 < nk) iteration(lds1, lds2, lds0, kt + 1);
-    if (kt + 2 < nk) iteration(lds2, lds3, lds1, kt + 2);
 
     // Every DMA (including the clamped ones past the last tile) has landed and
     // every wave's last fragment reads are done before the ring is reused;
@@ -526,6 +553,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
     constexpr int WPA = (int)(sizeof(lds0) / STG);        // waves per ring stage
     static_assert(CPR >= 1 && CPR <= 64 && 64 % CPR == 0 && 32 % RPI == 0, "staging shape");
     static_assert(WPA * (NSTAGE - 1) >= NW, "staging must fit in ring stages 1 to 3");
+    // the next tile's first k-tile and bias, the row loads of the one after
+    auto prefetch_next = [&]() {
+      const TileCoord nx = coords(LL1, b ^ 1);
+      setup(nx);
+      dma(lds0, 0);
+      bias_load(nx);
+      if (LL2 >= 0) row_loads(coords(LL2, b));
+    };
+    // (a wave without valid rows stages zeros and stores nothing)
     const int wa = wv / WPA;
     char* stg = (char*)(wa == 0 ? lds1 : wa == 1 ? lds2 : lds3) + (wv % WPA) * STG;
     const int colw = SWIGLU ? cur.nt * (BN / 2) + wn * (BN / 2 / WGN) : cur.nt * BN + wn * WN;
@@ -576,13 +612,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
         if (m < cur.rows && col < a.Nout)
           *(u32x4*)(obase + ((long long)(cur.start + m) * a.Nout + col) * ES) = val;
       }
-      if (i == 0 && more) {   // the next tile's first k-tile and bias, the row loads of the one after
-        const TileCoord nx = coords(LL1, b ^ 1);
-        setup(nx);
-        dma(lds0, 0);
-        bias_load(nx);
-        if (LL2 >= 0) row_loads(coords(LL2, b));
-      }
+      if (i == 0 && more) prefetch_next();
     }
     if (!more) break;
     cur = coords(LL1, b ^ 1);
