@@ -26,6 +26,13 @@
 // of one expert weight stay within one XCD's L2.
 #include "moe_internal.h"
 
+#ifndef MOE_SCHED_FRONT
+#define MOE_SCHED_FRONT 1
+#endif
+#ifndef MOE_SCHED_PER
+#define MOE_SCHED_PER 2   // fragment reads per MFMA at the start of a k-substep
+#endif
+
 namespace moe {
 namespace {
 
@@ -91,6 +98,23 @@ __device__ __forceinline__ void sched_interleave_pair() {
     SGB(MA, 1);
     if constexpr (I < NB) SGB(MB, (I + 1 < N) ? 1 : NB - I);
     sched_interleave_pair<N, MA, MB, NB, I + 1>();
+  }
+}
+
+// NM MFMAs; while group A lasts (NA in total), each MFMA is followed by up
+// to PER of its instructions, then each by one of group B (NB in total);
+// leftovers follow the last MFMA.  Front-loading the fragment reads gives
+// them the remaining MFMAs of the substep to complete in.
+template <int NM, int MA, int NA, int PER, int MB, int NB, int I = 0, int A = 0, int B = 0>
+__device__ __forceinline__ void sched_front() {
+  if constexpr (I < NM) {
+    SGB(SG_MFMA, 1);
+    constexpr bool last = I + 1 == NM;
+    constexpr int a = last ? NA - A : (NA - A < PER ? NA - A : PER);
+    if constexpr (a > 0) SGB(MA, a);
+    constexpr int b = last ? NB - B : ((a == 0 && NB > B) ? 1 : 0);
+    if constexpr (b > 0) SGB(MB, b);
+    sched_front<NM, MA, NA, PER, MB, NB, I + 1, A + a, B + b>();
   }
 }
 
@@ -480,7 +504,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
         mfmas(wf[s4 & 1], xf[s4 & 1]);
       }
       // substep 0: the DMA interleaved with its MFMAs and the next fragments
+#if MOE_SCHED_FRONT
+      sched_front<NM, SG_DS_READ, NFR, MOE_SCHED_PER, SG_VMEM_READ, NDMA>();
+#else
       sched_interleave<NM, SG_VMEM_READ, NDMA, SG_DS_READ, NFR>();
+#endif
 #pragma unroll
       for (int s4 = 1; s4 + 1 < NSUB; ++s4)
         sched_interleave<NM, SG_DS_READ, NFR, SG_VMEM_READ, 0>();
@@ -489,7 +517,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
       __asm__ volatile("" ::: "memory");   // no LDS read moves above the barrier
       frag_load(next_st, wf[0], xf[0], 0);
       mfmas(wf[(NSUB - 1) & 1], xf[(NSUB - 1) & 1]);
+#if MOE_SCHED_FRONT
+      sched_front<NM, SG_DS_READ, NFR, MOE_SCHED_PER, SG_VMEM_READ, 0>();
+#else
       sched_interleave<NM, SG_DS_READ, NFR, SG_VMEM_READ, 0>();
+#endif
     };
     // A wave without valid rows only issues its DMA share and keeps the
     // block's barriers.
