@@ -73,8 +73,11 @@ enum { MOE_ROUTER_BIAS = 1, MOE_EXPERT_BIAS = 2,        /* flags                
  * always-on shared experts, per-expert capacity (<= 0: unlimited).
  *
  * Limits (MOE_ERR_UNSUPPORTED beyond them): E <= 64, top_k <= 8,
- * E + S <= 128, T * (top_k + S) < 2^31; for MOE_BF16, d_model and d_ff are
- * multiples of 64.  GELU is the exact erf form; SwiGLU has no biases.
+ * E + S <= 128, T * (top_k + S) < 2^31, F1 * d_model < 2^30 (F1 = d_ff, or
+ * 2 d_ff for SwiGLU: one expert's weights); for MOE_BF16, d_model and d_ff
+ * are multiples of 64 and T * d_model, T * d_ff < 2^31 (the kernels address
+ * token rows and one expert's rows with 32-bit byte offsets).  GELU is the
+ * exact erf form; SwiGLU has no biases.
  * MOE_W_FP8 (expert weights quantized to 8 bits, 0539edu page 5.2) needs
  * MOE_BF16, T <= 16 (the weight-streaming decode path) and d_model, d_ff
  * multiples of 128.

@@ -23,9 +23,14 @@
 // every block derives the per-segment m-tile counts, their prefix sum, and its
 // own (segment, n-tile, m-tile).  Block ids are remapped so that each of the 8
 // XCDs (block b runs on XCD b % 8) gets a contiguous range of tiles: the tiles
-// of one expert weight stay within one XCD's L2.
+// of one expert weight stay within one XCD's L2.  The launch is persistent
+// (at most one block per compute unit, looping over its tiles), and a block's
+// consecutive tiles overlap: the next tile's first k-tile loads while the
+// current tile's epilogue runs.
 #include "moe_internal.h"
 
+// 1: a k-substep's fragment reads are issued first, MOE_SCHED_PER per MFMA,
+// then the DMA; 0: one DMA and one fragment read after each MFMA.
 #ifndef MOE_SCHED_FRONT
 #define MOE_SCHED_FRONT 1
 #endif

@@ -129,6 +129,11 @@ static moe_status check_problem(const moe_problem* p, Shape& s) {
   // one expert's weight matrix must stay below 4 GiB (32-bit offsets in the kernels)
   const long long f1 = p->activation == MOE_SWIGLU ? 2LL * p->d_ff : p->d_ff;
   if (f1 * p->d_model * 4 >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
+  // the grouped GEMM addresses token rows of x, and one segment's rows of h,
+  // with 32-bit byte offsets
+  if (p->dtype == MOE_BF16 && ((long long)p->T * p->d_model * 2 >= (1LL << 32) ||
+                               (long long)p->T * p->d_ff * 2 >= (1LL << 32)))
+    return MOE_ERR_UNSUPPORTED;
   s.T = p->T;
   s.d = p->d_model;
   s.f = p->d_ff;

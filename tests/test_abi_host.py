@@ -66,6 +66,9 @@ def test_workspace_size_grows_with_problem():
     (dict(num_experts=64, num_shared=65), M.MOE_ERR_UNSUPPORTED),
     (dict(d_model=100), M.MOE_ERR_UNSUPPORTED),
     (dict(d_ff=96), M.MOE_ERR_UNSUPPORTED),
+    # token rows beyond 32-bit byte offsets (T * d_model * 2 >= 2^32)
+    (dict(T=1 << 20, d_model=2048, d_ff=256, top_k=1), M.MOE_ERR_UNSUPPORTED),
+    (dict(T=1 << 18, d_model=256, d_ff=8192, top_k=1), M.MOE_ERR_UNSUPPORTED),
 ])
 def test_invalid_problems_rejected(kw, status):
     p = _problem(**kw)
@@ -75,6 +78,11 @@ def test_invalid_problems_rejected(kw, status):
 
 def test_fp32_allows_any_width():
     assert M.moe_workspace_size(_problem(dtype="f32", d_model=33, d_ff=70)) > 0
+
+
+def test_largest_token_rows_accepted():
+    # T * d_model * 2 and T * d_ff * 2 just below 2^32
+    assert M.moe_workspace_size(_problem(T=(1 << 20) - 64, d_model=2048, d_ff=256, top_k=1)) > 0
 
 
 def test_forward_rejects_before_launch():
