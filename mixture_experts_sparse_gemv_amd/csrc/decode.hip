@@ -26,8 +26,9 @@
 //
 // Up:   item = (segment, DR rows of W1) -> h columns, bias + activation.
 // Down: item = (segment, DR rows of W2 = DR columns of y, one of nsplit
-//       slices of K); the slice partials are summed in a fixed order (and the
-//       bias added) by split_reduce_kernel.
+//       slices of K); slice 0 (with the bias) writes y_exp, the others
+//       partials that are added to it in slice order (by the combine, or by
+//       part_add_kernel when y_exp must be whole).
 #include "moe_internal.h"
 
 namespace moe {
@@ -62,8 +63,9 @@ struct DecodeArgs {
   const uint16_t* X;       // up: x [T, d] bf16; down: h [rows, f] fp16
   const void* W;           // [segments][Wrows][K] bf16, or FP8 E4M3 codes
   const float* wscale;     // FP8 only: [segments][Wrows] row scales
-  const uint16_t* bias;    // up: [segments][Wrows] bf16, or null
-  void* out;               // up: h [rows, f] fp16; down: y_part [nsplit][rows][d] fp32
+  const uint16_t* bias;    // [segments][Wrows] bf16, or null (down: added by K slice 0)
+  void* out;               // up: h [rows, f] fp16; down: y_exp [rows, d] fp32 (K slice 0)
+  float* part;             // down: K slices 1.. at part + (slice - 1) * part_stride
   const int32_t* offsets;
   const int32_t* sorted_assign;
   int T, k, E, S, K, Wrows, f, nsplit, items_per_seg;
@@ -313,9 +315,18 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   }
   const long long orow = start + tl;
   if (DOWN) {
-    float* out = (float*)a.out + ks * a.part_stride + orow * a.Wrows + nt * DR + 4 * g;
+    float* out = (ks == 0 ? (float*)a.out : a.part + (ks - 1) * a.part_stride) + orow * a.Wrows +
+                 nt * DR + 4 * g;
 #pragma unroll
-    for (int q = 0; q < RG; ++q) *(f32x4*)(out + 16 * q) = acc[q];
+    for (int q = 0; q < RG; ++q) {
+      f32x4 v = acc[q];
+      if (ks == 0 && a.bias) {
+        const uint16_t* b = a.bias + (long long)seg * a.Wrows + nt * DR + 16 * q + 4 * g;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] += bf16_to_f32(b[r]);
+      }
+      *(f32x4*)(out + 16 * q) = v;
+    }
   } else if (SWIGLU) {
     _Float16* hrow = (_Float16*)a.out + orow * a.f + nt * (DR / 2) + 4 * g;
 #pragma unroll
@@ -341,36 +352,19 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   }
 }
 
-// y_exp[r, :] = sum over the K slices (in order) of y_part + b2.
-__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ y_part,
-                                                           const uint16_t* __restrict__ b_down,
-                                                           float* __restrict__ y_exp,
-                                                           const int32_t* offsets, int T, int E,
-                                                           int S, int d, int nsplit,
-                                                           long long part_stride) {
+// y_exp[r, :] += the partials of K slices 1 .. nparts, in slice order.
+__global__ __launch_bounds__(256) void part_add_kernel(float* __restrict__ y_exp,
+                                                       const float* __restrict__ y_part,
+                                                       const int32_t* offsets, int T, int E,
+                                                       int S, int d, int nparts,
+                                                       long long part_stride) {
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const int d4 = d / 4;
   const long long r = gid / d4;
   const int c = (int)(gid % d4) * 4;
-  const int off_E = offsets[E];
-  if (r >= (long long)off_E + (long long)S * T) return;
-  f32x4 acc = *(const f32x4*)(y_part + r * d + c);
-  for (int ks = 1; ks < nsplit; ++ks) acc += *(const f32x4*)(y_part + ks * part_stride + r * d + c);
-  if (b_down) {
-    int seg;
-    if (r < off_E) {
-      int lo = 0, hi = E;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (offsets[mid] <= r) lo = mid; else hi = mid;
-      }
-      seg = lo;
-    } else {
-      seg = E + (int)((r - off_E) / T);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += bf16_to_f32(b_down[(long long)seg * d + c + i]);
-  }
+  if (r >= (long long)offsets[E] + (long long)S * T) return;
+  f32x4 acc = *(const f32x4*)(y_exp + r * d + c);
+  for (int p = 0; p < nparts; ++p) acc += *(const f32x4*)(y_part + p * part_stride + r * d + c);
   *(f32x4*)(y_exp + r * d + c) = acc;
 }
 
@@ -384,7 +378,7 @@ hipError_t launch_decode_up(const Shape& s, const void* x, const void* w_up, con
   const int items_per_seg = s.act == MOE_SWIGLU ? s.f / (DR / 2) : s.f / DR;
   const long long items = (long long)nseg * items_per_seg;
   DecodeArgs a{(const uint16_t*)x, w_up, s_up,
-               s.expert_bias() ? (const uint16_t*)b_up : nullptr, h, offsets, sorted_assign,
+               s.expert_bias() ? (const uint16_t*)b_up : nullptr, h, nullptr, offsets, sorted_assign,
                s.T, s.tok_div(), s.E, s.S, s.d, s.up_rows(), s.f, 1, items_per_seg, 0,
                (long long)s.T * s.d * 2};
 #define MOE_DECODE_UP(A, F)                                      \
@@ -402,29 +396,32 @@ hipError_t launch_decode_up(const Shape& s, const void* x, const void* w_up, con
   return hipGetLastError();
 }
 
-hipError_t launch_decode_down(const Shape& s, const void* h, const void* w_down,
-                              const void* b_down, const float* s_down, const int32_t* offsets,
-                              float* y_exp, float* y_part, hipStream_t st) {
-  const int nseg = s.E + s.S;
+int decode_nsplit(const Shape& s) {
   // K slices of a whole number of stages (64 elements; 128 for FP8 weights)
   const int sk = s.w_fp8() ? 128 : 64;
-  const int nsplit = (s.f % (sk * kDecodeSplitK) == 0) ? kDecodeSplitK
-                     : (s.f % (2 * sk) == 0 ? 2 : 1);
+  return (s.f % (sk * kDecodeSplitK) == 0) ? kDecodeSplitK : (s.f % (2 * sk) == 0 ? 2 : 1);
+}
+
+hipError_t launch_decode_down(const Shape& s, const void* h, const void* w_down,
+                              const void* b_down, const float* s_down, const int32_t* offsets,
+                              float* y_exp, float* y_part, bool complete, hipStream_t st) {
+  const int nseg = s.E + s.S;
+  const int nsplit = decode_nsplit(s);
   const int DR = s.w_fp8() ? DecodeTile<true>::DR : DecodeTile<false>::DR;
   const int items_per_seg = (s.d / DR) * nsplit;
   const long long items = (long long)nseg * items_per_seg;
   const long long part_stride = s.max_rows() * s.d;
-  DecodeArgs a{(const uint16_t*)h, w_down, s_down, nullptr, y_part, offsets, nullptr,
+  const uint16_t* b = s.expert_bias() ? (const uint16_t*)b_down : nullptr;
+  DecodeArgs a{(const uint16_t*)h, w_down, s_down, b, y_exp, y_part, offsets, nullptr,
                s.T, s.tok_div(), s.E, s.S, s.f, s.d, s.f, nsplit, items_per_seg, part_stride,
                s.max_rows() * s.f * 2};
   if (s.w_fp8()) decode_kernel<DEC_DOWN, true><<<(int)items, 64, 0, st>>>(a);
   else decode_kernel<DEC_DOWN, false><<<(int)items, 64, 0, st>>>(a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !complete || nsplit == 1) return e;
   const long long n = s.max_rows() * (s.d / 4);
-  const uint16_t* b = s.expert_bias() ? (const uint16_t*)b_down : nullptr;
-  split_reduce_kernel<<<(int)((n + 255) / 256), 256, 0, st>>>(y_part, b, y_exp, offsets, s.T, s.E,
-                                                             s.S, s.d, nsplit, part_stride);
+  part_add_kernel<<<(int)((n + 255) / 256), 256, 0, st>>>(y_exp, y_part, offsets, s.T, s.E, s.S,
+                                                         s.d, nsplit - 1, part_stride);
   return hipGetLastError();
 }
 

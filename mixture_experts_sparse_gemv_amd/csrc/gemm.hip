@@ -793,12 +793,14 @@ int down_ksplit(const Shape& s) {
 
 int bwd_dx_ksplit(const Shape& s) { return gemm_ksplit(s, s.up_rows(), s.d); }
 
+int down_parts(const Shape& s) { return s.decode() ? decode_nsplit(s) - 1 : down_ksplit(s) - 1; }
+
 hipError_t launch_decode_up(const Shape& s, const void* x, const void* w_up, const void* b_up,
                             const float* s_up, const int32_t* offsets,
                             const int32_t* sorted_assign, void* h, hipStream_t st);
 hipError_t launch_decode_down(const Shape& s, const void* h, const void* w_down,
                               const void* b_down, const float* s_down, const int32_t* offsets,
-                              float* y_exp, float* y_part, hipStream_t st);
+                              float* y_exp, float* y_part, bool complete, hipStream_t st);
 
 hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void* b_up,
                      const float* s_up, const int32_t* offsets, const int32_t* sorted_assign,
@@ -857,7 +859,7 @@ hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const 
     return hipGetLastError();
   }
   if (s.decode())
-    return launch_decode_down(s, h, w_down, b_down, s_down, offsets, y_exp, y_part, st);
+    return launch_decode_down(s, h, w_down, b_down, s_down, offsets, y_exp, y_part, complete, st);
   const int ks = down_ksplit(s);
   const long long part_elems = s.max_rows() * s.d;
   GemmArgs a{(const uint16_t*)h, (const uint16_t*)w_down, (const uint16_t*)bias, y_exp, offsets,

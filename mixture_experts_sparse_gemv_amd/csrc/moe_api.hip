@@ -44,7 +44,7 @@ WsLayout ws_layout(const Shape& s) {
   w.l_aux = take(4);
   w.h = take(rows * s.f * (s.dtype == MOE_F32 ? 4 : 2));
   w.y_exp = take(rows * s.d * 4);
-  const int nparts = s.decode() ? kDecodeSplitK : down_ksplit(s) - 1;
+  const int nparts = down_parts(s);
   w.y_part = nparts > 0 ? take((size_t)nparts * rows * s.d * 4) : o;
   w.total = o;
   return w;
@@ -382,7 +382,7 @@ moe_status moe_ffn_forward(const moe_problem* p, const moe_weights* w, const voi
     e = launch_up(s, x, w->w_up, w->b_up, w->s_up, offsets, sorted_assign, h, stream);
   // The down projection's K slices (if any) are summed by the combine.
   float* y_part = at<float>(ws, L.y_part);
-  const int nparts = s.decode() ? 0 : down_ksplit(s) - 1;
+  const int nparts = down_parts(s);
   if (e == hipSuccess)
     e = launch_down(s, h, w->w_down, w->b_down, w->s_down, offsets, y_exp, y_part, nparts == 0, stream);
   if (e == hipSuccess)

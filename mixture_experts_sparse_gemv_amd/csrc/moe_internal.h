@@ -53,6 +53,12 @@ constexpr int kDecodeSplitK = 4;
 // is written to y_exp, slice i > 0 to y_part + (i - 1) * max_rows * d, and
 // the slices are summed in slice order (by the combine, or by a fold pass).
 int down_ksplit(const Shape& s);
+// K slices of the decode down projection (slice 0 into y_exp with the bias,
+// slice i > 0 into y_part + (i - 1) * max_rows * d_model).
+int decode_nsplit(const Shape& s);
+// Partial slices of the down projection that y_part holds for the combine
+// when launch_down runs with complete = false.
+int down_parts(const Shape& s);
 
 // ---------------------------------------------------------------- workspace
 struct WsLayout {
@@ -166,8 +172,8 @@ hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void
                      const float* s_up, const int32_t* offsets, const int32_t* sorted_assign,
                      void* h, hipStream_t st);
 // complete = true: y_exp holds the whole result on return (K slices folded);
-// false: slices 1.. stay in y_part for the combine to add (down_ksplit(s) - 1
-// of them).
+// false: slices 1.. stay in y_part for the combine to add (down_parts(s) of
+// them).
 hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const void* b_down,
                        const float* s_down, const int32_t* offsets, float* y_exp, float* y_part,
                        bool complete, hipStream_t st);
