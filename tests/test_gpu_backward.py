@@ -40,6 +40,8 @@ CASES = {
     "all_experts": (scaled(RUNS["gpt2"], T=200, d_model=256, d_ff=256, top_k=8), 0.1),
     "capacity_one": (scaled(RUNS["gpt2"], T=300, d_model=256, d_ff=256, capacity_factor=0.01),
                      0.1),
+    # long shared-expert reductions (4500 rows each) next to short routed ones
+    "fine_shared_T4500": (scaled(RUNS["fine_shared"], T=4500, d_model=256, d_ff=128), 0.01),
 }
 
 
