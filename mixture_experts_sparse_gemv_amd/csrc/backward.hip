@@ -10,7 +10,7 @@
 // returns, instead of being stored by it:
 //   Z  = x_rows W1^T + b1                 grouped GEMM, fp32 [rows, F1]
 //   G  = dy_rows W2                        grouped GEMM against W2 transposed
-//   per tile of 32 rows x 64 columns of h: h = act(Z), dZ = act'(Z) * (w G)
+//   per tile of 64 rows x 64 columns of h: h = act(Z), dZ = act'(Z) * (w G)
 //            (SwiGLU: [w G u silu'(g); w G silu(g)]), written row-major and
 //            transposed, and the partial sums of <h, G>; the gate weight's
 //            gradient dw = (sum of the partials) + <b2, dy>
@@ -117,65 +117,80 @@ __global__ __launch_bounds__(64) void wgrad_offsets_kernel(const int32_t* __rest
 
 // out[c][poff[seg] + i] = scale(row) * src[token(row)][c] for the segment's
 // rows i (bf16), 0 in the padding.  SRC32: fp32 source (else bf16); SCALE:
-// times the row's gate weight.  Block = 32 padded rows x 64 columns.
+// times the row's gate weight.  Block = 64 padded rows (two 32-row halves,
+// each inside one segment) x 64 columns; thread = a pair of adjacent rows x 8
+// columns, staged in LDS as [column][row pair] bf16 pairs so each output row
+// leaves as 128 contiguous bytes written by 8 lanes.
+constexpr int ST_R = 64;   // padded rows per block
 template <bool SRC32, bool SCALE>
 __global__ __launch_bounds__(256) void seg_transpose_kernel(
     const void* __restrict__ src, int C, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_assign, const float* __restrict__ topk_w,
     const int32_t* __restrict__ poff, int T, int k, int E, int S, uint16_t* __restrict__ out,
     int ldk) {
-  __shared__ uint16_t tile[32][64 + 2];
-  __shared__ int sh_seg;
-  const int p0 = blockIdx.x * 32, c0 = blockIdx.y * 64;
+  constexpr int PW = ST_R / 2 + 4;   // words per staged column: 32 row pairs + 16 bytes
+  __shared__ uint32_t tile[64][PW];
+  __shared__ int sh_seg[2];
+  const int p0 = blockIdx.x * ST_R, c0 = blockIdx.y * 64;
   const int tid = threadIdx.x;
   const int nseg = E + S;
-  if (p0 >= poff[nseg]) return;   // beyond the used columns (uniform)
-  if (tid < nseg && poff[tid] <= p0 && p0 < poff[tid + 1]) sh_seg = tid;
-  __syncthreads();
-  const int seg = sh_seg;
-  const int rows = seg < E ? offsets[seg + 1] - offsets[seg] : T;
-  const int base = seg < E ? offsets[seg] : offsets[E] + (seg - E) * T;
-  {
-    const int ri = tid / 8, cq = (tid % 8) * 8;
-    const int i = p0 - poff[seg] + ri;
-    float v[8];
-    if (i < rows) {
-      const int r = base + i;
-      int srow = i;   // shared expert: row i is token i
-      float sc = 1.0f;
-      if (seg < E) {
-        const int a = sorted_assign[r];
-        srow = a / k;
-        if (SCALE) sc = topk_w[a];
-      }
-      if (SRC32) {
-        const float* sp = (const float*)src + (long long)srow * C + c0 + cq;
-        const f32x4 a0 = *(const f32x4*)sp, a1 = *(const f32x4*)(sp + 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = a0[j] * sc, v[4 + j] = a1[j] * sc;
-      } else {
-        const u32x4 a = *(const u32x4*)((const uint16_t*)src + (long long)srow * C + c0 + cq);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[2 * j] = __uint_as_float(a[j] << 16) * sc;
-          v[2 * j + 1] = __uint_as_float(a[j] & 0xffff0000u) * sc;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) tile[ri][cq + j] = f32_to_bf16_rne(v[j]);
+  const int pend = poff[nseg];   // end of the used columns (a multiple of 32)
+  if (p0 >= pend) return;        // uniform
+  if (tid < nseg) {
+    const int lo = poff[tid], hi = poff[tid + 1];
+    if (lo <= p0 && p0 < hi) sh_seg[0] = tid;
+    if (lo <= p0 + 32 && p0 + 32 < hi) sh_seg[1] = tid;
   }
   __syncthreads();
-  // write 64 output rows (columns of the source) x 32 padded rows: 4 threads per row
-  const int cc = tid / 4, part = (tid % 4) * 8;
-  u32x4 o;
+  const int pr = tid / 8, cq = (tid % 8) * 8;   // row pair, first of 8 columns
+  const int hf = pr >> 4;                       // the 32-row half (uniform per wave)
+  const bool used = p0 + 32 * hf < pend;
+  const int seg = used ? sh_seg[hf] : 0;
+  const int rows = seg < E ? offsets[seg + 1] - offsets[seg] : T;
+  const int base = seg < E ? offsets[seg] : offsets[E] + (seg - E) * T;
+  float v[2][8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    o[j] = (uint32_t)tile[part + 2 * j][cc] | ((uint32_t)tile[part + 2 * j + 1][cc] << 16);
-  *(u32x4*)(out + (long long)(c0 + cc) * ldk + p0 + part) = o;
+  for (int rr = 0; rr < 2; ++rr) {
+    const int i = p0 + 2 * pr + rr - poff[seg];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[rr][j] = 0.0f;
+    if (!used || i >= rows) continue;
+    const int r = base + i;
+    int srow = i;   // shared expert: row i is token i
+    float sc = 1.0f;
+    if (seg < E) {
+      const int a = sorted_assign[r];
+      srow = a / k;
+      if (SCALE) sc = topk_w[a];
+    }
+    if (SRC32) {
+      const float* sp = (const float*)src + (long long)srow * C + c0 + cq;
+      const f32x4 a0 = *(const f32x4*)sp, a1 = *(const f32x4*)(sp + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[rr][j] = a0[j] * sc, v[rr][4 + j] = a1[j] * sc;
+    } else {
+      const u32x4 a = *(const u32x4*)((const uint16_t*)src + (long long)srow * C + c0 + cq);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[rr][2 * j] = __uint_as_float(a[j] << 16) * sc;
+        v[rr][2 * j + 1] = __uint_as_float(a[j] & 0xffff0000u) * sc;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    tile[cq + j][pr] = (uint32_t)f32_to_bf16_rne(v[0][j]) | ((uint32_t)f32_to_bf16_rne(v[1][j]) << 16);
+  __syncthreads();
+  // output row cc, rows p0 + 8 ch .. + 7 (16 bytes); chunks past the used
+  // columns (whole 32-row halves) are not written
+  const int ch = tid & 7;
+  if (p0 + 8 * ch < pend) {
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int cc = (tid >> 3) + 32 * pass;
+      *(u32x4*)(out + (long long)(c0 + cc) * ldk + p0 + 8 * ch) = *(const u32x4*)&tile[cc][4 * ch];
+    }
+  }
 }
 
 // db[seg][c] = sum over the segment's padded columns of M[c][.] (bf16), in
@@ -221,15 +236,20 @@ __device__ __forceinline__ float gelu_grad_f(float z) {
   return fmaf(z, pdf, cdf);
 }
 
-// One block per 32 padded rows of one segment (the weight-gradient layout
-// of wgrad_offsets_kernel) and 64 columns c of h.  For each row it forms
-// h = act(Z), dZ = act'(Z) w G (SwiGLU: the gate and the up column) and the
-// partial sum <h, G> over its 64 columns; it writes dZ row-major (the dX
-// product's operand) and both transposed weight-gradient operands, dZ^T
+// One block per 64 padded rows (the weight-gradient layout of
+// wgrad_offsets_kernel: segments start at multiples of 32, so each 32-row
+// half of the block lies in one segment) and 64 columns c of h.  For each row
+// it forms h = act(Z), dZ = act'(Z) w G (SwiGLU: the gate and the up column)
+// and the partial sum <h, G> over its 64 columns; it writes dZ row-major (the
+// dX product's operand) and both transposed weight-gradient operands, dZ^T
 // into A1 [F1][ldk] and h^T into B2 [f][ldk] (zero in the padding rows), so
-// no separate transposes are needed.  dwpart[row][c / 64] holds the partial
-// sums of routed rows; slot_grad_kernel adds them in column order.
+// no separate transposes are needed.  Thread = a pair of adjacent rows x 8
+// columns; the pairs are staged in LDS as [column][row pair] bf16 pairs, so
+// each transposed row leaves as 128 contiguous bytes written by 8 lanes.
+// dwpart[row][c / 64] holds the partial sums of routed rows;
+// slot_grad_kernel adds them in column order.
 constexpr int AB_C = 64;   // columns of h per block
+constexpr int AB_R = 64;   // padded rows per block
 template <int ACT>
 __global__ __launch_bounds__(256) void act_backward_kernel(
     const float* __restrict__ Z, const float* __restrict__ G, const int32_t* __restrict__ offsets,
@@ -238,26 +258,36 @@ __global__ __launch_bounds__(256) void act_backward_kernel(
     uint16_t* __restrict__ dZ, uint16_t* __restrict__ A1, uint16_t* __restrict__ B2,
     float* __restrict__ dwpart, int nparts) {
   constexpr bool SWIGLU = ACT == MOE_SWIGLU;
-  __shared__ uint16_t th[32][AB_C + 2], tz[32][AB_C + 2], tu[SWIGLU ? 32 : 1][AB_C + 2];
-  __shared__ int sh_seg;
-  const int p0 = blockIdx.x * 32, c0 = blockIdx.y * AB_C;
+  constexpr int PW = AB_R / 2 + 4;   // words per staged column: 32 row pairs + 16 bytes
+  __shared__ uint32_t th[AB_C][PW], tz[AB_C][PW], tu[SWIGLU ? AB_C : 1][PW];
+  __shared__ int sh_seg[2];
+  const int p0 = blockIdx.x * AB_R, c0 = blockIdx.y * AB_C;
   const int tid = threadIdx.x;
   const int nseg = E + S;
-  if (p0 >= poff[nseg]) return;   // beyond the used columns (uniform)
-  if (tid < nseg && poff[tid] <= p0 && p0 < poff[tid + 1]) sh_seg = tid;
+  const int pend = poff[nseg];   // end of the used columns (a multiple of 32)
+  if (p0 >= pend) return;        // uniform
+  if (tid < nseg) {
+    const int lo = poff[tid], hi = poff[tid + 1];
+    if (lo <= p0 && p0 < hi) sh_seg[0] = tid;
+    if (lo <= p0 + 32 && p0 + 32 < hi) sh_seg[1] = tid;
+  }
   __syncthreads();
-  const int seg = sh_seg;
+  const int pr = tid >> 3, cq = (tid & 7) * 8;   // row pair, first of 8 columns
+  const int hf = pr >> 4;                        // the 32-row half (uniform per wave)
+  const bool used = p0 + 32 * hf < pend;
+  const int seg = used ? sh_seg[hf] : 0;
   const int rows = seg < E ? offsets[seg + 1] - offsets[seg] : T;
   const int base = seg < E ? offsets[seg] : offsets[E] + (seg - E) * T;
   const int F1 = SWIGLU ? 2 * f : f;
-  const int ri = tid >> 3, cq = (tid & 7) * 8;   // row of the tile, first of 8 columns
-  const int i = p0 - poff[seg] + ri;
-  const bool valid = i < rows;
-  const long long r = base + i;
-  float h[8], dz[8], du[8], dot = 0.0f;
+  float h[2][8], dz[2][8], du[2][8], dot[2];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) h[q] = dz[q] = du[q] = 0.0f;
-  if (valid) {
+  for (int rr = 0; rr < 2; ++rr) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) h[rr][q] = dz[rr][q] = du[rr][q] = 0.0f;
+    dot[rr] = 0.0f;
+    const int i = p0 + 2 * pr + rr - poff[seg];
+    if (!used || i >= rows) continue;
+    const long long r = base + i;
     const float wgt = seg < E ? topk_w[sorted_assign[r]] : 1.0f;
     const float* zr = Z + r * F1 + c0 + cq;
     const float* gr = G + r * f + c0 + cq;
@@ -271,54 +301,67 @@ __global__ __launch_bounds__(256) void act_backward_kernel(
       const float g = q < 4 ? g0[q] : g1[q - 4];
       const float wg = wgt * g;
       if (ACT == MOE_RELU) {
-        h[q] = fmaxf(z, 0.0f);
-        dz[q] = z > 0.0f ? wg : 0.0f;
+        h[rr][q] = fmaxf(z, 0.0f);
+        dz[rr][q] = z > 0.0f ? wg : 0.0f;
       } else if (ACT == MOE_GELU) {
-        h[q] = gelu_f(z);
-        dz[q] = wg * gelu_grad_f(z);
+        h[rr][q] = gelu_f(z);
+        dz[rr][q] = wg * gelu_grad_f(z);
       } else {
         const float u = q < 4 ? u0[q] : u1[q - 4];
         const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp(-z));
         const float si = z * sg;
-        h[q] = si * u;
-        dz[q] = wg * u * sg * fmaf(z, 1.0f - sg, 1.0f);
-        du[q] = wg * si;
+        h[rr][q] = si * u;
+        dz[rr][q] = wg * u * sg * fmaf(z, 1.0f - sg, 1.0f);
+        du[rr][q] = wg * si;
       }
-      dot = fmaf(h[q], g, dot);
+      dot[rr] = fmaf(h[rr][q], g, dot[rr]);
     }
     u32x4 zo, uo;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      zo[q] = (uint32_t)f32_to_bf16_rne(dz[2 * q]) | ((uint32_t)f32_to_bf16_rne(dz[2 * q + 1]) << 16);
-      uo[q] = (uint32_t)f32_to_bf16_rne(du[2 * q]) | ((uint32_t)f32_to_bf16_rne(du[2 * q + 1]) << 16);
+      zo[q] = (uint32_t)f32_to_bf16_rne(dz[rr][2 * q]) |
+              ((uint32_t)f32_to_bf16_rne(dz[rr][2 * q + 1]) << 16);
+      uo[q] = (uint32_t)f32_to_bf16_rne(du[rr][2 * q]) |
+              ((uint32_t)f32_to_bf16_rne(du[rr][2 * q + 1]) << 16);
     }
     *(u32x4*)(dZ + r * F1 + c0 + cq) = zo;
     if (SWIGLU) *(u32x4*)(dZ + r * F1 + f + c0 + cq) = uo;
   }
-  // the row's partial <h, G>: its 8 threads are consecutive lanes
-  dot += __shfl_xor(dot, 1);
-  dot += __shfl_xor(dot, 2);
-  dot += __shfl_xor(dot, 4);
-  if (valid && seg < E && (tid & 7) == 0) dwpart[r * nparts + blockIdx.y] = dot;
+  // each row's partial <h, G>: its 8 threads are consecutive lanes
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    float v = dot[rr];
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    const int i = p0 + 2 * pr + rr - poff[seg];
+    if (used && i < rows && seg < E && (tid & 7) == 0)
+      dwpart[(base + i) * (long long)nparts + blockIdx.y] = v;
+  }
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    th[ri][cq + q] = f32_to_bf16_rne(h[q]);
-    tz[ri][cq + q] = f32_to_bf16_rne(dz[q]);
-    if (SWIGLU) tu[ri][cq + q] = f32_to_bf16_rne(du[q]);
+    th[cq + q][pr] = (uint32_t)f32_to_bf16_rne(h[0][q]) | ((uint32_t)f32_to_bf16_rne(h[1][q]) << 16);
+    tz[cq + q][pr] =
+        (uint32_t)f32_to_bf16_rne(dz[0][q]) | ((uint32_t)f32_to_bf16_rne(dz[1][q]) << 16);
+    if (SWIGLU)
+      tu[cq + q][pr] =
+          (uint32_t)f32_to_bf16_rne(du[0][q]) | ((uint32_t)f32_to_bf16_rne(du[1][q]) << 16);
   }
   __syncthreads();
-  // transposed: 64 output rows (columns of h) x 32 padded rows, 4 threads per row
-  const int cc = tid >> 2, part = (tid & 3) * 8;
-  u32x4 vh, vz, vu;
+  // transposed: column cc, rows p0 + 8 ch .. + 7 (16 bytes); a column's 8
+  // chunks are 8 consecutive lanes.  Chunks past the used columns (whole
+  // 32-row halves) are not written.
+  const int ch = tid & 7;
+  if (p0 + 8 * ch < pend) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    vh[q] = (uint32_t)th[part + 2 * q][cc] | ((uint32_t)th[part + 2 * q + 1][cc] << 16);
-    vz[q] = (uint32_t)tz[part + 2 * q][cc] | ((uint32_t)tz[part + 2 * q + 1][cc] << 16);
-    if (SWIGLU) vu[q] = (uint32_t)tu[part + 2 * q][cc] | ((uint32_t)tu[part + 2 * q + 1][cc] << 16);
+    for (int pass = 0; pass < 2; ++pass) {
+      const int cc = (tid >> 3) + 32 * pass;
+      const long long o = (long long)(c0 + cc) * ldk + p0 + 8 * ch;
+      *(u32x4*)(B2 + o) = *(const u32x4*)&th[cc][4 * ch];
+      *(u32x4*)(A1 + o) = *(const u32x4*)&tz[cc][4 * ch];
+      if (SWIGLU) *(u32x4*)(A1 + (long long)f * ldk + o) = *(const u32x4*)&tu[cc][4 * ch];
+    }
   }
-  *(u32x4*)(B2 + (long long)(c0 + cc) * ldk + p0 + part) = vh;
-  *(u32x4*)(A1 + (long long)(c0 + cc) * ldk + p0 + part) = vz;
-  if (SWIGLU) *(u32x4*)(A1 + (long long)(f + c0 + cc) * ldk + p0 + part) = vu;
 }
 
 // dwslot[t*k + s] = <h, G> + <b2_e, dy_t> for a kept slot (0 if dropped):
@@ -611,7 +654,7 @@ hipError_t launch_seg_transpose(const Shape& s, int kind, const void* src, int C
                                 const int32_t* offsets, const int32_t* sorted_assign,
                                 const float* topk_w, const int32_t* poff, uint16_t* out, int ldk,
                                 hipStream_t st) {
-  const dim3 grid(ldk / 32, C / 64);
+  const dim3 grid((ldk + ST_R - 1) / ST_R, C / 64);
   if (kind == 0)
     seg_transpose_kernel<true, true><<<grid, 256, 0, st>>>(
         src, C, offsets, sorted_assign, topk_w, poff, s.T, s.k, s.E, s.S, out, ldk);
@@ -635,7 +678,7 @@ hipError_t launch_act_backward(const Shape& s, const float* Z, const float* G, c
                                const int32_t* poff, const int32_t* assign_row,
                                const int32_t* topk_idx, int ldk, uint16_t* dZ, uint16_t* A1,
                                uint16_t* B2, float* dwpart, float* dwslot, hipStream_t st) {
-  const dim3 grid(ldk / 32, s.f / AB_C);
+  const dim3 grid((ldk + AB_R - 1) / AB_R, s.f / AB_C);
   const int nparts = s.f / AB_C;
   const uint16_t* b2 = (const uint16_t*)b_down;
 #define MOE_ACT_BWD(A)                                                                          \
