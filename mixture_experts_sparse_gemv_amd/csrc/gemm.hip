@@ -186,33 +186,51 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   const int NT = (a.Nout + NOUT_TILE - 1) / NOUT_TILE;
   const int off_E = a.offsets[a.E];
 
-  // ---- tile schedule: prefix sum of m-tiles per segment (wave 0, 2 segments
-  // per lane), with each segment's row count and first row.  WGRAD: every
-  // segment has the same M tiles; the prefix is that of the padded row counts
-  // (the segment's k range), kept in seg_kpos.
+  // ---- tile schedule (wave 0, 2 segments per lane): each segment's row
+  // count and first row, and two prefix sums over the segments.  A tile whose
+  // rows fill at most half of BM (a segment's last, ragged m-tile) keeps only
+  // the waves of its first half busy, about half the time of a full tile: such
+  // "light" tiles form a list of their own (seg_lt: prefix of their count),
+  // the others are "heavy" (seg_tile: prefix of heavy m-tiles; a segment's
+  // light tile comes after its heavy ones).  Without the split seg_tile is
+  // the prefix of all m-tiles and the light list is empty.  WGRAD: every segment has the
+  // same M tiles; the prefix is that of the padded row counts (the segment's
+  // k range), kept in seg_kpos.
   __shared__ int seg_kpos[WG ? kMaxSegments + 1 : 1];
+  __shared__ int seg_lt[WG ? 1 : kMaxSegments + 1];
+  const int nsplit = KSPLIT ? a.ksplit : 1;
+  const int nslots = gridDim.x >> 3;   // blocks per XCD
   if (wave == 0) {
-    int c0 = 0, c1 = 0, r, st;
+    int c0 = 0, c1 = 0, l0 = 0, l1 = 0, r, st;
     const int s0 = 2 * lane, s1 = 2 * lane + 1;
+    auto classify = [&](int rr, int& c, int& l) {
+      if (WG) {
+        c = wgrad_pad(rr);
+      } else {
+        const int rag = rr % BM;
+        c = rr / BM + (rag > BM / 2 ? 1 : 0);
+        l = (rag > 0 && rag <= BM / 2) ? 1 : 0;
+      }
+    };
     if (s0 < nseg) {
       segment_rows(a, s0, off_E, r, st);
-      c0 = WG ? wgrad_pad(r) : (r + BM - 1) / BM;
+      classify(r, c0, l0);
       seg_nrows[s0] = r;
       seg_row0[s0] = st;
     }
     if (s1 < nseg) {
       segment_rows(a, s1, off_E, r, st);
-      c1 = WG ? wgrad_pad(r) : (r + BM - 1) / BM;
+      classify(r, c1, l1);
       seg_nrows[s1] = r;
       seg_row0[s1] = st;
     }
-    int v = c0 + c1, incl = v;
+    int v = c0 + c1, incl = v, lv = l0 + l1, lincl = lv;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      int u = __shfl_up(incl, o);
-      if (lane >= o) incl += u;
+      const int u = __shfl_up(incl, o), lu = __shfl_up(lincl, o);
+      if (lane >= o) incl += u, lincl += lu;
     }
-    const int excl = incl - v;
+    const int excl = incl - v, lexcl = lincl - lv;
     if (WG) {
       const int mtw = (a.M + BM - 1) / BM;
       if (s0 < nseg) seg_kpos[s0] = excl;
@@ -222,24 +240,35 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
       if (s1 < nseg) seg_tile[s1] = s1 * mtw;
       if (lane == 63) seg_tile[nseg] = nseg * mtw;
     } else {
-      if (s0 < nseg) seg_tile[s0] = excl;
-      if (s1 < nseg) seg_tile[s1] = excl + c0;
-      if (lane == 63) seg_tile[nseg] = incl;
+      // The two lists are kept apart only when that lowers the number of
+      // rounds of heavy tiles per block; otherwise every tile is "heavy":
+      // one list in segment order, a segment's last tile after its others.
+      const int nh = __shfl(incl, 63), nl = __shfl(lincl, 63);
+      const int h = nh * NT * nsplit, all = (nh + nl) * NT * nsplit;
+      const bool two = ((h + 7) / 8 + nslots - 1) / nslots < ((all + 7) / 8 + nslots - 1) / nslots;
+      const int pe = two ? excl : excl + lexcl, pi = two ? incl : incl + lincl;
+      if (s0 < nseg) seg_tile[s0] = pe, seg_lt[s0] = lexcl;
+      if (s1 < nseg) seg_tile[s1] = pe + c0 + (two ? 0 : l0), seg_lt[s1] = lexcl + l0;
+      if (lane == 63) seg_tile[nseg] = pi, seg_lt[nseg] = two ? lincl : 0;
     }
   }
   __syncthreads();
-  // Tiles per K slice; with several slices the slice is the slowest index.
-  const int nsplit = KSPLIT ? a.ksplit : 1;
+  // Heavy and light tiles per K slice; with several slices the slice is the
+  // slowest index of each list.  Tile ids: the heavy list, then the light.
   const int tiles = seg_tile[nseg] * NT;
-  const int total = tiles * nsplit;
+  const int ltiles = WG ? 0 : seg_lt[nseg] * NT;
+  const int nheavy = tiles * nsplit, nlight = ltiles * nsplit;
   // Persistent blocks, one per compute unit: the blocks of XCD xcd (block b
-  // runs on XCD b % 8) walk that XCD's contiguous range of tiles in steps of
-  // their count, so the tiles of one expert weight stay within one L2.
+  // runs on XCD b % 8) walk that XCD's sequence of tiles in steps of their
+  // count: its contiguous eighth of the heavy list (so the tiles of one
+  // expert weight stay within one L2), then its eighth of the light list.
+  // Every XCD thus gets the same number of heavy tiles and of light tiles,
+  // and light tiles come last, where they fill the last round unevenly.
   // WGRAD tiles differ in length (a segment's k range is its padded row
   // count: a shared expert's is every token), so there the XCD ranges split
   // the cumulative k-tiles instead of the tile count: XCD x takes the tiles
   // whose midpoints fall in its eighth of the k-tiles.
-  const int xcd = blockIdx.x & 7, nslots = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7;
   int it = blockIdx.x >> 3;
   int wg_first = 0, wg_end = 0;
   if (WG) {
@@ -269,25 +298,47 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
     wg_first = sh_range[0];
     wg_end = sh_range[1];
   }
-  const int per = (total + 7) >> 3;
+  const int per = (nheavy + 7) >> 3, lper = (nlight + 7) >> 3;
+  const int hlen = min(max(nheavy - xcd * per, 0), per);
+  const int llen = min(max(nlight - xcd * lper, 0), lper);
   auto tile_at = [&](int i) {
     if (WG) return wg_first + i < wg_end ? wg_first + i : -1;
-    return i < per && xcd * per + i < total ? xcd * per + i : -1;
+    if (i < hlen) return xcd * per + i;
+    i -= hlen;
+    return i < llen ? nheavy + xcd * lper + i : -1;
   };
   const int step = nslots;
   // The thread of the segment that holds tile LL records it in sh_seg[b].
+  // A tile id decodes the same way in either list: the list's prefix of
+  // m-tiles per segment (heavy: seg_tile; light: seg_lt, 0 or 1 per
+  // segment), its tiles per K slice and its first id; a light tile's m-tile
+  // index follows its segment's heavy ones.  The thread of the segment that
+  // holds tile LL records the segment and the tile's K slice, n-tile and
+  // m-tile in slot b.
+  __shared__ int sh_coord[2][3];
   auto locate = [&](int LL, int b) {
-    const int L = LL % tiles;
-    if (tid < nseg && seg_tile[tid] * NT <= L && L < seg_tile[tid + 1] * NT) sh_seg[b] = tid;
+    const bool lt = !WG && LL >= nheavy;
+    const int* P = lt ? seg_lt : seg_tile;
+    const int i = LL - (lt ? nheavy : 0), tl = lt ? ltiles : tiles;
+    const int ks = KSPLIT ? i / tl : 0;   // one K slice: i < tl
+    const int L = i - ks * tl;
+    if (tid < nseg && P[tid] * NT <= L && L < P[tid + 1] * NT) {
+      const int hm = seg_tile[tid + 1] - seg_tile[tid];   // heavy m-tiles
+      const int m = lt ? 1 : hm;                          // m-tiles in this list
+      const int local = L - P[tid] * NT;
+      sh_seg[b] = tid;
+      sh_coord[b][0] = ks;
+      sh_coord[b][1] = local / m;
+      sh_coord[b][2] = local % m + (lt ? hm : 0);
+    }
   };
   auto coords = [&](int LL, int b) {
+    (void)LL;
     TileCoord c;
     c.seg = __builtin_amdgcn_readfirstlane(sh_seg[b]);
-    c.ks = LL / tiles;
-    const int local = LL - c.ks * tiles - seg_tile[c.seg] * NT;
-    const int mtiles = seg_tile[c.seg + 1] - seg_tile[c.seg];
-    c.nt = local / mtiles;
-    c.mt = local % mtiles;
+    c.ks = __builtin_amdgcn_readfirstlane(sh_coord[b][0]);
+    c.nt = __builtin_amdgcn_readfirstlane(sh_coord[b][1]);
+    c.mt = __builtin_amdgcn_readfirstlane(sh_coord[b][2]);
     if (WG) {   // output rows of this segment's gradient; no gather, no row offset
       c.rows = a.M;
       c.start = c.seg * a.M;
