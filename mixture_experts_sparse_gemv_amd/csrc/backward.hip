@@ -367,7 +367,7 @@ __global__ __launch_bounds__(256) void act_backward_kernel(
 // dwslot[t*k + s] = <h, G> + <b2_e, dy_t> for a kept slot (0 if dropped):
 // one wave per token; for each slot the lanes split the column partials of
 // its row (dwpart[row][.]) and the d products of the bias term, then a fixed
-// butterfly adds them.
+// sum over the wave (DPP row steps, then the row results) adds them.
 __global__ __launch_bounds__(256) void slot_grad_kernel(
     const int32_t* __restrict__ assign_row, const int32_t* __restrict__ topk_idx,
     const float* __restrict__ dwpart, int nparts, const uint16_t* __restrict__ b_down,
@@ -386,8 +386,7 @@ __global__ __launch_bounds__(256) void slot_grad_kernel(
         for (int j = lane; j < d; j += 64) v = fmaf(bf16_to_f32(br[j]), dyr[j], v);
       }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    v = wave_sum_dpp(v);
     if (lane == 0) dwslot[(long long)t * k + s] = v;
   }
 }
@@ -423,20 +422,14 @@ __global__ __launch_bounds__(256) void router_backward_kernel(
     const float l = act ? logits[(long long)t * E + lane] : 0.0f;
     float key, p, sig = 0.0f, tot = 1.0f;
     if (gating == MOE_SOFTMAX) {
-      float m = act ? l : -INFINITY;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      const float m = wave_max_dpp(act ? l : -INFINITY);
       const float ex = act ? fast_exp(l - m) : 0.0f;
-      float sum = ex;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+      const float sum = wave_sum_dpp(ex);
       p = ex / sum;
       key = p;
     } else {
       sig = act ? 1.0f / (1.0f + fast_exp(-l)) : 0.0f;
-      tot = sig;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
+      tot = wave_sum_dpp(sig);
       p = sig / tot;
       key = sig;
     }
@@ -451,7 +444,8 @@ __global__ __launch_bounds__(256) void router_backward_kernel(
         es[s] = topk_idx[(long long)t * k + s];
         dws[s] = assign_row[(long long)t * k + s] >= 0 ? dwslot[(long long)t * k + s] : 0.0f;
       }
-      ks_[s] = __shfl(key, es[s]);
+      es[s] = __builtin_amdgcn_readfirstlane(es[s]);   // the same entry in every lane
+      ks_[s] = lane_f(key, es[s]);
       if (s < k) S += ks_[s];
     }
 #pragma unroll
@@ -464,14 +458,10 @@ __global__ __launch_bounds__(256) void router_backward_kernel(
     float dl;
     if (gating == MOE_SOFTMAX) {
       const float g = dkey + dp;
-      float pg = act ? p * g : 0.0f;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) pg += __shfl_xor(pg, o);
+      const float pg = wave_sum_dpp(act ? p * g : 0.0f);
       dl = act ? p * (g - pg) : 0.0f;
     } else {
-      float pd = act ? p * dp : 0.0f;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) pd += __shfl_xor(pd, o);
+      const float pd = wave_sum_dpp(act ? p * dp : 0.0f);
       const float ds = dkey + (dp - pd) / tot;
       dl = act ? ds * sig * (1.0f - sig) : 0.0f;
     }
@@ -495,7 +485,7 @@ __global__ __launch_bounds__(256) void router_backward_kernel(
     for (int e = 0; e < E; ++e) {
       float de[RBT];
 #pragma unroll
-      for (int i = 0; i < RBT; ++i) de[i] = __shfl(dls[i], e);
+      for (int i = 0; i < RBT; ++i) de[i] = lane_f(dls[i], e);
       if (j < d) {
         const u32x4 wv = *(const u32x4*)(wr + (long long)e * d + j);
 #pragma unroll

@@ -98,6 +98,34 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
   return r;
 }
 
+// Wave-wide reductions without the LDS crossbar: four DPP steps inside each
+// row of 16 lanes (quad swaps across 1 and 2 lanes, then the half-row and
+// row mirrors, after which every lane of a row holds the row's result), then
+// the four row results read as scalars and combined in a fixed order.  Every
+// lane returns the result.  Call with the whole wave active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {   // l uniform
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+
 // exp(x) through the hardware base-2 exponential.
 __device__ __forceinline__ float fast_exp(float x) {
   return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);

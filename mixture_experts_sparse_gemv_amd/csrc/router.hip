@@ -12,9 +12,12 @@
 // steps at once; the eight partial logit tiles are summed in LDS in a fixed
 // order.  The gate and the top-k then run one token per wave pass (two
 // tokens per wave) with one lane per expert (E <= 64): wave-wide max and sum
-// by butterfly shuffles, and k rounds of a wave-wide argmax in which the
-// lower lane wins a tie.  Experts are ranked by logit (monotone in both
-// gates, so ranking and weights match ranking by score).  Each block also
+// by DPP row steps and scalar reads of the row results; each lane counts the
+// experts that beat it (a larger logit, or an equal one at a lower index),
+// reading their logits as scalars, so the experts of rank 0 .. k-1 are the
+// top k in order (ties to the lower index).  Experts are ranked by logit
+// (monotone in both gates, so ranking and weights match ranking by score).
+// No step goes through the LDS crossbar.  Each block also
 // writes the sum of its 16 tokens' probabilities per expert (token order);
 // these partial sums are reduced in block order for P.  It also writes the
 // number of selections of each expert in its 16 tokens (the dispatch's
@@ -27,26 +30,6 @@ namespace {
 constexpr int RT = kRouterTokens;  // 16 tokens per block
 constexpr int RW = 8;              // waves per block
 constexpr int RB = 8;              // K steps whose loads a wave issues together
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-// Wave-wide argmax; among equal values the lower index wins.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float ov = __shfl_xor(v, o);
-    const int oi = __shfl_xor(i, o);
-    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
-  }
-}
 
 struct RouterArgs {
   const void* x;
@@ -153,31 +136,36 @@ __global__ __launch_bounds__(64 * RW) void router_kernel(RouterArgs a) {
     }
     float score, denom;
     if (a.gating == MOE_SOFTMAX) {
-      const float mx = wave_max(l);
+      const float mx = wave_max_dpp(l);
       score = lane < E ? fast_exp(l - mx) : 0.f;   // unnormalized, exp(l - max)
-      denom = wave_sum(score);
+      denom = wave_sum_dpp(score);
     } else {
       score = lane < E ? __builtin_amdgcn_rcpf(1.0f + fast_exp(-l)) : 0.f;   // sigma(l)
-      denom = wave_sum(score);
+      denom = wave_sum_dpp(score);
     }
     const float p = score / denom;
     if (lane < E) {
       if (a.probs) a.probs[(long long)t * E + lane] = p;
       psum += p;
     }
-    // k rounds of argmax over the logits; remember each winner's score
-    float key = l;
+    // rank of each expert: the experts with a larger logit, or an equal one
+    // and a lower index (a NaN logit ranks below every number); lanes >= E
+    // rank E or more.  The experts of rank 0 .. k-1 are the top k, in order.
+    const float key = (l == l) ? l : NEG_INF;
+    int rank = 0;
+    for (int j = 0; j < E; ++j) {
+      const float kj = lane_f(key, j);
+      rank += (kj > key || (kj == key && j < lane)) ? 1 : 0;
+    }
+    if (rank < a.k) ++nsel;
     int my_idx = 0;
     float my_score = 0.f, sel_sum = 0.f;
     for (int s = 0; s < a.k; ++s) {
-      float bv = key;
-      int bi = lane;
-      wave_argmax(bv, bi);
-      bi = bi < E ? bi : E - 1;   // only NaN logits can leave the winner outside [0, E)
-      const float bs = __shfl(score, bi);
+      const uint64_t m = __ballot(rank == s);   // exactly one lane
+      const int bi = m ? __builtin_ctzll(m) : 0;
+      const float bs = lane_f(score, bi);
       sel_sum += bs;
       if (lane == s) { my_idx = bi; my_score = bs; }
-      if (lane == bi) { key = NEG_INF; ++nsel; }
     }
     if (lane < a.k && a.topk_idx) {   // (expert-choice routing uses the probabilities only)
       a.topk_idx[(long long)t * a.k + lane] = my_idx;
