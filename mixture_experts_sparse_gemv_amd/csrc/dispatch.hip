@@ -9,8 +9,10 @@
 //      each block forms the expert totals (so kept = min(count, capacity)
 //      and the row offsets, an exclusive scan of kept) and its own base
 //      ranks, then ranks and scatters its assignments; block 0 writes
-//      counts, kept and offsets and, with the router's per-chunk probability
-//      sums, reduces them in a fixed order to colsum, f, P and L_aux.
+//      counts, kept and offsets.  Given the router's per-chunk probability
+//      sums, one extra block (the last) forms the totals the same way and
+//      reduces them in a fixed order to colsum, f, P and L_aux, beside the
+//      scatter rather than after block 0's share of it.
 // Ranks are the token order within each expert, so an expert keeps its C
 // lowest-token assignments, bit-exactly and independently of scheduling.
 #include "moe_internal.h"
@@ -111,7 +113,7 @@ struct DispatchArgs {
 
 constexpr int PMAX = 32;   // per-thread probability partial sums prefetched
 
-// Aux statistics (block 0): colsum, f, P, L_aux and the routing health
+// Aux statistics (the extra last block): colsum, f, P, L_aux and the routing health
 // indicators from the router's per-chunk probability sums and the routed
 // counts tot_s.  Sums run per thread in chunk order, over the wave's j in
 // xor-butterfly order, then over the waves in order.  Thread (e, j) as in
@@ -167,8 +169,9 @@ __device__ void aux_block(const DispatchArgs& a, const int* tot_s, int e, int j,
 // the lanes below it in its wave holding the same expert (six bit-plane
 // ballots) — and scatters: rank < kept gives row offsets[e] + rank,
 // otherwise the assignment is dropped and goes after all kept rows, grouped
-// by expert.  Block 0 also writes counts, kept and offsets and, given the
-// router's probability sums, the aux statistics.
+// by expert.  Block 0 also writes counts, kept and offsets.  Given the
+// router's probability sums, the grid has one more block, which computes
+// the aux statistics and scatters nothing.
 // Thread (e, j) = (tid % EP, tid / EP) while summing, EP = E rounded up to a
 // power of two, J = ST / EP threads per expert.
 __global__ __launch_bounds__(ST) void dispatch_kernel(DispatchArgs a) {
@@ -180,7 +183,9 @@ __global__ __launch_bounds__(ST) void dispatch_kernel(DispatchArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E;
   const long long n = (long long)a.T * a.k;
-  const long long A0 = (long long)blockIdx.x * kScatterTokens * a.k;
+  // with aux statistics the last block computes them and scatters nothing
+  const bool aux_blk = a.prob_part && blockIdx.x == gridDim.x - 1;
+  const long long A0 = aux_blk ? n : (long long)blockIdx.x * kScatterTokens * a.k;
   const long long A1 = A0 + (long long)kScatterTokens * a.k < n ? A0 + (long long)kScatterTokens * a.k : n;
   // this block's expert ids, loaded before anything waits
   constexpr int MAXP = kScatterTokens * kMaxTopK / ST;   // passes of ST assignments
@@ -258,7 +263,10 @@ __global__ __launch_bounds__(ST) void dispatch_kernel(DispatchArgs a) {
     if (blockIdx.x == 0 && lane == 0) a.offsets[E] = offE;
   }
   __syncthreads();
-  if (blockIdx.x == 0 && a.prob_part) aux_block(a, tot_s, e, j, EP, J, wsum, sp);
+  if (aux_blk) {   // uniform over the block
+    aux_block(a, tot_s, e, j, EP, J, wsum, sp);
+    return;
+  }
 
   const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
@@ -347,7 +355,7 @@ hipError_t launch_dispatch(const Shape& s, const int32_t* topk_idx, int32_t* chu
   DispatchArgs da{topk_idx, chunk_counts, counts, kept, offsets, sorted_assign, assign_row,
                   drop_mask, prob_part, colsum, f, P, l_aux, prob_part ? stats : nullptr,
                   s.T, s.k, s.E, s.cap, nchunk};
-  dispatch_kernel<<<nsb, ST, 0, st>>>(da);
+  dispatch_kernel<<<nsb + (prob_part ? 1 : 0), ST, 0, st>>>(da);
   return hipGetLastError();
 }
 
