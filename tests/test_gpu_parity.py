@@ -80,6 +80,52 @@ def test_router_topk(name):
     assert_close(colsum.cpu().numpy(), pr.sum(0), "colsum", rel=1e-4, mabs=1e-2)
 
 
+# Exact ties between experts: router rows duplicated in groups, so the
+# duplicated experts' logits are equal in any precision; the selection must
+# then take the lower expert index first (top-k with ties to the lower
+# index, renormalized weights), on both top-k paths of the router kernel
+# (up to 16 experts: a rank count over all experts; more: a radix select).
+TIE_CASES = {
+    "E8_top2_softmax": (scaled(RUNS["gpt2"], T=300, d_model=256, d_ff=256, router_bias="none"),
+                        [(0, 1), (2, 5), (3, 4, 7)]),
+    "E64_top6_sigmoid": (scaled(RUNS["fine_shared"], T=300, d_model=256, d_ff=128,
+                                router_bias="none"),
+                         [(2 * q, 2 * q + 1) for q in range(24)] + [(50, 51, 52, 60)]),
+}
+
+
+@pytest.mark.parametrize("name", list(TIE_CASES))
+def test_router_ties_to_lower_index(name):
+    run, groups = TIE_CASES[name]
+    _say(f"[router ties] {name}")
+    inp = dict(make_inputs(run))
+    wr = inp["w_router"].clone()
+    for grp in groups:
+        for e in grp[1:]:
+            wr[e] = wr[grp[0]]
+    inp["w_router"] = wr
+    g = gpu_inputs(inp)
+    p = problem_of(run)
+    T, k, E = run.T, run.top_k, run.num_experts
+    idx = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T * k, dtype=torch.float32, device="cuda")
+    M.moe_router_topk(p, g["x"], weights_of(g), idx, w, ws=M.workspace(p))
+    torch.cuda.synchronize()
+    logits = O.router_logits(to_f64(inp["x"]), to_f64(wr), None)
+    pr = O.gate(logits, run.gating)
+    oi, ow = O.topk_renorm(pr, k)
+    gi = idx.view(T, k).cpu().numpy()
+    # tokens whose top k+1 scores are exactly tied or clearly apart
+    top = -np.sort(-pr, axis=1)[:, :k + 1]
+    d = top[:, :-1] - top[:, 1:]
+    clear = np.all((d == 0) | (d > GAP), axis=1)
+    tied = np.any(d[clear] == 0, axis=1)
+    _say(f"  tokens compared {clear.sum()} of {T}, with an exact tie among them {tied.sum()}")
+    assert clear.sum() >= T // 2 and tied.sum() >= 20
+    assert np.array_equal(gi[clear], oi[clear])
+    assert_close(w.view(T, k).cpu().numpy()[clear], ow[clear], "topk_w")
+
+
 def _dispatch_cases():
     rng = np.random.default_rng(123)
     cases = []

@@ -1,0 +1,91 @@
+"""CPU model of the grouped GEMM's persistent tile schedule (gemm.hip): the
+two tile lists (full tiles, and a segment's last tile when it fills at most
+half of the block's rows), the run-time choice between one and two lists,
+the per-XCD ranges of each list, and the decode of a tile id into (K slice,
+segment, n-tile, m-tile).  The model follows the kernel's integer
+arithmetic step by step; every tile of every segment must be visited
+exactly once, for any grid size, K split and mix of segment lengths."""
+import random
+
+import pytest
+
+BM = 256
+
+
+def schedule(rows, NT, nsplit, grid):
+    nseg = len(rows)
+    nslots = grid >> 3
+    heavy = [r // BM + (1 if r % BM > BM // 2 else 0) for r in rows]
+    light = [1 if 0 < r % BM <= BM // 2 else 0 for r in rows]
+    pre_h, pre_l = [0], [0]
+    for s in range(nseg):
+        pre_h.append(pre_h[-1] + heavy[s])
+        pre_l.append(pre_l[-1] + light[s])
+    h = pre_h[nseg] * NT * nsplit
+    al = h + pre_l[nseg] * NT * nsplit
+    two = ((h + 7) // 8 + nslots - 1) // nslots < ((al + 7) // 8 + nslots - 1) // nslots
+    seg_tile = pre_h if two else [a + b for a, b in zip(pre_h, pre_l)]
+    seg_lt = pre_l if two else [0] * (nseg + 1)
+    tiles, ltiles = seg_tile[nseg] * NT, seg_lt[nseg] * NT
+    nheavy, nlight = tiles * nsplit, ltiles * nsplit
+    per, lper = (nheavy + 7) >> 3, (nlight + 7) >> 3
+    seen = []
+    for b in range(grid):
+        xcd = b & 7
+        hlen = min(max(nheavy - xcd * per, 0), per)
+        llen = min(max(nlight - xcd * lper, 0), lper)
+        it = b >> 3
+        while True:
+            i = it
+            if i < hlen:
+                LL = xcd * per + i
+            elif i - hlen < llen:
+                LL = nheavy + xcd * lper + (i - hlen)
+            else:
+                break
+            lt = LL >= nheavy
+            P = seg_lt if lt else seg_tile
+            k = LL - (nheavy if lt else 0)
+            tl = ltiles if lt else tiles
+            ks = k // tl
+            L = k - ks * tl
+            found = [s for s in range(nseg) if P[s] * NT <= L < P[s + 1] * NT]
+            assert len(found) == 1
+            s = found[0]
+            hm = seg_tile[s + 1] - seg_tile[s]
+            m = 1 if lt else hm
+            local = L - P[s] * NT
+            seen.append((ks, s, local // m, local % m + (hm if lt else 0)))
+            it += nslots
+    return seen, two
+
+
+def expected(rows, NT, nsplit):
+    return sorted((ks, s, n, m) for ks in range(nsplit) for s, r in enumerate(rows)
+                  for n in range(NT) for m in range((r + BM - 1) // BM))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_every_tile_exactly_once(seed):
+    rng = random.Random(seed)
+    both = set()
+    for _ in range(150):
+        nseg = rng.randint(1, 130 if rng.random() < 0.1 else 12)
+        rows = [rng.choice([0, 1, 64, 128, 129, 255, 256, 257, 384, 385, 1000,
+                            rng.randint(0, 3000)]) for _ in range(nseg)]
+        NT, nsplit, grid = rng.randint(1, 20), rng.choice([1, 1, 2, 4]), 8 * rng.randint(1, 32)
+        seen, two = schedule(rows, NT, nsplit, grid)
+        assert sorted(seen) == expected(rows, NT, nsplit)
+        both.add(two)
+    assert both == {False, True}
+
+
+def test_large_prefill_down_shape_takes_two_lists():
+    """The routed row counts of the seeded large prefill run (8 experts, in
+    ascending order; 16 n-tiles in the down projection): 64 full m-tiles
+    fill exactly four rounds of 256 blocks and the five half-empty ones
+    follow, instead of a fifth round of full tiles."""
+    rows = [1991, 1996, 1997, 2050, 2052, 2080, 2086, 2132]
+    assert sum(rows) == 8192 * 2
+    seen, two = schedule(rows, 16, 1, 256)
+    assert two and sorted(seen) == expected(rows, 16, 1)
