@@ -399,25 +399,22 @@ __global__ __launch_bounds__(256) void slot_grad_kernel(
 //   dp[e]      = alpha E f_e / T                    (aux loss through P)
 //   softmax:  dl = p (dkey + dp - sum p (dkey + dp))
 //   sigmoid:  dl = (dkey + (dp - sum p dp) / sum sigma) sigma (1 - sigma)
-// and dx_router[t] = sum_e dl_e Wr[e, :] (each Wr load serves RBT tokens).
-constexpr int RBT = 4;
+// written to dlogits [T, E]; router_dx_kernel then forms dx_router = dl Wr.
+template <int RBT>
 __global__ __launch_bounds__(256) void router_backward_kernel(
-    const float* __restrict__ logits, const uint16_t* __restrict__ wr,
-    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ assign_row,
-    const float* __restrict__ dwslot, const int32_t* __restrict__ counts, float alpha, int T,
-    int d, int E, int k, int gating, float* __restrict__ dlogits, float* __restrict__ d_topk_w,
-    float* __restrict__ dxr) {
+    const float* __restrict__ logits, const int32_t* __restrict__ topk_idx,
+    const int32_t* __restrict__ assign_row, const float* __restrict__ dwslot,
+    const int32_t* __restrict__ counts, float alpha, int T, int E, int k, int gating,
+    float* __restrict__ dlogits, float* __restrict__ d_topk_w) {
   const int lane = threadIdx.x & 63;
   const int tb = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RBT;
   if (tb >= T) return;   // per wave
   const bool act = lane < E;
   const float dp = act ? alpha * (float)E * ((float)counts[act ? lane : 0] / ((float)T * k)) / T
                        : 0.0f;
-  float dls[RBT];
 #pragma unroll
   for (int i = 0; i < RBT; ++i) {
     const int t = tb + i;
-    dls[i] = 0.0f;
     if (t >= T) continue;   // uniform over the wave
     const float l = act ? logits[(long long)t * E + lane] : 0.0f;
     float key, p, sig = 0.0f, tot = 1.0f;
@@ -465,7 +462,6 @@ __global__ __launch_bounds__(256) void router_backward_kernel(
       const float ds = dkey + (dp - pd) / tot;
       dl = act ? ds * sig * (1.0f - sig) : 0.0f;
     }
-    dls[i] = dl;
     if (act) dlogits[(long long)t * E + lane] = dl;
     if (d_topk_w && lane < k) {
       float v = 0.0f;
@@ -474,39 +470,46 @@ __global__ __launch_bounds__(256) void router_backward_kernel(
       d_topk_w[(long long)t * k + lane] = v;
     }
   }
-  // dx_router[t, j] = sum_e dl_e Wr[e, j]; lane covers 8 columns per 512
-  for (int j0 = 0; j0 < d; j0 += 512) {
-    const int j = j0 + lane * 8;
-    float acc[RBT][8];
+}
+
+// dx_router[t, j] = sum_e dl[t, e] Wr[e, j] on the fp32 matrix cores
+// (MFMA 16x16x4: A = 16 tokens x 4 experts of dl, B = 4 experts x 16 columns
+// of Wr widened from bf16; the experts are padded to a multiple of 4 with
+// zeros).  One wave per 16 tokens x 64 columns, K = E in steps of 4.
+__global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict__ dl,
+                                                        const uint16_t* __restrict__ wr, int T,
+                                                        int d, int E, float* __restrict__ dxr) {
+  const int lane = threadIdx.x & 63;
+  const int ntj = (d + 63) / 64;
+  const long long wid = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long t0 = wid / ntj * 16;
+  const int j0 = (int)(wid % ntj) * 64;
+  if (t0 >= T) return;   // per wave
+  const int i = lane & 15, kq = lane >> 4;
+  const long long t = t0 + i < T ? t0 + i : T - 1;
+  f32x4 acc[4];
 #pragma unroll
-    for (int i = 0; i < RBT; ++i)
+  for (int n = 0; n < 4; ++n) acc[n] = f32x4{};
+  for (int e0 = 0; e0 < E; e0 += 4) {
+    const int e = e0 + kq;
+    const float av = e < E ? dl[t * E + e] : 0.0f;
+    float bv[4];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[i][q] = 0.0f;
-    for (int e = 0; e < E; ++e) {
-      float de[RBT];
-#pragma unroll
-      for (int i = 0; i < RBT; ++i) de[i] = lane_f(dls[i], e);
-      if (j < d) {
-        const u32x4 wv = *(const u32x4*)(wr + (long long)e * d + j);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float w0 = __uint_as_float(wv[q] << 16), w1 = __uint_as_float(wv[q] & 0xffff0000u);
-#pragma unroll
-          for (int i = 0; i < RBT; ++i) {
-            acc[i][2 * q] = fmaf(de[i], w0, acc[i][2 * q]);
-            acc[i][2 * q + 1] = fmaf(de[i], w1, acc[i][2 * q + 1]);
-          }
-        }
-      }
+    for (int n = 0; n < 4; ++n) {
+      const int j = j0 + n * 16 + i;
+      bv[n] = (e < E && j < d) ? bf16_to_f32(wr[(long long)e * d + j]) : 0.0f;
     }
-    if (j < d) {
 #pragma unroll
-      for (int i = 0; i < RBT; ++i) {
-        if (tb + i >= T) break;
-        float* o = dxr + (long long)(tb + i) * d + j;
-        *(f32x4*)o = f32x4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
-        *(f32x4*)(o + 4) = f32x4{acc[i][4], acc[i][5], acc[i][6], acc[i][7]};
-      }
+    for (int n = 0; n < 4; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[n], acc[n], 0, 0, 0);
+  }
+  // lane holds tokens t0 + 4 kq + r (r = 0..3) of column i of each 16-column tile
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int j = j0 + n * 16 + i;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const long long tr = t0 + 4 * kq + r;
+      if (tr < T && j < d) dxr[tr * d + j] = acc[n][r];
     }
   }
 }
@@ -515,20 +518,26 @@ __global__ __launch_bounds__(256) void router_backward_kernel(
 // 64): part[slice][e][j] = sum over the slice's tokens (in order) of
 // dl[t, e] x[t, j]; bpart[slice][e] likewise of dl[t, e] (blocks of column
 // chunk 0).  Block = 256 columns; the slice moves through LDS 64 tokens at a
-// time (x by 16-byte loads, dl as [64][EB]); thread = one column, EB
-// accumulators (E <= EB).
+// time (x by 16-byte loads, dl as [64][EB]).  Thread = CPT adjacent columns
+// x EB / CPT experts (a wave shares its experts, so their dl values are LDS
+// broadcasts): with many experts each LDS read of dl feeds CPT products.
 template <int EB>
 __global__ __launch_bounds__(256) void router_wgrad_part_kernel(
     const float* __restrict__ dl, const uint16_t* __restrict__ x, int T, int d, int E, int tpb,
     float* __restrict__ part, float* __restrict__ bpart) {
+  constexpr int CPT = EB >= 32 ? EB / 16 : 1;   // columns per thread = expert groups
+  constexpr int EPT = EB / CPT;                 // experts per thread
   __shared__ __attribute__((aligned(16))) uint16_t xs[64][256 + 8];
   __shared__ __attribute__((aligned(16))) float sdl[64][EB];
   const int tid = threadIdx.x;
-  const int c0 = blockIdx.x * 256, j = c0 + tid;
+  const int eg = tid / (256 / CPT), cg = tid % (256 / CPT);   // expert group, column group
+  const int c0 = blockIdx.x * 256, jc = cg * CPT;             // first column of the thread
   const int ts = blockIdx.y * tpb, te = min(T, ts + tpb);
-  float acc[EB];
+  float acc[EPT][CPT];
 #pragma unroll
-  for (int e = 0; e < EB; ++e) acc[e] = 0.0f;
+  for (int e = 0; e < EPT; ++e)
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) acc[e][c] = 0.0f;
   float bsum = 0.0f;
   for (int t0 = ts; t0 < te; t0 += 64) {
     __syncthreads();   // the previous tile's reads are done
@@ -547,22 +556,39 @@ __global__ __launch_bounds__(256) void router_wgrad_part_kernel(
     __syncthreads();
 #pragma unroll 4
     for (int rr = 0; rr < 64; ++rr) {
-      const float xv = bf16_to_f32(xs[rr][tid]);
+      float xv[CPT];
+      if (CPT == 4) {
+        const u32x2 p = *(const u32x2*)&xs[rr][jc];
+        xv[0] = __uint_as_float(p[0] << 16);
+        xv[1 % CPT] = __uint_as_float(p[0] & 0xffff0000u);
+        xv[2 % CPT] = __uint_as_float(p[1] << 16);
+        xv[3 % CPT] = __uint_as_float(p[1] & 0xffff0000u);
+      } else {
 #pragma unroll
-      for (int e = 0; e < EB; e += 4) {
-        const f32x4 dv = *(const f32x4*)&sdl[rr][e];
-        acc[e] = fmaf(dv[0], xv, acc[e]);
-        acc[e + 1] = fmaf(dv[1], xv, acc[e + 1]);
-        acc[e + 2] = fmaf(dv[2], xv, acc[e + 2]);
-        acc[e + 3] = fmaf(dv[3], xv, acc[e + 3]);
+        for (int c = 0; c < CPT; ++c) xv[c] = bf16_to_f32(xs[rr][jc + c]);
+      }
+#pragma unroll
+      for (int e = 0; e < EPT; e += 4) {
+        const f32x4 dv = *(const f32x4*)&sdl[rr][eg * EPT + e];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+          acc[e][c] = fmaf(dv[0], xv[c], acc[e][c]);
+          acc[e + 1][c] = fmaf(dv[1], xv[c], acc[e + 1][c]);
+          acc[e + 2][c] = fmaf(dv[2], xv[c], acc[e + 2][c]);
+          acc[e + 3][c] = fmaf(dv[3], xv[c], acc[e + 3][c]);
+        }
       }
       if (blockIdx.x == 0 && tid < E) bsum += sdl[rr][tid];
     }
   }
-  if (j < d) {
 #pragma unroll
-    for (int e = 0; e < EB; ++e)
-      if (e < E) part[((long long)blockIdx.y * E + e) * d + j] = acc[e];
+  for (int e = 0; e < EPT; ++e) {
+    const int ee = eg * EPT + e;
+    if (ee >= E) continue;
+    float* o = part + ((long long)blockIdx.y * E + ee) * d + c0 + jc;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+      if (c0 + jc + c < d) o[c] = acc[e][c];
   }
   if (blockIdx.x == 0 && tid < E) bpart[(long long)blockIdx.y * E + tid] = bsum;
 }
@@ -692,10 +718,15 @@ hipError_t launch_router_backward(const Shape& s, const float* logits, const voi
                                   const int32_t* topk_idx, const int32_t* assign_row,
                                   const float* dwslot, const int32_t* counts, float alpha,
                                   float* dlogits, float* d_topk_w, float* dxr, hipStream_t st) {
-  const int per_block = 4 * RBT;
-  router_backward_kernel<<<(s.T + per_block - 1) / per_block, 256, 0, st>>>(
-      logits, (const uint16_t*)wr, topk_idx, assign_row, dwslot, counts, alpha, s.T, s.d, s.E,
-      s.k, s.gating, dlogits, d_topk_w, dxr);
+  constexpr int R = 4;   // tokens per wave
+  router_backward_kernel<R><<<(s.T + 4 * R - 1) / (4 * R), 256, 0, st>>>(
+      logits, topk_idx, assign_row, dwslot, counts, alpha, s.T, s.E, s.k, s.gating, dlogits,
+      d_topk_w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long waves = (long long)(s.T + 15) / 16 * ((s.d + 63) / 64);
+  router_dx_kernel<<<(int)((waves + 3) / 4), 256, 0, st>>>(dlogits, (const uint16_t*)wr, s.T, s.d,
+                                                          s.E, dxr);
   return hipGetLastError();
 }
 
