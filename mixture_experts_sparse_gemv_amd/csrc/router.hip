@@ -6,12 +6,13 @@
 //   top-k by descending score, ties to the lower expert index; weights =
 //   selected scores / their sum                              (0539edu 2.1; kamacoder 三)
 //
-// A block handles 16 tokens with 8 waves.  For bf16 inputs the router
+// A block handles 16 tokens with 8 waves (16 when there are at most 64
+// blocks, i.e. T <= 1024).  For bf16 inputs the router
 // product runs on bf16 MFMA 16x16x32 (A = 16 router rows, B = 16 token rows),
-// each wave covering every 8th 32-wide K step and issuing the loads of 8
-// steps at once; the eight partial logit tiles are summed in LDS in a fixed
+// each wave covering every 8th (16th) 32-wide K step and issuing the loads of 8
+// steps at once; the partial logit tiles of the waves are summed in LDS in a fixed
 // order.  The gate and the top-k then run one token per wave pass (two
-// tokens per wave) with one lane per expert (E <= 64): wave-wide max and sum
+// tokens per wave, or one with 16 waves) with one lane per expert (E <= 64): wave-wide max and sum
 // by DPP row steps and scalar reads of the row results; each lane counts the
 // experts that beat it (a larger logit, or an equal one at a lower index),
 // reading their logits as scalars, so the experts of rank 0 .. k-1 are the
@@ -28,7 +29,8 @@ namespace moe {
 namespace {
 
 constexpr int RT = kRouterTokens;  // 16 tokens per block
-constexpr int RW = 8;              // waves per block
+// waves per block: 8, or 16 when there are few blocks (small T), so a block's
+// K steps spread over more waves (one token per wave in the gate)
 constexpr int RB = 8;              // K steps whose loads a wave issues together
 
 struct RouterArgs {
@@ -44,7 +46,7 @@ struct RouterArgs {
   int T, d, E, k, gating, dtype;
 };
 
-template <int NE16>  // expert tiles of 16 (bf16 path); 0 = fp32 path
+template <int NE16, int RW>  // expert tiles of 16 (bf16 path; 0 = fp32 path), waves
 __global__ __launch_bounds__(64 * RW) void router_kernel(RouterArgs a) {
   __shared__ float red[RW][RT][kMaxExperts + 1];
   __shared__ float colp[RW][kMaxExperts];
@@ -286,15 +288,22 @@ hipError_t launch_router(const Shape& s, const void* x, const void* wr, const vo
   RouterArgs a{x, wr, s.router_bias() ? br : nullptr, topk_idx, topk_w, probs, prob_part,
                chunk_counts, logits, s.T, s.d, s.E, s.k, s.gating, s.dtype};
   const int blocks = router_blocks(s);
+  const bool wide = blocks <= 64;   // few blocks: 16 waves each
+#define MOE_ROUTER(NE)                                            \
+  do {                                                            \
+    if (wide) router_kernel<NE, 16><<<blocks, 1024, 0, st>>>(a);  \
+    else router_kernel<NE, 8><<<blocks, 512, 0, st>>>(a);         \
+  } while (0)
   if (s.dtype == MOE_F32) {
-    router_kernel<0><<<blocks, 64 * RW, 0, st>>>(a);
+    router_kernel<0, 8><<<blocks, 512, 0, st>>>(a);
   } else {
     const int ne16 = (s.E + 15) / 16;
-    if (ne16 == 1) router_kernel<1><<<blocks, 64 * RW, 0, st>>>(a);
-    else if (ne16 == 2) router_kernel<2><<<blocks, 64 * RW, 0, st>>>(a);
-    else if (ne16 == 3) router_kernel<3><<<blocks, 64 * RW, 0, st>>>(a);
-    else router_kernel<4><<<blocks, 64 * RW, 0, st>>>(a);
+    if (ne16 == 1) MOE_ROUTER(1);
+    else if (ne16 == 2) MOE_ROUTER(2);
+    else if (ne16 == 3) MOE_ROUTER(3);
+    else MOE_ROUTER(4);
   }
+#undef MOE_ROUTER
   return hipGetLastError();
 }
 
