@@ -25,6 +25,9 @@ SMALL = {
     "large_T300": scaled(RUNS["large_prefill"], T=300),
     "fine_shared_T1000": scaled(RUNS["fine_shared"], T=1000),
     "fine_shared_T1000_literal": scaled(RUNS["fine_shared"], T=1000, capacity_factor=1.25 / 6),
+    # more than 64 16-token router blocks (8 waves each, not 16) with 64
+    # experts and 2 shared ones, at a width the oracle finishes quickly
+    "fine_shared_T1100_d256": scaled(RUNS["fine_shared"], T=1100, d_model=256, d_ff=128),
 }
 
 
