@@ -29,8 +29,8 @@ METRIC = "MoE-FFN fwd tokens/s + TFLOP/s (% bf16 MFMA peak / % HBM BW), 1 MI355X
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default=None, help="workload name (default: gpt2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
