@@ -400,7 +400,7 @@ __global__ __launch_bounds__(256) void slot_grad_kernel(
 //   softmax:  dl = p (dkey + dp - sum p (dkey + dp))
 //   sigmoid:  dl = (dkey + (dp - sum p dp) / sum sigma) sigma (1 - sigma)
 // written to dlogits [T, E]; router_dx_kernel then forms dx_router = dl Wr.
-template <int RBT>
+constexpr int RBT = 4;   // tokens per wave
 __global__ __launch_bounds__(256) void router_backward_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ topk_idx,
     const int32_t* __restrict__ assign_row, const float* __restrict__ dwslot,
@@ -718,8 +718,7 @@ hipError_t launch_router_backward(const Shape& s, const float* logits, const voi
                                   const int32_t* topk_idx, const int32_t* assign_row,
                                   const float* dwslot, const int32_t* counts, float alpha,
                                   float* dlogits, float* d_topk_w, float* dxr, hipStream_t st) {
-  constexpr int R = 4;   // tokens per wave
-  router_backward_kernel<R><<<(s.T + 4 * R - 1) / (4 * R), 256, 0, st>>>(
+  router_backward_kernel<<<(s.T + 4 * RBT - 1) / (4 * RBT), 256, 0, st>>>(
       logits, topk_idx, assign_row, dwslot, counts, alpha, s.T, s.E, s.k, s.gating, dlogits,
       d_topk_w);
   hipError_t e = hipGetLastError();

@@ -332,8 +332,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
       sh_coord[b][2] = local % m + (lt ? hm : 0);
     }
   };
-  auto coords = [&](int LL, int b) {
-    (void)LL;
+  auto coords = [&](int b) {   // the tile located in slot b
     TileCoord c;
     c.seg = __builtin_amdgcn_readfirstlane(sh_seg[b]);
     c.ks = __builtin_amdgcn_readfirstlane(sh_coord[b][0]);
@@ -496,11 +495,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   locate(LL, 0);
   if (LL1 >= 0) locate(LL1, 1);
   __syncthreads();
-  TileCoord cur = coords(LL, 0);
+  TileCoord cur = coords(0);
   row_loads(cur);
   setup(cur);
   dma(lds0, 0);
-  if (LL1 >= 0) row_loads(coords(LL1, 1));
+  if (LL1 >= 0) row_loads(coords(1));
   bias_load(cur);
   lds_barrier();     // sh_seg has been read everywhere before it is rewritten
   int b = 0;         // sh_seg slot of this tile and of the tile two ahead
@@ -643,11 +642,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
     static_assert(WPA * (NSTAGE - 1) >= NW, "staging must fit in ring stages 1 to 3");
     // the next tile's first k-tile and bias, the row loads of the one after
     auto prefetch_next = [&]() {
-      const TileCoord nx = coords(LL1, b ^ 1);
+      const TileCoord nx = coords(b ^ 1);
       setup(nx);
       dma(lds0, 0);
       bias_load(nx);
-      if (LL2 >= 0) row_loads(coords(LL2, b));
+      if (LL2 >= 0) row_loads(coords(b));
     };
     // (a wave without valid rows stages zeros and stores nothing)
     const int wa = wv / WPA;
@@ -703,7 +702,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
       if (i == 0 && more) prefetch_next();
     }
     if (!more) break;
-    cur = coords(LL1, b ^ 1);
+    cur = coords(b ^ 1);
     it += step;
     LL1 = LL2;
     b ^= 1;

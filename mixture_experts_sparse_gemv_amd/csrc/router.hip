@@ -72,7 +72,7 @@ __global__ __launch_bounds__(64 * RW) void router_kernel(RouterArgs a) {
 #pragma unroll
     for (int j = 0; j < NE16; ++j) acc[j] = f32x4{};
     const int nsteps = a.d / 32;
-    if (NE16 <= 2) {
+    if constexpr (NE16 <= 2) {
       for (int s0 = wave; s0 < nsteps; s0 += RW * RB) {
         u32x4 xv[RB], wv[RB][NE16 > 0 ? NE16 : 1];
 #pragma unroll
