@@ -28,6 +28,12 @@ SMALL = {
     # more than 64 16-token router blocks (8 waves each, not 16) with 64
     # experts and 2 shared ones, at a width the oracle finishes quickly
     "fine_shared_T1100_d256": scaled(RUNS["fine_shared"], T=1100, d_model=256, d_ff=128),
+    # 64 experts of 683..1278 rows: exactly 256 full m-tiles and 35 half-empty
+    # ones, so both grouped GEMMs take the two-list tile schedule (checked on
+    # the oracle's routing in test_split_lists_case_takes_two_lists)
+    "relu_E64_T16384_split_lists": scaled(RUNS["gpt2"], T=16384, d_model=256, d_ff=128,
+                                          num_experts=64, top_k=4, activation="relu",
+                                          capacity_factor=None),
 }
 
 

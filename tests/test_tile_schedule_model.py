@@ -89,3 +89,21 @@ def test_large_prefill_down_shape_takes_two_lists():
     assert sum(rows) == 8192 * 2
     seen, two = schedule(rows, 16, 1, 256)
     assert two and sorted(seen) == expected(rows, 16, 1)
+
+
+def test_split_lists_case_takes_two_lists():
+    """The GPU parity case relu_E64_T16384_split_lists routes (by the
+    oracle's top-k on its seeded inputs) into 256 full m-tiles plus
+    half-empty ones, which makes both of its grouped GEMMs (one 256-column
+    tile each way, 256 blocks) take the two-list schedule."""
+    import numpy as np
+    import oracle as O
+    from synth import RUNS, make_inputs, scaled, to_f64
+    run = scaled(RUNS["gpt2"], T=16384, d_model=256, d_ff=128, num_experts=64, top_k=4,
+                 activation="relu", capacity_factor=None)
+    inp = make_inputs(run)
+    logits = O.router_logits(to_f64(inp["x"]), to_f64(inp["w_router"]), to_f64(inp["b_router"]))
+    idx = np.argsort(-logits, axis=1, kind="stable")[:, :run.top_k]
+    rows = [int(c) for c in np.bincount(idx.ravel(), minlength=run.num_experts)]
+    seen, two = schedule(rows, 1, 1, 256)
+    assert two and sorted(seen) == expected(rows, 1, 1)
