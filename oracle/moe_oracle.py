@@ -91,9 +91,25 @@ def topk_renorm(scores, k):
     # expert order, so a tie goes to the lower index.
     order = np.argsort(-scores, axis=1, kind="stable")
     idx = order[:, :k].astype(np.int32)
-    sel = np.take_along_axis(scores, idx.astype(np.int64), axis=1)
-    w = sel / sel.sum(axis=1, keepdims=True)
-    return idx, w
+    return idx, renorm(scores, idx)
+
+
+def renorm(scores, idx):
+    """w[t, s] = scores[t, idx[t, s]] / sum over the token's selected experts
+    of their scores: the selected probabilities renormalized to sum to 1
+    ([0539edu] 2.1; [kamacoder] 三 top_k_routing), for a given selection."""
+    sel = np.take_along_axis(np.asarray(scores, dtype=np.float64),
+                             np.asarray(idx, dtype=np.int64), axis=1)
+    return sel / sel.sum(axis=1, keepdims=True)
+
+
+def routing(x, w_router, b_router, *, top_k, gating):
+    """Router -> gate -> top-k + renorm over all tokens: logits, probs, the
+    oracle's own selection idx [T, k] with weights w, and the selection gap."""
+    logits = router_logits(x, w_router, b_router)
+    probs = gate(logits, gating)
+    idx, w = topk_renorm(probs, top_k)
+    return dict(logits=logits, probs=probs, idx=idx, w=w, gap=selection_gap(probs, top_k))
 
 
 def selection_gap(scores, k):
@@ -295,13 +311,10 @@ def expert_choice_select(probs, C):
     [T] (how many experts picked each token; 0 = an orphan token)."""
     T, E = probs.shape
     sel = np.empty((E, C), dtype=np.int64)
-    row_of = np.full((T, E), -1, dtype=np.int64)
     for e in range(E):
         order = np.lexsort((np.arange(T), -probs[:, e]))   # by score desc, then token asc
-        chosen = np.sort(order[:C])
-        sel[e] = chosen
-        row_of[chosen, e] = e * C + np.arange(C)
-    token_experts = (row_of >= 0).sum(axis=1)
+        sel[e] = np.sort(order[:C])
+    row_of, token_experts = expert_choice_rows(sel, T)
     return sel, row_of, token_experts
 
 
@@ -315,17 +328,37 @@ def expert_choice_gap(probs, C):
     return srt[C - 1] - srt[C]
 
 
+def expert_choice_rows(sel, T):
+    """row_of [T, E] (row e*C + position of (t, e) in expert e's ascending
+    token list, -1 if e did not pick t) and token_experts [T] for a given
+    selection sel [E, C] of ascending token lists."""
+    sel = np.asarray(sel, dtype=np.int64)
+    E, C = sel.shape
+    row_of = np.full((T, E), -1, dtype=np.int64)
+    for e in range(E):
+        row_of[sel[e], e] = e * C + np.arange(C)
+    return row_of, (row_of >= 0).sum(axis=1)
+
+
 def forward_expert_choice(x, w_router, b_router, w_up, b_up, w_down, b_down, *, capacity,
-                          num_shared, gating, activation, token_subset=None):
+                          num_shared, gating, activation, token_subset=None, sel=None):
     """MoE-FFN forward with expert-choice routing: router -> gate -> each
     expert takes its top-C tokens -> expert FFNs -> y[t] = sum over the
     experts e that picked t of p[t, e] * FFN_e(x_t) (no renormalization; an
-    orphan token gets only the shared experts) + shared experts."""
+    orphan token gets only the shared experts) + shared experts.
+
+    sel [E, C]: evaluate the layer at this selection (each expert's tokens in
+    ascending order) instead of the oracle's own; gap stays that of the
+    oracle's own scores."""
     T, d = x.shape
     E = w_router.shape[0]
     logits = router_logits(x, w_router, b_router)
     probs = gate(logits, gating)
-    sel, row_of, token_experts = expert_choice_select(probs, capacity)
+    if sel is None:
+        sel, row_of, token_experts = expert_choice_select(probs, capacity)
+    else:
+        sel = np.asarray(sel, dtype=np.int64).reshape(E, capacity)
+        row_of, token_experts = expert_choice_rows(sel, T)
     toks = np.arange(T) if token_subset is None else np.asarray(token_subset)
     pos = {int(t): i for i, t in enumerate(toks)}
     y = np.zeros((len(toks), d), dtype=np.float64)
@@ -404,7 +437,7 @@ def dequantize_fp8_rows(codes, scales):
 
 
 def forward(x, w_router, b_router, w_up, b_up, w_down, b_down, *, top_k, num_shared,
-            gating, activation, cap=None, token_subset=None):
+            gating, activation, cap=None, token_subset=None, idx=None):
     """The whole MoE-FFN forward: router -> gate -> top-k + renorm -> dispatch
     with capacity -> expert FFNs -> gate-weighted combine (+ shared experts)
     -> f, P, L_aux.  ([0539edu] 1.3 flow and 4.1 MoEFFN; [kamacoder] 二 data
@@ -412,12 +445,21 @@ def forward(x, w_router, b_router, w_up, b_up, w_down, b_down, *, top_k, num_sha
 
     Routing, dispatch and the aux statistics always cover all T tokens (the
     capacity couples tokens).  If token_subset is given, y is evaluated only
-    for those tokens (rows of y in subset order); otherwise for all."""
+    for those tokens (rows of y in subset order); otherwise for all.
+
+    idx [T, k]: evaluate the layer at this selection (slot order as given)
+    instead of the oracle's own top-k; the weights, dispatch, drops, FFNs,
+    combine and f then follow from it, and gap stays that of the oracle's
+    own scores."""
     T, d = x.shape
     E = w_router.shape[0]
     logits = router_logits(x, w_router, b_router)
     probs = gate(logits, gating)
-    idx, w = topk_renorm(probs, top_k)
+    if idx is None:
+        idx, w = topk_renorm(probs, top_k)
+    else:
+        idx = np.asarray(idx, dtype=np.int32).reshape(T, top_k)
+        w = renorm(probs, idx)
     disp = dispatch(idx, E, cap)
     f, P, l_aux = aux_stats(idx, probs, E)
 

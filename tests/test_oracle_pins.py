@@ -605,3 +605,119 @@ def test_expert_choice_orphans_get_only_shared_experts():
             ref = ref + out["probs"][t, e] * O.expert_ffn(x[[t]], w_up[e], None, w_dn[e], None,
                                                           "gelu")[0]
     assert np.allclose(out["y"][t], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_expert_choice_gap_hand_values():
+    # expert 0 column (.9, .5, .3, .2): C = 2 -> .5 - .3; C = 3 -> .3 - .2
+    # expert 1 column (.4, .4, .1, 0): C = 1 -> an exact tie, gap 0
+    probs = np.array([[0.9, 0.4], [0.5, 0.4], [0.3, 0.1], [0.2, 0.0]])
+    g2 = O.expert_choice_gap(probs, 2)
+    assert g2[0] == pytest.approx(0.2, abs=1e-15) and g2[1] == pytest.approx(0.3, abs=1e-15)
+    g1 = O.expert_choice_gap(probs, 1)
+    assert g1[0] == pytest.approx(0.4, abs=1e-15) and g1[1] == 0.0
+    g3 = O.expert_choice_gap(probs, 3)
+    assert g3[0] == pytest.approx(0.1, abs=1e-15) and g3[1] == pytest.approx(0.1, abs=1e-15)
+    # every token taken: nothing is left out, the gap is infinite
+    assert np.all(O.expert_choice_gap(probs, 4) == np.inf)
+    assert np.all(O.expert_choice_gap(probs, 9) == np.inf)
+    # the gap is the C-th best minus the (C+1)-th best, whatever the token order
+    rng = np.random.default_rng(12)
+    p = rng.random((11, 3))
+    for C in range(1, 11):
+        for e in range(3):
+            col = sorted(p[:, e], reverse=True)
+            assert O.expert_choice_gap(p, C)[e] == col[C - 1] - col[C]
+
+
+def _selection_bruteforce(P, idx, probs, E, S, act, cap):
+    """y at a given selection, written out per token: w = the selected
+    probabilities renormalized, a slot is dropped once its expert already holds
+    cap earlier assignments (token order, then slot), shared experts unmasked."""
+    T, k = idx.shape
+    bu = lambda q: None if P["b_up"] is None else P["b_up"][q]
+    bd = lambda q: None if P["b_down"] is None else P["b_down"][q]
+    outs = [_torch_ffn(P["x"], P["w_up"][q], bu(q), P["w_down"][q], bd(q), act)
+            for q in range(E + S)]
+    seen = [0] * E
+    y = np.zeros((T, P["x"].shape[1]))
+    for t in range(T):
+        tot = sum(probs[t, int(e)] for e in idx[t])
+        for s in range(k):
+            e = int(idx[t, s])
+            if cap is None or seen[e] < cap:
+                y[t] += probs[t, e] / tot * outs[e][t]
+            seen[e] += 1
+        for q in range(E, E + S):
+            y[t] += outs[q][t]
+    return y
+
+
+@pytest.mark.parametrize("gating,act,cap", [("softmax", "gelu", None), ("softmax", "relu", 5),
+                                            ("sigmoid_norm", "swiglu", 4)])
+def test_forward_at_a_given_selection(gating, act, cap):
+    rng = np.random.default_rng(21)
+    T, d, f, E, S, k = 16, 6, 8, 5, 1, 2
+    P = _tiny_problem(rng, T, d, f, E, S, act, act != "swiglu")
+    own = O.forward(**P, top_k=k, num_shared=S, gating=gating, activation=act, cap=cap)
+    # the oracle's own selection given back reproduces the forward exactly
+    same = O.forward(**P, top_k=k, num_shared=S, gating=gating, activation=act, cap=cap,
+                     idx=own["idx"])
+    for key in ("y", "w", "l_aux", "f", "counts", "offsets", "sorted_assign", "assign_row",
+                "drop_mask"):
+        assert np.array_equal(np.asarray(same[key]), np.asarray(own[key])), key
+    # another selection: second-best and third-best experts on every other
+    # token, slot order reversed on token 1
+    order = np.argsort(-own["probs"], axis=1, kind="stable")
+    idx = own["idx"].copy()
+    idx[::2] = order[::2, 1:3]
+    idx[1] = idx[1, ::-1]
+    out = O.forward(**P, top_k=k, num_shared=S, gating=gating, activation=act, cap=cap, idx=idx)
+    assert np.array_equal(out["idx"], idx)
+    np.testing.assert_allclose(out["w"].sum(1), 1.0, rtol=1e-15)
+    sel = np.take_along_axis(own["probs"], idx.astype(np.int64), axis=1)
+    np.testing.assert_allclose(out["w"], sel / sel.sum(1, keepdims=True), rtol=1e-15)
+    ref = _selection_bruteforce(P, idx, own["probs"], E, S, act, cap)
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-11, atol=1e-12)
+    # f follows the given selection, P the gate (unchanged), gap the own scores
+    np.testing.assert_array_equal(out["f"], np.bincount(idx.reshape(-1), minlength=E) / (T * k))
+    np.testing.assert_array_equal(out["P"], own["P"])
+    np.testing.assert_array_equal(out["gap"], own["gap"])
+    assert out["l_aux"] == pytest.approx(E * np.sum(out["f"] * own["P"]), rel=1e-15)
+
+
+def test_routing_matches_the_forward():
+    rng = np.random.default_rng(22)
+    P = _tiny_problem(rng, 12, 6, 8, 4, 0, "relu", True)
+    r = O.routing(P["x"], P["w_router"], P["b_router"], top_k=2, gating="softmax")
+    fw = O.forward(**P, top_k=2, num_shared=0, gating="softmax", activation="relu")
+    for key in ("logits", "probs", "idx", "w", "gap"):
+        assert np.array_equal(r[key], fw[key]), key
+
+
+def test_expert_choice_at_a_given_selection():
+    rng = np.random.default_rng(23)
+    T, d, f, E, S, C = 12, 5, 6, 3, 1, 4
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d))
+    w_up = rng.standard_normal((E + S, f, d)) * 0.3
+    w_dn = rng.standard_normal((E + S, d, f)) * 0.3
+    kw = dict(capacity=C, num_shared=S, gating="softmax", activation="relu")
+    own = O.forward_expert_choice(x, wr, None, w_up, None, w_dn, None, **kw)
+    same = O.forward_expert_choice(x, wr, None, w_up, None, w_dn, None, sel=own["sel"], **kw)
+    for key in ("y", "sel", "row_of", "token_experts"):
+        assert np.array_equal(same[key], own[key]), key
+    # expert 0 takes its C worst tokens instead
+    sel = own["sel"].copy()
+    sel[0] = np.sort(np.argsort(own["probs"][:, 0], kind="stable")[:C])
+    out = O.forward_expert_choice(x, wr, None, w_up, None, w_dn, None, sel=sel, **kw)
+    ref = O.expert_ffn(x, w_up[E], None, w_dn[E], None, "relu")
+    for e in range(E):
+        fe = O.expert_ffn(x, w_up[e], None, w_dn[e], None, "relu")
+        for t in sel[e]:
+            ref[t] += own["probs"][t, e] * fe[t]
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-13)
+    row_of = out["row_of"]
+    for e in range(E):
+        assert np.array_equal(np.flatnonzero(row_of[:, e] >= 0), sel[e])
+        assert np.array_equal(row_of[sel[e], e], e * C + np.arange(C))
+    assert np.array_equal(out["token_experts"], (row_of >= 0).sum(1))
