@@ -31,7 +31,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", default=None, help="workload name (default: gpt2)")
+    ap.add_argument("--config", default=None, help="workload name (default: large_prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="also time the forward captured in a HIP graph (graph_ms_per_step)")
@@ -164,7 +164,8 @@ def main():
     run = RUNS[name]
     inp = make_inputs(run)
     g = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
-    del inp
+    if a.no_cpu_baseline:
+        del inp
     if run.w_fp8:
         # one-time preparation (untimed): per-row FP8 E4M3 codes and scales
         for name_w, name_s in (("w_up", "s_up"), ("w_down", "s_down")):
@@ -297,23 +298,29 @@ def main():
                 for j, n in enumerate(names)}
     up_ms = stage_ms["expert_up"]
 
+    dn_ms = stage_ms["expert_down"]
     if decode:
         up_bytes = (touched * F1 * (run.d_model * wsz + (4 if run.w_fp8 else 0)) +
                     T * run.d_model * esz + rows * run.d_ff * 2)
+        dn_bytes = touched * run.d_model * (run.d_ff * wsz + (4 if run.w_fp8 else 0))
         achieved = up_bytes / (up_ms * 1e-3) / 1e9
         roof = {"kernel": "decode_kernel (up)", "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                 "traffic": traffic_for("decode_kernel", name)}
+        stage_frac = {"up": roof["frac"],
+                      "down": round(dn_bytes / (dn_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
     else:
         achieved = up_fl / (up_ms * 1e-3) / 1e12
         roof = {"kernel": "grouped_gemm_kernel (up)", "bound": "mfma",
                 "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic_for("grouped_gemm_kernel", name)}
+        stage_frac = {"up": roof["frac"],
+                      "down": round(down_fl / (dn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
     cpu = None
     if not a.no_cpu_baseline:
-        cpu = cpu_baseline(run, cap, a.cpu_seconds)
+        cpu = cpu_baseline(run, cap, a.cpu_seconds, inp)
 
     step_tflops = step_flops / step_s / 1e12
     step_gbps = step_bytes / step_s / 1e9
@@ -341,6 +348,7 @@ def main():
         "stage_ms": {n: round(v, 5) for n, v in stage_ms.items()},
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
         "roofline": roof,
+        "roofline_frac_by_projection": stage_frac,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
@@ -477,19 +485,30 @@ def traffic_for(kernel, workload):
         return None
 
 
-def cpu_baseline(run, cap, seconds):
-    """The oracle's whole forward on the same workload, repeated until about
-    `seconds` of host time have passed; tokens/s over the repetitions."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(run, cap, seconds, inp):
+    """The oracle's whole forward on the same workload (the same CPU input
+    tensors), repeated until about `seconds` of host time have passed;
+    tokens/s over the repetitions."""
     import numpy as np
 
     import oracle as O
-    from synth import make_inputs, to_f64
+    from synth import to_f64
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count()
-    inp = make_inputs(run)
     f64 = lambda t: None if t is None else _Lazy(t)
     # FP8 expert weights: the oracle's own quantization, dequantized exactly
     f64w = (lambda t: _LazyFP8(t, O)) if run.w_fp8 else f64
@@ -515,8 +534,9 @@ def cpu_baseline(run, cap, seconds):
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 50:
             break
-    sample = (f"oracle forward over the whole {run.T}-token batch (routing, dispatch, aux) "
-              f"with expert FFNs for {n_tok} tokens, x{reps} repetitions in {el:.1f} s")
+    sample = (f"float64 numpy oracle forward over the whole {run.T}-token batch (routing, "
+              f"dispatch, aux) with expert FFNs for {n_tok} tokens, x{reps} repetitions in "
+              f"{el:.1f} s, {threads} BLAS threads on {cpu_model()}")
     return {"value": round(n_tok * reps / el, 1), "unit": "tokens/s", "cores": threads,
             "kind": "oracle", "sample": sample}
 

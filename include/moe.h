@@ -219,9 +219,14 @@ moe_status moe_dispatch(const moe_problem* p, const int32_t* topk_idx, int32_t* 
  * row offsets[E] + q*T + t is token t through shared expert q.
  *   y_exp [T*k + S*T, d] float32 out (only rows < offsets[E] + S*T written)
  * moe_expert_ffn = moe_expert_up followed by moe_expert_down with h in the
- * workspace.  h is [T*k + S*T, d_ff], fp16 for MOE_BF16 problems (bit
- * patterns in uint16) and float32 for MOE_F32.  moe_expert_up uses no
- * workspace (ws may be NULL); the others need moe_workspace_size() bytes.
+ * workspace.  h is [T*k + S*T, d_ff], float32 for MOE_F32 problems.  For
+ * MOE_BF16 problems h holds fp16 bit patterns (uint16) of the activation
+ * times 2^-8, and moe_expert_down multiplies its sums by 2^8 again: fp16
+ * keeps 11 significant bits for |h| >= 2^-6 (an absolute step of 2^-16
+ * below), and activations up to 65504 * 2^8 (about 1.68e7) in magnitude are
+ * represented; larger ones saturate to that value (never inf; NaN stays NaN).
+ * moe_expert_up uses no workspace (ws may be NULL); the others need
+ * moe_workspace_size() bytes.
  */
 moe_status moe_expert_ffn(const moe_problem* p, const void* x, const moe_weights* w,
                           const int32_t* offsets, const int32_t* sorted_assign, float* y_exp,

@@ -319,7 +319,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
                  nt * DR + 4 * g;
 #pragma unroll
     for (int q = 0; q < RG; ++q) {
-      f32x4 v = acc[q];
+      f32x4 v = acc[q] * kHLoadScale;   // h was stored scaled by 2^-8
       if (ks == 0 && a.bias) {
         const uint16_t* b = a.bias + (long long)seg * a.Wrows + nt * DR + 16 * q + 4 * g;
 #pragma unroll
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     for (int q = 0; q < RG / 2; ++q) {
       f16x4 v;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = (_Float16)(silu_f(acc[q][r]) * acc[q + RG / 2][r]);
+      for (int r = 0; r < 4; ++r) v[r] = h_to_f16(silu_f(acc[q][r]) * acc[q + RG / 2][r]);
       *(f16x4*)(hrow + 16 * q) = v;
     }
   } else {
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       for (int r = 0; r < 4; ++r) {
         float z = acc[q][r];
         if (a.bias) z += bf16_to_f32(a.bias[(long long)seg * a.Wrows + nt * DR + 16 * q + 4 * g + r]);
-        v[r] = (_Float16)(MODE == MOE_RELU ? fmaxf(z, 0.f) : gelu_f(z));
+        v[r] = h_to_f16(MODE == MOE_RELU ? fmaxf(z, 0.f) : gelu_f(z));
       }
       *(f16x4*)(hrow + 16 * q) = v;
     }

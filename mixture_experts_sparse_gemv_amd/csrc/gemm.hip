@@ -665,6 +665,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
           float v[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = acc[j][i][4 * g + r];
+          if (CVT16) {   // h was stored scaled by 2^-8
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] *= kHLoadScale;
+          }
           if (SWIGLU) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = silu_f(v[r]) * acc[j + NI / 2][i][4 * g + r];
@@ -684,7 +688,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
               if (MODE == MODE_RELU) v[r] = fmaxf(v[r], 0.0f);
               if (MODE == MODE_GELU) v[r] = gelu_f(v[r]);
             }
-            *(f16x4*)dst = f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+            *(f16x4*)dst = f16x4{h_to_f16(v[0]), h_to_f16(v[1]), h_to_f16(v[2]), h_to_f16(v[3])};
           }
         }
       }

@@ -82,6 +82,19 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t u) {
   return __uint_as_float(((uint32_t)u) << 16);
 }
 
+// The intermediate h of bf16 problems is stored in fp16 scaled by 2^-8 (the
+// down projection multiplies its fp32 sums by 2^8, exactly).  fp16 keeps 11
+// significant bits for |h| >= 2^-6 and an absolute step of 2^-16 below, and
+// the scale moves its overflow from 65504 to 65504 * 2^8 ~ 1.68e7.  Larger
+// magnitudes saturate to +-65504 * 2^8 (never inf); NaN stays NaN.
+constexpr float kHStoreScale = 0.00390625f;   // 2^-8
+constexpr float kHLoadScale = 256.0f;         // 2^8
+__device__ __forceinline__ _Float16 h_to_f16(float v) {
+  v *= kHStoreScale;
+  v = fabsf(v) > 65504.0f ? copysignf(65504.0f, v) : v;
+  return (_Float16)v;
+}
+
 // Eight bf16 values (16 bytes) -> eight fp16 values.  bf16 -> fp32 is exact
 // (a shift); fp32 -> fp16 is exact for magnitudes in [2^-14, 65504], which is
 // where bf16 weights of a trained or N(0, 0.02^2) layer lie; smaller values

@@ -116,9 +116,74 @@ def make_problem(T, d_model, d_ff, num_experts, top_k, num_shared=0, capacity=0,
 
 
 def make_weights(w_router, b_router, w_up, b_up, w_down, b_down, s_up=None, s_down=None):
-    """s_up / s_down: the FP8 row scales when w_up / w_down hold E4M3 codes."""
-    return moe_weights(*[_ptr(t) for t in (w_router, b_router, w_up, b_up, w_down, b_down,
-                                           s_up, s_down)])
+    """s_up / s_down: the FP8 row scales when w_up / w_down hold E4M3 codes.
+    The tensors stay attached to the returned struct, so that every entry
+    point checks their dtypes and sizes against its problem."""
+    t = (w_router, b_router, w_up, b_up, w_down, b_down, s_up, s_down)
+    w = moe_weights(*[_ptr(v) for v in t])
+    w._tensors = dict(zip(("w_router", "b_router", "w_up", "b_up", "w_down", "b_down", "s_up",
+                           "s_down"), t))
+    return w
+
+
+def _act_dtype(p):
+    return torch.bfloat16 if p.dtype == MOE_BF16 else torch.float32
+
+
+def _check_x(p, x):
+    if x is None:
+        raise ValueError("x is required")
+    _need(x, p.T * p.d_model, _act_dtype(p), "x")
+
+
+def _check_weights(p, w):
+    """dtype and size of each weight tensor the problem reads (FP8 codes are
+    uint8 with float32 row scales)."""
+    t = getattr(w, "_tensors", None)
+    if t is None:
+        return
+    E, S, d, f = p.num_experts, p.num_shared, p.d_model, p.d_ff
+    F1 = 2 * f if p.activation == MOE_SWIGLU else f
+    act = _act_dtype(p)
+    wdt = torch.uint8 if p.flags & MOE_W_FP8 else act
+    _need(t["w_router"], E * d, act, "w_router")
+    _need(t["b_router"], E, act, "b_router")
+    _need(t["w_up"], (E + S) * F1 * d, wdt, "w_up")
+    _need(t["w_down"], (E + S) * d * f, wdt, "w_down")
+    _need(t["b_up"], (E + S) * F1, act, "b_up")
+    _need(t["b_down"], (E + S) * d, act, "b_down")
+    if p.flags & MOE_W_FP8:
+        _need(t["s_up"], (E + S) * F1, torch.float32, "s_up")
+        _need(t["s_down"], (E + S) * d, torch.float32, "s_down")
+
+
+def routing_sizes(p):
+    """(element count, dtype) of every moe_routing field for problem p."""
+    T, k, E = p.T, p.top_k, p.num_experts
+    i32, f32 = torch.int32, torch.float32
+    if p.flags & MOE_EXPERT_CHOICE:
+        n = E * p.capacity
+        return dict(topk_idx=(0, i32), topk_w=(0, f32), probs=(T * E, f32), counts=(E, i32),
+                    kept=(E, i32), offsets=(E + 1, i32), sorted_assign=(n, i32),
+                    assign_row=(T * E, i32), drop_mask=(0, torch.uint8), f=(E, f32), P=(E, f32),
+                    l_aux=(1, f32), stats=(8, i32), token_experts=(T, i32))
+    return dict(topk_idx=(T * k, i32), topk_w=(T * k, f32), probs=(T * E, f32), counts=(E, i32),
+                kept=(E, i32), offsets=(E + 1, i32), sorted_assign=(T * k, i32),
+                assign_row=(T * k, i32), drop_mask=(T * k, torch.uint8), f=(E, f32), P=(E, f32),
+                l_aux=(1, f32), stats=(8, i32), token_experts=(0, i32))
+
+
+def _routing_struct(p, routing):
+    sizes = routing_sizes(p)
+    for name, t in routing.items():
+        if name not in sizes:
+            raise ValueError(f"unknown routing field {name}")
+        n, dt = sizes[name]
+        if name == "stats" and t is not None and t.numel() * t.element_size() < 32:
+            raise ValueError("stats: need 32 bytes")
+        elif name != "stats":
+            _need(t, n, dt, name)
+    return moe_routing(**{k: _ptr(v) for k, v in routing.items()})
 
 
 def _ptr(t):
@@ -190,6 +255,8 @@ def workspace(p, device="cuda"):
 
 def moe_router_topk(p, x, w, topk_idx, topk_w, probs=None, prob_colsum=None, ws=None,
                     stream=None):
+    _check_x(p, x)
+    _check_weights(p, w)
     _need(topk_idx, p.T * p.top_k, torch.int32, "topk_idx")
     _need(topk_w, p.T * p.top_k, torch.float32, "topk_w")
     _need(probs, p.T * p.num_experts, torch.float32, "probs")
@@ -215,6 +282,8 @@ def moe_dispatch(p, topk_idx, counts, kept, offsets, sorted_assign, assign_row, 
 
 
 def moe_expert_ffn(p, x, w, offsets, sorted_assign, y_exp, ws, stream=None):
+    _check_x(p, x)
+    _check_weights(p, w)
     _need(y_exp, max_rows(p) * p.d_model, torch.float32, "y_exp")
     wp, wb = _ws(ws)
     _check("moe_expert_ffn", _lib.moe_expert_ffn(
@@ -223,6 +292,8 @@ def moe_expert_ffn(p, x, w, offsets, sorted_assign, y_exp, ws, stream=None):
 
 
 def moe_expert_up(p, x, w, offsets, sorted_assign, h, ws=None, stream=None):
+    _check_x(p, x)
+    _check_weights(p, w)
     _need(h, max_rows(p) * p.d_ff, h_dtype(p), "h")
     wp, wb = _ws(ws)
     _check("moe_expert_up", _lib.moe_expert_up(
@@ -231,6 +302,7 @@ def moe_expert_up(p, x, w, offsets, sorted_assign, h, ws=None, stream=None):
 
 
 def moe_expert_down(p, w, offsets, h, y_exp, ws, stream=None):
+    _check_weights(p, w)
     _need(h, max_rows(p) * p.d_ff, h_dtype(p), "h")
     _need(y_exp, max_rows(p) * p.d_model, torch.float32, "y_exp")
     wp, wb = _ws(ws)
@@ -306,9 +378,11 @@ def moe_quantize_fp8(w, q, scale, stream=None):
 def moe_ffn_forward(p, w, x, y, ws, routing=None, stream=None):
     """routing: optional dict of output tensors named as moe_routing's fields."""
     _need(y, p.T * p.d_model, torch.float32, "y")
+    _check_x(p, x)
+    _check_weights(p, w)
     r = None
     if routing:
-        r = moe_routing(**{k: _ptr(v) for k, v in routing.items()})
+        r = _routing_struct(p, routing)
     wp, wb = _ws(ws)
     _check("moe_ffn_forward", _lib.moe_ffn_forward(
         ctypes.byref(p), ctypes.byref(w), _ptr(x), _ptr(y),
@@ -346,7 +420,9 @@ def moe_ffn_backward(p, w, x, dy, alpha, routing, grads, ws, stream=None):
         if k not in sizes:
             raise ValueError(f"unknown gradient {k}")
         _need(v, sizes[k], torch.float32, k)
-    r = moe_routing(**{k: _ptr(v) for k, v in routing.items()})
+    _check_x(p, x)
+    _check_weights(p, w)
+    r = _routing_struct(p, routing)
     g = moe_grads(**{k: _ptr(v) for k, v in grads.items()})
     wp, wb = _ws(ws)
     _check("moe_ffn_backward", _lib.moe_ffn_backward(

@@ -78,21 +78,31 @@ def weights_of(g):
 
 class LazyDeqFP8:
     """Per-expert float64 weights of a [n, rows, K] bf16 tensor as the oracle
-    quantizes them (codes and scales from the oracle's own quantizer)."""
+    quantizes them (codes and scales from the oracle's own quantizer).  The
+    codes of all experts are computed up front, several experts at a time
+    (numpy releases the interpreter lock in its array operations), with a
+    line per expert; each access dequantizes one expert."""
 
-    def __init__(self, t):
+    def __init__(self, t, workers=8):
+        from concurrent.futures import ThreadPoolExecutor
         self.t = t
         self.shape = tuple(t.shape)
 
+        def one(i):
+            q = O.quantize_fp8_rows(t[i].to(torch.float32).numpy())
+            print(f"  oracle FP8 codes of expert {i} ({tuple(t.shape[1:])})", flush=True)
+            return q
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            self.codes = list(ex.map(one, range(t.shape[0])))
+
     def __getitem__(self, i):
-        w = self.t[i].to(torch.float32).numpy()
-        codes, scales = O.quantize_fp8_rows(w)
-        return O.dequantize_fp8_rows(codes, scales)
+        return O.dequantize_fp8_rows(*self.codes[i])
 
 
-def oracle_forward(run, inp, cap="run", token_subset=None, w_fp8=None):
+def oracle_forward(run, inp, cap="run", token_subset=None, w_fp8=None, idx=None, sel=None):
     """w_fp8 (default: run.w_fp8): expert weights as the oracle's own FP8
-    quantization of the bf16 weights, dequantized exactly."""
+    quantization of the bf16 weights, dequantized exactly.  idx (token
+    choice) / sel (expert choice): evaluate the layer at that selection."""
     c = oracle_capacity(run) if cap == "run" else cap
     fp8 = run.w_fp8 if w_fp8 is None else w_fp8
     lazy = lambda t: None if t is None else LazyF64(t)
@@ -102,12 +112,19 @@ def oracle_forward(run, inp, cap="run", token_subset=None, w_fp8=None):
             to_f64(inp["x"]), to_f64(inp["w_router"]), to_f64(inp["b_router"]),
             lazyw(inp["w_up"]), lazy(inp["b_up"]), lazyw(inp["w_down"]), lazy(inp["b_down"]),
             capacity=c, num_shared=run.num_shared, gating=run.gating,
-            activation=run.activation, token_subset=token_subset)
+            activation=run.activation, token_subset=token_subset, sel=sel)
     return O.forward(to_f64(inp["x"]), to_f64(inp["w_router"]), to_f64(inp["b_router"]),
                      lazyw(inp["w_up"]), lazy(inp["b_up"]), lazyw(inp["w_down"]),
                      lazy(inp["b_down"]), top_k=run.top_k, num_shared=run.num_shared,
                      gating=run.gating, activation=run.activation, cap=c,
-                     token_subset=token_subset)
+                     token_subset=token_subset, idx=idx)
+
+
+def oracle_routing(run, inp):
+    """The oracle's own routing over every token (logits, probs, idx, w, gap),
+    without the expert FFNs (token choice)."""
+    return O.routing(to_f64(inp["x"]), to_f64(inp["w_router"]), to_f64(inp["b_router"]),
+                     top_k=run.top_k, gating=run.gating)
 
 
 def assert_close(got, ref, name, rel=REL_FROB, mabs=MAX_ABS):
@@ -158,19 +175,6 @@ def check_dispatch_bitexact(gpu, orc, E):
     assert np.array_equal(gpu["drop_mask"], orc["drop_mask"]), "drop_mask"
 
 
-def check_dispatch_consistent(gpu, gpu_idx, E, cap):
-    """Properties of a dispatch given its own routing (used where routing
-    differs from the oracle on near-tie tokens)."""
-    flat = np.asarray(gpu_idx).reshape(-1)
-    n = flat.size
-    counts = np.bincount(flat, minlength=E)
-    assert np.array_equal(gpu["counts"], counts)
-    kept = counts if not cap else np.minimum(counts, cap)
-    assert np.array_equal(gpu["kept"], kept)
-    assert np.array_equal(gpu["offsets"], np.concatenate([[0], np.cumsum(kept)]))
-    assert sorted(gpu["sorted_assign"].tolist()) == list(range(n))
-
-
 def routing_outputs(p, device="cuda"):
     T, k, E = p.T, p.top_k, p.num_experts
     i32 = dict(dtype=torch.int32, device=device)
@@ -206,45 +210,36 @@ def run_forward(run, g, p=None, routing=True):
     return out
 
 
-def compare_forward(run, gpu, orc, token_subset=None):
-    """Full comparison of a forward pass against the oracle."""
+def compare_forward(run, gpu, orc, inp=None, token_subset=None, w_fp8=None):
+    """Full comparison of a forward pass against the oracle.
+
+    orc: the oracle's own forward (or only its routing, oracle_routing).  The
+    GPU's selection is checked against the oracle's own (check_routing); then
+    the layer is compared at the GPU's selection: when that differs from the
+    oracle's (a near-tie flip, or slots in another order) or orc holds no y,
+    the oracle is evaluated again at the GPU's topk_idx (needs inp), so the
+    dispatch outputs are bit-exact and y is compared on every token."""
     k, E, T = run.top_k, run.num_experts, run.T
     gi = gpu["topk_idx"].reshape(T, k)
     same = check_routing(gi, orc, k)
-    cap = oracle_capacity(run)
-    if same.all():
-        check_dispatch_bitexact(gpu, orc, E)
-    else:
-        check_dispatch_consistent(gpu, gi, E, cap)
-    # weights and probabilities
-    exact = np.all(gi == orc["idx"], axis=1)
-    assert_close(gpu["topk_w"].reshape(T, k)[exact], orc["w"][exact], "topk_w")
+    if not np.array_equal(gi, orc["idx"]) or "y" not in orc:
+        assert inp is not None, "the oracle at the GPU's selection needs the inputs"
+        n_flip = int((~np.all(gi == orc["idx"], axis=1)).sum())
+        print(f"  oracle evaluated at the GPU's selection ({n_flip} tokens differ from its own)",
+              flush=True)
+        orc = oracle_forward(run, inp, token_subset=token_subset, w_fp8=w_fp8, idx=gi)
+    check_dispatch_bitexact(gpu, orc, E)
+    assert_close(gpu["topk_w"].reshape(T, k), orc["w"], "topk_w")
     assert_close(gpu["probs"].reshape(T, E), orc["probs"], "probs")
-    # y on tokens whose routing and drops agree
-    gdrop = gpu["drop_mask"].reshape(T, k)
-    odrop = orc["drop_mask"].reshape(T, k)
-    gperm = np.argsort(gi, axis=1)
-    operm = np.argsort(orc["idx"], axis=1)
-    agree = same & np.all(np.take_along_axis(gdrop, gperm, 1) ==
-                          np.take_along_axis(odrop, operm, 1), axis=1)
-    n_dis = int((~agree).sum())
-    assert n_dis <= max(2, int(0.002 * T)), f"{n_dis} tokens disagree"
     toks = orc["tokens"]
-    mask = agree[toks]
-    assert_close(gpu["y"][toks][mask], orc["y"][mask], "y")
-    # aux statistics
-    n_flip = int((~same).sum())
-    tol = LAUX_REL * abs(orc["l_aux"]) + n_flip * E * float(orc["P"].max()) / (T * k)
+    assert_close(gpu["y"][toks], orc["y"], "y")
+    # aux statistics (f from the shared selection's counts, P from the gate)
     print(f"  l_aux gpu={float(gpu['l_aux'][0]):.6f} oracle={orc['l_aux']:.6f}", flush=True)
-    assert abs(float(gpu["l_aux"][0]) - orc["l_aux"]) <= tol
+    assert abs(float(gpu["l_aux"][0]) - orc["l_aux"]) <= LAUX_REL * abs(orc["l_aux"])
     assert_close(gpu["P"], orc["P"], "P", rel=1e-4, mabs=1e-5)
-    # routing health: the kernel's arithmetic on its own counts, kept and P,
-    # and the oracle's values where the routing agrees
-    check_route_stats(gpu["stats"], O.routing_stats(gpu["counts"], gpu["kept"], gpu["P"]))
-    if same.all():
-        np.testing.assert_allclose(gpu["f"], orc["f"], rtol=1e-6)
-        check_route_stats(gpu["stats"], orc["stats"])
-    return agree
+    np.testing.assert_allclose(gpu["f"], orc["f"], rtol=1e-6)
+    check_route_stats(gpu["stats"], orc["stats"])
+    return same
 
 
 def check_route_stats(got, ref):
@@ -260,12 +255,12 @@ def inputs_for(run):
     return make_inputs(run)
 
 
-def compare_forward_ec(run, gpu, orc):
+def compare_forward_ec(run, gpu, orc, inp=None, token_subset=None):
     """Expert-choice forward against the oracle.  Selection: experts whose
     C-th and (C+1)-th best scores differ by more than GAP pick exactly the
     oracle's tokens; elsewhere every picked token scores within GAP of the
-    oracle's C-th best.  y is compared on the tokens picked by the same set
-    of experts."""
+    oracle's C-th best.  When the selections differ the oracle is evaluated
+    again at the GPU's selection (needs inp); y is compared on every token."""
     T, E = run.T, run.num_experts
     C = oracle_capacity(run)
     probs = orc["probs"]
@@ -280,18 +275,16 @@ def compare_forward_ec(run, gpu, orc):
             assert np.array_equal(gsel[e], orc["sel"][e]), f"expert {e} picked other tokens"
         else:
             assert np.all(probs[gsel[e], e] >= kth[e] - GAP)
+    if not np.array_equal(gsel, orc["sel"]):
+        assert inp is not None, "the oracle at the GPU's selection needs the inputs"
+        n = int((gsel != orc["sel"]).any(axis=1).sum())
+        print(f"  oracle evaluated at the GPU's selection ({n} experts differ)", flush=True)
+        orc = oracle_forward(run, inp, token_subset=token_subset, sel=gsel)
     row_of = gpu["assign_row"].reshape(T, E)
-    for e in range(E):   # row_of is consistent with the GPU's own selection
-        assert np.array_equal(np.flatnonzero(row_of[:, e] >= 0), gsel[e])
-        assert np.array_equal(row_of[gsel[e], e], e * C + np.arange(C))
-    assert np.array_equal(gpu["token_experts"], (row_of >= 0).sum(1))
-    agree = np.all((row_of >= 0) == (orc["row_of"] >= 0), axis=1)
-    n_dis = int((~agree).sum())
-    assert n_dis <= max(2, int(0.002 * T)), f"{n_dis} tokens picked by other experts"
+    assert np.array_equal(row_of, orc["row_of"]), "row_of"
+    assert np.array_equal(gpu["token_experts"], orc["token_experts"])
     toks = orc["tokens"]
-    mask = agree[toks]
-    assert_close(gpu["y"][toks][mask], orc["y"][mask], "y")
+    assert_close(gpu["y"][toks], orc["y"], "y")
     np.testing.assert_allclose(gpu["f"], np.full(E, 1.0 / E), rtol=1e-6)
     assert_close(gpu["P"], probs.mean(0), "P", rel=1e-4, mabs=1e-5)
     check_route_stats(gpu["stats"], O.routing_stats(gpu["counts"], gpu["kept"], gpu["P"]))
-    return agree

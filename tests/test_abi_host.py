@@ -166,3 +166,42 @@ def test_fp8_weights_validation():
     assert lib.moe_quantize_fp8(fake, 0, 64, fake, fake, None) == M.MOE_ERR_INVALID_ARG
     assert lib.moe_quantize_fp8(fake, 4, 60, fake, fake, None) == M.MOE_ERR_UNSUPPORTED
     assert lib.moe_quantize_fp8(fake, 1 << 31, 64, fake, fake, None) == M.MOE_ERR_UNSUPPORTED
+
+
+def test_binding_checks_routing_x_and_weights_before_any_call():
+    """moe_ffn_forward / moe_ffn_backward check every routing buffer, x and the
+    weight tensors against the problem on the host (a wrong dtype or an
+    undersized buffer raises before the library is called)."""
+    import torch
+    p = _problem()
+    T, k, E, d = p.T, p.top_k, p.num_experts, p.d_model
+    y = torch.empty(T * d)
+    x64 = torch.empty(T * d, dtype=torch.float32)    # bf16 problem: wrong dtype
+    with pytest.raises(ValueError, match="x:"):
+        M.moe_ffn_forward(p, M.moe_weights(), x64, y, None)
+    xs = torch.empty(T * d - 1, dtype=torch.bfloat16)  # one element short
+    with pytest.raises(ValueError, match="x:"):
+        M.moe_ffn_forward(p, M.moe_weights(), xs, y, None)
+    x = torch.empty(T * d, dtype=torch.bfloat16)
+    for name, bad in (("topk_idx", torch.empty(T * k, dtype=torch.int64)),
+                      ("sorted_assign", torch.empty(T * k - 1, dtype=torch.int32)),
+                      ("probs", torch.empty(T * E, dtype=torch.float16)),
+                      ("drop_mask", torch.empty(T * k, dtype=torch.int32)),
+                      ("offsets", torch.empty(E, dtype=torch.int32))):
+        with pytest.raises(ValueError, match=name):
+            M.moe_ffn_forward(p, M.moe_weights(), x, y, None, routing={name: bad})
+    with pytest.raises(ValueError, match="unknown routing field"):
+        M.moe_ffn_forward(p, M.moe_weights(), x, y, None, routing={"idx": x})
+
+    class W:   # the tensors make_weights attaches, without GPU pointers
+        _tensors = dict(w_router=torch.empty(E * d, dtype=torch.bfloat16), b_router=None,
+                        w_up=torch.empty(E * 2 * p.d_ff * d - 8, dtype=torch.bfloat16),
+                        b_up=None, w_down=torch.empty(E * d * p.d_ff, dtype=torch.bfloat16),
+                        b_down=None, s_up=None, s_down=None)
+    with pytest.raises(ValueError, match="w_up"):
+        M._check_weights(p, W())
+    W._tensors["w_up"] = torch.empty(E * 2 * p.d_ff * d, dtype=torch.bfloat16)
+    M._check_weights(p, W())
+    W._tensors["w_router"] = torch.empty(E * d, dtype=torch.float32)
+    with pytest.raises(ValueError, match="w_router"):
+        M._check_weights(p, W())

@@ -65,7 +65,7 @@ def test_forward_fp8_weights(name):
     gpu = run_forward(run, g)
     del g
     orc = oracle_forward(run, inp)
-    compare_forward(run, gpu, orc)
+    compare_forward(run, gpu, orc, inp)
     # error budget: FP8 weights against the bf16 weights (oracle both ways)
     ref = oracle_forward(run, inp, w_fp8=False)
     e = orc["y"] - ref["y"]

@@ -60,7 +60,7 @@ def test_forward_small(name):
          f"k={run.top_k} S={run.num_shared} seed={run.seed}")
     g = gpu_inputs(inp)
     gpu = run_forward(run, g)
-    compare_forward(run, gpu, _oracle(name))
+    compare_forward(run, gpu, _oracle(name), inp)
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -293,3 +293,41 @@ def test_routing_stats_entry_point_given_oracle_inputs():
                             torch.tensor(Pv, dtype=torch.float32, device="cuda"), st)
         torch.cuda.synchronize()
         check_route_stats(M.route_stats_dict(st), ref)
+
+
+# Activations far beyond fp16's range: x drawn with std 128 (256 for the
+# 16-token case, which has fewer rows to reach the tail), so that the SwiGLU
+# intermediate silu(x Wg) * (x Wu) reaches |h| above 65504 (checked on the
+# oracle's side below); the grouped GEMM path (T = 300) and the decode path
+# (T = 16).  y then reaches about 1e4, so the absolute bound is taken
+# relative to max |y|: 2e-3 max |y_ref| (the runs at the workloads' scale
+# have max |y| of about 10 against the 2e-2 bound).
+LARGE_H = {
+    "swiglu_T300_x128": scaled(RUNS["large_prefill"], T=300, d_model=1024, d_ff=1024,
+                               x_std=128.0, seed=31),
+    "swiglu_decode_T16_x256": scaled(RUNS["large_prefill"], T=16, d_model=1024, d_ff=1024,
+                                     x_std=256.0, seed=32),
+}
+
+
+@pytest.mark.parametrize("name", list(LARGE_H))
+def test_forward_h_beyond_fp16_range(name):
+    run = LARGE_H[name]
+    _say(f"[forward large h] {name}: T={run.T} d={run.d_model} f={run.d_ff} x_std={run.x_std}")
+    inp = make_inputs(run)
+    g = gpu_inputs(inp)
+    gpu = run_forward(run, g)
+    orc = oracle_forward(run, inp, idx=gpu["topk_idx"].reshape(run.T, run.top_k))
+    # the case exercises what it is for: |h| beyond 65504 on the selected rows
+    x = to_f64(inp["x"])
+    hmax = 0.0
+    for e in range(run.num_experts):
+        rows = orc["sorted_assign"][orc["offsets"][e]:orc["offsets"][e + 1]] // run.top_k
+        if rows.size:
+            z = x[rows] @ inp["w_up"][e].to(torch.float64).numpy().T
+            hmax = max(hmax, float(np.abs(O.silu(z[:, :run.d_ff]) * z[:, run.d_ff:]).max()))
+    _say(f"  max |h| = {hmax:.3e}")
+    assert hmax > 65504.0
+    check_dispatch_bitexact(gpu, orc, run.num_experts)
+    ymax = float(np.abs(orc["y"]).max())
+    assert_close(gpu["y"], orc["y"], "y", mabs=2e-3 * ymax)

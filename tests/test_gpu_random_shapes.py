@@ -81,7 +81,7 @@ def test_forward_random_shape(i):
     inp = _inputs(i)
     g = gpu_inputs(inp)
     gpu = run_forward(run, g)
-    compare_forward(run, gpu, oracle_forward(run, inp))
+    compare_forward(run, gpu, oracle_forward(run, inp), inp)
 
 
 BWD = [i for i, r in enumerate(CASES) if r.dtype == "bf16"][:10]
