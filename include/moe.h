@@ -295,6 +295,24 @@ moe_status moe_ffn_forward(const moe_problem* p, const moe_weights* w, const voi
                            hipStream_t stream);
 
 /*
+ * moe_ffn_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same kernels and results, with the workspace taken from a file-scope
+ * device array of MOE_STATIC_SCRATCH_BYTES that the library holds on every
+ * device it runs on until the process ends (looked up, once per device, on
+ * the first call with that device current; the stream must belong to the
+ * current device).  Arguments as moe_ffn_forward without ws / ws_bytes.
+ * Returns MOE_ERR_WORKSPACE, launching nothing, when the problem's
+ * moe_workspace_size exceeds MOE_STATIC_SCRATCH_BYTES.  Allocates nothing.
+ * Every call on a device shares that device's array, which keeps the last
+ * call's contents (the forward needs none of it cleared): calls that overlap
+ * on one device (other streams, other host threads) race.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (128u << 20)
+moe_status moe_ffn_forward_static(const moe_problem* p, const moe_weights* w, const void* x,
+                                  float* y, const moe_routing* out, hipStream_t stream);
+
+/*
  * Per-row FP8 E4M3 quantization (0539edu page 5.2: expert parameters in 8
  * bits), a one-time preparation of weights for MOE_W_FP8.  Row r of the
  * [rows, cols] bf16 matrix w gets scale[r] = max_j |w[r, j]| / 448 (1 for an

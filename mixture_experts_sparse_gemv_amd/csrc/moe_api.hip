@@ -94,6 +94,8 @@ static moe_status fail_hip(hipError_t e) {
   return MOE_ERR_HIP;
 }
 
+moe_status hip_failure(hipError_t e) { return fail_hip(e); }
+
 // Validate the problem; on success fill `s`.
 static moe_status check_problem(const moe_problem* p, Shape& s) {
   if (!p) return MOE_ERR_INVALID_ARG;

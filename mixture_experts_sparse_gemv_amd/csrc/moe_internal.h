@@ -66,6 +66,9 @@ struct WsLayout {
       assign_row, drop_mask, f, P, l_aux, h, y_exp, y_part, total;
 };
 WsLayout ws_layout(const Shape& s);
+// MOE_OK for hipSuccess; otherwise records e as the thread's last HIP error
+// (moe_last_hip_error) and returns MOE_ERR_HIP.
+moe_status hip_failure(hipError_t e);
 
 // ---------------------------------------------------------------- vector types
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

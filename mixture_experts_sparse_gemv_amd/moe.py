@@ -25,6 +25,7 @@ MOE_ROUTER_BIAS, MOE_EXPERT_BIAS, MOE_W_FP8, MOE_EXPERT_CHOICE = 1, 2, 8, 16
 EXPORTS = ("moe_capacity", "moe_workspace_size", "moe_router_topk", "moe_dispatch",
            "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_aux_stats",
            "moe_routing_stats", "moe_quantize_fp8", "moe_expert_choice", "moe_ffn_forward",
+           "moe_ffn_forward_static",
            "moe_backward_workspace_size", "moe_ffn_backward", "moe_status_string",
            "moe_last_hip_error")
 
@@ -86,6 +87,7 @@ def _load(path=LIB_PATH):
         "moe_quantize_fp8": (I32, [V, ctypes.c_int64, I32, V, V, V]),
         "moe_expert_choice": (I32, [pp, V, V, V, V, V, V, SZ, V]),
         "moe_ffn_forward": (I32, [pp, pw, V, V, pr, V, SZ, V]),
+        "moe_ffn_forward_static": (I32, [pp, pw, V, V, pr, V]),
         "moe_backward_workspace_size": (I32, [pp, P(SZ)]),
         "moe_ffn_backward": (I32, [pp, pw, V, V, ctypes.c_float, pr, pg, V, SZ, V]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
@@ -387,6 +389,22 @@ def moe_ffn_forward(p, w, x, y, ws, routing=None, stream=None):
     _check("moe_ffn_forward", _lib.moe_ffn_forward(
         ctypes.byref(p), ctypes.byref(w), _ptr(x), _ptr(y),
         ctypes.byref(r) if r is not None else None, wp, wb, _stream(stream)))
+
+
+# bytes of the library's own scratch array (moe_ffn_forward_static)
+STATIC_SCRATCH_BYTES = 128 << 20
+
+
+def moe_ffn_forward_static(p, w, x, y, routing=None, stream=None):
+    """moe_ffn_forward with the library's own device scratch array instead
+    of a workspace (allocates nothing; calls that overlap on one GPU race)."""
+    _need(y, p.T * p.d_model, torch.float32, "y")
+    _check_x(p, x)
+    _check_weights(p, w)
+    r = _routing_struct(p, routing) if routing else None
+    _check("moe_ffn_forward_static", _lib.moe_ffn_forward_static(
+        ctypes.byref(p), ctypes.byref(w), _ptr(x), _ptr(y),
+        ctypes.byref(r) if r is not None else None, _stream(stream)))
 
 
 def moe_backward_workspace_size(p):
