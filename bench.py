@@ -32,6 +32,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default=None, help="workload name (default: large_prefill)")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="run the workload's layer on this many tokens instead of its T "
+                         "(the first T rows of its x draw; weights unchanged)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="also time the forward captured in a HIP graph (graph_ms_per_step)")
@@ -162,6 +165,10 @@ def main():
 
     name = a.config or HEADLINE_RUN
     run = RUNS[name]
+    if a.tokens:
+        from synth import scaled
+        run = scaled(run, T=a.tokens, x_rows=max(run.rows_drawn, a.tokens))
+        name = f"{name}_T{a.tokens}"
     inp = make_inputs(run)
     g = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
     if a.no_cpu_baseline:
@@ -254,7 +261,7 @@ def main():
                                  ((F1 + run.d_model) * 4 if run.w_fp8 else 0))
     step_bytes = (T * run.d_model * esz + E * run.d_model * esz + w_bytes_touched +
                   T * run.d_model * 4)
-    decode = run.dtype == "bf16" and T <= 16
+    decode = run.dtype == "bf16" and T <= 64   # the library's weight-streaming path
 
     # ---- per-stage pass: the same steps through the stage entry points, with
     # events around each stage on the launch stream

@@ -1,12 +1,12 @@
-// Expert FFNs for decode-sized batches (T <= 16): the sparse-GEMV regime
+// Expert FFNs for decode-sized batches (T <= 64): the sparse-GEMV regime
 // ("MoE混合专家模型" 5.2: with few tokens the layer is a stream of the
 // touched experts' weights).
 //
-// Each expert sees at most T <= 16 rows, so the work is a stream of the
+// Each expert sees at most T <= 64 rows, so the work is a stream of the
 // touched experts' weights through the matrix cores with the (few) token
-// rows as the 16-wide MFMA operand: bf16 MFMA 16x16x32 for the up
-// projection, fp16 MFMA 16x16x32 for the down projection (W2 converted to
-// fp16 in registers).  Every weight byte of a touched expert is read from
+// rows as the 16-wide MFMA operand, in up to 4 groups of 16: bf16 MFMA
+// 16x16x32 for the up projection, fp16 MFMA 16x16x32 for the down projection
+// (W2 converted to fp16 in registers).  Every weight byte of a touched expert is read from
 // HBM exactly once; experts with no rows are skipped without reading their
 // weights.
 //
@@ -115,7 +115,9 @@ __device__ __forceinline__ u32x4 e4m3x8_to_16(u32x2 c) {
 // F8: the weights are E4M3 codes with per-row scales (applied to the
 // accumulated sums); a stage then covers 128 K-elements (128 weight bytes
 // per row, as for bf16 with 64) and carries 256 bytes of each token row.
-template <int MODE, bool F8>
+// TG: groups of 16 token rows (a segment of up to 16 TG rows); each weight
+// stage feeds the MFMAs of every group that holds rows of the segment.
+template <int MODE, bool F8, int TG>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   constexpr bool DOWN = MODE == DEC_DOWN, SWIGLU = MODE == MOE_SWIGLU;
   constexpr int DR = DecodeTile<F8>::DR;    // weight rows per work item
@@ -127,8 +129,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   constexpr int SK = F8 ? 128 : 64;      // K elements per stage
   constexpr int NSUBK = SK / 32;         // MFMA k-substeps per stage
   // token rows in registers (XREG) or as XR 128-byte LDS rows per stage
-  constexpr bool XREG = MOE_DECODE_XREG == 2 || (MOE_DECODE_XREG == 1 && F8 && !DOWN);
-  constexpr int XR = XREG ? 0 : (F8 ? 32 : 16);
+  constexpr bool XREG = TG == 1 && (MOE_DECODE_XREG == 2 || (MOE_DECODE_XREG == 1 && F8 && !DOWN));
+  constexpr int XR = XREG ? 0 : (F8 ? 32 : 16) * TG;
   constexpr int NDX = XR / 8;            // their DMA instructions
   constexpr int LR = DR + XR;            // LDS rows per stage: weights, then token rows
   // The ring as distinct arrays ([row][8 chunks of 16 bytes] each): the
@@ -142,6 +144,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   int rows, start;
   seg_info(a.offsets, seg, a.E, a.T, rows, start);
   if (rows <= 0) return;   // untouched expert: its weights are never read
+  const int ntg = (rows + 15) >> 4;   // token groups holding rows (<= TG)
 
   const int nt = DOWN ? it / a.nsplit : it;       // row block of the weight matrix
   const int ks = DOWN ? it % a.nsplit : 0;        // K slice
@@ -185,8 +188,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     const int c = (lane & 7) ^ (((DR + rl) >> 1) & 7);
     xoff[q] = (brow * (uint32_t)a.K + (uint32_t)(half * 64 + c * 8)) * 2u;
   }
-  // fragment reads (byte offsets in a stage): A rows 16q + tl, B token row tl;
-  // k-substep u covers K elements 32u .. 32u+31 of the stage
+  // fragment reads (byte offsets in a stage): A rows 16q + tl, B token row
+  // 16 tg + tl; k-substep u covers K elements 32u .. 32u+31 of the stage
   const int tl = lane & 15, g = lane >> 4;
   const bool tvalid = tl < rows;
   // XREG: the lane's token row (K elements 32u + 8g .. +7 of substep u)
@@ -199,7 +202,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     xroff = (brow * (uint32_t)a.K + (uint32_t)(8 * g)) * 2u;
   }
   (void)xroff;   // read by the device pass only
-  int fpos[RG][NSUBK], bpos[NSUBK];
+  int fpos[RG][NSUBK], bpos[TG][NSUBK];
 #pragma unroll
   for (int u = 0; u < NSUBK; ++u) {
 #pragma unroll
@@ -208,16 +211,22 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       if (F8) fpos[q][u] = r * 128 + (((2 * u + (g >> 1)) ^ ((r >> 1) & 7)) * 16) + 8 * (g & 1);
       else fpos[q][u] = r * 128 + (((4 * u + g) ^ ((r >> 1) & 7)) * 16);
     }
-    const int rb = F8 ? DR + 2 * tl + (u >> 1) : DR + tl;
-    const int cb = F8 ? 4 * (u & 1) + g : 4 * u + g;
-    bpos[u] = rb * 128 + ((cb ^ ((rb >> 1) & 7)) * 16);
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) {
+      const int tr = 16 * tg + tl;
+      const int rb = F8 ? DR + 2 * tr + (u >> 1) : DR + tr;
+      const int cb = F8 ? 4 * (u & 1) + g : 4 * u + g;
+      bpos[tg][u] = rb * 128 + ((cb ^ ((rb >> 1) & 7)) * 16);
+    }
   }
 
   // called with indices that are constants after unrolling
   auto slot = [&](int i) -> u32x4* { return i == 0 ? ring0 : i == 1 ? ring1 : i == 2 ? ring2 : ring3; };
-  f32x4 acc[RG];
+  f32x4 acc[TG][RG];
 #pragma unroll
-  for (int q = 0; q < RG; ++q) acc[q] = f32x4{};
+  for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+    for (int q = 0; q < RG; ++q) acc[tg][q] = f32x4{};
   // XREG: token fragments of the stages in flight, one set per ring slot
   u32x4 xr[XREG ? NST : 1][NSUBK];
 
@@ -244,18 +253,26 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     const char* b = (const char*)buf;
 #pragma unroll
     for (int u = 0; u < NSUBK; ++u) {
-      const u32x4 xv = XREG ? xs[u] : *(const u32x4*)(b + bpos[u]);
+      u32x4 w[RG];
 #pragma unroll
       for (int q = 0; q < RG; ++q) {
-        u32x4 w;
-        if (F8) w = e4m3x8_to_16<DOWN>(*(const u32x2*)(b + fpos[q][u]));
-        else w = DOWN ? bf16x8_to_f16x8(*(const u32x4*)(b + fpos[q][u])) : *(const u32x4*)(b + fpos[q][u]);
-        if (DOWN)
-          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              __builtin_bit_cast(f16x8, w), __builtin_bit_cast(f16x8, xv), acc[q], 0, 0, 0);
-        else
-          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, xv), acc[q], 0, 0, 0);
+        if (F8) w[q] = e4m3x8_to_16<DOWN>(*(const u32x2*)(b + fpos[q][u]));
+        else w[q] = DOWN ? bf16x8_to_f16x8(*(const u32x4*)(b + fpos[q][u])) : *(const u32x4*)(b + fpos[q][u]);
+      }
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg) {
+        if (tg >= ntg) break;   // uniform: no rows of the segment in this group
+        const u32x4 xv = XREG ? xs[u] : *(const u32x4*)(b + bpos[tg][u]);
+#pragma unroll
+        for (int q = 0; q < RG; ++q) {
+          if (DOWN)
+            acc[tg][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                __builtin_bit_cast(f16x8, w[q]), __builtin_bit_cast(f16x8, xv), acc[tg][q], 0, 0, 0);
+          else
+            acc[tg][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, w[q]), __builtin_bit_cast(bf16x8, xv), acc[tg][q], 0, 0,
+                0);
+        }
       }
     }
   };
@@ -302,52 +319,59 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       }
     }
   }
-  if (!tvalid) return;
-
-  // D[row][token]: lane holds token tl and rows 16q + 4g + 0..3 of group q
-  // (consecutive weight rows, so their FP8 scales are one 16-byte load).
+  // D[row][token]: lane holds token 16 tg + tl and rows 16q + 4g + 0..3 of
+  // group q (consecutive weight rows, so their FP8 scales are one 16-byte load).
+  f32x4 sc[RG];
   if (F8) {
 #pragma unroll
-    for (int q = 0; q < RG; ++q) {
-      const f32x4 sc = *(const f32x4*)(a.wscale + (long long)seg * a.Wrows + weight_row(16 * q + 4 * g));
-      acc[q] *= sc;
-    }
+    for (int q = 0; q < RG; ++q)
+      sc[q] = *(const f32x4*)(a.wscale + (long long)seg * a.Wrows + weight_row(16 * q + 4 * g));
   }
-  const long long orow = start + tl;
-  if (DOWN) {
-    float* out = (ks == 0 ? (float*)a.out : a.part + (ks - 1) * a.part_stride) + orow * a.Wrows +
-                 nt * DR + 4 * g;
 #pragma unroll
-    for (int q = 0; q < RG; ++q) {
-      f32x4 v = acc[q] * kHLoadScale;   // h was stored scaled by 2^-8
-      if (ks == 0 && a.bias) {
-        const uint16_t* b = a.bias + (long long)seg * a.Wrows + nt * DR + 16 * q + 4 * g;
+  for (int tg = 0; tg < TG; ++tg) {
+    const int t = 16 * tg + tl;
+    if (t >= rows) break;   // the rows of a segment are 0 .. rows - 1
+    f32x4* ac = acc[tg];
+    if (F8) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] += bf16_to_f32(b[r]);
-      }
-      *(f32x4*)(out + 16 * q) = v;
+      for (int q = 0; q < RG; ++q) ac[q] *= sc[q];
     }
-  } else if (SWIGLU) {
-    _Float16* hrow = (_Float16*)a.out + orow * a.f + nt * (DR / 2) + 4 * g;
+    const long long orow = start + t;
+    if (DOWN) {
+      float* out = (ks == 0 ? (float*)a.out : a.part + (ks - 1) * a.part_stride) + orow * a.Wrows +
+                   nt * DR + 4 * g;
 #pragma unroll
-    for (int q = 0; q < RG / 2; ++q) {
-      f16x4 v;
+      for (int q = 0; q < RG; ++q) {
+        f32x4 v = ac[q] * kHLoadScale;   // h was stored scaled by 2^-8
+        if (ks == 0 && a.bias) {
+          const uint16_t* b = a.bias + (long long)seg * a.Wrows + nt * DR + 16 * q + 4 * g;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = h_to_f16(silu_f(acc[q][r]) * acc[q + RG / 2][r]);
-      *(f16x4*)(hrow + 16 * q) = v;
-    }
-  } else {
-    _Float16* hrow = (_Float16*)a.out + orow * a.f + nt * DR + 4 * g;
-#pragma unroll
-    for (int q = 0; q < RG; ++q) {
-      f16x4 v;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float z = acc[q][r];
-        if (a.bias) z += bf16_to_f32(a.bias[(long long)seg * a.Wrows + nt * DR + 16 * q + 4 * g + r]);
-        v[r] = h_to_f16(MODE == MOE_RELU ? fmaxf(z, 0.f) : gelu_f(z));
+          for (int r = 0; r < 4; ++r) v[r] += bf16_to_f32(b[r]);
+        }
+        *(f32x4*)(out + 16 * q) = v;
       }
-      *(f16x4*)(hrow + 16 * q) = v;
+    } else if (SWIGLU) {
+      _Float16* hrow = (_Float16*)a.out + orow * a.f + nt * (DR / 2) + 4 * g;
+#pragma unroll
+      for (int q = 0; q < RG / 2; ++q) {
+        f16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = h_to_f16(silu_f(ac[q][r]) * ac[q + RG / 2][r]);
+        *(f16x4*)(hrow + 16 * q) = v;
+      }
+    } else {
+      _Float16* hrow = (_Float16*)a.out + orow * a.f + nt * DR + 4 * g;
+#pragma unroll
+      for (int q = 0; q < RG; ++q) {
+        f16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float z = ac[q][r];
+          if (a.bias) z += bf16_to_f32(a.bias[(long long)seg * a.Wrows + nt * DR + 16 * q + 4 * g + r]);
+          v[r] = h_to_f16(MODE == MOE_RELU ? fmaxf(z, 0.f) : gelu_f(z));
+        }
+        *(f16x4*)(hrow + 16 * q) = v;
+      }
     }
   }
 }
@@ -370,6 +394,10 @@ __global__ __launch_bounds__(256) void part_add_kernel(float* __restrict__ y_exp
 
 }  // namespace
 
+// Groups of 16 token rows the decode kernels carry: enough for any segment
+// (a routed expert holds at most T rows, a shared one exactly T).
+static int decode_token_groups(const Shape& s) { return s.T <= 16 ? 1 : s.T <= 32 ? 2 : 4; }
+
 hipError_t launch_decode_up(const Shape& s, const void* x, const void* w_up, const void* b_up,
                             const float* s_up, const int32_t* offsets,
                             const int32_t* sorted_assign, void* h, hipStream_t st) {
@@ -381,8 +409,11 @@ hipError_t launch_decode_up(const Shape& s, const void* x, const void* w_up, con
                s.expert_bias() ? (const uint16_t*)b_up : nullptr, h, nullptr, offsets, sorted_assign,
                s.T, s.tok_div(), s.E, s.S, s.d, s.up_rows(), s.f, 1, items_per_seg, 0,
                (long long)s.T * s.d * 2};
-#define MOE_DECODE_UP(A, F)                                      \
-  decode_kernel<A, F><<<(int)items, 64, 0, st>>>(a)
+  const int tg = decode_token_groups(s);
+#define MOE_DECODE_UP(A, F)                                                      \
+  (tg == 1   ? decode_kernel<A, F, 1><<<(int)items, 64, 0, st>>>(a)              \
+   : tg == 2 ? decode_kernel<A, F, 2><<<(int)items, 64, 0, st>>>(a)              \
+             : decode_kernel<A, F, 4><<<(int)items, 64, 0, st>>>(a))
   if (s.w_fp8()) {
     if (s.act == MOE_SWIGLU) MOE_DECODE_UP(MOE_SWIGLU, true);
     else if (s.act == MOE_GELU) MOE_DECODE_UP(MOE_GELU, true);
@@ -415,8 +446,14 @@ hipError_t launch_decode_down(const Shape& s, const void* h, const void* w_down,
   DecodeArgs a{(const uint16_t*)h, w_down, s_down, b, y_exp, y_part, offsets, nullptr,
                s.T, s.tok_div(), s.E, s.S, s.f, s.d, s.f, nsplit, items_per_seg, part_stride,
                s.max_rows() * s.f * 2};
-  if (s.w_fp8()) decode_kernel<DEC_DOWN, true><<<(int)items, 64, 0, st>>>(a);
-  else decode_kernel<DEC_DOWN, false><<<(int)items, 64, 0, st>>>(a);
+  const int tg = decode_token_groups(s);
+#define MOE_DECODE_DOWN(F)                                                       \
+  (tg == 1   ? decode_kernel<DEC_DOWN, F, 1><<<(int)items, 64, 0, st>>>(a)       \
+   : tg == 2 ? decode_kernel<DEC_DOWN, F, 2><<<(int)items, 64, 0, st>>>(a)       \
+             : decode_kernel<DEC_DOWN, F, 4><<<(int)items, 64, 0, st>>>(a))
+  if (s.w_fp8()) MOE_DECODE_DOWN(true);
+  else MOE_DECODE_DOWN(false);
+#undef MOE_DECODE_DOWN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !complete || nsplit == 1) return e;
   const long long n = s.max_rows() * (s.d / 4);

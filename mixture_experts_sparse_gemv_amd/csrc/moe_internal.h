@@ -13,7 +13,16 @@ namespace moe {
 constexpr int kMaxExperts = 64;       // routed experts: one wave lane per expert
 constexpr int kMaxTopK = 8;
 constexpr int kMaxSegments = 128;     // routed + shared experts
-constexpr int kDecodeMaxT = 16;       // T at or below which the streaming decode path runs
+// T at or below which the streaming decode path runs (at most 64: its kernels
+// carry up to 4 groups of 16 token rows per weight stage).  Measured on the
+// large-expert shape (d_model 4096, SwiGLU 14336, 8 experts, top-2), ms per
+// forward, decode path vs 256-row grouped GEMM tiles: T = 24: 0.47 vs 0.66,
+// 32: 0.47 vs 0.67, 48: 0.54 vs 0.67, 64: 0.56 vs 0.68 (T = 128 by GEMM: 0.69).
+#ifndef MOE_DECODE_MAX_T
+#define MOE_DECODE_MAX_T 64
+#endif
+constexpr int kDecodeMaxT = MOE_DECODE_MAX_T;
+static_assert(kDecodeMaxT >= 1 && kDecodeMaxT <= 64, "decode token groups");
 constexpr int kEcMaxT = 16384;        // expert-choice selection keeps a column of T scores in LDS
 constexpr int kNumCUs = 256;          // MI355X compute units (sizes the K split of small GEMMs)
 

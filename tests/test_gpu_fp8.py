@@ -52,6 +52,12 @@ FP8_CASES = {
     # in both projections: d = 1024, and d_ff = 4096 in 4 K slices)
     "fp8_swiglu_T16_d1024_f4096": scaled(RUNS["large_decode_fp8"], d_model=1024, d_ff=4096,
                                          x_rows=0, seed=11),
+    # 2 and 4 groups of 16 token rows per weight stage
+    "fp8_swiglu_T29": scaled(RUNS["large_decode_fp8"], T=29, d_model=512, d_ff=1024, x_rows=0,
+                             seed=14),
+    "fp8_gelu_bias_T64_shared": scaled(RUNS["large_decode_fp8"], T=64, d_model=256, d_ff=384,
+                                       activation="gelu", expert_bias=True, num_shared=1,
+                                       router_bias="learned", x_rows=0, seed=15),
 }
 
 

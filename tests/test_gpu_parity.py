@@ -23,6 +23,9 @@ SMALL = {
     "swiglu_skew_T3000": scaled(RUNS["swiglu_skew"], T=3000),
     "large_decode": RUNS["large_decode"],
     "large_T300": scaled(RUNS["large_prefill"], T=300),
+    # the weight-streaming path with 2 and 4 groups of 16 token rows
+    "decode_T40_d1024": scaled(RUNS["large_prefill"], T=40, d_model=1024, d_ff=2048),
+    "decode_T64_shared_sigmoid": scaled(RUNS["fine_shared"], T=64, d_model=512, d_ff=768),
     "fine_shared_T1000": scaled(RUNS["fine_shared"], T=1000),
     "fine_shared_T1000_literal": scaled(RUNS["fine_shared"], T=1000, capacity_factor=1.25 / 6),
     # more than 64 16-token router blocks (8 waves each, not 16) with 64

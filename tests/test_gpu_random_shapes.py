@@ -27,7 +27,7 @@ N_CASES = 24
 def _draw(i):
     rng = random.Random(1000 + i)
     dtype = "f32" if i % 8 == 7 else "bf16"
-    T = rng.choice([1, 5, 16, 17, 63, 200, 255, 257, 513, 777])
+    T = rng.choice([1, 5, 16, 17, 33, 63, 64, 65, 200, 255, 257, 513, 777])
     if dtype == "bf16":
         d = rng.choice([64, 128, 192, 320, 512])
         f = rng.choice([64, 128, 192, 448, 640])
@@ -65,6 +65,7 @@ def test_sweep_is_varied():
     """The drawn shapes cover the paths the sweep is for (CPU-side check)."""
     runs = CASES
     assert any(r.T <= 16 and r.dtype == "bf16" for r in runs)        # decode kernels
+    assert any(16 < r.T <= 64 and r.dtype == "bf16" for r in runs)  # several token groups
     assert any(r.T > 256 and r.dtype == "bf16" for r in runs)        # several m-tiles
     assert any(r.num_shared > 0 for r in runs)
     assert any(r.capacity_factor is not None for r in runs)
