@@ -75,9 +75,12 @@ enum { MOE_ROUTER_BIAS = 1, MOE_EXPERT_BIAS = 2,        /* flags                
  * Limits (MOE_ERR_UNSUPPORTED beyond them): E <= 64, top_k <= 8,
  * E + S <= 128, T * (top_k + S) < 2^31, F1 * d_model < 2^30 (F1 = d_ff, or
  * 2 d_ff for SwiGLU: one expert's weights); for MOE_BF16, d_model and d_ff
- * are multiples of 64 and T * d_model, T * d_ff < 2^31 (the kernels address
- * token rows and one expert's rows with 32-bit byte offsets).  GELU is the
- * exact erf form; SwiGLU has no biases.
+ * are multiples of 8 and T * d_model, T * d_ff < 2^31 (the kernels address
+ * token rows and one expert's rows with 32-bit byte offsets).  When both are
+ * multiples of 64 the expert FFNs run on the tiled grouped GEMMs (and the
+ * weight-streaming kernels for T <= 64); otherwise on an untiled grouped GEMM
+ * that is correct for any multiple of 8 but slower.  GELU is the exact erf
+ * form; SwiGLU has no biases.
  * MOE_W_FP8 (expert weights quantized to 8 bits, 0539edu page 5.2) needs
  * MOE_BF16, T <= 64 (the weight-streaming decode path) and d_model, d_ff
  * multiples of 128.
@@ -336,8 +339,9 @@ moe_status moe_quantize_fp8(const void* w, int64_t rows, int32_t cols, uint8_t* 
  * sends none to its expert or gate weight; the router receives gradient
  * through the renormalized top-k weights and through P_e.
  *
- * Limits: dtype MOE_BF16, token-choice routing (no MOE_EXPERT_CHOICE), bf16
- * expert weights (no MOE_W_FP8); otherwise MOE_ERR_UNSUPPORTED.  Also
+ * Limits: dtype MOE_BF16 with d_model and d_ff multiples of 64, token-choice
+ * routing (no MOE_EXPERT_CHOICE), bf16 expert weights (no MOE_W_FP8);
+ * otherwise MOE_ERR_UNSUPPORTED.  Also
  * unsupported when a transposed gradient operand would reach 4 GiB
  * (F1 or d_model times the padded row count, times 2 bytes).
  *

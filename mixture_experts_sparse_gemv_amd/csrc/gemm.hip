@@ -841,7 +841,7 @@ static int gemm_ksplit(const Shape& s, int K, int N) {
 }
 
 int down_ksplit(const Shape& s) {
-  if (s.dtype != MOE_BF16 || s.decode()) return 1;
+  if (s.dtype != MOE_BF16 || s.decode() || s.generic()) return 1;
   return gemm_ksplit(s, s.f, s.d);
 }
 
@@ -880,6 +880,7 @@ hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void
                                                           s.up_rows(), s.f);
     return hipGetLastError();
   }
+  if (s.generic()) return launch_up_generic(s, x, w_up, b_up, offsets, sorted_assign, h, st);
   if (s.decode()) return launch_decode_up(s, x, w_up, b_up, s_up, offsets, sorted_assign, h, st);
   GemmArgs a{(const uint16_t*)x, (const uint16_t*)w_up, (const uint16_t*)bias, h, offsets,
              sorted_assign, s.T, s.tok_div(), s.E, s.S, s.d, s.f, s.up_rows(), s.f, 1, nullptr, 0, 0};
@@ -912,6 +913,7 @@ hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const 
         s.tok_div(), s.E, s.S, s.f, s.d, s.d, s.f);
     return hipGetLastError();
   }
+  if (s.generic()) return launch_down_generic(s, h, w_down, b_down, offsets, y_exp, st);
   if (s.decode())
     return launch_decode_down(s, h, w_down, b_down, s_down, offsets, y_exp, y_part, complete, st);
   const int ks = down_ksplit(s);

@@ -122,7 +122,7 @@ static moe_status check_problem(const moe_problem* p, Shape& s) {
   if (rows >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   if ((long long)rows * p->d_ff >= (1LL << 40) || (long long)rows * p->d_model >= (1LL << 40))
     return MOE_ERR_UNSUPPORTED;
-  if (p->dtype == MOE_BF16 && (p->d_model % 64 != 0 || p->d_ff % 64 != 0))
+  if (p->dtype == MOE_BF16 && (p->d_model % 8 != 0 || p->d_ff % 8 != 0))
     return MOE_ERR_UNSUPPORTED;
   if (p->flags & MOE_W_FP8) {   // FP8 expert weights: the weight-streaming decode path only
     if (p->dtype != MOE_BF16 || p->T > kDecodeMaxT || p->d_model % 128 != 0 || p->d_ff % 128 != 0)
@@ -396,6 +396,7 @@ moe_status moe_ffn_forward(const moe_problem* p, const moe_weights* w, const voi
 // Backward limits beyond check_problem's.
 static moe_status check_backward(const Shape& s) {
   if (s.dtype != MOE_BF16 || s.ec() || s.w_fp8()) return MOE_ERR_UNSUPPORTED;
+  if (s.d % 64 != 0 || s.f % 64 != 0) return MOE_ERR_UNSUPPORTED;   // tiled kernels only
   const long long ldk = wgrad_ldk(s);
   // transposed operands [F1 or d, ldk] bf16 are addressed with 32-bit offsets
   if ((long long)s.up_rows() * ldk * 2 >= (1LL << 32) || (long long)s.d * ldk * 2 >= (1LL << 32) ||

@@ -40,7 +40,10 @@ struct Shape {
   long long max_rows() const { return routed_rows() + (long long)S * T; }
   bool router_bias() const { return flags & MOE_ROUTER_BIAS; }
   bool expert_bias() const { return (flags & MOE_EXPERT_BIAS) && act != MOE_SWIGLU; }
-  bool decode() const { return dtype == MOE_BF16 && T <= kDecodeMaxT; }
+  // bf16 widths that are multiples of 8 but not of 64: the untiled grouped
+  // GEMM (csrc/gemm_generic.hip) instead of the tiled and streaming kernels
+  bool generic() const { return dtype == MOE_BF16 && (d % 64 != 0 || f % 64 != 0); }
+  bool decode() const { return dtype == MOE_BF16 && T <= kDecodeMaxT && !generic(); }
   bool w_fp8() const { return flags & MOE_W_FP8; }
 };
 
@@ -230,6 +233,12 @@ hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void
 hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const void* b_down,
                        const float* s_down, const int32_t* offsets, float* y_exp, float* y_part,
                        bool complete, hipStream_t st);
+hipError_t launch_up_generic(const Shape& s, const void* x, const void* w_up, const void* b_up,
+                             const int32_t* offsets, const int32_t* sorted_assign, void* h,
+                             hipStream_t st);
+hipError_t launch_down_generic(const Shape& s, const void* h, const void* w_down,
+                               const void* b_down, const int32_t* offsets, float* y_exp,
+                               hipStream_t st);
 // y_part/nparts: K-slice partials of y_exp still to be added (nparts = 0: none).
 hipError_t launch_quantize_fp8(const void* w, long long rows, int cols, uint8_t* q, float* scales,
                                hipStream_t st);

@@ -128,6 +128,19 @@ __global__ __launch_bounds__(64 * RW) void router_kernel(RouterArgs a) {
         }
       }
     }
+    // The last, partial K step when d is not a multiple of 32 (d is a
+    // multiple of 8: a lane's 8 elements are all in the row or all past it,
+    // and those past it count as zero), taken by the wave next in turn.
+    if (a.d % 32 != 0 && wave == nsteps % RW) {
+      const bool in = nsteps * 32 + kg * 8 < a.d;
+      const u32x4 xv = in ? *(const u32x4*)(xp + nsteps * 32) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < NE16; ++j) {
+        const u32x4 wv = in ? *(const u32x4*)(wp[j] + nsteps * 32) : u32x4{0, 0, 0, 0};
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, wv), __builtin_bit_cast(bf16x8, xv), acc[j], 0, 0, 0);
+      }
+    }
     // D[expert][token]: lane holds token lane & 15, experts 16j + 4*(lane>>4) + r
 #pragma unroll
     for (int j = 0; j < NE16; ++j)

@@ -67,7 +67,8 @@ def test_workspace_size_grows_with_problem():
     (dict(num_experts=16, top_k=9), M.MOE_ERR_UNSUPPORTED),
     (dict(num_experts=64, num_shared=65), M.MOE_ERR_UNSUPPORTED),
     (dict(d_model=100), M.MOE_ERR_UNSUPPORTED),
-    (dict(d_ff=96), M.MOE_ERR_UNSUPPORTED),
+    (dict(d_ff=260), M.MOE_ERR_UNSUPPORTED),
+    (dict(d_ff=100), M.MOE_ERR_UNSUPPORTED),
     # token rows beyond 32-bit byte offsets (T * d_model * 2 >= 2^32)
     (dict(T=1 << 20, d_model=2048, d_ff=256, top_k=1), M.MOE_ERR_UNSUPPORTED),
     (dict(T=1 << 18, d_model=256, d_ff=8192, top_k=1), M.MOE_ERR_UNSUPPORTED),
@@ -80,6 +81,17 @@ def test_invalid_problems_rejected(kw, status):
 
 def test_fp32_allows_any_width():
     assert M.moe_workspace_size(_problem(dtype="f32", d_model=33, d_ff=70)) > 0
+
+
+def test_bf16_widths_multiple_of_8():
+    # the forward takes any multiple of 8; the backward only multiples of 64
+    for d, f in ((776, 1416), (520, 2056), (64, 264), (8, 8)):
+        p = _problem(d_model=d, d_ff=f)
+        assert M.moe_workspace_size(p) > 0
+        n = ctypes.c_size_t(0)
+        assert M._lib.moe_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)) == \
+            M.MOE_ERR_UNSUPPORTED
+    assert M.moe_backward_workspace_size(_problem(d_model=512, d_ff=192)) > 0
 
 
 def test_largest_token_rows_accepted():

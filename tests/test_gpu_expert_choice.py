@@ -51,6 +51,7 @@ EC_CASES = {
     "ec_decode_T16": scaled(RUNS["gpt2_ec"], T=16, d_model=1024, d_ff=2048,
                             activation="swiglu", expert_bias=False, router_bias="none",
                             capacity_factor=1.0, seed=13),
+    "ec_d392_f584_T500": scaled(RUNS["gpt2_ec"], T=500, d_model=392, d_ff=584, seed=16),
     "gpt2_ec": RUNS["gpt2_ec"],
 }
 

@@ -23,6 +23,14 @@ SMALL = {
     "swiglu_skew_T3000": scaled(RUNS["swiglu_skew"], T=3000),
     "large_decode": RUNS["large_decode"],
     "large_T300": scaled(RUNS["large_prefill"], T=300),
+    # bf16 widths that are multiples of 8 but not of 64 (the untiled grouped
+    # GEMM, and the router's partial K step of 8, 16 or 24 elements)
+    "gelu_bias_d776_f1416_T300": scaled(RUNS["gpt2"], T=300, d_model=776, d_ff=1416),
+    "swiglu_d520_f2056_T200": scaled(RUNS["large_prefill"], T=200, d_model=520, d_ff=2056),
+    "shared_sigmoid_d400_f328_T150": scaled(RUNS["fine_shared"], T=150, d_model=400, d_ff=328),
+    "small_T12_d1048_f776": scaled(RUNS["large_prefill"], T=12, d_model=1048, d_ff=776),
+    "relu_d64_f200_T500": scaled(RUNS["gpt2"], T=500, d_model=64, d_ff=200, activation="relu",
+                                 capacity_factor=None),
     # the weight-streaming path with 2 and 4 groups of 16 token rows
     "decode_T40_d1024": scaled(RUNS["large_prefill"], T=40, d_model=1024, d_ff=2048),
     "decode_T64_shared_sigmoid": scaled(RUNS["fine_shared"], T=64, d_model=512, d_ff=768),
@@ -226,9 +234,10 @@ def test_aux_stats_given_oracle_sums():
     assert abs(float(l.item()) - orc["l_aux"]) <= 1e-4 * orc["l_aux"]
 
 
-def test_deterministic_and_no_out_of_bounds_writes():
-    run, inp = _inputs("fine_shared_T1000")
-    _say("[determinism+canary] fine_shared_T1000")
+@pytest.mark.parametrize("name", ["fine_shared_T1000", "shared_sigmoid_d400_f328_T150"])
+def test_deterministic_and_no_out_of_bounds_writes(name):
+    run, inp = _inputs(name)
+    _say(f"[determinism+canary] {name}")
     g = gpu_inputs(inp)
     p = problem_of(run)
     T, d = run.T, run.d_model
@@ -246,7 +255,8 @@ def test_deterministic_and_no_out_of_bounds_writes():
     assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32)), "not bit-identical"
 
 
-@pytest.mark.parametrize("name", ["gpt2_T700", "swiglu_skew_T3000", "large_T300", "large_decode"])
+@pytest.mark.parametrize("name", ["gpt2_T700", "swiglu_skew_T3000", "large_T300", "large_decode",
+                                  "gelu_bias_d776_f1416_T300"])
 def test_stage_entry_points_equal_fused_forward(name):
     """The per-stage entry points (router, dispatch, up, down with its K slices
     folded, combine) give bit-identical y to the fused forward, which adds the
