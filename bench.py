@@ -517,8 +517,13 @@ def cpu_baseline(run, cap, seconds, inp):
     except Exception:
         threads = os.cpu_count()
     f64 = lambda t: None if t is None else _Lazy(t)
-    # FP8 expert weights: the oracle's own quantization, dequantized exactly
-    f64w = (lambda t: _LazyFP8(t, O)) if run.w_fp8 else f64
+    # FP8 expert weights: the oracle's own quantization (codes computed once,
+    # untimed, as the GPU path quantizes once), dequantized exactly per use
+    if run.w_fp8:
+        qup, qdown = _LazyFP8(inp["w_up"], O), _LazyFP8(inp["w_down"], O)
+        f64w = lambda t: qup if t is inp["w_up"] else qdown
+    else:
+        f64w = f64
     x, wr = to_f64(inp["x"]), to_f64(inp["w_router"])
     br = None if inp["b_router"] is None else to_f64(inp["b_router"])
     ocap = O.capacity(run.T, run.top_k, run.num_experts, run.capacity_factor)
@@ -558,13 +563,20 @@ class _Lazy:
 
 
 class _LazyFP8(_Lazy):
-    def __init__(self, t, oracle):
+    """The oracle's FP8 codes of every expert, computed once (several experts
+    at a time); each access dequantizes one expert."""
+
+    def __init__(self, t, oracle, workers=8):
+        from concurrent.futures import ThreadPoolExecutor
         super().__init__(t)
         self.O = oracle
+        torch = __import__("torch")
+        one = lambda i: oracle.quantize_fp8_rows(t[i].to(torch.float32).numpy())
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            self.codes = list(ex.map(one, range(t.shape[0])))
 
     def __getitem__(self, i):
-        codes, scales = self.O.quantize_fp8_rows(self.t[i].to(__import__("torch").float32).numpy())
-        return self.O.dequantize_fp8_rows(codes, scales)
+        return self.O.dequantize_fp8_rows(*self.codes[i])
 
 
 if __name__ == "__main__":
