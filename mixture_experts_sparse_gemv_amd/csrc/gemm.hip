@@ -139,8 +139,9 @@ struct TileCoord {
   int ks, seg, nt, mt, rows, start;
 };
 
-// OCC: waves per SIMD the register budget must allow.
-template <int BM, int BN, int WGM, int WGN, int MODE, int OCC = 1>
+// OCC: waves per SIMD the register budget must allow.  MF: the MFMA shape,
+// 16 (16x16x32) or 32 (32x32x16).
+template <int BM, int BN, int WGM, int WGN, int MODE, int OCC = 1, int MF = 16>
 __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmArgs a) {
   constexpr int BK = 32;                   // k-tile depth
   constexpr int NSTAGE = 4;                // LDS ring stages (DMA runs NSTAGE-1 tiles ahead)
@@ -153,19 +154,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   constexpr bool WG = MODE == MODE_WGRAD;
   constexpr bool BIAS = !SWIGLU && !WG;         // an optional per-column bias
   constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile: token rows x weight rows
-  constexpr int MI = WM / 32, NI = WN / 32;
+  constexpr int MI = WM / MF, NI = WN / MF;
+  typedef float accv __attribute__((ext_vector_type(MF * MF / 64)));
   constexpr int NOUT_TILE = SWIGLU ? BN / 2 : BN;
   constexpr int ROWCH = BK / 8;            // 16-byte chunks per tile row
   constexpr int RPB = 16 / ROWCH;          // tile rows per 256 bytes (all 64 LDS banks)
   constexpr int RI = 64 / ROWCH;           // tile rows filled by one DMA instruction
-  constexpr int NSUB = BK / 16;            // MFMA k-substeps per k-tile
+  constexpr int NSUB = MF == 32 ? BK / 16 : BK / 32;   // MFMA k-substeps per k-tile
   constexpr int NFR = NI + MI;             // fragment reads per wave per k-substep
   constexpr int NM = NI * MI;              // MFMAs per wave per k-substep
   constexpr int QWW = BN / RI / NW, QWX = BM / RI / NW;   // DMA instructions per wave and k-tile
   constexpr int STAGE = (BM + BN) * ROWCH;                // 16-byte chunks per stage
   static_assert(MI >= 1 && NI >= 1 && QWW * RI * NW == BN && QWX * RI * NW == BM, "tile shape");
   static_assert(!SWIGLU || (NI % 2 == 0), "SwiGLU pairs gate and up sub-tiles");
-  static_assert(NSUB >= 2, "cross-barrier pipelining needs two k-substeps per tile");
+  static_assert(MF == 16 || MF == 32, "MFMA shape");
+  // 32x32x16: the last of the k-substeps runs after the barrier; 16x16x32:
+  // one substep per k-tile, its fragments double-buffered across k-tiles.
+  static_assert(MF == 16 ? NSUB == 1 : NSUB >= 2, "k-substeps per k-tile");
 
   // The LDS ring as distinct arrays: the compiler sees that the DMA into one
   // stage never aliases the fragment reads of another.
@@ -424,24 +429,30 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
       bias_reg = col < a.Nout ? *(const uint32_t*)(a.bias + (long long)c.seg * a.Wrows + col) : 0u;
     }
   };
-  // Fragment rows are 32-aligned bases plus lane & 31, so the swizzle term
-  // depends on the lane only: one per-lane offset per k-substep.
+  // Fragment rows are MF-aligned bases plus lane % MF, so the swizzle term
+  // depends on the lane only: one per-lane offset per k-substep.  32x32x16:
+  // lane l reads row l & 31, chunk 2 s + (l >> 5) of k-substep s; 16x16x32:
+  // row l & 15, chunk l >> 4 (the whole 32-deep k-tile).
   int fro[NSUB];
 #pragma unroll
-  for (int s4 = 0; s4 < NSUB; ++s4)
-    fro[s4] = (lane & 31) * ROWCH + ((2 * s4 + (lane >> 5)) ^ (((lane & 31) / RPB) % ROWCH));
-  int wrb[NI], xrb[MI];  // 32-row base of each fragment, in chunks
+  for (int s4 = 0; s4 < NSUB; ++s4) {
+    if (MF == 32)
+      fro[s4] = (lane & 31) * ROWCH + ((2 * s4 + (lane >> 5)) ^ (((lane & 31) / RPB) % ROWCH));
+    else
+      fro[s4] = (lane & 15) * ROWCH + ((lane >> 4) ^ (((lane & 15) / RPB) % ROWCH));
+  }
+  int wrb[NI], xrb[MI];  // MF-row base of each fragment, in chunks
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     if (SWIGLU) {
       const int jj = j < NI / 2 ? j : j - NI / 2;
-      wrb[j] = ((j < NI / 2 ? 0 : BN / 2) + wn * (BN / 2 / WGN) + jj * 32) * ROWCH;
+      wrb[j] = ((j < NI / 2 ? 0 : BN / 2) + wn * (BN / 2 / WGN) + jj * MF) * ROWCH;
     } else {
-      wrb[j] = (wn * WN + j * 32) * ROWCH;
+      wrb[j] = (wn * WN + j * MF) * ROWCH;
     }
   }
 #pragma unroll
-  for (int i = 0; i < MI; ++i) xrb[i] = (BN + wm * WM + i * 32) * ROWCH;
+  for (int i = 0; i < MI; ++i) xrb[i] = (BN + wm * WM + i * MF) * ROWCH;
 
   typedef __attribute__((address_space(3))) void lds_void_t;
   auto dma = [&](u32x4* buf, int kt) {
@@ -467,10 +478,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
 
   constexpr int NDMA = QWW + QWX;
   constexpr int INFLIGHT = (NSTAGE - 2) * NDMA;   // DMAs that may stay in flight
-  static_assert(INFLIGHT <= 63, "vmcnt range");
+  static_assert((NSTAGE - 1) * NDMA <= 63, "vmcnt range");
   // s_waitcnt immediate: vmcnt = INFLIGHT, expcnt and lgkmcnt = 0 (every
   // fragment read of this tile has completed before the barrier).
   constexpr int WAIT_IMM = (INFLIGHT & 15) | ((INFLIGHT >> 4) << 14);
+  // the same with NSTAGE - 1 k-tiles' DMAs in flight (16x16x32 tile start)
+  constexpr int INFLIGHT3 = (NSTAGE - 1) * NDMA;
+  constexpr int WAIT_IMM3 = (INFLIGHT3 & 15) | ((INFLIGHT3 >> 4) << 14);
   // A barrier after this wave's LDS operations have completed, with no wait
   // for its global loads and stores in flight (s_waitcnt lgkmcnt(0) only:
   // vmcnt 63, expcnt 7).
@@ -510,19 +524,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
     auto clampk = [&](int t) { return t < nk ? t : nk - 1; };
     dma(lds1, clampk(1));
     dma(lds2, clampk(2));
-    // stage 0 has landed; the DMAs of stages 1 and 2 may stay in flight
-    __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+    // stage 0 has landed; the DMAs of stages 1 and 2 (16x16x32: and 3) may
+    // stay in flight
+    if constexpr (MF == 16) {
+      dma(lds3, clampk(3));
+      __builtin_amdgcn_s_waitcnt(WAIT_IMM3);
+    } else {
+      __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+    }
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
 
     u32x4 wf[2][NI], xf[2][MI];
     // this wave's token rows hold valid rows of the tile (uniform per wave)
     const bool wact = cur.mt * BM + wm * WM < cur.rows;
-    f32x16 acc[NI][MI];
+    accv acc[NI][MI];
 #pragma unroll
     for (int j = 0; j < NI; ++j)
 #pragma unroll
-      for (int i = 0; i < MI; ++i) acc[j][i] = f32x16{};
+      for (int i = 0; i < MI; ++i) acc[j][i] = accv{};
     auto mfmas = [&](const u32x4(&wf)[NI], const u32x4(&xf)[MI]) {
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
@@ -530,14 +550,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
         const u32x4 w = CVT16 ? bf16x8_to_f16x8(wf[j]) : wf[j];
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
-          if (CVT16)
-            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                __builtin_bit_cast(f16x8, w), __builtin_bit_cast(f16x8, xf[i]), acc[j][i], 0, 0,
-                0);
-          else
-            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, xf[i]), acc[j][i], 0,
-                0, 0);
+          if constexpr (MF == 32) {
+            if (CVT16)
+              acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                  __builtin_bit_cast(f16x8, w), __builtin_bit_cast(f16x8, xf[i]), acc[j][i], 0, 0,
+                  0);
+            else
+              acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, xf[i]), acc[j][i], 0,
+                  0, 0);
+          } else {
+            if (CVT16)
+              acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                  __builtin_bit_cast(f16x8, w), __builtin_bit_cast(f16x8, xf[i]), acc[j][i], 0, 0,
+                  0);
+            else
+              acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, xf[i]), acc[j][i], 0,
+                  0, 0);
+          }
         }
       }
     };
@@ -586,7 +617,124 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
       __builtin_amdgcn_s_barrier();
       __asm__ volatile("" ::: "memory");
     };
-    if (wact) {
+    // ---- 16x16x32: the whole 32-deep k-tile is one MFMA k-step.  The
+    // operand with more fragments per wave (W for the up projection's 64 x
+    // 128 wave tiles, the token rows for the down projection's 128 x 64) is
+    // read in two halves, the other operand double-buffered across k-tiles,
+    // so a wave holds 16 fragments instead of two full sets of 12.  Iteration
+    // kt: phase A runs the MFMAs of the first half under the reads of the
+    // second half (tile kt); then it waits until tile kt+1 has landed (tiles
+    // kt+2 and kt+3 may stay in flight) and crosses the barrier, after which
+    // every wave's reads of tile kt's stage are done; phase B runs the MFMAs
+    // of the second half under the reads of tile kt+1's other operand and
+    // first half and the DMA of tile kt+4 into tile kt's stage.  The DMA thus
+    // runs four tiles ahead.  P selects the double buffer of the tile.
+    constexpr bool SPW = NI >= MI;   // W fragments split in halves (else token rows)
+    u32x4 w16[SPW ? 1 : 2][NI], x16[SPW ? 2 : 1][MI];
+    auto lw = [&](const u32x4* buf, u32x4(&d)[NI], int j0, int j1) {
+#pragma unroll
+      for (int j = j0; j < j1; ++j) d[j] = buf[wrb[j] + fro[0]];
+    };
+    auto lx = [&](const u32x4* buf, u32x4(&d)[MI], int i0, int i1) {
+#pragma unroll
+      for (int i = i0; i < i1; ++i) d[i] = buf[xrb[i] + fro[0]];
+    };
+    auto mm = [&](const u32x4(&wv)[NI], const u32x4(&xv)[MI], int j0, int j1, int i0, int i1) {
+#pragma unroll
+      for (int j = j0; j < j1; ++j) {
+        const u32x4 w = CVT16 ? bf16x8_to_f16x8(wv[j]) : wv[j];
+#pragma unroll
+        for (int i = i0; i < i1; ++i) {
+          if constexpr (MF == 16) {
+            if (CVT16)
+              acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                  __builtin_bit_cast(f16x8, w), __builtin_bit_cast(f16x8, xv[i]), acc[j][i], 0, 0,
+                  0);
+            else
+              acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, xv[i]), acc[j][i], 0,
+                  0, 0);
+          }
+        }
+      }
+    };
+    constexpr int NRA = SPW ? NI / 2 : MI / 2;        // phase A reads (second half, tile kt)
+    constexpr int NRB = SPW ? MI + NI / 2 : NI + MI / 2;   // phase B reads (tile kt+1)
+    auto iteration16 = [&](const u32x4* cur_st, const u32x4* next_st, u32x4* free_st, int kt,
+                           int P) {
+      if constexpr (SPW) {
+        lw(cur_st, w16[0], NI / 2, NI);
+        if (P == 0) mm(w16[0], x16[0], 0, NI / 2, 0, MI);
+        else mm(w16[0], x16[1], 0, NI / 2, 0, MI);
+      } else {
+        lx(cur_st, x16[0], MI / 2, MI);
+        if (P == 0) mm(w16[0], x16[0], 0, NI, 0, MI / 2);
+        else mm(w16[1], x16[0], 0, NI, 0, MI / 2);
+      }
+      sched_front<NM / 2, SG_DS_READ, NRA, MOE_SCHED_PER, SG_VMEM_READ, 0>();
+      // phase A's MFMAs stay above the barrier, phase B's below it
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");   // no LDS read moves above the barrier
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (SPW) {
+        if (P == 0) lx(next_st, x16[1], 0, MI);
+        else lx(next_st, x16[0], 0, MI);
+        lw(next_st, w16[0], 0, NI / 2);
+      } else {
+        if (P == 0) lw(next_st, w16[1], 0, NI);
+        else lw(next_st, w16[0], 0, NI);
+        lx(next_st, x16[0], 0, MI / 2);
+      }
+      dma(free_st, clampk(kt + NSTAGE));
+      if constexpr (SPW) {
+        if (P == 0) mm(w16[0], x16[0], NI / 2, NI, 0, MI);
+        else mm(w16[0], x16[1], NI / 2, NI, 0, MI);
+      } else {
+        if (P == 0) mm(w16[0], x16[0], 0, NI, MI / 2, MI);
+        else mm(w16[1], x16[0], 0, NI, MI / 2, MI);
+      }
+      sched_front<NM / 2, SG_DS_READ, NRB, MOE_SCHED_PER, SG_VMEM_READ, NDMA>();
+    };
+    auto idle16 = [&](u32x4* free_st, int kt) {
+      __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+      dma(free_st, clampk(kt + NSTAGE));
+    };
+    if constexpr (MF == 16) {
+      if (wact) {
+        if constexpr (SPW) {
+          lx(lds0, x16[0], 0, MI);
+          lw(lds0, w16[0], 0, NI / 2);
+        } else {
+          lw(lds0, w16[0], 0, NI);
+          lx(lds0, x16[0], 0, MI / 2);
+        }
+        int kt = 0;
+        for (; kt + 3 < nk; kt += 4) {
+          iteration16(lds0, lds1, lds0, kt, 0);
+          iteration16(lds1, lds2, lds1, kt + 1, 1);
+          iteration16(lds2, lds3, lds2, kt + 2, 0);
+          iteration16(lds3, lds0, lds3, kt + 3, 1);
+        }
+        if (kt < nk) iteration16(lds0, lds1, lds0, kt, 0);
+        if (kt + 1 < nk) iteration16(lds1, lds2, lds1, kt + 1, 1);
+        if (kt + 2 < nk) iteration16(lds2, lds3, lds2, kt + 2, 0);
+      } else {
+        int kt = 0;
+        for (; kt + 3 < nk; kt += 4) {
+          idle16(lds0, kt);
+          idle16(lds1, kt + 1);
+          idle16(lds2, kt + 2);
+          idle16(lds3, kt + 3);
+        }
+        if (kt < nk) idle16(lds0, kt);
+        if (kt + 1 < nk) idle16(lds1, kt + 1);
+        if (kt + 2 < nk) idle16(lds2, kt + 2);
+      }
+    } else if (wact) {
       frag_load(lds0, wf[0], xf[0], 0);
       int kt = 0;
       for (; kt + 3 < nk; kt += 4) {
@@ -621,17 +769,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
-    // ---- epilogue.  Lane holds token row (lane & 31) of each 32x32 tile
-    // and, in register group g, the four consecutive weight rows 8g +
-    // 4*(lane>>5) + 0..3.  Stored directly, one instruction would touch 32
-    // rows with 16-32 bytes each; instead each wave stages one 32-row slab of
-    // its output (after bias and activation, in the output type) in a padded
+    // ---- epilogue.  32x32x16: lane holds token row (lane & 31) of each 32x32
+    // tile and, in register group g, the four consecutive weight rows 8g +
+    // 4*(lane>>5) + 0..3; 16x16x32: token row (lane & 15) of each 16x16 tile
+    // and the weight rows 4*(lane>>4) + 0..3.  Stored directly, one
+    // instruction would touch 16-32 rows with 16-32 bytes each; instead each
+    // wave stages one 32-row slab of its output (one 32-row fragment, or two
+    // 16-row ones; after bias and activation, in the output type) in a padded
     // LDS region of ring stages 1 to 3 and writes it back as whole 16-byte
     // chunks of rows, CPR lanes per row, so a store instruction covers RPI
     // rows of contiguous bytes.  The padding keeps the staging writes and
     // reads free of bank conflicts.
     constexpr int NJ = SWIGLU ? NI / 2 : NI;
-    constexpr int WNOUT = NJ * 32;                       // output columns of a wave
+    constexpr int WNOUT = NJ * MF;                       // output columns of a wave
+    constexpr int FPS = 32 / MF;                         // token fragments per slab
+    static_assert(MI % FPS == 0, "whole 32-row slabs");
     constexpr int ES = OUT32 ? 4 : 2;                     // output element bytes
     constexpr int PITCH = WNOUT * ES + (OUT32 ? 16 : 8);  // staging row pitch, bytes
     constexpr int CPR = WNOUT * ES / 16;                  // 16-byte chunks per row
@@ -655,40 +807,45 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
     char* obase =
         cur.ks == 0 ? (char*)a.out : (char*)(a.out2 + (long long)(cur.ks - 1) * a.part_elems);
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
+    for (int sl = 0; sl < MI / FPS; ++sl) {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
+      for (int i2 = 0; i2 < FPS; ++i2) {
+        const int i = sl * FPS + i2;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int nloc = j * 32 + 8 * g + 4 * (lane >> 5);
-          const int col = colw + nloc;
-          float v[4];
+        for (int j = 0; j < NJ; ++j) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = acc[j][i][4 * g + r];
-          if (CVT16) {   // h was stored scaled by 2^-8
+          for (int g = 0; g < MF * MF / 256; ++g) {   // groups of 4 accumulators
+            // four consecutive output columns nloc.. of slab row srow
+            const int nloc = MF == 32 ? j * 32 + 8 * g + 4 * (lane >> 5) : j * 16 + 4 * (lane >> 4);
+            const int srow = MF == 32 ? (lane & 31) : 16 * i2 + (lane & 15);
+            float v[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] *= kHLoadScale;
-          }
-          if (SWIGLU) {
+            for (int r = 0; r < 4; ++r) v[r] = acc[j][i][4 * g + r];
+            if (CVT16) {   // h was stored scaled by 2^-8
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = silu_f(v[r]) * acc[j + NI / 2][i][4 * g + r];
-          } else if (BIAS && a.bias && cur.ks == 0) {
-            const u32x2 bb = *(const u32x2*)(sh_bias + (wn * WN + nloc) / 2);
-            v[0] += __uint_as_float(bb[0] << 16);
-            v[1] += __uint_as_float(bb[0] & 0xffff0000u);
-            v[2] += __uint_as_float(bb[1] << 16);
-            v[3] += __uint_as_float(bb[1] & 0xffff0000u);
-          }
-          char* dst = stg + (lane & 31) * PITCH + nloc * ES;
-          if (OUT32) {
-            *(f32x4*)dst = f32x4{v[0], v[1], v[2], v[3]};
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if (MODE == MODE_RELU) v[r] = fmaxf(v[r], 0.0f);
-              if (MODE == MODE_GELU) v[r] = gelu_f(v[r]);
+              for (int r = 0; r < 4; ++r) v[r] *= kHLoadScale;
             }
-            *(f16x4*)dst = f16x4{h_to_f16(v[0]), h_to_f16(v[1]), h_to_f16(v[2]), h_to_f16(v[3])};
+            if (SWIGLU) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) v[r] = silu_f(v[r]) * acc[j + NI / 2][i][4 * g + r];
+            } else if (BIAS && a.bias && cur.ks == 0) {
+              const u32x2 bb = *(const u32x2*)(sh_bias + (wn * WN + nloc) / 2);
+              v[0] += __uint_as_float(bb[0] << 16);
+              v[1] += __uint_as_float(bb[0] & 0xffff0000u);
+              v[2] += __uint_as_float(bb[1] << 16);
+              v[3] += __uint_as_float(bb[1] & 0xffff0000u);
+            }
+            char* dst = stg + srow * PITCH + nloc * ES;
+            if (OUT32) {
+              *(f32x4*)dst = f32x4{v[0], v[1], v[2], v[3]};
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                if (MODE == MODE_RELU) v[r] = fmaxf(v[r], 0.0f);
+                if (MODE == MODE_GELU) v[r] = gelu_f(v[r]);
+              }
+              *(f16x4*)dst = f16x4{h_to_f16(v[0]), h_to_f16(v[1]), h_to_f16(v[2]), h_to_f16(v[3])};
+            }
           }
         }
       }
@@ -698,12 +855,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
       for (int q = 0; q < 32 / RPI; ++q) {
         const int r = q * RPI + lane / CPR, c = lane % CPR;
         const u32x4 val = *(const u32x4*)(stg + r * PITCH + c * 16);
-        const int m = cur.mt * BM + wm * WM + i * 32 + r;
+        const int m = cur.mt * BM + wm * WM + sl * 32 + r;
         const int col = colw + c * (16 / ES);
         if (m < cur.rows && col < a.Nout)
           *(u32x4*)(obase + ((long long)(cur.start + m) * a.Nout + col) * ES) = val;
       }
-      if (i == 0 && more) prefetch_next();
+      if (sl == 0 && more) prefetch_next();
     }
     if (!more) break;
     cur = coords(b ^ 1);
@@ -856,6 +1013,22 @@ hipError_t launch_decode_down(const Shape& s, const void* h, const void* w_down,
                               const void* b_down, const float* s_down, const int32_t* offsets,
                               float* y_exp, float* y_part, bool complete, hipStream_t st);
 
+// MFMA shape by launch length: 16x16x32 runs the long main loops of large
+// layers about 4% faster (it holds a higher clock at the same matrix-pipe
+// occupancy); 32x32x16 is a few percent faster on short launches (a few
+// hundred tiles of short reductions), where tile start-up dominates.
+// Long: at least 256 GFLOP (about 0.2 ms) in the projection, 2 x rows x
+// depth x width at the upper bound of the rows.
+static bool long_launch(const Shape& s, long long depth, long long width) {
+  return 2.0 * (double)s.max_rows() * (double)depth * (double)width >= 256e9;
+}
+
+template <int MODE, int MF>
+static void up_gemm(const Shape& s, const GemmArgs& a, int NT, hipStream_t st) {
+  grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE, UP_OCC, MF>
+      <<<grid_blocks(s, UP_BM, NT, 1, UP_OCC), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
+}
+
 hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void* b_up,
                      const float* s_up, const int32_t* offsets, const int32_t* sorted_assign,
                      void* h, hipStream_t st) {
@@ -884,18 +1057,20 @@ hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void
   if (s.decode()) return launch_decode_up(s, x, w_up, b_up, s_up, offsets, sorted_assign, h, st);
   GemmArgs a{(const uint16_t*)x, (const uint16_t*)w_up, (const uint16_t*)bias, h, offsets,
              sorted_assign, s.T, s.tok_div(), s.E, s.S, s.d, s.f, s.up_rows(), s.f, 1, nullptr, 0, 0};
+  const bool mf16 = long_launch(s, s.d, s.up_rows());
   if (s.act == MOE_SWIGLU) {
     const int NT = (s.f + UP_BN / 2 - 1) / (UP_BN / 2);
-    grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_SWIGLU, UP_OCC>
-        <<<grid_blocks(s, UP_BM, NT, 1, UP_OCC), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
+    if (mf16) up_gemm<MODE_SWIGLU, 16>(s, a, NT, st);
+    else up_gemm<MODE_SWIGLU, 32>(s, a, NT, st);
   } else {
     const int NT = (s.f + UP_BN - 1) / UP_BN;
-    if (s.act == MOE_RELU)
-      grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_RELU, UP_OCC>
-          <<<grid_blocks(s, UP_BM, NT, 1, UP_OCC), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
-    else
-      grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE_GELU, UP_OCC>
-          <<<grid_blocks(s, UP_BM, NT, 1, UP_OCC), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
+    if (s.act == MOE_RELU) {
+      if (mf16) up_gemm<MODE_RELU, 16>(s, a, NT, st);
+      else up_gemm<MODE_RELU, 32>(s, a, NT, st);
+    } else {
+      if (mf16) up_gemm<MODE_GELU, 16>(s, a, NT, st);
+      else up_gemm<MODE_GELU, 32>(s, a, NT, st);
+    }
   }
   return hipGetLastError();
 }
@@ -921,8 +1096,12 @@ hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const 
   GemmArgs a{(const uint16_t*)h, (const uint16_t*)w_down, (const uint16_t*)bias, y_exp, offsets,
              nullptr, s.T, s.tok_div(), s.E, s.S, s.f, s.d, s.d, s.f, ks, y_part, part_elems, 0};
   const int NT = (s.d + DN_BN - 1) / DN_BN;
-  grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DOWN, DN_OCC>
-      <<<grid_blocks(s, DN_BM, NT, ks, DN_OCC), 64 * DN_WGM * DN_WGN, 0, st>>>(a);
+  if (long_launch(s, s.f, s.d))
+    grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DOWN, DN_OCC, 16>
+        <<<grid_blocks(s, DN_BM, NT, ks, DN_OCC), 64 * DN_WGM * DN_WGN, 0, st>>>(a);
+  else
+    grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DOWN, DN_OCC, 32>
+        <<<grid_blocks(s, DN_BM, NT, ks, DN_OCC), 64 * DN_WGM * DN_WGN, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ks == 1 || !complete) return e;
   const long long n = s.max_rows() * (s.d / 4);
