@@ -377,6 +377,22 @@ moe_status moe_ffn_backward(const moe_problem* p, const moe_weights* w, const vo
                             const float* dy, float alpha, const moe_routing* fwd,
                             const moe_grads* g, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Host only.  Process-wide choice of the grouped GEMM's main loop, a tuning
+ * and testing control that does not change results (both loops accumulate
+ * every output in the same order, so their outputs are bit-identical):
+ *   MOE_GEMM_AUTO (default): 16x16x32 MFMAs with 64-deep k-tiles for long
+ *     launches (at least 256 GFLOP in the projection), 32x32x16 MFMAs with
+ *     32-deep k-tiles for shorter ones;
+ *   MOE_GEMM_MF32: always the 32x32x16 loop;
+ *   MOE_GEMM_MF16: the 16x16x32 loop wherever the reduction allows it (K
+ *     slices of whole 64-deep k-tiles; otherwise the 32x32x16 loop).
+ * Applies to launches issued after the call; MOE_ERR_INVALID_ARG for any
+ * other value. */
+#define MOE_GEMM_AUTO 0
+#define MOE_GEMM_MF32 1
+#define MOE_GEMM_MF16 2
+moe_status moe_set_gemm_policy(int32_t policy);
+
 /* Human-readable name of a status code (static string). */
 const char* moe_status_string(moe_status s);
 /* hipError_t of this thread's last MOE_ERR_HIP (0 if none). */

@@ -27,6 +27,8 @@
 // (at most one block per compute unit, looping over its tiles), and a block's
 // consecutive tiles overlap: the next tile's first k-tile loads while the
 // current tile's epilogue runs.
+#include <atomic>
+
 #include "moe_internal.h"
 
 // 1: a k-substep's fragment reads are issued first, MOE_SCHED_PER per MFMA,
@@ -140,11 +142,11 @@ struct TileCoord {
 };
 
 // OCC: waves per SIMD the register budget must allow.  MF: the MFMA shape,
-// 16 (16x16x32) or 32 (32x32x16).
-template <int BM, int BN, int WGM, int WGN, int MODE, int OCC = 1, int MF = 16>
+// 16 (16x16x32) or 32 (32x32x16).  BK: the k-tile depth, 32 (4-stage LDS
+// ring) or, with 16x16x32, 64 (2-stage ring, whole 128-byte rows per DMA).
+template <int BM, int BN, int WGM, int WGN, int MODE, int OCC = 1, int MF = 16, int BK = 32>
 __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmArgs a) {
-  constexpr int BK = 32;                   // k-tile depth
-  constexpr int NSTAGE = 4;                // LDS ring stages (DMA runs NSTAGE-1 tiles ahead)
+  constexpr int NSTAGE = BK == 64 ? 2 : 4;   // LDS ring stages
   constexpr int NW = WGM * WGN;            // waves: WGM along tokens x WGN along weights
   constexpr bool SWIGLU = MODE == MODE_SWIGLU;
   constexpr bool GATHER = MODE <= MODE_SWIGLU || MODE == MODE_LIN;   // token rows via sorted_assign
@@ -168,13 +170,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   static_assert(MI >= 1 && NI >= 1 && QWW * RI * NW == BN && QWX * RI * NW == BM, "tile shape");
   static_assert(!SWIGLU || (NI % 2 == 0), "SwiGLU pairs gate and up sub-tiles");
   static_assert(MF == 16 || MF == 32, "MFMA shape");
+  static_assert(BK == 32 || (BK == 64 && MF == 16), "k-tile depth");
   // 32x32x16: the last of the k-substeps runs after the barrier; 16x16x32:
-  // one substep per k-tile, its fragments double-buffered across k-tiles.
-  static_assert(MF == 16 ? NSUB == 1 : NSUB >= 2, "k-substeps per k-tile");
+  // one or two 32-deep MFMA k-steps per k-tile (see below).
+  static_assert(MF == 16 ? NSUB == BK / 32 : NSUB >= 2, "k-substeps per k-tile");
 
   // The LDS ring as distinct arrays: the compiler sees that the DMA into one
   // stage never aliases the fragment reads of another.
-  __shared__ u32x4 lds0[STAGE], lds1[STAGE], lds2[STAGE], lds3[STAGE];
+  __shared__ u32x4 lds0[STAGE], lds1[STAGE], lds2[NSTAGE > 2 ? STAGE : 1],
+      lds3[NSTAGE > 3 ? STAGE : 1];
   __shared__ int seg_tile[kMaxSegments + 1];
   __shared__ int seg_nrows[kMaxSegments], seg_row0[kMaxSegments];
   __shared__ int sh_seg[2];
@@ -432,14 +436,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   // Fragment rows are MF-aligned bases plus lane % MF, so the swizzle term
   // depends on the lane only: one per-lane offset per k-substep.  32x32x16:
   // lane l reads row l & 31, chunk 2 s + (l >> 5) of k-substep s; 16x16x32:
-  // row l & 15, chunk l >> 4 (the whole 32-deep k-tile).
+  // row l & 15, chunk 4 s + (l >> 4) of 32-deep k-step s.
   int fro[NSUB];
 #pragma unroll
   for (int s4 = 0; s4 < NSUB; ++s4) {
     if (MF == 32)
       fro[s4] = (lane & 31) * ROWCH + ((2 * s4 + (lane >> 5)) ^ (((lane & 31) / RPB) % ROWCH));
     else
-      fro[s4] = (lane & 15) * ROWCH + ((lane >> 4) ^ (((lane & 15) / RPB) % ROWCH));
+      fro[s4] = (lane & 15) * ROWCH + ((4 * s4 + (lane >> 4)) ^ (((lane & 15) / RPB) % ROWCH));
   }
   int wrb[NI], xrb[MI];  // MF-row base of each fragment, in chunks
 #pragma unroll
@@ -522,14 +526,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
     const int LL2 = more ? tile_at(it + 2 * step) : -1;
     const int nk = kslice / BK;
     auto clampk = [&](int t) { return t < nk ? t : nk - 1; };
-    dma(lds1, clampk(1));
-    dma(lds2, clampk(2));
-    // stage 0 has landed; the DMAs of stages 1 and 2 (16x16x32: and 3) may
-    // stay in flight
-    if constexpr (MF == 16) {
+    // stage 0 has landed; the DMAs of the later stages may stay in flight
+    if constexpr (BK == 64) {
+      dma(lds1, clampk(1));
+      __builtin_amdgcn_s_waitcnt(WAIT_IMM3);
+    } else if constexpr (MF == 16) {
+      dma(lds1, clampk(1));
+      dma(lds2, clampk(2));
       dma(lds3, clampk(3));
       __builtin_amdgcn_s_waitcnt(WAIT_IMM3);
     } else {
+      dma(lds1, clampk(1));
+      dma(lds2, clampk(2));
       __builtin_amdgcn_s_waitcnt(WAIT_IMM);
     }
     __builtin_amdgcn_s_barrier();
@@ -631,13 +639,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
     // runs four tiles ahead.  P selects the double buffer of the tile.
     constexpr bool SPW = NI >= MI;   // W fragments split in halves (else token rows)
     u32x4 w16[SPW ? 1 : 2][NI], x16[SPW ? 2 : 1][MI];
-    auto lw = [&](const u32x4* buf, u32x4(&d)[NI], int j0, int j1) {
+    auto lw = [&](const u32x4* buf, u32x4(&d)[NI], int j0, int j1, int ks = 0) {
 #pragma unroll
-      for (int j = j0; j < j1; ++j) d[j] = buf[wrb[j] + fro[0]];
+      for (int j = j0; j < j1; ++j) d[j] = buf[wrb[j] + fro[ks]];
     };
-    auto lx = [&](const u32x4* buf, u32x4(&d)[MI], int i0, int i1) {
+    auto lx = [&](const u32x4* buf, u32x4(&d)[MI], int i0, int i1, int ks = 0) {
 #pragma unroll
-      for (int i = i0; i < i1; ++i) d[i] = buf[xrb[i] + fro[0]];
+      for (int i = i0; i < i1; ++i) d[i] = buf[xrb[i] + fro[ks]];
     };
     auto mm = [&](const u32x4(&wv)[NI], const u32x4(&xv)[MI], int j0, int j1, int i0, int i1) {
 #pragma unroll
@@ -703,7 +711,81 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
       __asm__ volatile("" ::: "memory");
       dma(free_st, clampk(kt + NSTAGE));
     };
-    if constexpr (MF == 16) {
+    // ---- 64-deep k-tiles (16x16x32, 2-stage ring): two MFMA k-steps per
+    // k-tile, each in the two phases above, but one barrier per k-tile: in
+    // the last phase, after the barrier, the reads of tile kt+1's first
+    // k-step and the DMA of tile kt+2 into tile kt's stage run under the
+    // MFMAs.  K-step s uses double buffer s.  The DMA runs one k-tile ahead.
+    auto iteration64 = [&](const u32x4* cur_st, const u32x4* next_st, u32x4* free_st, int kt) {
+      if constexpr (SPW) {
+        lw(cur_st, w16[0], NI / 2, NI, 0);
+        mm(w16[0], x16[0], 0, NI / 2, 0, MI);
+        sched_front<NM / 2, SG_DS_READ, NRA, MOE_SCHED_PER, SG_VMEM_READ, 0>();
+        lx(cur_st, x16[1], 0, MI, 1);
+        lw(cur_st, w16[0], 0, NI / 2, 1);
+        mm(w16[0], x16[0], NI / 2, NI, 0, MI);
+        sched_front<NM / 2, SG_DS_READ, NRB, MOE_SCHED_PER, SG_VMEM_READ, 0>();
+        lw(cur_st, w16[0], NI / 2, NI, 1);
+        mm(w16[0], x16[1], 0, NI / 2, 0, MI);
+      } else {
+        lx(cur_st, x16[0], MI / 2, MI, 0);
+        mm(w16[0], x16[0], 0, NI, 0, MI / 2);
+        sched_front<NM / 2, SG_DS_READ, NRA, MOE_SCHED_PER, SG_VMEM_READ, 0>();
+        lw(cur_st, w16[1], 0, NI, 1);
+        lx(cur_st, x16[0], 0, MI / 2, 1);
+        mm(w16[0], x16[0], 0, NI, MI / 2, MI);
+        sched_front<NM / 2, SG_DS_READ, NRB, MOE_SCHED_PER, SG_VMEM_READ, 0>();
+        lx(cur_st, x16[0], MI / 2, MI, 1);
+        mm(w16[1], x16[0], 0, NI, 0, MI / 2);
+      }
+      sched_front<NM / 2, SG_DS_READ, NRA, MOE_SCHED_PER, SG_VMEM_READ, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(WAIT_IMM);   // tile kt+1 has landed
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (SPW) {
+        lx(next_st, x16[0], 0, MI, 0);
+        lw(next_st, w16[0], 0, NI / 2, 0);
+      } else {
+        lw(next_st, w16[0], 0, NI, 0);
+        lx(next_st, x16[0], 0, MI / 2, 0);
+      }
+      dma(free_st, clampk(kt + 2));
+      if constexpr (SPW) mm(w16[0], x16[1], NI / 2, NI, 0, MI);
+      else mm(w16[1], x16[0], 0, NI, MI / 2, MI);
+      sched_front<NM / 2, SG_DS_READ, NRB, MOE_SCHED_PER, SG_VMEM_READ, NDMA>();
+    };
+    auto idle64 = [&](u32x4* free_st, int kt) {
+      __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+      dma(free_st, clampk(kt + 2));
+    };
+    if constexpr (BK == 64) {
+      if (wact) {
+        if constexpr (SPW) {
+          lx(lds0, x16[0], 0, MI, 0);
+          lw(lds0, w16[0], 0, NI / 2, 0);
+        } else {
+          lw(lds0, w16[0], 0, NI, 0);
+          lx(lds0, x16[0], 0, MI / 2, 0);
+        }
+        int kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
+          iteration64(lds0, lds1, lds0, kt);
+          iteration64(lds1, lds0, lds1, kt + 1);
+        }
+        if (kt < nk) iteration64(lds0, lds1, lds0, kt);
+      } else {
+        int kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
+          idle64(lds0, kt);
+          idle64(lds1, kt + 1);
+        }
+        if (kt < nk) idle64(lds0, kt);
+      }
+    } else if constexpr (MF == 16) {
       if (wact) {
         if constexpr (SPW) {
           lx(lds0, x16[0], 0, MI);
@@ -782,16 +864,20 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
     // reads free of bank conflicts.
     constexpr int NJ = SWIGLU ? NI / 2 : NI;
     constexpr int WNOUT = NJ * MF;                       // output columns of a wave
-    constexpr int FPS = 32 / MF;                         // token fragments per slab
-    static_assert(MI % FPS == 0, "whole 32-row slabs");
     constexpr int ES = OUT32 ? 4 : 2;                     // output element bytes
     constexpr int PITCH = WNOUT * ES + (OUT32 ? 16 : 8);  // staging row pitch, bytes
     constexpr int CPR = WNOUT * ES / 16;                  // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;                         // rows per store instruction
-    constexpr int STG = 32 * PITCH;                       // staging bytes per wave
+    // slab height: 32 rows, or 16 (16x16x32) when 32-row slabs of every wave
+    // do not fit in the ring stages the epilogue may use (all but stage 0)
+    constexpr int SLAB =
+        (MF == 16 && 32 * PITCH * NW > (NSTAGE - 1) * (int)sizeof(lds0)) ? 16 : 32;
+    constexpr int FPS = SLAB / MF;                       // token fragments per slab
+    static_assert(FPS >= 1 && MI % FPS == 0, "whole slabs");
+    constexpr int STG = SLAB * PITCH;                     // staging bytes per wave
     constexpr int WPA = (int)(sizeof(lds0) / STG);        // waves per ring stage
-    static_assert(CPR >= 1 && CPR <= 64 && 64 % CPR == 0 && 32 % RPI == 0, "staging shape");
-    static_assert(WPA * (NSTAGE - 1) >= NW, "staging must fit in ring stages 1 to 3");
+    static_assert(CPR >= 1 && CPR <= 64 && 64 % CPR == 0 && SLAB % RPI == 0, "staging shape");
+    static_assert(WPA * (NSTAGE - 1) >= NW, "staging must fit in the ring stages after the first");
     // the next tile's first k-tile and bias, the row loads of the one after
     auto prefetch_next = [&]() {
       const TileCoord nx = coords(b ^ 1);
@@ -852,10 +938,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
       // LDS operations of one wave complete in order: the reads below see the
       // writes above, and the next slab's writes follow these reads.
 #pragma unroll
-      for (int q = 0; q < 32 / RPI; ++q) {
+      for (int q = 0; q < SLAB / RPI; ++q) {
         const int r = q * RPI + lane / CPR, c = lane % CPR;
         const u32x4 val = *(const u32x4*)(stg + r * PITCH + c * 16);
-        const int m = cur.mt * BM + wm * WM + sl * 32 + r;
+        const int m = cur.mt * BM + wm * WM + sl * SLAB + r;
         const int col = colw + c * (16 / ES);
         if (m < cur.rows && col < a.Nout)
           *(u32x4*)(obase + ((long long)(cur.start + m) * a.Nout + col) * ES) = val;
@@ -1019,13 +1105,27 @@ hipError_t launch_decode_down(const Shape& s, const void* h, const void* w_down,
 // hundred tiles of short reductions), where tile start-up dominates.
 // Long: at least 256 GFLOP (about 0.2 ms) in the projection, 2 x rows x
 // depth x width at the upper bound of the rows.
-static bool long_launch(const Shape& s, long long depth, long long width) {
-  return 2.0 * (double)s.max_rows() * (double)depth * (double)width >= 256e9;
+static std::atomic<int> g_gemm_policy{MOE_GEMM_AUTO};
+
+void set_gemm_policy(int policy) { g_gemm_policy.store(policy, std::memory_order_relaxed); }
+
+static bool long_flops(double flops) {
+  const int policy = g_gemm_policy.load(std::memory_order_relaxed);
+  if (policy == MOE_GEMM_MF32) return false;
+  if (policy == MOE_GEMM_MF16) return true;
+  return flops >= 256e9;
 }
 
+static bool long_launch(const Shape& s, long long depth, long long width) {
+  return long_flops(2.0 * (double)s.max_rows() * (double)depth * (double)width);
+}
+
+#ifndef MOE_MF16_BK
+#define MOE_MF16_BK 64   // k-tile depth of the 16x16x32 loops
+#endif
 template <int MODE, int MF>
 static void up_gemm(const Shape& s, const GemmArgs& a, int NT, hipStream_t st) {
-  grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE, UP_OCC, MF>
+  grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE, UP_OCC, MF, MF == 16 ? MOE_MF16_BK : 32>
       <<<grid_blocks(s, UP_BM, NT, 1, UP_OCC), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
 }
 
@@ -1096,8 +1196,9 @@ hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const 
   GemmArgs a{(const uint16_t*)h, (const uint16_t*)w_down, (const uint16_t*)bias, y_exp, offsets,
              nullptr, s.T, s.tok_div(), s.E, s.S, s.f, s.d, s.d, s.f, ks, y_part, part_elems, 0};
   const int NT = (s.d + DN_BN - 1) / DN_BN;
-  if (long_launch(s, s.f, s.d))
-    grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DOWN, DN_OCC, 16>
+  // (64-deep k-tiles need K slices of whole 64-deep tiles)
+  if (long_launch(s, s.f, s.d) && (s.f / ks) % MOE_MF16_BK == 0)
+    grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DOWN, DN_OCC, 16, MOE_MF16_BK>
         <<<grid_blocks(s, DN_BM, NT, ks, DN_OCC), 64 * DN_WGM * DN_WGN, 0, st>>>(a);
   else
     grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DOWN, DN_OCC, 32>
@@ -1119,8 +1220,13 @@ hipError_t launch_bwd_lin(const Shape& s, const void* X, const void* W, const vo
   GemmArgs a{(const uint16_t*)X, (const uint16_t*)W, (const uint16_t*)bias, out, offsets,
              sorted_assign, s.T, s.tok_div(), s.E, s.S, K, Wrows, Wrows, s.f, 1, nullptr, 0, 0};
   const int NT = (Wrows + DN_BN - 1) / DN_BN;
-  grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_LIN, DN_OCC>
-      <<<grid_blocks(s, DN_BM, NT), 64 * DN_WGM * DN_WGN, 0, st>>>(a);
+  const dim3 grid(grid_blocks(s, DN_BM, NT)), block(64 * DN_WGM * DN_WGN);
+  if (long_launch(s, K, Wrows) && K % MOE_MF16_BK == 0)
+    grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_LIN, DN_OCC, 16, MOE_MF16_BK>
+        <<<grid, block, 0, st>>>(a);
+  else
+    grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_LIN, DN_OCC, 32>
+        <<<grid, block, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -1133,8 +1239,13 @@ hipError_t launch_bwd_dx(const Shape& s, const void* X, const void* W, int K, in
   GemmArgs a{(const uint16_t*)X, (const uint16_t*)W, nullptr, out, offsets, nullptr, s.T,
              s.tok_div(), s.E, s.S, K, N, N, s.f, ksplit, out2, part_elems, 0};
   const int NT = (N + DN_BN - 1) / DN_BN;
-  grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DXB, DN_OCC>
-      <<<grid_blocks(s, DN_BM, NT, ksplit), 64 * DN_WGM * DN_WGN, 0, st>>>(a);
+  const dim3 grid(grid_blocks(s, DN_BM, NT, ksplit)), block(64 * DN_WGM * DN_WGN);
+  if (long_launch(s, K, N) && (K / ksplit) % MOE_MF16_BK == 0)
+    grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DXB, DN_OCC, 16, MOE_MF16_BK>
+        <<<grid, block, 0, st>>>(a);
+  else
+    grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DXB, DN_OCC, 32>
+        <<<grid, block, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -1148,8 +1259,14 @@ hipError_t launch_bwd_wgrad(const Shape& s, const void* A, const void* B, int M,
                           ((N + DN_BN - 1) / DN_BN);
   long long g = tiles > kNumCUs ? kNumCUs : tiles;
   g = (g + 7) / 8 * 8;
-  grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_WGRAD, DN_OCC>
-      <<<(int)g, 64 * DN_WGM * DN_WGN, 0, st>>>(a);
+  // the reduction runs over every segment's padded rows (multiples of 32:
+  // 32-deep k-tiles); long launches take the 16x16x32 loop
+  if (long_flops(2.0 * (double)M * (double)N * (double)ldk))
+    grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_WGRAD, DN_OCC, 16, 32>
+        <<<(int)g, 64 * DN_WGM * DN_WGN, 0, st>>>(a);
+  else
+    grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_WGRAD, DN_OCC, 32>
+        <<<(int)g, 64 * DN_WGM * DN_WGN, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -519,4 +519,11 @@ const char* moe_status_string(moe_status s) {
 
 int32_t moe_last_hip_error(void) { return g_last_hip_error; }
 
+moe_status moe_set_gemm_policy(int32_t policy) {
+  if (policy != MOE_GEMM_AUTO && policy != MOE_GEMM_MF32 && policy != MOE_GEMM_MF16)
+    return MOE_ERR_INVALID_ARG;
+  moe::set_gemm_policy(policy);
+  return MOE_OK;
+}
+
 }  // extern "C"

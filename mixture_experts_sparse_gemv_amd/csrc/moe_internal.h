@@ -65,6 +65,8 @@ constexpr int kDecodeSplitK = 4;
 // is written to y_exp, slice i > 0 to y_part + (i - 1) * max_rows * d, and
 // the slices are summed in slice order (by the combine, or by a fold pass).
 int down_ksplit(const Shape& s);
+// The grouped GEMM's main-loop choice (MOE_GEMM_AUTO / _MF32 / _MF16).
+void set_gemm_policy(int policy);
 // K slices of the decode down projection (slice 0 into y_exp with the bias,
 // slice i > 0 into y_part + (i - 1) * max_rows * d_model).
 int decode_nsplit(const Shape& s);

@@ -20,14 +20,15 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID_NORM = 0, 1
 MOE_RELU, MOE_GELU, MOE_SWIGLU = 0, 1, 2
 MOE_ROUTER_BIAS, MOE_EXPERT_BIAS, MOE_W_FP8, MOE_EXPERT_CHOICE = 1, 2, 8, 16
+MOE_GEMM_AUTO, MOE_GEMM_MF32, MOE_GEMM_MF16 = 0, 1, 2
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_capacity", "moe_workspace_size", "moe_router_topk", "moe_dispatch",
            "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_aux_stats",
            "moe_routing_stats", "moe_quantize_fp8", "moe_expert_choice", "moe_ffn_forward",
            "moe_ffn_forward_static",
-           "moe_backward_workspace_size", "moe_ffn_backward", "moe_status_string",
-           "moe_last_hip_error")
+           "moe_backward_workspace_size", "moe_ffn_backward", "moe_set_gemm_policy",
+           "moe_status_string", "moe_last_hip_error")
 
 
 class moe_problem(ctypes.Structure):
@@ -90,6 +91,7 @@ def _load(path=LIB_PATH):
         "moe_ffn_forward_static": (I32, [pp, pw, V, V, pr, V]),
         "moe_backward_workspace_size": (I32, [pp, P(SZ)]),
         "moe_ffn_backward": (I32, [pp, pw, V, V, ctypes.c_float, pr, pg, V, SZ, V]),
+        "moe_set_gemm_policy": (I32, [I32]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
         "moe_last_hip_error": (I32, []),
     }
@@ -405,6 +407,12 @@ def moe_ffn_forward_static(p, w, x, y, routing=None, stream=None):
     _check("moe_ffn_forward_static", _lib.moe_ffn_forward_static(
         ctypes.byref(p), ctypes.byref(w), _ptr(x), _ptr(y),
         ctypes.byref(r) if r is not None else None, _stream(stream)))
+
+
+def moe_set_gemm_policy(policy):
+    """Process-wide grouped GEMM main loop: MOE_GEMM_AUTO (by launch size),
+    MOE_GEMM_MF32 or MOE_GEMM_MF16; outputs are the same bit for bit."""
+    _check("moe_set_gemm_policy", _lib.moe_set_gemm_policy(int(policy)))
 
 
 def moe_backward_workspace_size(p):

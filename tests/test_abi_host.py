@@ -219,3 +219,13 @@ def test_binding_checks_routing_x_and_weights_before_any_call():
     W._tensors["w_router"] = torch.empty(E * d, dtype=torch.float32)
     with pytest.raises(ValueError, match="w_router"):
         M._check_weights(p, W())
+
+
+def test_gemm_policy_values():
+    """moe_set_gemm_policy takes the three documented values (host only)."""
+    for v in (M.MOE_GEMM_MF16, M.MOE_GEMM_MF32, M.MOE_GEMM_AUTO):
+        M.moe_set_gemm_policy(v)
+    for bad in (-1, 3):
+        with pytest.raises(M.MoeError) as e:
+            M.moe_set_gemm_policy(bad)
+        assert e.value.status == M.MOE_ERR_INVALID_ARG
