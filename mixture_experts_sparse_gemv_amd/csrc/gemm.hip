@@ -175,9 +175,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   // one or two 32-deep MFMA k-steps per k-tile (see below).
   static_assert(MF == 16 ? NSUB == BK / 32 : NSUB >= 2, "k-substeps per k-tile");
 
+  // Epilogue staging geometry (see the epilogue): each wave stages 32-row
+  // slabs of its output, PITCH bytes per row, in the ring stages after the
+  // first; with a 2-stage ring the waves that do not fit in stage 1 stage in
+  // a small extra region.
+  constexpr int NJ = SWIGLU ? NI / 2 : NI;
+  constexpr int WNOUT = NJ * MF;                       // output columns of a wave
+  constexpr int ES = OUT32 ? 4 : 2;                     // output element bytes
+  constexpr int PITCH = WNOUT * ES + (OUT32 ? 16 : 8);  // staging row pitch, bytes
+  constexpr int STG = 32 * PITCH;                       // staging bytes per wave
+  constexpr int WPA = STAGE * 16 / STG;                 // waves per ring stage
+  constexpr int XTRA = (NSTAGE == 2 && WPA < NW) ? (NW - WPA) * STG : 0;
+  static_assert(WPA * (NSTAGE - 1) >= NW || NSTAGE == 2, "staging must fit in stages 1 to 3");
+
   // The LDS ring as distinct arrays: the compiler sees that the DMA into one
   // stage never aliases the fragment reads of another.
-  __shared__ u32x4 lds0[STAGE], lds1[STAGE], lds2[NSTAGE > 2 ? STAGE : 1],
+  __shared__ u32x4 lds0[STAGE], lds1[STAGE], lds2[NSTAGE > 2 ? STAGE : (XTRA + 15) / 16 + 1],
       lds3[NSTAGE > 3 ? STAGE : 1];
   __shared__ int seg_tile[kMaxSegments + 1];
   __shared__ int seg_nrows[kMaxSegments], seg_row0[kMaxSegments];
@@ -762,7 +775,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
       __asm__ volatile("" ::: "memory");
       dma(free_st, clampk(kt + 2));
     };
-    if constexpr (BK == 64) {
+    if constexpr (MF == 16 && BK == 64) {
       if (wact) {
         if constexpr (SPW) {
           lx(lds0, x16[0], 0, MI, 0);
@@ -862,22 +875,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
     // chunks of rows, CPR lanes per row, so a store instruction covers RPI
     // rows of contiguous bytes.  The padding keeps the staging writes and
     // reads free of bank conflicts.
-    constexpr int NJ = SWIGLU ? NI / 2 : NI;
-    constexpr int WNOUT = NJ * MF;                       // output columns of a wave
-    constexpr int ES = OUT32 ? 4 : 2;                     // output element bytes
-    constexpr int PITCH = WNOUT * ES + (OUT32 ? 16 : 8);  // staging row pitch, bytes
     constexpr int CPR = WNOUT * ES / 16;                  // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;                         // rows per store instruction
-    // slab height: 32 rows, or 16 (16x16x32) when 32-row slabs of every wave
-    // do not fit in the ring stages the epilogue may use (all but stage 0)
-    constexpr int SLAB =
-        (MF == 16 && 32 * PITCH * NW > (NSTAGE - 1) * (int)sizeof(lds0)) ? 16 : 32;
-    constexpr int FPS = SLAB / MF;                       // token fragments per slab
+    constexpr int SLAB = 32;                              // slab rows
+    constexpr int FPS = SLAB / MF;                        // token fragments per slab
     static_assert(FPS >= 1 && MI % FPS == 0, "whole slabs");
-    constexpr int STG = SLAB * PITCH;                     // staging bytes per wave
-    constexpr int WPA = (int)(sizeof(lds0) / STG);        // waves per ring stage
     static_assert(CPR >= 1 && CPR <= 64 && 64 % CPR == 0 && SLAB % RPI == 0, "staging shape");
-    static_assert(WPA * (NSTAGE - 1) >= NW, "staging must fit in the ring stages after the first");
     // the next tile's first k-tile and bias, the row loads of the one after
     auto prefetch_next = [&]() {
       const TileCoord nx = coords(b ^ 1);
@@ -887,8 +890,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
       if (LL2 >= 0) row_loads(coords(b));
     };
     // (a wave without valid rows stages zeros and stores nothing)
-    const int wa = wv / WPA;
-    char* stg = (char*)(wa == 0 ? lds1 : wa == 1 ? lds2 : lds3) + (wv % WPA) * STG;
+    char* stg;
+    if constexpr (NSTAGE == 2) {
+      stg = wv < WPA ? (char*)lds1 + wv * STG : (char*)lds2 + (wv - WPA) * STG;
+    } else {
+      const int wa = wv / WPA;
+      stg = (char*)(wa == 0 ? lds1 : wa == 1 ? lds2 : lds3) + (wv % WPA) * STG;
+    }
     const int colw = SWIGLU ? cur.nt * (BN / 2) + wn * (BN / 2 / WGN) : cur.nt * BN + wn * WN;
     char* obase =
         cur.ks == 0 ? (char*)a.out : (char*)(a.out2 + (long long)(cur.ks - 1) * a.part_elems);
@@ -1120,13 +1128,24 @@ static bool long_launch(const Shape& s, long long depth, long long width) {
   return long_flops(2.0 * (double)s.max_rows() * (double)depth * (double)width);
 }
 
-#ifndef MOE_MF16_BK
-#define MOE_MF16_BK 64   // k-tile depth of the 16x16x32 loops
-#endif
+// The up projection reduces over d_model, a multiple of 64 on the tiled path:
+// the 16x16x32 loop always takes 64-deep k-tiles.
 template <int MODE, int MF>
 static void up_gemm(const Shape& s, const GemmArgs& a, int NT, hipStream_t st) {
-  grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE, UP_OCC, MF, MF == 16 ? MOE_MF16_BK : 32>
+  grouped_gemm_kernel<UP_BM, UP_BN, UP_WGM, UP_WGN, MODE, UP_OCC, MF, MF == 16 ? 64 : 32>
       <<<grid_blocks(s, UP_BM, NT, 1, UP_OCC), 64 * UP_WGM * UP_WGN, 0, st>>>(a);
+}
+
+// A down-style launch (MODE_DOWN, _LIN, _DXB) over the grid: 16x16x32 with
+// 64-deep k-tiles for long launches whose K slices are whole 64-deep tiles,
+// otherwise 32x32x16 with 32-deep k-tiles.
+template <int MODE>
+static void dn_gemm(bool long_run, int kslice, const GemmArgs& a, dim3 grid, hipStream_t st) {
+  const dim3 block(64 * DN_WGM * DN_WGN);
+  if (long_run && kslice % 64 == 0)
+    grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE, DN_OCC, 16, 64><<<grid, block, 0, st>>>(a);
+  else
+    grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE, DN_OCC, 32, 32><<<grid, block, 0, st>>>(a);
 }
 
 hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void* b_up,
@@ -1196,13 +1215,8 @@ hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const 
   GemmArgs a{(const uint16_t*)h, (const uint16_t*)w_down, (const uint16_t*)bias, y_exp, offsets,
              nullptr, s.T, s.tok_div(), s.E, s.S, s.f, s.d, s.d, s.f, ks, y_part, part_elems, 0};
   const int NT = (s.d + DN_BN - 1) / DN_BN;
-  // (64-deep k-tiles need K slices of whole 64-deep tiles)
-  if (long_launch(s, s.f, s.d) && (s.f / ks) % MOE_MF16_BK == 0)
-    grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DOWN, DN_OCC, 16, MOE_MF16_BK>
-        <<<grid_blocks(s, DN_BM, NT, ks, DN_OCC), 64 * DN_WGM * DN_WGN, 0, st>>>(a);
-  else
-    grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DOWN, DN_OCC, 32>
-        <<<grid_blocks(s, DN_BM, NT, ks, DN_OCC), 64 * DN_WGM * DN_WGN, 0, st>>>(a);
+  dn_gemm<MODE_DOWN>(long_launch(s, s.f, s.d), s.f / ks, a,
+                     dim3(grid_blocks(s, DN_BM, NT, ks, DN_OCC)), st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ks == 1 || !complete) return e;
   const long long n = s.max_rows() * (s.d / 4);
@@ -1220,13 +1234,7 @@ hipError_t launch_bwd_lin(const Shape& s, const void* X, const void* W, const vo
   GemmArgs a{(const uint16_t*)X, (const uint16_t*)W, (const uint16_t*)bias, out, offsets,
              sorted_assign, s.T, s.tok_div(), s.E, s.S, K, Wrows, Wrows, s.f, 1, nullptr, 0, 0};
   const int NT = (Wrows + DN_BN - 1) / DN_BN;
-  const dim3 grid(grid_blocks(s, DN_BM, NT)), block(64 * DN_WGM * DN_WGN);
-  if (long_launch(s, K, Wrows) && K % MOE_MF16_BK == 0)
-    grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_LIN, DN_OCC, 16, MOE_MF16_BK>
-        <<<grid, block, 0, st>>>(a);
-  else
-    grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_LIN, DN_OCC, 32>
-        <<<grid, block, 0, st>>>(a);
+  dn_gemm<MODE_LIN>(long_launch(s, K, Wrows), K, a, dim3(grid_blocks(s, DN_BM, NT)), st);
   return hipGetLastError();
 }
 
@@ -1239,13 +1247,8 @@ hipError_t launch_bwd_dx(const Shape& s, const void* X, const void* W, int K, in
   GemmArgs a{(const uint16_t*)X, (const uint16_t*)W, nullptr, out, offsets, nullptr, s.T,
              s.tok_div(), s.E, s.S, K, N, N, s.f, ksplit, out2, part_elems, 0};
   const int NT = (N + DN_BN - 1) / DN_BN;
-  const dim3 grid(grid_blocks(s, DN_BM, NT, ksplit)), block(64 * DN_WGM * DN_WGN);
-  if (long_launch(s, K, N) && (K / ksplit) % MOE_MF16_BK == 0)
-    grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DXB, DN_OCC, 16, MOE_MF16_BK>
-        <<<grid, block, 0, st>>>(a);
-  else
-    grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_DXB, DN_OCC, 32>
-        <<<grid, block, 0, st>>>(a);
+  dn_gemm<MODE_DXB>(long_launch(s, K, N), K / ksplit, a,
+                    dim3(grid_blocks(s, DN_BM, NT, ksplit)), st);
   return hipGetLastError();
 }
 
