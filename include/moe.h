@@ -380,9 +380,9 @@ moe_status moe_ffn_backward(const moe_problem* p, const moe_weights* w, const vo
 /* Host only.  Process-wide choice of the grouped GEMM's main loop, a tuning
  * and testing control that does not change results (both loops accumulate
  * every output in the same order, so their outputs are bit-identical):
- *   MOE_GEMM_AUTO (default): 16x16x32 MFMAs with 64-deep k-tiles for long
- *     launches (at least 256 GFLOP in the projection), 32x32x16 MFMAs with
- *     32-deep k-tiles for shorter ones;
+ *   MOE_GEMM_AUTO (default): 16x16x32 MFMAs with 64-deep k-tiles for the
+ *     up projection and for long down-style launches (at least 256 GFLOP),
+ *     32x32x16 MFMAs with 32-deep k-tiles for shorter ones;
  *   MOE_GEMM_MF32: always the 32x32x16 loop;
  *   MOE_GEMM_MF16: the 16x16x32 loop wherever the reduction allows it (K
  *     slices of whole 64-deep k-tiles; otherwise the 32x32x16 loop).

@@ -1107,12 +1107,13 @@ hipError_t launch_decode_down(const Shape& s, const void* h, const void* w_down,
                               const void* b_down, const float* s_down, const int32_t* offsets,
                               float* y_exp, float* y_part, bool complete, hipStream_t st);
 
-// MFMA shape by launch length: 16x16x32 runs the long main loops of large
-// layers about 4% faster (it holds a higher clock at the same matrix-pipe
-// occupancy); 32x32x16 is a few percent faster on short launches (a few
-// hundred tiles of short reductions), where tile start-up dominates.
-// Long: at least 256 GFLOP (about 0.2 ms) in the projection, 2 x rows x
-// depth x width at the upper bound of the rows.
+// MFMA shape: the up projection always runs 16x16x32 with 64-deep k-tiles
+// (faster at every measured size: at the same matrix-pipe occupancy it holds
+// a higher clock); the down-style projections do so when long, at least 256
+// GFLOP (about 0.2 ms; 2 x rows x depth x width at the upper bound of the
+// rows), and otherwise keep 32x32x16 with 32-deep k-tiles, which is 2-6%
+// faster on short launches (a few hundred tiles, K often split), where tile
+// start-up dominates.
 static std::atomic<int> g_gemm_policy{MOE_GEMM_AUTO};
 
 void set_gemm_policy(int policy) { g_gemm_policy.store(policy, std::memory_order_relaxed); }
@@ -1176,7 +1177,7 @@ hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void
   if (s.decode()) return launch_decode_up(s, x, w_up, b_up, s_up, offsets, sorted_assign, h, st);
   GemmArgs a{(const uint16_t*)x, (const uint16_t*)w_up, (const uint16_t*)bias, h, offsets,
              sorted_assign, s.T, s.tok_div(), s.E, s.S, s.d, s.f, s.up_rows(), s.f, 1, nullptr, 0, 0};
-  const bool mf16 = long_launch(s, s.d, s.up_rows());
+  const bool mf16 = g_gemm_policy.load(std::memory_order_relaxed) != MOE_GEMM_MF32;
   if (s.act == MOE_SWIGLU) {
     const int NT = (s.f + UP_BN / 2 - 1) / (UP_BN / 2);
     if (mf16) up_gemm<MODE_SWIGLU, 16>(s, a, NT, st);

@@ -1,7 +1,8 @@
 """The grouped GEMM's two main loops (16x16x32 MFMAs with 64-deep k-tiles, and
-32x32x16 MFMAs with 32-deep k-tiles) on the same problems.  By default the
-choice follows the launch size, so only full-size layers would reach the
-16x16x32 loop; here moe_set_gemm_policy forces each loop on shapes the oracle
+32x32x16 MFMAs with 32-deep k-tiles) on the same problems.  By default the up
+projection takes the 16x16x32 loop and the down-style projections take it
+only when long, so only full-size layers would reach it there; here
+moe_set_gemm_policy forces each loop everywhere, on shapes the oracle
 finishes in seconds: ragged and half-empty m-tiles, waves without rows,
 shared experts, biases, every activation, one-k-tile and odd k-tile
 reductions, K-sliced down projections, and the two-list tile schedule.  Both
