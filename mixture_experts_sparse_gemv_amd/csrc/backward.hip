@@ -110,7 +110,7 @@ __global__ __launch_bounds__(64) void wgrad_offsets_kernel(const int32_t* __rest
   for (int seg = 0; seg < E + S; ++seg) {
     poff[seg] = acc;
     const int rows = seg < E ? offsets[seg + 1] - offsets[seg] : T;
-    acc += rows <= 0 ? 32 : (rows + 31) / 32 * 32;
+    acc += wgrad_pad(rows);
   }
   poff[E + S] = acc;
 }
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void seg_transpose_kernel(
   const int p0 = blockIdx.x * ST_R, c0 = blockIdx.y * 64;
   const int tid = threadIdx.x;
   const int nseg = E + S;
-  const int pend = poff[nseg];   // end of the used columns (a multiple of 32)
+  const int pend = poff[nseg];   // end of the used columns (a multiple of 64)
   if (p0 >= pend) return;        // uniform
   if (tid < nseg) {
     const int lo = poff[tid], hi = poff[tid + 1];
@@ -237,7 +237,7 @@ __device__ __forceinline__ float gelu_grad_f(float z) {
 }
 
 // One block per 64 padded rows (the weight-gradient layout of
-// wgrad_offsets_kernel: segments start at multiples of 32, so each 32-row
+// wgrad_offsets_kernel: segments start at multiples of 64, so each 32-row
 // half of the block lies in one segment) and 64 columns c of h.  For each row
 // it forms h = act(Z), dZ = act'(Z) w G (SwiGLU: the gate and the up column)
 // and the partial sum <h, G> over its 64 columns; it writes dZ row-major (the
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void act_backward_kernel(
   const int p0 = blockIdx.x * AB_R, c0 = blockIdx.y * AB_C;
   const int tid = threadIdx.x;
   const int nseg = E + S;
-  const int pend = poff[nseg];   // end of the used columns (a multiple of 32)
+  const int pend = poff[nseg];   // end of the used columns (a multiple of 64)
   if (p0 >= pend) return;        // uniform
   if (tid < nseg) {
     const int lo = poff[tid], hi = poff[tid + 1];

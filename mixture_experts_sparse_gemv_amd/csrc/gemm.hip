@@ -72,13 +72,6 @@ struct GemmArgs {
   int M;
 };
 
-// Weight-gradient layout: segment seg's rows occupy columns poff .. poff+pad
-// of the transposed operands, pad = rows rounded up to a multiple of 32 (at
-// least 32; the padding is zero), so every segment has a whole, non-empty
-// number of 32-deep k-tiles.
-__host__ __device__ __forceinline__ int wgrad_pad(int rows) {
-  return rows <= 0 ? 32 : (rows + 31) / 32 * 32;
-}
 
 // Per-segment row count and first row.
 __device__ __forceinline__ void segment_rows(const GemmArgs& a, int seg, int off_E, int& rows,
@@ -1263,10 +1256,10 @@ hipError_t launch_bwd_wgrad(const Shape& s, const void* A, const void* B, int M,
                           ((N + DN_BN - 1) / DN_BN);
   long long g = tiles > kNumCUs ? kNumCUs : tiles;
   g = (g + 7) / 8 * 8;
-  // the reduction runs over every segment's padded rows (multiples of 32:
-  // 32-deep k-tiles); long launches take the 16x16x32 loop
+  // the reduction runs over every segment's padded rows (multiples of 64);
+  // long launches take the 16x16x32 loop with 64-deep k-tiles
   if (long_flops(2.0 * (double)M * (double)N * (double)ldk))
-    grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_WGRAD, DN_OCC, 16, 32>
+    grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_WGRAD, DN_OCC, 16, 64>
         <<<(int)g, 64 * DN_WGM * DN_WGN, 0, st>>>(a);
   else
     grouped_gemm_kernel<DN_BM, DN_BN, DN_WGM, DN_WGN, MODE_WGRAD, DN_OCC, 32>

@@ -251,10 +251,17 @@ hipError_t launch_combine(const Shape& s, const float* topk_w, const int32_t* as
 // ---------------------------------------------------------------- backward
 // K slices of the dX GEMM (reduction over F1, d outputs), as down_ksplit.
 int bwd_dx_ksplit(const Shape& s);
+// Weight-gradient layout: segment seg's rows occupy columns poff .. poff+pad
+// of the transposed operands, pad = rows rounded up to a multiple of 64 (at
+// least 64; the padding is zero), so every segment has a whole, non-empty
+// number of 64-deep (and 32-deep) k-tiles.
+__host__ __device__ __forceinline__ int wgrad_pad(int rows) {
+  return rows <= 0 ? 64 : (rows + 63) / 64 * 64;
+}
 // Row stride of the transposed weight-gradient operands: every segment's
-// rows padded to a multiple of 32 (at least 32) fit.
+// padded rows fit.
 inline int wgrad_ldk(const Shape& s) {
-  return (int)(((s.max_rows() + 31) / 32) * 32 + 32LL * (s.E + s.S));
+  return (int)(((s.max_rows() + 63) / 64) * 64 + 64LL * (s.E + s.S));
 }
 int router_wgrad_slices(const Shape& s);
 struct BwdLayout {
