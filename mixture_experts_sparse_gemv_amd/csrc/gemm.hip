@@ -163,10 +163,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   static_assert(MI >= 1 && NI >= 1 && QWW * RI * NW == BN && QWX * RI * NW == BM, "tile shape");
   static_assert(!SWIGLU || (NI % 2 == 0), "SwiGLU pairs gate and up sub-tiles");
   static_assert(MF == 16 || MF == 32, "MFMA shape");
-  static_assert(BK == 32 || (BK == 64 && MF == 16), "k-tile depth");
+  static_assert((MF == 16) == (BK == 64), "16x16x32 runs 64-deep k-tiles, 32x32x16 32-deep");
   // 32x32x16: the last of the k-substeps runs after the barrier; 16x16x32:
-  // one or two 32-deep MFMA k-steps per k-tile (see below).
-  static_assert(MF == 16 ? NSUB == BK / 32 : NSUB >= 2, "k-substeps per k-tile");
+  // two 32-deep MFMA k-steps per k-tile (see below).
+  static_assert(MF == 16 ? NSUB == 2 : NSUB >= 2, "k-substeps per k-tile");
 
   // Epilogue staging geometry (see the epilogue): each wave stages 32-row
   // slabs of its output, PITCH bytes per row, in the ring stages after the
@@ -492,7 +492,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   // s_waitcnt immediate: vmcnt = INFLIGHT, expcnt and lgkmcnt = 0 (every
   // fragment read of this tile has completed before the barrier).
   constexpr int WAIT_IMM = (INFLIGHT & 15) | ((INFLIGHT >> 4) << 14);
-  // the same with NSTAGE - 1 k-tiles' DMAs in flight (16x16x32 tile start)
+  // the same with NSTAGE - 1 k-tiles' DMAs in flight (2-stage ring, tile start)
   constexpr int INFLIGHT3 = (NSTAGE - 1) * NDMA;
   constexpr int WAIT_IMM3 = (INFLIGHT3 & 15) | ((INFLIGHT3 >> 4) << 14);
   // A barrier after this wave's LDS operations have completed, with no wait
@@ -535,11 +535,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
     // stage 0 has landed; the DMAs of the later stages may stay in flight
     if constexpr (BK == 64) {
       dma(lds1, clampk(1));
-      __builtin_amdgcn_s_waitcnt(WAIT_IMM3);
-    } else if constexpr (MF == 16) {
-      dma(lds1, clampk(1));
-      dma(lds2, clampk(2));
-      dma(lds3, clampk(3));
       __builtin_amdgcn_s_waitcnt(WAIT_IMM3);
     } else {
       dma(lds1, clampk(1));
@@ -631,18 +626,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
       __builtin_amdgcn_s_barrier();
       __asm__ volatile("" ::: "memory");
     };
-    // ---- 16x16x32: the whole 32-deep k-tile is one MFMA k-step.  The
-    // operand with more fragments per wave (W for the up projection's 64 x
-    // 128 wave tiles, the token rows for the down projection's 128 x 64) is
-    // read in two halves, the other operand double-buffered across k-tiles,
-    // so a wave holds 16 fragments instead of two full sets of 12.  Iteration
-    // kt: phase A runs the MFMAs of the first half under the reads of the
-    // second half (tile kt); then it waits until tile kt+1 has landed (tiles
-    // kt+2 and kt+3 may stay in flight) and crosses the barrier, after which
-    // every wave's reads of tile kt's stage are done; phase B runs the MFMAs
-    // of the second half under the reads of tile kt+1's other operand and
-    // first half and the DMA of tile kt+4 into tile kt's stage.  The DMA thus
-    // runs four tiles ahead.  P selects the double buffer of the tile.
+    // ---- 16x16x32 with 64-deep k-tiles in a 2-stage ring: two 32-deep MFMA
+    // k-steps per k-tile, each in two phases.  The operand with more
+    // fragments per wave (W for the up projection's 64 x 128 wave tiles, the
+    // token rows for the down projection's 128 x 64) is read in two halves,
+    // one per phase; the other operand is double-buffered across k-steps
+    // (k-step s uses buffer s), so a wave holds 16 fragments instead of two
+    // full sets of 12.  Each phase's MFMAs run under the fragment reads of
+    // the next phase.  There is one barrier per k-tile, before its last
+    // phase: it waits until tile kt+1 has landed, after which every wave's
+    // reads of tile kt's stage are done, so the last phase also issues the
+    // DMA of tile kt+2 into that stage, and the reads of tile kt+1's first
+    // k-step.  The DMA thus runs one k-tile ahead.
     constexpr bool SPW = NI >= MI;   // W fragments split in halves (else token rows)
     u32x4 w16[SPW ? 1 : 2][NI], x16[SPW ? 2 : 1][MI];
     auto lw = [&](const u32x4* buf, u32x4(&d)[NI], int j0, int j1, int ks = 0) {
@@ -674,54 +669,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
     };
     constexpr int NRA = SPW ? NI / 2 : MI / 2;        // phase A reads (second half, tile kt)
     constexpr int NRB = SPW ? MI + NI / 2 : NI + MI / 2;   // phase B reads (tile kt+1)
-    auto iteration16 = [&](const u32x4* cur_st, const u32x4* next_st, u32x4* free_st, int kt,
-                           int P) {
-      if constexpr (SPW) {
-        lw(cur_st, w16[0], NI / 2, NI);
-        if (P == 0) mm(w16[0], x16[0], 0, NI / 2, 0, MI);
-        else mm(w16[0], x16[1], 0, NI / 2, 0, MI);
-      } else {
-        lx(cur_st, x16[0], MI / 2, MI);
-        if (P == 0) mm(w16[0], x16[0], 0, NI, 0, MI / 2);
-        else mm(w16[1], x16[0], 0, NI, 0, MI / 2);
-      }
-      sched_front<NM / 2, SG_DS_READ, NRA, MOE_SCHED_PER, SG_VMEM_READ, 0>();
-      // phase A's MFMAs stay above the barrier, phase B's below it
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(WAIT_IMM);
-      __builtin_amdgcn_s_barrier();
-      __asm__ volatile("" ::: "memory");   // no LDS read moves above the barrier
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (SPW) {
-        if (P == 0) lx(next_st, x16[1], 0, MI);
-        else lx(next_st, x16[0], 0, MI);
-        lw(next_st, w16[0], 0, NI / 2);
-      } else {
-        if (P == 0) lw(next_st, w16[1], 0, NI);
-        else lw(next_st, w16[0], 0, NI);
-        lx(next_st, x16[0], 0, MI / 2);
-      }
-      dma(free_st, clampk(kt + NSTAGE));
-      if constexpr (SPW) {
-        if (P == 0) mm(w16[0], x16[0], NI / 2, NI, 0, MI);
-        else mm(w16[0], x16[1], NI / 2, NI, 0, MI);
-      } else {
-        if (P == 0) mm(w16[0], x16[0], 0, NI, MI / 2, MI);
-        else mm(w16[1], x16[0], 0, NI, MI / 2, MI);
-      }
-      sched_front<NM / 2, SG_DS_READ, NRB, MOE_SCHED_PER, SG_VMEM_READ, NDMA>();
-    };
-    auto idle16 = [&](u32x4* free_st, int kt) {
-      __builtin_amdgcn_s_waitcnt(WAIT_IMM);
-      __builtin_amdgcn_s_barrier();
-      __asm__ volatile("" ::: "memory");
-      dma(free_st, clampk(kt + NSTAGE));
-    };
-    // ---- 64-deep k-tiles (16x16x32, 2-stage ring): two MFMA k-steps per
-    // k-tile, each in the two phases above, but one barrier per k-tile: in
-    // the last phase, after the barrier, the reads of tile kt+1's first
-    // k-step and the DMA of tile kt+2 into tile kt's stage run under the
-    // MFMAs.  K-step s uses double buffer s.  The DMA runs one k-tile ahead.
     auto iteration64 = [&](const u32x4* cur_st, const u32x4* next_st, u32x4* free_st, int kt) {
       if constexpr (SPW) {
         lw(cur_st, w16[0], NI / 2, NI, 0);
@@ -768,7 +715,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
       __asm__ volatile("" ::: "memory");
       dma(free_st, clampk(kt + 2));
     };
-    if constexpr (MF == 16 && BK == 64) {
+    if constexpr (MF == 16) {
       if (wact) {
         if constexpr (SPW) {
           lx(lds0, x16[0], 0, MI, 0);
@@ -790,37 +737,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
           idle64(lds1, kt + 1);
         }
         if (kt < nk) idle64(lds0, kt);
-      }
-    } else if constexpr (MF == 16) {
-      if (wact) {
-        if constexpr (SPW) {
-          lx(lds0, x16[0], 0, MI);
-          lw(lds0, w16[0], 0, NI / 2);
-        } else {
-          lw(lds0, w16[0], 0, NI);
-          lx(lds0, x16[0], 0, MI / 2);
-        }
-        int kt = 0;
-        for (; kt + 3 < nk; kt += 4) {
-          iteration16(lds0, lds1, lds0, kt, 0);
-          iteration16(lds1, lds2, lds1, kt + 1, 1);
-          iteration16(lds2, lds3, lds2, kt + 2, 0);
-          iteration16(lds3, lds0, lds3, kt + 3, 1);
-        }
-        if (kt < nk) iteration16(lds0, lds1, lds0, kt, 0);
-        if (kt + 1 < nk) iteration16(lds1, lds2, lds1, kt + 1, 1);
-        if (kt + 2 < nk) iteration16(lds2, lds3, lds2, kt + 2, 0);
-      } else {
-        int kt = 0;
-        for (; kt + 3 < nk; kt += 4) {
-          idle16(lds0, kt);
-          idle16(lds1, kt + 1);
-          idle16(lds2, kt + 2);
-          idle16(lds3, kt + 3);
-        }
-        if (kt < nk) idle16(lds0, kt);
-        if (kt + 1 < nk) idle16(lds1, kt + 1);
-        if (kt + 2 < nk) idle16(lds2, kt + 2);
       }
     } else if (wact) {
       frag_load(lds0, wf[0], xf[0], 0);
