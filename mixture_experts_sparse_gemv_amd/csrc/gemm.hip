@@ -70,7 +70,14 @@ struct GemmArgs {
   // B = W [Nout, K] (row stride K); segment seg reduces over its padded row
   // range of the columns (wgrad_pad / wgrad_poff)
   int M;
+  // Bytes of X.  Below 2 GiB, the token-row loads of rows past a tile's
+  // valid rows carry an out-of-range buffer offset (0x80000000): the
+  // hardware returns zeros without reading memory, so ragged tiles fetch only
+  // their valid rows.  Otherwise such rows repeat the last valid row.
+  long long xbytes;
 };
+
+constexpr uint32_t kNoRow = 0x80000000u;   // out-of-range buffer offset (zeros, no fetch)
 
 
 // Per-segment row count and first row.
@@ -381,14 +388,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   // Source rows of this lane's token-row chunks: gathered tiles load their
   // sorted_assign entries (the token's assignment) ahead of the tile.
   int srow[QWX];
+  // Rows past the tile's valid rows: -1 (no row), or with a 2 GiB+ X the
+  // last valid row.
+  const bool x_oob = a.xbytes < (1LL << 31);
   auto row_loads = [&](const TileCoord& c) {
 #pragma unroll
     for (int j = 0; j < QWX; ++j) {
       const int q = BN / RI + wave * QWX + j;
       const int m = c.mt * BM + RI * q + lane / ROWCH - BN;
-      const int mm = m < c.rows ? m : c.rows - 1;
-      if (GATHER && c.seg < a.E) srow[j] = a.sorted_assign[c.start + mm];
-      else srow[j] = mm;
+      if (m >= c.rows && x_oob) {
+        srow[j] = -1;
+      } else {
+        const int mm = m < c.rows ? m : c.rows - 1;
+        if (GATHER && c.seg < a.E) srow[j] = a.sorted_assign[c.start + mm];
+        else srow[j] = mm;
+      }
     }
   };
   // K elements of the tile's slice (WGRAD: the segment's padded row range),
@@ -396,6 +410,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   int kslice;
   const char* xbase;
   const char* wbase;
+  long long xext;   // bytes of X from xbase
   uint32_t woff[QWW], xoff[QWX];
   auto setup = [&](const TileCoord& c) {
     kslice = WG ? seg_kpos[c.seg + 1] - seg_kpos[c.seg] : a.K / nsplit;
@@ -407,6 +422,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
       else xbase = (const char*)(a.X + (long long)c.start * a.K + (long long)c.ks * kslice);
       wbase = (const char*)(a.W + (long long)c.seg * a.Wrows * a.K + (long long)c.ks * kslice);
     }
+    xext = a.xbytes - (long long)(xbase - (const char*)a.X);
 #pragma unroll
     for (int j = 0; j < QWW; ++j) {
       const int q = wave * QWW + j;
@@ -426,8 +442,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
 #pragma unroll
     for (int j = 0; j < QWX; ++j) {
       const int q = BN / RI + wave * QWX + j;
-      const uint32_t row = (GATHER && c.seg < a.E) ? (uint32_t)(srow[j] / a.k) : (uint32_t)srow[j];
-      xoff[j] = (row * (uint32_t)a.K + (uint32_t)kc_dma(q) * 8u) * 2u;
+      const int sr = srow[j];
+      const uint32_t row = (GATHER && c.seg < a.E) ? (uint32_t)(sr / a.k) : (uint32_t)sr;
+      xoff[j] = sr < 0 ? kNoRow : (row * (uint32_t)a.K + (uint32_t)kc_dma(q) * 8u) * 2u;
     }
   };
   // The bias columns of a tile (K slice 0 only), two per thread of the first
@@ -465,19 +482,27 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   for (int i = 0; i < MI; ++i) xrb[i] = (BN + wm * WM + i * MF) * ROWCH;
 
   typedef __attribute__((address_space(3))) void lds_void_t;
+  // Token rows move through a buffer resource over X from the k-tile's
+  // column on (with x_oob its extent bounds every valid offset and the
+  // kNoRow offset of a missing row lies past it; otherwise it spans 4 GiB).
   auto dma = [&](u32x4* buf, int kt) {
     const char* wb = wbase + kt * (BK * 2);
-    const char* xb = xbase + kt * (BK * 2);
     u32x4* wdst = buf + wv * QWW * 64;
     u32x4* xdst = buf + BN * ROWCH + wv * QWX * 64;
 #pragma unroll
     for (int j = 0; j < QWW; ++j)
       __builtin_amdgcn_global_load_lds((const void*)(wb + woff[j]), (lds_void_t*)(wdst + j * 64),
                                        16, 0, 0);
+#if __HIP_DEVICE_COMPILE__   // (with template-dependent operands the host pass drops the kernel)
+    const long long xo = (long long)kt * (BK * 2);
+    const int nrec = x_oob ? (int)(xext - xo) : -1;
+    const __amdgpu_buffer_rsrc_t xres =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(xbase + xo), (short)0, nrec, 0x00020000);
 #pragma unroll
     for (int j = 0; j < QWX; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(xb + xoff[j]), (lds_void_t*)(xdst + j * 64),
-                                       16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_void_t*)(xdst + j * 64), 16, xoff[j], 0,
+                                               0, 0);
+#endif
   };
   auto frag_load = [&](const u32x4* buf, u32x4(&wf)[NI], u32x4(&xf)[MI], int s4) {
 #pragma unroll
@@ -1085,7 +1110,8 @@ hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void
   if (s.generic()) return launch_up_generic(s, x, w_up, b_up, offsets, sorted_assign, h, st);
   if (s.decode()) return launch_decode_up(s, x, w_up, b_up, s_up, offsets, sorted_assign, h, st);
   GemmArgs a{(const uint16_t*)x, (const uint16_t*)w_up, (const uint16_t*)bias, h, offsets,
-             sorted_assign, s.T, s.tok_div(), s.E, s.S, s.d, s.f, s.up_rows(), s.f, 1, nullptr, 0, 0};
+             sorted_assign, s.T, s.tok_div(), s.E, s.S, s.d, s.f, s.up_rows(), s.f, 1, nullptr, 0, 0,
+             (long long)s.T * s.d * 2};
   const bool mf16 = g_gemm_policy.load(std::memory_order_relaxed) != MOE_GEMM_MF32;
   if (s.act == MOE_SWIGLU) {
     const int NT = (s.f + UP_BN / 2 - 1) / (UP_BN / 2);
@@ -1123,7 +1149,8 @@ hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const 
   const int ks = down_ksplit(s);
   const long long part_elems = s.max_rows() * s.d;
   GemmArgs a{(const uint16_t*)h, (const uint16_t*)w_down, (const uint16_t*)bias, y_exp, offsets,
-             nullptr, s.T, s.tok_div(), s.E, s.S, s.f, s.d, s.d, s.f, ks, y_part, part_elems, 0};
+             nullptr, s.T, s.tok_div(), s.E, s.S, s.f, s.d, s.d, s.f, ks, y_part, part_elems, 0,
+             s.max_rows() * s.f * 2};
   const int NT = (s.d + DN_BN - 1) / DN_BN;
   dn_gemm<MODE_DOWN>(long_launch(s, s.f, s.d), s.f / ks, a,
                      dim3(grid_blocks(s, DN_BM, NT, ks, DN_OCC)), st);
@@ -1142,7 +1169,8 @@ hipError_t launch_bwd_lin(const Shape& s, const void* X, const void* W, const vo
                           int Wrows, int K, float* out, const int32_t* offsets,
                           const int32_t* sorted_assign, hipStream_t st) {
   GemmArgs a{(const uint16_t*)X, (const uint16_t*)W, (const uint16_t*)bias, out, offsets,
-             sorted_assign, s.T, s.tok_div(), s.E, s.S, K, Wrows, Wrows, s.f, 1, nullptr, 0, 0};
+             sorted_assign, s.T, s.tok_div(), s.E, s.S, K, Wrows, Wrows, s.f, 1, nullptr, 0, 0,
+             (long long)s.T * K * 2};
   const int NT = (Wrows + DN_BN - 1) / DN_BN;
   dn_gemm<MODE_LIN>(long_launch(s, K, Wrows), K, a, dim3(grid_blocks(s, DN_BM, NT)), st);
   return hipGetLastError();
@@ -1155,7 +1183,8 @@ hipError_t launch_bwd_dx(const Shape& s, const void* X, const void* W, int K, in
                          float* out2, long long part_elems, int ksplit, const int32_t* offsets,
                          hipStream_t st) {
   GemmArgs a{(const uint16_t*)X, (const uint16_t*)W, nullptr, out, offsets, nullptr, s.T,
-             s.tok_div(), s.E, s.S, K, N, N, s.f, ksplit, out2, part_elems, 0};
+             s.tok_div(), s.E, s.S, K, N, N, s.f, ksplit, out2, part_elems, 0,
+             s.max_rows() * K * 2};
   const int NT = (N + DN_BN - 1) / DN_BN;
   dn_gemm<MODE_DXB>(long_launch(s, K, N), K / ksplit, a,
                     dim3(grid_blocks(s, DN_BM, NT, ksplit)), st);
@@ -1167,7 +1196,7 @@ hipError_t launch_bwd_dx(const Shape& s, const void* X, const void* W, int K, in
 hipError_t launch_bwd_wgrad(const Shape& s, const void* A, const void* B, int M, int N, int ldk,
                             float* out, const int32_t* offsets, hipStream_t st) {
   GemmArgs a{(const uint16_t*)A, (const uint16_t*)B, nullptr, out, offsets, nullptr, s.T,
-             s.tok_div(), s.E, s.S, ldk, N, N, s.f, 1, nullptr, 0, M};
+             s.tok_div(), s.E, s.S, ldk, N, N, s.f, 1, nullptr, 0, M, (long long)M * ldk * 2};
   const long long tiles = (long long)(s.E + s.S) * ((M + DN_BM - 1) / DN_BM) *
                           ((N + DN_BN - 1) / DN_BN);
   long long g = tiles > kNumCUs ? kNumCUs : tiles;
