@@ -8,15 +8,19 @@
 // where row r belongs to expert e (offsets[e] <= r < offsets[e+1], token
 // sorted_assign[r] / k) or to a shared expert (token r - segment start).
 //
-// Dense contractions, so they run on the matrix cores: bf16 MFMA 32x32x16
-// for the up projection, fp16 MFMA 32x32x16 for the down projection (h is
-// fp16; each bf16 W2 fragment is converted to fp16 in registers after its
-// LDS read).  Accumulation is fp32.  Block = 8 waves (WGM x WGN grid); block
-// tile BM token rows x BN weight rows (256 x 256) x BK = 32, in a 4-stage
-// LDS ring filled by direct global-to-LDS DMA three k-tiles ahead, with an
-// XOR swizzle of the 16-byte chunks that keeps fragment reads conflict-free.
+// Dense contractions, so they run on the matrix cores: bf16 MFMAs for the up
+// projection, fp16 MFMAs for the down projection (h is fp16; each bf16 W2
+// fragment is converted to fp16 in registers after its LDS read).
+// Accumulation is fp32.  Block = 8 waves (WGM x WGN grid); block tile BM
+// token rows x BN weight rows (256 x 256).  Two main loops: 16x16x32 MFMAs
+// over 64-deep k-tiles in a 2-stage LDS ring (the DMA one k-tile ahead), for
+// the up projection and long down-style launches; 32x32x16 MFMAs over
+// 32-deep k-tiles in a 4-stage ring (the DMA three k-tiles ahead), for short
+// ones.  Both accumulate every output in the same order (bit-identical
+// results).  The ring is filled by direct global-to-LDS DMA, with an XOR
+// swizzle of the 16-byte chunks that keeps fragment reads conflict-free.
 // The MFMA "A" operand is the weight tile and "B" the token tile, so each
-// lane's accumulator holds four consecutive output columns of one token row;
+// lane's accumulators hold four consecutive output columns of one token row;
 // the epilogue stages each wave's rows in LDS and stores whole row segments.
 //
 // The tile schedule is computed on the device from offsets[] (no host sync):
@@ -186,7 +190,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   constexpr int STG = 32 * PITCH;                       // staging bytes per wave
   constexpr int WPA = STAGE * 16 / STG;                 // waves per ring stage
   constexpr int XTRA = (NSTAGE == 2 && WPA < NW) ? (NW - WPA) * STG : 0;
-  static_assert(WPA * (NSTAGE - 1) >= NW || NSTAGE == 2, "staging must fit in stages 1 to 3");
+  static_assert(WPA * (NSTAGE - 1) >= NW || NSTAGE == 2, "staging must fit in the ring stages after the first");
 
   // The LDS ring as distinct arrays: the compiler sees that the DMA into one
   // stage never aliases the fragment reads of another.
@@ -531,7 +535,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   };
 
   // ---- tile pipeline.  During a tile's epilogue (which stages its output in
-  // ring stages 1 to 3), once its first 32-row slab is out, the block's next
+  // the ring stages after the first), once its first 32-row slab is out, the block's next
   // tile issues the DMA of its first k-tile into stage 0 and loads its bias
   // columns, and the gathered source rows of the tile after that are
   // fetched.  Tile segments are located two tiles ahead (after a tile's main
@@ -805,7 +809,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
     // instruction would touch 16-32 rows with 16-32 bytes each; instead each
     // wave stages one 32-row slab of its output (one 32-row fragment, or two
     // 16-row ones; after bias and activation, in the output type) in a padded
-    // LDS region of ring stages 1 to 3 and writes it back as whole 16-byte
+    // LDS region of the ring stages after the first (with a 2-stage ring,
+    // stage 1 and a small extra region) and writes it back as whole 16-byte
     // chunks of rows, CPR lanes per row, so a store instruction covers RPI
     // rows of contiguous bytes.  The padding keeps the staging writes and
     // reads free of bank conflicts.
