@@ -190,7 +190,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   constexpr int STG = 32 * PITCH;                       // staging bytes per wave
   constexpr int WPA = STAGE * 16 / STG;                 // waves per ring stage
   constexpr int XTRA = (NSTAGE == 2 && WPA < NW) ? (NW - WPA) * STG : 0;
-  static_assert(WPA * (NSTAGE - 1) >= NW || NSTAGE == 2, "staging must fit in the ring stages after the first");
+  static_assert(WPA * (NSTAGE - 1) >= NW || NSTAGE == 2, "staging must fit in stages 1 to 3");
 
   // The LDS ring as distinct arrays: the compiler sees that the DMA into one
   // stage never aliases the fragment reads of another.
