@@ -10,13 +10,16 @@
 // blocks, i.e. T <= 1024).  For bf16 inputs the router
 // product runs on bf16 MFMA 16x16x32 (A = 16 router rows, B = 16 token rows),
 // each wave covering every 8th (16th) 32-wide K step and issuing the loads of 8
-// steps at once; the partial logit tiles of the waves are summed in LDS in a fixed
-// order.  The gate and the top-k then run one token per wave pass (two
-// tokens per wave, or one with 16 waves) with one lane per expert (E <= 64): wave-wide max and sum
-// by DPP row steps and scalar reads of the row results; each lane counts the
-// experts that beat it (a larger logit, or an equal one at a lower index),
-// reading their logits as scalars, so the experts of rank 0 .. k-1 are the
-// top k in order (ties to the lower index).  Experts are ranked by logit
+// steps at once (4 with three or four expert tiles); the partial logit tiles
+// of the waves are summed in LDS in a fixed order.  The gate and the top-k
+// then run one token per wave pass (two tokens per wave, or one with 16
+// waves) with one lane per expert (E <= 64): wave-wide max and sum by DPP
+// row steps and scalar reads of the row results.  Up to 16 experts,
+// each lane counts the experts that beat it (a larger logit, or an equal one
+// at a lower index), reading their logits as scalars, so the experts of rank
+// 0 .. k-1 are the top k in order (ties to the lower index); with more, the
+// k selections are taken one at a time as the largest remaining logit at its
+// lowest lane (a wave max, then a ballot).  Experts are ranked by logit
 // (monotone in both gates, so ranking and weights match ranking by score).
 // No step goes through the LDS crossbar.  Each block also
 // writes the sum of its 16 tokens' probabilities per expert (token order);
@@ -46,8 +49,12 @@ struct RouterArgs {
   int T, d, E, k, gating, dtype;
 };
 
+// At least 4 waves per SIMD (at most 128 VGPRs): two 8-wave blocks share a
+// compute unit, so T = 8192 (512 blocks) runs in one round also with four
+// expert tiles (measured at 64 experts, d = 2048: 41.7 -> 36.4 us).
 template <int NE16, int RW>  // expert tiles of 16 (bf16 path; 0 = fp32 path), waves
-__global__ __launch_bounds__(64 * RW) void router_kernel(RouterArgs a) {
+__global__ __launch_bounds__(64 * RW) __attribute__((amdgpu_waves_per_eu(4))) void router_kernel(
+    RouterArgs a) {
   __shared__ float red[RW][RT][kMaxExperts + 1];
   __shared__ float colp[RW][kMaxExperts];
   __shared__ int cntp[RW][kMaxExperts];
@@ -204,57 +211,40 @@ __global__ __launch_bounds__(64 * RW) void router_kernel(RouterArgs a) {
     // and a lower index (a NaN logit ranks below every number); lanes >= E
     // rank E or more.  The experts of rank 0 .. k-1 are the top k, in order.
     const float key = (l == l) ? l : NEG_INF;
-    int rank = 0;
+    int rank = a.k;
+    int my_idx = 0;
+    float my_score = 0.f, sel_sum = 0.f;
     if (E <= 16) {
+      rank = 0;
       for (int j = 0; j < E; ++j) {
         const float kj = lane_f(key, j);
         rank += (kj > key || (kj == key && j < lane)) ? 1 : 0;
       }
+      for (int s = 0; s < a.k; ++s) {
+        const uint64_t m = __ballot(rank == s);   // exactly one lane
+        const int bi = m ? __builtin_ctzll(m) : 0;
+        const float bs = lane_f(score, bi);
+        sel_sum += bs;
+        if (lane == s) { my_idx = bi; my_score = bs; }
+      }
     } else {
-      // Many experts: first find the selected set by a radix select on
-      // order-preserving 32-bit images of the logits (bit by bit from the
-      // top, ballots count the candidates with the bit set: the set "above"
-      // collects experts certainly selected, "cand" those equal to the k-th
-      // largest so far), take the lowest-index `need` of the experts equal to
-      // the k-th largest, then rank only the k selected ones.
-      const uint32_t kb = __float_as_uint(key + 0.0f);   // -0 -> +0
-      const uint32_t uk = lane < E ? ((kb & 0x80000000u) ? ~kb : (kb | 0x80000000u)) : 0u;
-      uint64_t cand = __ballot(lane < E), above = 0;
-      int need = a.k;
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint64_t hi = __ballot((uk >> bit) & 1u) & cand;
-        const int c = __popcll(hi);
-        if (c >= need) {
-          cand = hi;
-        } else {
-          need -= c;
-          above |= hi;
-          cand &= ~hi;
-        }
+      // Many experts: the k selections one at a time, each the largest
+      // remaining key (a wave max over DPP row steps) at its lowest lane
+      // (ballot of the lanes holding it among the remaining experts); the
+      // q-th selection is the expert of rank q.
+      uint64_t left = __ballot(lane < E);
+      for (int q = 0; q < a.k; ++q) {
+        const bool in = (left >> lane) & 1;
+        const float mx = wave_max_dpp(in ? key : NEG_INF);
+        const int j = __builtin_ctzll(__ballot(in && key == mx) & left);
+        const float bs = lane_f(score, j);
+        sel_sum += bs;
+        if (lane == j) rank = q;
+        if (lane == q) { my_idx = j; my_score = bs; }
+        left &= ~(1ull << j);
       }
-      uint64_t sel = above;
-      for (int q = 0; q < need; ++q) {
-        const uint64_t low = cand & (~cand + 1);   // lowest remaining candidate
-        sel |= low;
-        cand &= ~low;
-      }
-      for (uint64_t m = sel; m; m &= m - 1) {
-        const int j = __builtin_ctzll(m);
-        const uint32_t uj = __builtin_amdgcn_readlane(uk, j);
-        rank += (uj > uk || (uj == uk && j < lane)) ? 1 : 0;
-      }
-      if (!((sel >> lane) & 1)) rank = a.k;
     }
     if (rank < a.k) ++nsel;
-    int my_idx = 0;
-    float my_score = 0.f, sel_sum = 0.f;
-    for (int s = 0; s < a.k; ++s) {
-      const uint64_t m = __ballot(rank == s);   // exactly one lane
-      const int bi = m ? __builtin_ctzll(m) : 0;
-      const float bs = lane_f(score, bi);
-      sel_sum += bs;
-      if (lane == s) { my_idx = bi; my_score = bs; }
-    }
     if (lane < a.k && a.topk_idx) {   // (expert-choice routing uses the probabilities only)
       a.topk_idx[(long long)t * a.k + lane] = my_idx;
       a.topk_w[(long long)t * a.k + lane] = my_score / sel_sum;

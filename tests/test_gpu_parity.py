@@ -104,7 +104,8 @@ def test_router_topk(name):
 # duplicated experts' logits are equal in any precision; the selection must
 # then take the lower expert index first (top-k with ties to the lower
 # index, renormalized weights), on both top-k paths of the router kernel
-# (up to 16 experts: a rank count over all experts; more: a radix select).
+# (up to 16 experts: a rank count over all experts; more: k extractions of
+# the largest remaining logit at its lowest index).
 TIE_CASES = {
     "E8_top2_softmax": (scaled(RUNS["gpt2"], T=300, d_model=256, d_ff=256, router_bias="none"),
                         [(0, 1), (2, 5), (3, 4, 7)]),
