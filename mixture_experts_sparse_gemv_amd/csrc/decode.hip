@@ -151,6 +151,16 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   const int klen = DOWN ? a.K / a.nsplit : a.K;
   const int k0 = ks * klen;
   const int nk = klen / SK;
+  // Up projection: stage j of item i reads K stage (j + i) mod nk, so the
+  // items in flight at one moment read different columns of their rows.
+  // With every item at the same column (all rows of a matrix share their low
+  // address bits) the requests of a moment crowd the same DRAM channels:
+  // measured on the 8-expert d = 4096, f = 14336 layer, the bf16 up
+  // projection went from 0.77 to 0.83 of 8 TB/s and the FP8 one from 0.68 to
+  // 0.78.  The down projection's consecutive items are already different K
+  // slices (the same order there measured 1% slower).
+  const int rot = !DOWN && nk > 1 ? (int)(blockIdx.x % (unsigned)nk) : 0;
+  auto kpos = [&](int j) { const int p = j + rot; return p >= nk ? p - nk : p; };
 
   // Buffer-resource DMA: uniform bases (the expert's matrix and the token
   // rows, from column k0), per-lane 32-bit byte offsets that stay fixed over
@@ -236,16 +246,16 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int q = 0; q < NDMA; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t*)(buf + q * 64), 16, soff[q],
-                                               j * SK * WB, 0, 2 /* nt */);
+                                               kpos(j) * SK * WB, 0, 2 /* nt */);
 #pragma unroll
     for (int q = 0; q < NDX; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_void_t*)(buf + (DR / 8 + q) * 64), 16,
-                                               xoff[q], j * SK * 2, 0, 0);
+                                               xoff[q], kpos(j) * SK * 2, 0, 0);
     if (XREG) {
 #pragma unroll
       for (int u = 0; u < NSUBK; ++u)
         xs[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              xres, xroff + u * 64, j * SK * 2, 0));
+                                              xres, xroff + u * 64, kpos(j) * SK * 2, 0));
     }
 #endif
   };
