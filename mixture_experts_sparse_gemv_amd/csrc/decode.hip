@@ -440,7 +440,10 @@ hipError_t launch_decode_up(const Shape& s, const void* x, const void* w_up, con
 int decode_nsplit(const Shape& s) {
   // K slices of a whole number of stages (64 elements; 128 for FP8 weights)
   const int sk = s.w_fp8() ? 128 : 64;
-  return (s.f % (sk * kDecodeSplitK) == 0) ? kDecodeSplitK : (s.f % (2 * sk) == 0 ? 2 : 1);
+  const int want = s.w_fp8() ? kDecodeSplitK8 : kDecodeSplitK;
+  for (int n = want; n > 1; n /= 2)
+    if (s.f % (sk * n) == 0) return n;
+  return 1;
 }
 
 hipError_t launch_decode_down(const Shape& s, const void* h, const void* w_down,

@@ -57,8 +57,10 @@ inline int router_blocks(const Shape& s) { return (s.T + kRouterTokens - 1) / kR
 constexpr int kScatterTokens = 512;
 inline int scatter_blocks(const Shape& s) { return (s.T + kScatterTokens - 1) / kScatterTokens; }
 
-// Split of the reduction dimension in the decode down-projection.
-constexpr int kDecodeSplitK = 4;
+// Split of the reduction dimension in the decode down-projection (bf16 and
+// FP8 weights: FP8 stages hold twice the K elements, and 8 slices measured
+// 2% faster than 4 on the 8-expert d = 4096, f = 14336 layer; 16 slower).
+constexpr int kDecodeSplitK = 4, kDecodeSplitK8 = 8;
 
 // K slices of the (non-decode) down projection: 1, 2 or 4.  More than one
 // when its expected tile count would leave most compute units idle; slice 0
