@@ -261,7 +261,7 @@ def main():
                                  ((F1 + run.d_model) * 4 if run.w_fp8 else 0))
     step_bytes = (T * run.d_model * esz + E * run.d_model * esz + w_bytes_touched +
                   T * run.d_model * 4)
-    decode = run.dtype == "bf16" and T <= 64   # the library's weight-streaming path
+    decode = run.dtype == "bf16" and T <= 128   # the library's weight-streaming path
 
     # ---- per-stage pass: the same steps through the stage entry points, with
     # events around each stage on the launch stream

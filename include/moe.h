@@ -78,11 +78,11 @@ enum { MOE_ROUTER_BIAS = 1, MOE_EXPERT_BIAS = 2,        /* flags                
  * are multiples of 8 and T * d_model, T * d_ff < 2^31 (the kernels address
  * token rows and one expert's rows with 32-bit byte offsets).  When both are
  * multiples of 64 the expert FFNs run on the tiled grouped GEMMs (and the
- * weight-streaming kernels for T <= 64); otherwise on an untiled grouped GEMM
+ * weight-streaming kernels for T <= 128); otherwise on an untiled grouped GEMM
  * that is correct for any multiple of 8 but slower.  GELU is the exact erf
  * form; SwiGLU has no biases.
  * MOE_W_FP8 (expert weights quantized to 8 bits, 0539edu page 5.2) needs
- * MOE_BF16, T <= 64 (the weight-streaming decode path) and d_model, d_ff
+ * MOE_BF16, T <= 128 (the weight-streaming decode path) and d_model, d_ff
  * multiples of 128.
  * MOE_EXPERT_CHOICE ("MoE架构解析" 二 2.2: experts choose their tokens): every
  * expert takes exactly `capacity` tokens (1 <= capacity <= T, else

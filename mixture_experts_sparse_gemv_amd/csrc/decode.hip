@@ -1,14 +1,15 @@
-// Expert FFNs for decode-sized batches (T <= 64): the sparse-GEMV regime
+// Expert FFNs for decode-sized batches (T <= 128): the sparse-GEMV regime
 // ("MoE混合专家模型" 5.2: with few tokens the layer is a stream of the
 // touched experts' weights).
 //
-// Each expert sees at most T <= 64 rows, so the work is a stream of the
+// Each expert sees at most T <= 128 rows, so the work is a stream of the
 // touched experts' weights through the matrix cores with the (few) token
-// rows as the 16-wide MFMA operand, in up to 4 groups of 16: bf16 MFMA
+// rows as the 16-wide MFMA operand, in up to 4 groups of 16 (a segment with
+// more than 64 rows takes several passes, each streaming the weights): bf16 MFMA
 // 16x16x32 for the up projection, fp16 MFMA 16x16x32 for the down projection
-// (W2 converted to fp16 in registers).  Every weight byte of a touched expert is read from
-// HBM exactly once; experts with no rows are skipped without reading their
-// weights.
+// (W2 converted to fp16 in registers).  Every weight byte of a touched
+// expert is read from HBM once per pass (once when the expert has at most 64
+// rows); experts with no rows are skipped without reading their weights.
 //
 // One 64-lane wave (its own block) is one work item: DR consecutive rows of
 // one weight matrix (for SwiGLU DR/2 gate rows and the DR/2 matching up
@@ -141,10 +142,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   const int lane = threadIdx.x;
   const int seg = blockIdx.x / a.items_per_seg, it = blockIdx.x % a.items_per_seg;
   if (seg >= a.E + a.S) return;
-  int rows, start;
-  seg_info(a.offsets, seg, a.E, a.T, rows, start);
-  if (rows <= 0) return;   // untouched expert: its weights are never read
-  const int ntg = (rows + 15) >> 4;   // token groups holding rows (<= TG)
+  int rows_all, start_all;
+  seg_info(a.offsets, seg, a.E, a.T, rows_all, start_all);
+  if (rows_all <= 0) return;   // untouched expert: its weights are never read
 
   const int nt = DOWN ? it / a.nsplit : it;       // row block of the weight matrix
   const int ks = DOWN ? it % a.nsplit : 0;        // K slice
@@ -184,8 +184,13 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     soff[q] = (uint32_t)weight_row(r) * (uint32_t)a.K * WB + (uint32_t)c * 16u;
   }
+  // Passes over the segment's rows, 16 TG at a time: a segment with more rows
+  // than one pass holds streams the item's weights once per pass.
+  for (int p0 = 0; p0 < rows_all; p0 += 16 * TG) {
+  const int rows = min(16 * TG, rows_all - p0), start = start_all + p0;
+  const int ntg = (rows + 15) >> 4;   // token groups holding rows of this pass (<= TG)
   // token rows: x gathered through sorted_assign (up) or h (down); rows past
-  // the segment's count repeat a valid row and their outputs are not stored.
+  // the pass's count repeat a valid row and their outputs are not stored.
   // With F8 each token row of a stage spans two LDS rows (halves of 64).
 #pragma unroll
   for (int q = 0; q < NDX; ++q) {
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     const int tt = t < rows ? t : 0;
     uint32_t brow;
     if (DOWN) brow = (uint32_t)(start + tt);
-    else brow = (uint32_t)(seg < a.E ? a.sorted_assign[start + tt] / a.k : tt);
+    else brow = (uint32_t)(seg < a.E ? a.sorted_assign[start + tt] / a.k : p0 + tt);
     const int c = (lane & 7) ^ (((DR + rl) >> 1) & 7);
     xoff[q] = (brow * (uint32_t)a.K + (uint32_t)(half * 64 + c * 8)) * 2u;
   }
@@ -208,7 +213,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     const int tt = tvalid ? tl : 0;
     uint32_t brow;
     if (DOWN) brow = (uint32_t)(start + tt);
-    else brow = (uint32_t)(seg < a.E ? a.sorted_assign[start + tt] / a.k : tt);
+    else brow = (uint32_t)(seg < a.E ? a.sorted_assign[start + tt] / a.k : p0 + tt);
     xroff = (brow * (uint32_t)a.K + (uint32_t)(8 * g)) * 2u;
   }
   (void)xroff;   // read by the device pass only
@@ -384,6 +389,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       }
     }
   }
+  }   // passes
 }
 
 // y_exp[r, :] += the partials of K slices 1 .. nparts, in slice order.

@@ -13,16 +13,17 @@ namespace moe {
 constexpr int kMaxExperts = 64;       // routed experts: one wave lane per expert
 constexpr int kMaxTopK = 8;
 constexpr int kMaxSegments = 128;     // routed + shared experts
-// T at or below which the streaming decode path runs (at most 64: its kernels
-// carry up to 4 groups of 16 token rows per weight stage).  Measured on the
+// T at or below which the streaming decode path runs.  Its kernels carry up
+// to 4 groups of 16 token rows per weight stage; a segment with more rows
+// (above T = 64) streams its weights once per 64 rows.  Measured on the
 // large-expert shape (d_model 4096, SwiGLU 14336, 8 experts, top-2), ms per
 // forward, decode path vs 256-row grouped GEMM tiles: T = 24: 0.47 vs 0.66,
-// 32: 0.47 vs 0.67, 48: 0.54 vs 0.67, 64: 0.56 vs 0.68 (T = 128 by GEMM: 0.69).
+// 32: 0.47 vs 0.67, 48: 0.54 vs 0.67, 64: 0.56 vs 0.68, 128 by the GEMM 0.69.
 #ifndef MOE_DECODE_MAX_T
-#define MOE_DECODE_MAX_T 64
+#define MOE_DECODE_MAX_T 128
 #endif
 constexpr int kDecodeMaxT = MOE_DECODE_MAX_T;
-static_assert(kDecodeMaxT >= 1 && kDecodeMaxT <= 64, "decode token groups");
+static_assert(kDecodeMaxT >= 1 && kDecodeMaxT <= 128, "streaming path bound");
 constexpr int kEcMaxT = 16384;        // expert-choice selection keeps a column of T scores in LDS
 constexpr int kNumCUs = 256;          // MI355X compute units (sizes the K split of small GEMMs)
 

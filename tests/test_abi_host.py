@@ -51,8 +51,8 @@ def _problem(**kw):
 
 
 def test_workspace_size_grows_with_problem():
-    # within one path: the weight-streaming one (T <= 64) and the grouped GEMMs
-    for t0, t1 in ((16, 64), (128, 256)):
+    # within one path: the weight-streaming one (T <= 128) and the grouped GEMMs
+    for t0, t1 in ((16, 128), (256, 512)):
         a = M.moe_workspace_size(_problem(T=t0))
         b = M.moe_workspace_size(_problem(T=t1))
         assert 0 < a < b
@@ -163,8 +163,9 @@ def test_fp8_weights_validation():
     fake = 0x1000
     lib = M._lib
     byref = ctypes.byref
-    # FP8 expert weights are for the decode path only (T <= 64), bf16, d and f multiples of 128
-    for kw in (dict(T=65), dict(dtype="f32"), dict(d_model=192), dict(d_ff=320)):
+    # FP8 expert weights are for the weight-streaming path only (T <= 128), bf16, d and f
+    # multiples of 128
+    for kw in (dict(T=129), dict(dtype="f32"), dict(d_model=192), dict(d_ff=320)):
         args = dict(T=16, d_model=256, d_ff=512, num_experts=8, top_k=2, w_fp8=True)
         args.update(kw)
         p = M.make_problem(**args)

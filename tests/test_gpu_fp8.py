@@ -48,9 +48,9 @@ FP8_CASES = {
                                 num_experts=6, x_rows=0, seed=9),
     "fp8_shared_T5": scaled(RUNS["large_decode_fp8"], T=5, d_model=256, d_ff=384, num_shared=2,
                             gating="sigmoid_norm", num_experts=16, top_k=4, x_rows=0, seed=10),
-    # K long enough for the steady state of the decode ring (>= 7 stages of 128
-    # in both projections: d = 1024, and d_ff = 4096 in 4 K slices)
-    "fp8_swiglu_T16_d1024_f4096": scaled(RUNS["large_decode_fp8"], d_model=1024, d_ff=4096,
+    # K long enough for the steady state of the decode ring (at least 5 stages
+    # of 128 in both projections: d = 1024, and d_ff = 8192 in 8 K slices)
+    "fp8_swiglu_T16_d1024_f8192": scaled(RUNS["large_decode_fp8"], d_model=1024, d_ff=8192,
                                          x_rows=0, seed=11),
     # 2 and 4 groups of 16 token rows per weight stage
     "fp8_swiglu_T29": scaled(RUNS["large_decode_fp8"], T=29, d_model=512, d_ff=1024, x_rows=0,
@@ -58,6 +58,9 @@ FP8_CASES = {
     "fp8_gelu_bias_T64_shared": scaled(RUNS["large_decode_fp8"], T=64, d_model=256, d_ff=384,
                                        activation="gelu", expert_bias=True, num_shared=1,
                                        router_bias="learned", x_rows=0, seed=15),
+    # two row passes for the shared expert's 100 rows
+    "fp8_swiglu_T100_shared_two_passes": scaled(RUNS["large_decode_fp8"], T=100, d_model=256,
+                                                d_ff=384, num_shared=1, x_rows=0, seed=16),
 }
 
 

@@ -34,6 +34,11 @@ SMALL = {
     # the weight-streaming path with 2 and 4 groups of 16 token rows
     "decode_T40_d1024": scaled(RUNS["large_prefill"], T=40, d_model=1024, d_ff=2048),
     "decode_T64_shared_sigmoid": scaled(RUNS["fine_shared"], T=64, d_model=512, d_ff=768),
+    # segments of more than 64 rows on the weight-streaming path (T <= 128):
+    # two row passes, each streaming the weights again -- the skewed expert
+    # takes nearly every token; the shared experts take all 100
+    "decode_T128_skew_two_passes": scaled(RUNS["swiglu_skew"], T=128, top_k=2),
+    "decode_T100_shared_two_passes": scaled(RUNS["fine_shared"], T=100, d_model=512, d_ff=768),
     "fine_shared_T1000": scaled(RUNS["fine_shared"], T=1000),
     "fine_shared_T1000_literal": scaled(RUNS["fine_shared"], T=1000, capacity_factor=1.25 / 6),
     # more than 64 16-token router blocks (8 waves each, not 16) with 64
