@@ -187,208 +187,208 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   // Passes over the segment's rows, 16 TG at a time: a segment with more rows
   // than one pass holds streams the item's weights once per pass.
   for (int p0 = 0; p0 < rows_all; p0 += 16 * TG) {
-  const int rows = min(16 * TG, rows_all - p0), start = start_all + p0;
-  const int ntg = (rows + 15) >> 4;   // token groups holding rows of this pass (<= TG)
-  // token rows: x gathered through sorted_assign (up) or h (down); rows past
-  // the pass's count repeat a valid row and their outputs are not stored.
-  // With F8 each token row of a stage spans two LDS rows (halves of 64).
+    const int rows = min(16 * TG, rows_all - p0), start = start_all + p0;
+    const int ntg = (rows + 15) >> 4;   // token groups holding rows of this pass (<= TG)
+    // token rows: x gathered through sorted_assign (up) or h (down); rows past
+    // the pass's count repeat a valid row and their outputs are not stored.
+    // With F8 each token row of a stage spans two LDS rows (halves of 64).
 #pragma unroll
-  for (int q = 0; q < NDX; ++q) {
-    const int rl = 8 * q + (lane >> 3);
-    const int t = F8 ? rl >> 1 : rl, half = F8 ? rl & 1 : 0;
-    const int tt = t < rows ? t : 0;
-    uint32_t brow;
-    if (DOWN) brow = (uint32_t)(start + tt);
-    else brow = (uint32_t)(seg < a.E ? a.sorted_assign[start + tt] / a.k : p0 + tt);
-    const int c = (lane & 7) ^ (((DR + rl) >> 1) & 7);
-    xoff[q] = (brow * (uint32_t)a.K + (uint32_t)(half * 64 + c * 8)) * 2u;
-  }
-  // fragment reads (byte offsets in a stage): A rows 16q + tl, B token row
-  // 16 tg + tl; k-substep u covers K elements 32u .. 32u+31 of the stage
-  const int tl = lane & 15, g = lane >> 4;
-  const bool tvalid = tl < rows;
-  // XREG: the lane's token row (K elements 32u + 8g .. +7 of substep u)
-  uint32_t xroff = 0;
-  if (XREG) {
-    const int tt = tvalid ? tl : 0;
-    uint32_t brow;
-    if (DOWN) brow = (uint32_t)(start + tt);
-    else brow = (uint32_t)(seg < a.E ? a.sorted_assign[start + tt] / a.k : p0 + tt);
-    xroff = (brow * (uint32_t)a.K + (uint32_t)(8 * g)) * 2u;
-  }
-  (void)xroff;   // read by the device pass only
-  int fpos[RG][NSUBK], bpos[TG][NSUBK];
-#pragma unroll
-  for (int u = 0; u < NSUBK; ++u) {
-#pragma unroll
-    for (int q = 0; q < RG; ++q) {
-      const int r = 16 * q + tl;
-      if (F8) fpos[q][u] = r * 128 + (((2 * u + (g >> 1)) ^ ((r >> 1) & 7)) * 16) + 8 * (g & 1);
-      else fpos[q][u] = r * 128 + (((4 * u + g) ^ ((r >> 1) & 7)) * 16);
+    for (int q = 0; q < NDX; ++q) {
+      const int rl = 8 * q + (lane >> 3);
+      const int t = F8 ? rl >> 1 : rl, half = F8 ? rl & 1 : 0;
+      const int tt = t < rows ? t : 0;
+      uint32_t brow;
+      if (DOWN) brow = (uint32_t)(start + tt);
+      else brow = (uint32_t)(seg < a.E ? a.sorted_assign[start + tt] / a.k : p0 + tt);
+      const int c = (lane & 7) ^ (((DR + rl) >> 1) & 7);
+      xoff[q] = (brow * (uint32_t)a.K + (uint32_t)(half * 64 + c * 8)) * 2u;
     }
-#pragma unroll
-    for (int tg = 0; tg < TG; ++tg) {
-      const int tr = 16 * tg + tl;
-      const int rb = F8 ? DR + 2 * tr + (u >> 1) : DR + tr;
-      const int cb = F8 ? 4 * (u & 1) + g : 4 * u + g;
-      bpos[tg][u] = rb * 128 + ((cb ^ ((rb >> 1) & 7)) * 16);
-    }
-  }
-
-  // called with indices that are constants after unrolling
-  auto slot = [&](int i) -> u32x4* { return i == 0 ? ring0 : i == 1 ? ring1 : i == 2 ? ring2 : ring3; };
-  f32x4 acc[TG][RG];
-#pragma unroll
-  for (int tg = 0; tg < TG; ++tg)
-#pragma unroll
-    for (int q = 0; q < RG; ++q) acc[tg][q] = f32x4{};
-  // XREG: token fragments of the stages in flight, one set per ring slot
-  u32x4 xr[XREG ? NST : 1][NSUBK];
-
-  auto issue = [&](u32x4* buf, u32x4 (&xs)[NSUBK], int j) {
-#if __HIP_DEVICE_COMPILE__   // (with template-dependent operands the host pass drops the kernel)
-    typedef __attribute__((address_space(3))) void lds_void_t;
-#pragma unroll
-    for (int q = 0; q < NDMA; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t*)(buf + q * 64), 16, soff[q],
-                                               kpos(j) * SK * WB, 0, 2 /* nt */);
-#pragma unroll
-    for (int q = 0; q < NDX; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_void_t*)(buf + (DR / 8 + q) * 64), 16,
-                                               xoff[q], kpos(j) * SK * 2, 0, 0);
+    // fragment reads (byte offsets in a stage): A rows 16q + tl, B token row
+    // 16 tg + tl; k-substep u covers K elements 32u .. 32u+31 of the stage
+    const int tl = lane & 15, g = lane >> 4;
+    const bool tvalid = tl < rows;
+    // XREG: the lane's token row (K elements 32u + 8g .. +7 of substep u)
+    uint32_t xroff = 0;
     if (XREG) {
-#pragma unroll
-      for (int u = 0; u < NSUBK; ++u)
-        xs[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              xres, xroff + u * 64, kpos(j) * SK * 2, 0));
+      const int tt = tvalid ? tl : 0;
+      uint32_t brow;
+      if (DOWN) brow = (uint32_t)(start + tt);
+      else brow = (uint32_t)(seg < a.E ? a.sorted_assign[start + tt] / a.k : p0 + tt);
+      xroff = (brow * (uint32_t)a.K + (uint32_t)(8 * g)) * 2u;
     }
-#endif
-  };
-  auto compute = [&](const u32x4* buf, const u32x4 (&xs)[NSUBK]) {
-    const char* b = (const char*)buf;
+    (void)xroff;   // read by the device pass only
+    int fpos[RG][NSUBK], bpos[TG][NSUBK];
 #pragma unroll
     for (int u = 0; u < NSUBK; ++u) {
-      u32x4 w[RG];
 #pragma unroll
       for (int q = 0; q < RG; ++q) {
-        if (F8) w[q] = e4m3x8_to_16<DOWN>(*(const u32x2*)(b + fpos[q][u]));
-        else w[q] = DOWN ? bf16x8_to_f16x8(*(const u32x4*)(b + fpos[q][u])) : *(const u32x4*)(b + fpos[q][u]);
+        const int r = 16 * q + tl;
+        if (F8) fpos[q][u] = r * 128 + (((2 * u + (g >> 1)) ^ ((r >> 1) & 7)) * 16) + 8 * (g & 1);
+        else fpos[q][u] = r * 128 + (((4 * u + g) ^ ((r >> 1) & 7)) * 16);
       }
 #pragma unroll
       for (int tg = 0; tg < TG; ++tg) {
-        if (tg >= ntg) break;   // uniform: no rows of the segment in this group
-        const u32x4 xv = XREG ? xs[u] : *(const u32x4*)(b + bpos[tg][u]);
-#pragma unroll
-        for (int q = 0; q < RG; ++q) {
-          if (DOWN)
-            acc[tg][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                __builtin_bit_cast(f16x8, w[q]), __builtin_bit_cast(f16x8, xv), acc[tg][q], 0, 0, 0);
-          else
-            acc[tg][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, w[q]), __builtin_bit_cast(bf16x8, xv), acc[tg][q], 0, 0,
-                0);
-        }
+        const int tr = 16 * tg + tl;
+        const int rb = F8 ? DR + 2 * tr + (u >> 1) : DR + tr;
+        const int cb = F8 ? 4 * (u & 1) + g : 4 * u + g;
+        bpos[tg][u] = rb * 128 + ((cb ^ ((rb >> 1) & 7)) * 16);
       }
     }
-  };
-  // Each stage is NDMA + NDX DMA loads (+ NSUBK token loads with XREG); they
-  // complete in issue order.
-  constexpr int PER = NDMA + NDX + (XREG ? NSUBK : 0);
-  auto xslot = [&](int i) -> u32x4(&)[NSUBK] { return xr[XREG ? i : 0]; };
-  auto wait_stage = [&](int ahead) {   // stages issued after the one to consume
-    if (NST >= 4 && ahead >= 3) wait_vm<3 * PER>();
-    else if (NST >= 3 && ahead >= 2) wait_vm<2 * PER>();
-    else if (ahead >= 1) wait_vm<PER>();
-    else wait_vm<0>();
-    __asm__ volatile("" ::: "memory");
-  };
+
+    // called with indices that are constants after unrolling
+    auto slot = [&](int i) -> u32x4* { return i == 0 ? ring0 : i == 1 ? ring1 : i == 2 ? ring2 : ring3; };
+    f32x4 acc[TG][RG];
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+      for (int q = 0; q < RG; ++q) acc[tg][q] = f32x4{};
+    // XREG: token fragments of the stages in flight, one set per ring slot
+    u32x4 xr[XREG ? NST : 1][NSUBK];
+
+    auto issue = [&](u32x4* buf, u32x4 (&xs)[NSUBK], int j) {
+#if __HIP_DEVICE_COMPILE__   // (with template-dependent operands the host pass drops the kernel)
+      typedef __attribute__((address_space(3))) void lds_void_t;
+#pragma unroll
+      for (int q = 0; q < NDMA; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t*)(buf + q * 64), 16, soff[q],
+                                                 kpos(j) * SK * WB, 0, 2 /* nt */);
+#pragma unroll
+      for (int q = 0; q < NDX; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_void_t*)(buf + (DR / 8 + q) * 64), 16,
+                                                 xoff[q], kpos(j) * SK * 2, 0, 0);
+      if (XREG) {
+#pragma unroll
+        for (int u = 0; u < NSUBK; ++u)
+          xs[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                xres, xroff + u * 64, kpos(j) * SK * 2, 0));
+      }
+#endif
+    };
+    auto compute = [&](const u32x4* buf, const u32x4 (&xs)[NSUBK]) {
+      const char* b = (const char*)buf;
+#pragma unroll
+      for (int u = 0; u < NSUBK; ++u) {
+        u32x4 w[RG];
+#pragma unroll
+        for (int q = 0; q < RG; ++q) {
+          if (F8) w[q] = e4m3x8_to_16<DOWN>(*(const u32x2*)(b + fpos[q][u]));
+          else w[q] = DOWN ? bf16x8_to_f16x8(*(const u32x4*)(b + fpos[q][u])) : *(const u32x4*)(b + fpos[q][u]);
+        }
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) {
+          if (tg >= ntg) break;   // uniform: no rows of the segment in this group
+          const u32x4 xv = XREG ? xs[u] : *(const u32x4*)(b + bpos[tg][u]);
+#pragma unroll
+          for (int q = 0; q < RG; ++q) {
+            if (DOWN)
+              acc[tg][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                  __builtin_bit_cast(f16x8, w[q]), __builtin_bit_cast(f16x8, xv), acc[tg][q], 0, 0, 0);
+            else
+              acc[tg][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8, w[q]), __builtin_bit_cast(bf16x8, xv), acc[tg][q], 0, 0,
+                  0);
+          }
+        }
+      }
+    };
+    // Each stage is NDMA + NDX DMA loads (+ NSUBK token loads with XREG); they
+    // complete in issue order.
+    constexpr int PER = NDMA + NDX + (XREG ? NSUBK : 0);
+    auto xslot = [&](int i) -> u32x4(&)[NSUBK] { return xr[XREG ? i : 0]; };
+    auto wait_stage = [&](int ahead) {   // stages issued after the one to consume
+      if (NST >= 4 && ahead >= 3) wait_vm<3 * PER>();
+      else if (NST >= 3 && ahead >= 2) wait_vm<2 * PER>();
+      else if (ahead >= 1) wait_vm<PER>();
+      else wait_vm<0>();
+      __asm__ volatile("" ::: "memory");
+    };
 
 #pragma unroll
-  for (int j = 0; j < NST - 1; ++j)
-    if (j < nk) issue(slot(j), xslot(j), j);
-  // Stage j lives in ring slot j % NST (loops unrolled over the slots).
-  // Steady state: every step issues stage j + NST - 1 and waits for stage j
-  // with NST - 1 stages still in flight.
-  int j0 = 0;
-  for (; j0 + 2 * NST - 1 <= nk; j0 += NST) {
+    for (int j = 0; j < NST - 1; ++j)
+      if (j < nk) issue(slot(j), xslot(j), j);
+    // Stage j lives in ring slot j % NST (loops unrolled over the slots).
+    // Steady state: every step issues stage j + NST - 1 and waits for stage j
+    // with NST - 1 stages still in flight.
+    int j0 = 0;
+    for (; j0 + 2 * NST - 1 <= nk; j0 += NST) {
 #pragma unroll
-    for (int sl = 0; sl < NST; ++sl) {
-      __asm__ volatile("" ::: "memory");   // slot (j-1) % NST has been read
-      issue(slot((sl + NST - 1) % NST), xslot((sl + NST - 1) % NST), j0 + sl + NST - 1);
-      wait_vm<(NST - 1) * PER>();
-      __asm__ volatile("" ::: "memory");
-      compute(slot(sl), xslot(sl));
-    }
-  }
-  // the last (fewer than 2 NST - 1) stages
-  for (; j0 < nk; j0 += NST) {
-#pragma unroll
-    for (int sl = 0; sl < NST; ++sl) {
-      const int j = j0 + sl;
-      if (j < nk) {
+      for (int sl = 0; sl < NST; ++sl) {
+        __asm__ volatile("" ::: "memory");   // slot (j-1) % NST has been read
+        issue(slot((sl + NST - 1) % NST), xslot((sl + NST - 1) % NST), j0 + sl + NST - 1);
+        wait_vm<(NST - 1) * PER>();
         __asm__ volatile("" ::: "memory");
-        if (j + NST - 1 < nk)
-          issue(slot((sl + NST - 1) % NST), xslot((sl + NST - 1) % NST), j + NST - 1);
-        wait_stage(min(NST - 1, nk - 1 - j));
         compute(slot(sl), xslot(sl));
       }
     }
-  }
-  // D[row][token]: lane holds token 16 tg + tl and rows 16q + 4g + 0..3 of
-  // group q (consecutive weight rows, so their FP8 scales are one 16-byte load).
-  f32x4 sc[RG];
-  if (F8) {
+    // the last (fewer than 2 NST - 1) stages
+    for (; j0 < nk; j0 += NST) {
 #pragma unroll
-    for (int q = 0; q < RG; ++q)
-      sc[q] = *(const f32x4*)(a.wscale + (long long)seg * a.Wrows + weight_row(16 * q + 4 * g));
-  }
-#pragma unroll
-  for (int tg = 0; tg < TG; ++tg) {
-    const int t = 16 * tg + tl;
-    if (t >= rows) break;   // the rows of a segment are 0 .. rows - 1
-    f32x4* ac = acc[tg];
+      for (int sl = 0; sl < NST; ++sl) {
+        const int j = j0 + sl;
+        if (j < nk) {
+          __asm__ volatile("" ::: "memory");
+          if (j + NST - 1 < nk)
+            issue(slot((sl + NST - 1) % NST), xslot((sl + NST - 1) % NST), j + NST - 1);
+          wait_stage(min(NST - 1, nk - 1 - j));
+          compute(slot(sl), xslot(sl));
+        }
+      }
+    }
+    // D[row][token]: lane holds token 16 tg + tl and rows 16q + 4g + 0..3 of
+    // group q (consecutive weight rows, so their FP8 scales are one 16-byte load).
+    f32x4 sc[RG];
     if (F8) {
 #pragma unroll
-      for (int q = 0; q < RG; ++q) ac[q] *= sc[q];
+      for (int q = 0; q < RG; ++q)
+        sc[q] = *(const f32x4*)(a.wscale + (long long)seg * a.Wrows + weight_row(16 * q + 4 * g));
     }
-    const long long orow = start + t;
-    if (DOWN) {
-      float* out = (ks == 0 ? (float*)a.out : a.part + (ks - 1) * a.part_stride) + orow * a.Wrows +
-                   nt * DR + 4 * g;
 #pragma unroll
-      for (int q = 0; q < RG; ++q) {
-        f32x4 v = ac[q] * kHLoadScale;   // h was stored scaled by 2^-8
-        if (ks == 0 && a.bias) {
-          const uint16_t* b = a.bias + (long long)seg * a.Wrows + nt * DR + 16 * q + 4 * g;
+    for (int tg = 0; tg < TG; ++tg) {
+      const int t = 16 * tg + tl;
+      if (t >= rows) break;   // the rows of a segment are 0 .. rows - 1
+      f32x4* ac = acc[tg];
+      if (F8) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] += bf16_to_f32(b[r]);
-        }
-        *(f32x4*)(out + 16 * q) = v;
+        for (int q = 0; q < RG; ++q) ac[q] *= sc[q];
       }
-    } else if (SWIGLU) {
-      _Float16* hrow = (_Float16*)a.out + orow * a.f + nt * (DR / 2) + 4 * g;
+      const long long orow = start + t;
+      if (DOWN) {
+        float* out = (ks == 0 ? (float*)a.out : a.part + (ks - 1) * a.part_stride) + orow * a.Wrows +
+                     nt * DR + 4 * g;
 #pragma unroll
-      for (int q = 0; q < RG / 2; ++q) {
-        f16x4 v;
+        for (int q = 0; q < RG; ++q) {
+          f32x4 v = ac[q] * kHLoadScale;   // h was stored scaled by 2^-8
+          if (ks == 0 && a.bias) {
+            const uint16_t* b = a.bias + (long long)seg * a.Wrows + nt * DR + 16 * q + 4 * g;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = h_to_f16(silu_f(ac[q][r]) * ac[q + RG / 2][r]);
-        *(f16x4*)(hrow + 16 * q) = v;
-      }
-    } else {
-      _Float16* hrow = (_Float16*)a.out + orow * a.f + nt * DR + 4 * g;
-#pragma unroll
-      for (int q = 0; q < RG; ++q) {
-        f16x4 v;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float z = ac[q][r];
-          if (a.bias) z += bf16_to_f32(a.bias[(long long)seg * a.Wrows + nt * DR + 16 * q + 4 * g + r]);
-          v[r] = h_to_f16(MODE == MOE_RELU ? fmaxf(z, 0.f) : gelu_f(z));
+            for (int r = 0; r < 4; ++r) v[r] += bf16_to_f32(b[r]);
+          }
+          *(f32x4*)(out + 16 * q) = v;
         }
-        *(f16x4*)(hrow + 16 * q) = v;
+      } else if (SWIGLU) {
+        _Float16* hrow = (_Float16*)a.out + orow * a.f + nt * (DR / 2) + 4 * g;
+#pragma unroll
+        for (int q = 0; q < RG / 2; ++q) {
+          f16x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = h_to_f16(silu_f(ac[q][r]) * ac[q + RG / 2][r]);
+          *(f16x4*)(hrow + 16 * q) = v;
+        }
+      } else {
+        _Float16* hrow = (_Float16*)a.out + orow * a.f + nt * DR + 4 * g;
+#pragma unroll
+        for (int q = 0; q < RG; ++q) {
+          f16x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float z = ac[q][r];
+            if (a.bias) z += bf16_to_f32(a.bias[(long long)seg * a.Wrows + nt * DR + 16 * q + 4 * g + r]);
+            v[r] = h_to_f16(MODE == MOE_RELU ? fmaxf(z, 0.f) : gelu_f(z));
+          }
+          *(f16x4*)(hrow + 16 * q) = v;
+        }
       }
     }
-  }
   }   // passes
 }
 
