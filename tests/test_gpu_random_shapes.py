@@ -1,6 +1,7 @@
 """GPU parity of the forward (and, for bf16 token choice, the backward) on a
 seeded sweep of small, irregular layer shapes: token counts around the
-decode bound and the 256-row tile (1, 5, 16, 17, 255, 257, ...), widths
+decode bounds and the 256-row tile (1, 5, 16, 17, 65, 128, 129, 255, 257,
+...), widths
 that leave partial 256- and 128-column tiles, one to 64 experts with odd
 counts, top-k up to 8, shared experts, both gates, every activation with and
 without biases, and capacities from unlimited to tight.  Each case is drawn
@@ -21,13 +22,15 @@ from _parity import (compare_forward, gpu_inputs, oracle_capacity, oracle_forwar
                      run_forward, weights_of, routing_outputs)
 from test_gpu_backward import LazyF64, assert_grad_close, grad_outputs
 
-N_CASES = 24
+N_CASES = 36
 
 
 def _draw(i):
     rng = random.Random(1000 + i)
     dtype = "f32" if i % 8 == 7 else "bf16"
     T = rng.choice([1, 5, 16, 17, 33, 63, 64, 65, 200, 255, 257, 513, 777])
+    if i >= 24:   # around the streaming path's bound (row passes of 64 above T = 64)
+        T = rng.choice([65, 96, 127, 128, 129, 160])
     if dtype == "bf16":
         d = rng.choice([64, 128, 192, 320, 512])
         f = rng.choice([64, 128, 192, 448, 640])
@@ -66,6 +69,7 @@ def test_sweep_is_varied():
     runs = CASES
     assert any(r.T <= 16 and r.dtype == "bf16" for r in runs)        # decode kernels
     assert any(16 < r.T <= 64 and r.dtype == "bf16" for r in runs)  # several token groups
+    assert any(64 < r.T <= 128 and r.dtype == "bf16" for r in runs)  # row passes
     assert any(r.T > 256 and r.dtype == "bf16" for r in runs)        # several m-tiles
     assert any(r.num_shared > 0 for r in runs)
     assert any(r.capacity_factor is not None for r in runs)
