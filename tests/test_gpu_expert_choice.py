@@ -52,6 +52,9 @@ EC_CASES = {
                             activation="swiglu", expert_bias=False, router_bias="none",
                             capacity_factor=1.0, seed=13),
     "ec_d392_f584_T500": scaled(RUNS["gpt2_ec"], T=500, d_model=392, d_ff=584, seed=16),
+    # the streaming path with 128 rows per expert: two row passes
+    "ec_T128_two_passes": scaled(RUNS["gpt2_ec"], T=128, d_model=256, d_ff=512, num_experts=2,
+                                 seed=17),
     "gpt2_ec": RUNS["gpt2_ec"],
 }
 
