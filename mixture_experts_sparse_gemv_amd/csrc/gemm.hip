@@ -342,6 +342,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   // holds tile LL records the segment and the tile's K slice, n-tile and
   // m-tile in slot b.
   __shared__ int sh_coord[2][3];
+  // Within a segment the m-tiles run fastest: the blocks working at once
+  // share one n-tile of W, and X is read again for every n-tile, from the
+  // L2 and the MALL while it fits there.  A weight gradient whose X (the
+  // transposed gradient of the up projection's pre-activations, 2 d_ff or
+  // d_ff rows per segment) is both the larger operand and larger than half
+  // the 256 MB MALL runs the n-tiles fastest instead, so that X is read
+  // once and the smaller W again (large_prefill dW1: 4.65 -> 3.85 ms).
+  const bool nfast = WG && a.M > a.Nout && a.xbytes > (128LL << 20);
   auto locate = [&](int LL, int b) {
     const bool lt = !WG && LL >= nheavy;
     const int* P = lt ? seg_lt : seg_tile;
@@ -354,8 +362,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
       const int local = L - P[tid] * NT;
       sh_seg[b] = tid;
       sh_coord[b][0] = ks;
-      sh_coord[b][1] = local / m;
-      sh_coord[b][2] = local % m + (lt ? hm : 0);
+      sh_coord[b][1] = nfast ? local % NT : local / m;
+      sh_coord[b][2] = nfast ? local / NT : local % m + (lt ? hm : 0);
     }
   };
   auto coords = [&](int b) {   // the tile located in slot b

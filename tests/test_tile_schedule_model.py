@@ -4,7 +4,9 @@ half of the block's rows), the run-time choice between one and two lists,
 the per-XCD ranges of each list, and the decode of a tile id into (K slice,
 segment, n-tile, m-tile).  The model follows the kernel's integer
 arithmetic step by step; every tile of every segment must be visited
-exactly once, for any grid size, K split and mix of segment lengths."""
+exactly once, for any grid size, K split and mix of segment lengths.  The
+weight-gradient mode's schedule (XCD ranges split by k-tiles, m-tiles or
+n-tiles fastest) is modelled the same way."""
 import random
 
 import pytest
@@ -107,3 +109,55 @@ def test_split_lists_case_takes_two_lists():
     rows = [int(c) for c in np.bincount(idx.ravel(), minlength=run.num_experts)]
     seen, two = schedule(rows, 1, 1, 256)
     assert two and sorted(seen) == expected(rows, 1, 1)
+
+
+def wgrad_schedule(kpad, mtw, NT, grid, nfast):
+    """The weight-gradient schedule: every segment has mtw m-tiles and NT
+    n-tiles, each tile reducing over the segment's kpad padded rows; XCD x
+    takes the tile ids whose k-tile midpoints fall in its eighth of all
+    k-tiles, and a tile id decodes with the m-tiles fastest or, when nfast,
+    the n-tiles fastest."""
+    nseg = len(kpad)
+    kpos = [0]
+    for p in kpad:
+        kpos.append(kpos[-1] + p)
+    Ts = mtw * NT
+    W = (kpos[nseg] // 32) * Ts
+    G = 8
+    nslots = grid >> 3
+    seen = []
+    for b in range(grid):
+        xcd = b & 7
+        rng = []
+        for e in (0, 1):
+            X0 = 2 * (xcd + e) * W
+            cnt = 0
+            for sg in range(nseg):
+                w = (kpos[sg + 1] - kpos[sg]) // 32
+                X = X0 - 2 * G * ((kpos[sg] // 32) * Ts)
+                c = ((X - 1) // (G * w) + 1) // 2 if X >= 1 else 0
+                cnt += min(c, Ts)
+            rng.append(cnt)
+        first, end = rng
+        it = b >> 3
+        while first + it < end:
+            LL = first + it
+            s = LL // Ts
+            local = LL - s * Ts
+            nt, mt = (local % NT, local // NT) if nfast else (local // mtw, local % mtw)
+            assert nt < NT and mt < mtw
+            seen.append((s, nt, mt))
+            it += nslots
+    return seen
+
+
+@pytest.mark.parametrize("nfast", [False, True])
+def test_wgrad_every_tile_exactly_once(nfast):
+    rng = random.Random(5 + nfast)
+    for _ in range(200):
+        nseg = rng.randint(1, 70 if rng.random() < 0.2 else 10)
+        kpad = [64 * rng.choice([1, 1, 2, 17, rng.randint(1, 300)]) for _ in range(nseg)]
+        mtw, NT, grid = rng.randint(1, 12), rng.randint(1, 12), 8 * rng.randint(1, 32)
+        seen = wgrad_schedule(kpad, mtw, NT, grid, nfast)
+        assert sorted(seen) == sorted((s, n, m) for s in range(nseg) for n in range(NT)
+                                      for m in range(mtw))
