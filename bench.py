@@ -42,6 +42,8 @@ def parse():
                     help="backward: time moe_ffn_backward (gradients of the task loss plus "
                          "alpha * L_aux) instead of the forward")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--gemm-policy", choices=("auto", "mf32", "mf16"), default="auto",
+                    help="grouped GEMM main loop (moe_set_gemm_policy; results are identical)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (for counter scaling)")
     ap.add_argument("--record-traffic", nargs=6,
@@ -152,6 +154,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    M.moe_set_gemm_policy({"auto": M.MOE_GEMM_AUTO, "mf32": M.MOE_GEMM_MF32,
+                           "mf16": M.MOE_GEMM_MF16}[a.gemm_policy])
 
     if a.copy_calibration_mb:
         n = a.copy_calibration_mb * (1 << 20) // 4
