@@ -6,20 +6,18 @@
 // stores); the sum runs in slot order, then shared-expert order, so the
 // result does not depend on scheduling.  Every element of y is written.
 // When the down projection ran in K slices, a row of y_exp is its slice-0
-// value plus the other slices' partials, added here in slice order.  The
-// fused forward's tiled path stores y_exp and the partials in fp16 scaled by
-// 2^-8 (YT = _Float16): they are widened to fp32, summed, and scaled back.
+// value plus the other slices' partials, added here in slice order.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-template <int VEC, typename YT>
+template <int VEC>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ topk_w,
                                                       const int32_t* __restrict__ assign_row,
                                                       const int32_t* __restrict__ offsets,
-                                                      const YT* __restrict__ y_exp,
-                                                      const YT* __restrict__ y_part,
+                                                      const float* __restrict__ y_exp,
+                                                      const float* __restrict__ y_part,
                                                       int nparts, long long part_elems,
                                                       float* __restrict__ y, int T, int d, int k,
                                                       int E, int S) {
@@ -29,13 +27,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int t = (int)(gid / dv);
   const int c = (int)(gid % dv) * VEC;
   typedef float vec_t __attribute__((ext_vector_type(VEC)));
-  typedef YT yvec_t __attribute__((ext_vector_type(VEC)));
   // row value: y_exp plus the K-slice partials, in slice order
   auto row = [&](long long r) {
-    vec_t v = __builtin_convertvector(*(const yvec_t*)(y_exp + r * d + c), vec_t);
-    for (int p = 0; p < nparts; ++p)
-      v += __builtin_convertvector(*(const yvec_t*)(y_part + p * part_elems + r * d + c), vec_t);
-    if constexpr (sizeof(YT) == 2) v *= kHLoadScale;
+    vec_t v = *(const vec_t*)(y_exp + r * d + c);
+    for (int p = 0; p < nparts; ++p) v += *(const vec_t*)(y_part + p * part_elems + r * d + c);
     return v;
   };
   vec_t acc = {};
@@ -54,21 +49,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 hipError_t launch_combine(const Shape& s, const float* topk_w, const int32_t* assign_row,
                           const int32_t* offsets, const float* y_exp, const float* y_part,
-                          int nparts, float* y, hipStream_t st, bool y16) {
+                          int nparts, float* y, hipStream_t st) {
   const long long part_elems = s.max_rows() * s.d;
-  if (y16) {   // the tiled path: d is a multiple of 64
-    if (s.d % 4 != 0) return hipErrorInvalidValue;
+  if (s.d % 4 == 0) {
     const long long n = (long long)s.T * (s.d / 4);
-    combine_kernel<4, _Float16><<<(int)((n + 255) / 256), 256, 0, st>>>(
-        topk_w, assign_row, offsets, (const _Float16*)y_exp, (const _Float16*)y_part, nparts,
-        part_elems, y, s.T, s.d, s.k, s.E, s.S);
-  } else if (s.d % 4 == 0) {
-    const long long n = (long long)s.T * (s.d / 4);
-    combine_kernel<4, float><<<(int)((n + 255) / 256), 256, 0, st>>>(
+    combine_kernel<4><<<(int)((n + 255) / 256), 256, 0, st>>>(
         topk_w, assign_row, offsets, y_exp, y_part, nparts, part_elems, y, s.T, s.d, s.k, s.E, s.S);
   } else {
     const long long n = (long long)s.T * s.d;
-    combine_kernel<1, float><<<(int)((n + 255) / 256), 256, 0, st>>>(
+    combine_kernel<1><<<(int)((n + 255) / 256), 256, 0, st>>>(
         topk_w, assign_row, offsets, y_exp, y_part, nparts, part_elems, y, s.T, s.d, s.k, s.E, s.S);
   }
   return hipGetLastError();

@@ -160,14 +160,11 @@ __global__ __launch_bounds__(256) void token_experts_kernel(const int32_t* __res
   token_experts[t] = n;
 }
 
-// YT = _Float16: y_exp and the partials in fp16 scaled by 2^-8 (widened,
-// summed in fp32 and scaled back).
-template <typename YT>
 __global__ __launch_bounds__(256) void combine_ec_kernel(const float* __restrict__ probs,
                                                          const int32_t* __restrict__ row_of,
                                                          const int32_t* __restrict__ offsets,
-                                                         const YT* __restrict__ y_exp,
-                                                         const YT* __restrict__ y_part,
+                                                         const float* __restrict__ y_exp,
+                                                         const float* __restrict__ y_part,
                                                          int nparts, long long part_elems,
                                                          float* __restrict__ y, int T, int d, int E,
                                                          int S) {
@@ -176,12 +173,9 @@ __global__ __launch_bounds__(256) void combine_ec_kernel(const float* __restrict
   if (gid >= (long long)T * dv) return;
   const int t = (int)(gid / dv);
   const int c = (int)(gid % dv) * 4;
-  typedef YT yvec_t __attribute__((ext_vector_type(4)));
   auto row = [&](long long r) {
-    f32x4 v = __builtin_convertvector(*(const yvec_t*)(y_exp + r * d + c), f32x4);
-    for (int p = 0; p < nparts; ++p)
-      v += __builtin_convertvector(*(const yvec_t*)(y_part + p * part_elems + r * d + c), f32x4);
-    if constexpr (sizeof(YT) == 2) v *= kHLoadScale;
+    f32x4 v = *(const f32x4*)(y_exp + r * d + c);
+    for (int p = 0; p < nparts; ++p) v += *(const f32x4*)(y_part + p * part_elems + r * d + c);
     return v;
   };
   f32x4 acc = {};
@@ -214,15 +208,10 @@ hipError_t launch_token_experts(const Shape& s, const int32_t* row_of, int32_t* 
 
 hipError_t launch_combine_ec(const Shape& s, const float* probs, const int32_t* row_of,
                              const int32_t* offsets, const float* y_exp, const float* y_part,
-                             int nparts, float* y, hipStream_t st, bool y16) {
+                             int nparts, float* y, hipStream_t st) {
   const long long n = (long long)s.T * (s.d / 4);
-  if (y16)
-    combine_ec_kernel<_Float16><<<(int)((n + 255) / 256), 256, 0, st>>>(
-        probs, row_of, offsets, (const _Float16*)y_exp, (const _Float16*)y_part, nparts,
-        s.max_rows() * s.d, y, s.T, s.d, s.E, s.S);
-  else
-    combine_ec_kernel<float><<<(int)((n + 255) / 256), 256, 0, st>>>(
-        probs, row_of, offsets, y_exp, y_part, nparts, s.max_rows() * s.d, y, s.T, s.d, s.E, s.S);
+  combine_ec_kernel<<<(int)((n + 255) / 256), 256, 0, st>>>(
+      probs, row_of, offsets, y_exp, y_part, nparts, s.max_rows() * s.d, y, s.T, s.d, s.E, s.S);
   return hipGetLastError();
 }
 

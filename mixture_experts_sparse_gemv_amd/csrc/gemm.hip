@@ -48,16 +48,14 @@ namespace moe {
 namespace {
 
 // Up projection with activation (RELU/GELU/SWIGLU, fp16 h out), down
-// projection (DOWN: fp16 h times W2 converted to fp16, fp32 out; DOWN16: the
-// same with y_exp stored in fp16, scaled by 2^-8 like h, for the fused
-// forward, whose combine reads it back).  The
+// projection (DOWN: fp16 h times W2 converted to fp16, fp32 out).  The
 // backward pass adds: LIN, gathered token rows times bf16 weights with an
 // optional bias and fp32 out (no activation); DXB, like DOWN with bf16 rows
 // and weights; WGRAD, the per-expert weight gradient, whose reduction runs
 // over the expert's rows (see wgrad_* below).
 enum {
   MODE_RELU = 0, MODE_GELU = 1, MODE_SWIGLU = 2, MODE_DOWN = 3, MODE_LIN = 4, MODE_DXB = 5,
-  MODE_WGRAD = 6, MODE_DOWN16 = 7
+  MODE_WGRAD = 6
 };
 
 struct GemmArgs {
@@ -69,9 +67,8 @@ struct GemmArgs {
   const int32_t* sorted_assign;
   int T, k, E, S, K, Nout, Wrows, f;
   // DOWN / DXB: K slices; slice i > 0 writes to out2 + (i - 1) * part_elems
-  // (elements of the output type)
   int ksplit;
-  void* out2;
+  float* out2;
   long long part_elems;
   // WGRAD: out[seg] = A_seg B_seg^T, [M, Nout] fp32, with A = X [M, K] and
   // B = W [Nout, K] (row stride K); segment seg reduces over its padded row
@@ -157,11 +154,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
   constexpr int NW = WGM * WGN;            // waves: WGM along tokens x WGN along weights
   constexpr bool SWIGLU = MODE == MODE_SWIGLU;
   constexpr bool GATHER = MODE <= MODE_SWIGLU || MODE == MODE_LIN;   // token rows via sorted_assign
-  constexpr bool DOWN = MODE == MODE_DOWN || MODE == MODE_DOWN16;
-  constexpr bool CVT16 = DOWN;                   // fp16 rows: W converted bf16 -> fp16
-  // fp32 output; else fp16 scaled by 2^-8 (h, or DOWN16's y_exp)
-  constexpr bool OUT32 = MODE >= MODE_DOWN && MODE != MODE_DOWN16;
-  constexpr bool KSPLIT = DOWN || MODE == MODE_DXB;
+  constexpr bool CVT16 = MODE == MODE_DOWN;      // fp16 rows: W converted bf16 -> fp16
+  constexpr bool OUT32 = MODE >= MODE_DOWN;      // fp32 output (else fp16 h)
+  constexpr bool KSPLIT = MODE == MODE_DOWN || MODE == MODE_DXB;
   constexpr bool WG = MODE == MODE_WGRAD;
   constexpr bool BIAS = !SWIGLU && !WG;         // an optional per-column bias
   constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile: token rows x weight rows
@@ -850,8 +845,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void grouped_gemm_kernel(GemmA
       stg = (char*)(wa == 0 ? lds1 : wa == 1 ? lds2 : lds3) + (wv % WPA) * STG;
     }
     const int colw = SWIGLU ? cur.nt * (BN / 2) + wn * (BN / 2 / WGN) : cur.nt * BN + wn * WN;
-    char* obase = cur.ks == 0 ? (char*)a.out
-                              : (char*)a.out2 + (long long)(cur.ks - 1) * a.part_elems * ES;
+    char* obase =
+        cur.ks == 0 ? (char*)a.out : (char*)(a.out2 + (long long)(cur.ks - 1) * a.part_elems);
 #pragma unroll
     for (int sl = 0; sl < MI / FPS; ++sl) {
 #pragma unroll
@@ -1148,21 +1143,10 @@ hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void
   return hipGetLastError();
 }
 
-// fp16 y_exp pays where the reduction is short (d_ff <= 4096): there the
-// y_exp write and the combine's read are a larger share of the step (measured
-// A/B on one GPU: fine_shared 0.854 -> 0.834 ms, gpt2 0.139 -> 0.137 ms); on
-// the large prefill layer (d_ff 14336) the fp32 store measured faster (5.13
-// against 5.20 ms).
-bool down_y16(const Shape& s) {
-  return s.dtype == MOE_BF16 && !s.decode() && !s.generic() && s.f <= 4096;
-}
-
 hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const void* b_down,
                        const float* s_down, const int32_t* offsets, float* y_exp, float* y_part,
-                       bool complete, hipStream_t st, bool y16) {
+                       bool complete, hipStream_t st) {
   if (s.w_fp8() && !s.decode()) return hipErrorNotSupported;   // rejected by validation
-  // fp16 y_exp: the tiled path only, its K slices left to the combine
-  if (y16 && (!down_y16(s) || complete)) return hipErrorInvalidValue;
   const void* bias = s.expert_bias() ? b_down : nullptr;
   if (s.dtype == MOE_F32) {
     const long long n = s.max_rows() * s.d;
@@ -1181,9 +1165,8 @@ hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const 
              nullptr, s.T, s.tok_div(), s.E, s.S, s.f, s.d, s.d, s.f, ks, y_part, part_elems, 0,
              s.max_rows() * s.f * 2};
   const int NT = (s.d + DN_BN - 1) / DN_BN;
-  const dim3 grid(grid_blocks(s, DN_BM, NT, ks, DN_OCC));
-  if (y16) dn_gemm<MODE_DOWN16>(long_launch(s, s.f, s.d), s.f / ks, a, grid, st);
-  else dn_gemm<MODE_DOWN>(long_launch(s, s.f, s.d), s.f / ks, a, grid, st);
+  dn_gemm<MODE_DOWN>(long_launch(s, s.f, s.d), s.f / ks, a,
+                     dim3(grid_blocks(s, DN_BM, NT, ks, DN_OCC)), st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ks == 1 || !complete) return e;
   const long long n = s.max_rows() * (s.d / 4);

@@ -382,20 +382,14 @@ moe_status moe_ffn_forward(const moe_problem* p, const moe_weights* w, const voi
   }
   if (e == hipSuccess)
     e = launch_up(s, x, w->w_up, w->b_up, w->s_up, offsets, sorted_assign, h, stream);
-  // The down projection's K slices (if any) are summed by the combine.  On
-  // the tiled path y_exp and the slices pass to the combine in fp16 (scaled
-  // by 2^-8, like h): half the bytes of that round trip.
+  // The down projection's K slices (if any) are summed by the combine.
   float* y_part = at<float>(ws, L.y_part);
   const int nparts = down_parts(s);
-  const bool y16 = down_y16(s);
   if (e == hipSuccess)
-    e = launch_down(s, h, w->w_down, w->b_down, w->s_down, offsets, y_exp, y_part,
-                    !y16 && nparts == 0, stream, y16);
+    e = launch_down(s, h, w->w_down, w->b_down, w->s_down, offsets, y_exp, y_part, nparts == 0, stream);
   if (e == hipSuccess)
-    e = s.ec() ? launch_combine_ec(s, topk_w, assign_row, offsets, y_exp, y_part, nparts, y,
-                                   stream, y16)
-               : launch_combine(s, topk_w, assign_row, offsets, y_exp, y_part, nparts, y, stream,
-                                y16);
+    e = s.ec() ? launch_combine_ec(s, topk_w, assign_row, offsets, y_exp, y_part, nparts, y, stream)
+               : launch_combine(s, topk_w, assign_row, offsets, y_exp, y_part, nparts, y, stream);
   return fail_hip(e);
 }
 

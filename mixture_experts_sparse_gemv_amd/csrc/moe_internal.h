@@ -227,7 +227,7 @@ hipError_t launch_token_experts(const Shape& s, const int32_t* row_of, int32_t* 
 // y[t] = sum over experts e with row_of[t*E+e] >= 0 of probs[t*E+e] * y_exp row + shared rows.
 hipError_t launch_combine_ec(const Shape& s, const float* probs, const int32_t* row_of,
                              const int32_t* offsets, const float* y_exp, const float* y_part,
-                             int nparts, float* y, hipStream_t st, bool y16 = false);
+                             int nparts, float* y, hipStream_t st);
 // s_up / s_down: FP8 row scales (MOE_W_FP8), else ignored.
 hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void* b_up,
                      const float* s_up, const int32_t* offsets, const int32_t* sorted_assign,
@@ -235,13 +235,9 @@ hipError_t launch_up(const Shape& s, const void* x, const void* w_up, const void
 // complete = true: y_exp holds the whole result on return (K slices folded);
 // false: slices 1.. stay in y_part for the combine to add (down_parts(s) of
 // them).
-// y16 (tiled bf16 path, complete = false): y_exp and the K-slice partials are
-// stored in fp16 scaled by 2^-8 (saturating like h) for the combine to read;
-// down_y16(s): whether the fused forward takes it (tiled path, d_ff <= 4096).
-bool down_y16(const Shape& s);
 hipError_t launch_down(const Shape& s, const void* h, const void* w_down, const void* b_down,
                        const float* s_down, const int32_t* offsets, float* y_exp, float* y_part,
-                       bool complete, hipStream_t st, bool y16 = false);
+                       bool complete, hipStream_t st);
 hipError_t launch_up_generic(const Shape& s, const void* x, const void* w_up, const void* b_up,
                              const int32_t* offsets, const int32_t* sorted_assign, void* h,
                              hipStream_t st);
@@ -251,10 +247,9 @@ hipError_t launch_down_generic(const Shape& s, const void* h, const void* w_down
 // y_part/nparts: K-slice partials of y_exp still to be added (nparts = 0: none).
 hipError_t launch_quantize_fp8(const void* w, long long rows, int cols, uint8_t* q, float* scales,
                                hipStream_t st);
-// y16: y_exp and the partials are fp16 scaled by 2^-8 (launch_down's y16).
 hipError_t launch_combine(const Shape& s, const float* topk_w, const int32_t* assign_row,
                           const int32_t* offsets, const float* y_exp, const float* y_part,
-                          int nparts, float* y, hipStream_t st, bool y16 = false);
+                          int nparts, float* y, hipStream_t st);
 
 // ---------------------------------------------------------------- backward
 // K slices of the dX GEMM (reduction over F1, d outputs), as down_ksplit.

@@ -261,23 +261,12 @@ def test_deterministic_and_no_out_of_bounds_writes(name):
     assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32)), "not bit-identical"
 
 
-# (workload, whether its fused forward passes y_exp to the combine in fp16:
-# the tiled bf16 path does for d_ff <= 4096; the streaming decode, the untiled
-# path and longer reductions do not)
-@pytest.mark.parametrize("name,y16", [("gpt2_T700", True), ("swiglu_skew_T3000", True),
-                                      ("large_T300", False), ("large_decode", False),
-                                      ("gelu_bias_d776_f1416_T300", False)])
-def test_stage_entry_points_equal_fused_forward(name, y16):
+@pytest.mark.parametrize("name", ["gpt2_T700", "swiglu_skew_T3000", "large_T300", "large_decode",
+                                  "gelu_bias_d776_f1416_T300"])
+def test_stage_entry_points_equal_fused_forward(name):
     """The per-stage entry points (router, dispatch, up, down with its K slices
-    folded, combine; y_exp in fp32) against the fused forward, which adds the
-    down projection's K slices inside the combine.  Where the fused forward
-    keeps y_exp and the slices in fp32 the two are bit-identical.  On the
-    tiled path it stores each slice's partial sum in fp16 scaled by 2^-8:
-    within 2^-11 of its magnitude, or 2^-17 absolute below 2^-6 (round to
-    nearest).  A slice's partial is at most the sum of |h_j W2[n, j]| over
-    its columns (plus |b2| in slice 0), so y moves by at most 2^-11 of
-    w * (|h| |W2|^T + |b2|) summed over the token's rows, plus 2^-17 per
-    stored value (bound doubled for the fp32 sums)."""
+    folded, combine) give bit-identical y to the fused forward, which adds the
+    down projection's K slices inside the combine."""
     run, inp = _inputs(name)
     _say(f"[staged==forward] {name}")
     g = gpu_inputs(inp)
@@ -301,35 +290,7 @@ def test_stage_entry_points_equal_fused_forward(name, y16):
     M.moe_combine(p, tw, ar, off, y_exp, y)
     torch.cuda.synchronize()
     ys = y.view(T, d).cpu().numpy()
-    if not y16:
-        assert np.array_equal(ys.view(np.uint32), fwd["y"].view(np.uint32)), "staged != forward"
-        return
-    # |h| |W2|^T + |b2| per row of y_exp, segment by segment
-    f, S = run.d_ff, run.num_shared
-    hn = np.abs(h.view(-1, f).float().cpu().numpy().astype(np.float64)) * 256.0   # h is stored / 2^8
-    w2 = np.abs(g["w_down"].float().cpu().numpy().astype(np.float64)).reshape(E + S, d, f)
-    b2 = (np.abs(g["b_down"].float().cpu().numpy().astype(np.float64)).reshape(E + S, d)
-          if run.expert_bias and g["b_down"] is not None else np.zeros((E + S, d)))
-    offn = off.cpu().numpy()
-    starts = [int(offn[e]) for e in range(E)] + [int(offn[E]) + q * T for q in range(S)]
-    ends = [int(offn[e + 1]) for e in range(E)] + [int(offn[E]) + (q + 1) * T for q in range(S)]
-    absdot = np.zeros((ends[-1] if ends else 0, d))
-    for sg, (r0, r1) in enumerate(zip(starts, ends)):
-        if r1 > r0:
-            absdot[r0:r1] = hn[r0:r1] @ w2[sg].T + b2[sg]
-    nst = 4   # at most 4 stored values (K slices) per row
-    arn, twn = ar.cpu().numpy().reshape(T, k), tw.cpu().numpy().reshape(T, k)
-    bound = np.zeros((T, d))
-    for s in range(k):
-        sel = arn[:, s] >= 0
-        bound[sel] += np.abs(twn[sel, s, None]) * (2.0 ** -11 * absdot[arn[sel, s]] + nst * 2.0 ** -17)
-    for q in range(S):
-        bound += 2.0 ** -11 * absdot[starts[E + q]:ends[E + q]] + nst * 2.0 ** -17
-    bound *= 2.0
-    err = np.abs(ys.astype(np.float64) - fwd["y"].astype(np.float64))
-    _say(f"  fp16 y_exp: max |staged - forward| = {err.max():.3g}, "
-         f"max ratio to bound = {(err / bound).max():.3f}")
-    assert np.all(err <= bound), "staged and fused forward differ beyond the fp16 y_exp rounding"
+    assert np.array_equal(ys.view(np.uint32), fwd["y"].view(np.uint32)), "staged != forward"
 
 
 def test_routing_stats_entry_point_given_oracle_inputs():
