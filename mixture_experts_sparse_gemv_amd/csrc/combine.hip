@@ -69,7 +69,7 @@ hipError_t launch_combine(const Shape& s, const float* topk_w, const int32_t* as
                           const int32_t* offsets, const float* y_exp, const float* y_part,
                           int nparts, float* y, hipStream_t st) {
   const long long part_elems = s.max_rows() * s.d;
-  if (s.d % 16 == 0 && s.d >= 1024) {
+  if (s.d % 16 == 0 && s.d >= 256) {
     const long long n = (long long)s.T * (s.d / 16);
     combine_kernel<4, 4><<<(int)((n + 255) / 256), 256, 0, st>>>(
         topk_w, assign_row, offsets, y_exp, y_part, nparts, part_elems, y, s.T, s.d, s.k, s.E, s.S);
