@@ -160,6 +160,9 @@ __global__ __launch_bounds__(256) void token_experts_kernel(const int32_t* __res
   token_experts[t] = n;
 }
 
+// One thread per NV groups of 4 outputs of a token, group j at column
+// 4 (i + j d / (4 NV)) (as in the top-k combine).
+template <int NV>
 __global__ __launch_bounds__(256) void combine_ec_kernel(const float* __restrict__ probs,
                                                          const int32_t* __restrict__ row_of,
                                                          const int32_t* __restrict__ offsets,
@@ -168,26 +171,41 @@ __global__ __launch_bounds__(256) void combine_ec_kernel(const float* __restrict
                                                          int nparts, long long part_elems,
                                                          float* __restrict__ y, int T, int d, int E,
                                                          int S) {
-  const int dv = d / 4;
+  const int dv = d / (4 * NV);   // threads per token
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (long long)T * dv) return;
   const int t = (int)(gid / dv);
-  const int c = (int)(gid % dv) * 4;
-  auto row = [&](long long r) {
-    f32x4 v = *(const f32x4*)(y_exp + r * d + c);
-    for (int p = 0; p < nparts; ++p) v += *(const f32x4*)(y_part + p * part_elems + r * d + c);
-    return v;
+  const int c0 = (int)(gid % dv) * 4;
+  auto row = [&](long long r, f32x4 (&v)[NV]) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) v[j] = *(const f32x4*)(y_exp + r * d + c0 + j * dv * 4);
+    for (int p = 0; p < nparts; ++p) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j)
+        v[j] += *(const f32x4*)(y_part + p * part_elems + r * d + c0 + j * dv * 4);
+    }
   };
-  f32x4 acc = {};
+  f32x4 acc[NV] = {};
+  f32x4 v[NV];
   for (int e = 0; e < E; ++e) {
     const int r = row_of[(long long)t * E + e];
-    if (r >= 0) acc += probs[(long long)t * E + e] * row(r);
+    if (r >= 0) {
+      const float w = probs[(long long)t * E + e];
+      row(r, v);
+#pragma unroll
+      for (int j = 0; j < NV; ++j) acc[j] += w * v[j];
+    }
   }
   if (S > 0) {
     const long long base = offsets[E];
-    for (int q = 0; q < S; ++q) acc += row(base + (long long)q * T + t);
+    for (int q = 0; q < S; ++q) {
+      row(base + (long long)q * T + t, v);
+#pragma unroll
+      for (int j = 0; j < NV; ++j) acc[j] += v[j];
+    }
   }
-  *(f32x4*)(y + (long long)t * d + c) = acc;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) *(f32x4*)(y + (long long)t * d + c0 + j * dv * 4) = acc[j];
 }
 
 }  // namespace
@@ -209,9 +227,15 @@ hipError_t launch_token_experts(const Shape& s, const int32_t* row_of, int32_t* 
 hipError_t launch_combine_ec(const Shape& s, const float* probs, const int32_t* row_of,
                              const int32_t* offsets, const float* y_exp, const float* y_part,
                              int nparts, float* y, hipStream_t st) {
-  const long long n = (long long)s.T * (s.d / 4);
-  combine_ec_kernel<<<(int)((n + 255) / 256), 256, 0, st>>>(
-      probs, row_of, offsets, y_exp, y_part, nparts, s.max_rows() * s.d, y, s.T, s.d, s.E, s.S);
+  if (s.d % 16 == 0 && s.d >= 256) {
+    const long long n = (long long)s.T * (s.d / 16);
+    combine_ec_kernel<4><<<(int)((n + 255) / 256), 256, 0, st>>>(
+        probs, row_of, offsets, y_exp, y_part, nparts, s.max_rows() * s.d, y, s.T, s.d, s.E, s.S);
+  } else {
+    const long long n = (long long)s.T * (s.d / 4);
+    combine_ec_kernel<1><<<(int)((n + 255) / 256), 256, 0, st>>>(
+        probs, row_of, offsets, y_exp, y_part, nparts, s.max_rows() * s.d, y, s.T, s.d, s.E, s.S);
+  }
   return hipGetLastError();
 }
 
